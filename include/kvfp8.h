@@ -1,0 +1,215 @@
+/*
+ * kvfp8.h - C ABI of the MI355X (gfx950) FP8 e4m3 paged KV-cache library.
+ *
+ * Two operations make up one decode step of an attention layer:
+ *
+ *   kvq_kv_cache_write          quantise each new token's K and V into a paged
+ *                               cache (the role the vLLM FP8 KV-cache post
+ *                               gives to reshape_and_cache_flash, extended to
+ *                               one FP32 scale per KV head: "State of FP8 KV
+ *                               cache and attention quantization in vLLM",
+ *                               section "Kernel and vLLM improvements",
+ *                               paragraph "Per-head scales").
+ *   kvq_paged_decode_attention  GQA decode attention softmax(q k^T) v over that
+ *                               cache, with FP32 two-level accumulation (same
+ *                               post, same section, paragraph "Two-level
+ *                               accumulation") and split-context partitions
+ *                               merged by a separate FP32 reduce kernel.
+ *
+ * Each layer carries its own cache dtype, so sliding-window layers can stay in
+ * bf16 (same post, paragraph "Skip layers").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Every pointer argument named as device memory must point to memory on
+ *    the current HIP device, 16-byte aligned, contiguous in the layout stated.
+ *    The caller owns all memory. The library never allocates, frees or
+ *    synchronises on the calls listed as such, and keeps no per-call state:
+ *    it is safe to call from several host threads on different streams.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    All work is enqueued on that stream; the call returns before it runs.
+ *  - Return value: KVQ_OK (0) or a negative kvq_status. Every argument check
+ *    runs on the host before anything is launched, so a non-zero status means
+ *    no device memory was touched (KVQ_ERR_HIP aside: a launch failed).
+ *    Device-side faults surface on the caller's next synchronisation.
+ *
+ * E4M3 (OCP FP8): 1 sign, 4 exponent (bias 7), 3 mantissa bits; largest
+ * finite magnitude 448, smallest subnormal 2^-9, no infinities, NaN is
+ * S.1111.111 (0x7F / 0xFF). Quantisation of an input x with scale s is
+ *     code = E4M3_sat_RNE( fp32(x) / s )        (IEEE fp32 division)
+ * with round-to-nearest-even, saturation of finite and infinite overflow to
+ * +-448 (codes 0x7E / 0xFE), NaN to 0x7F|sign, and the sign of zero kept.
+ * The stored code c stands for decode(c) * s.
+ * (Format: "FP8量化与长上下文推理" section 1 table; max 448 and the saturating
+ * mode: "cooking-agi: FP8 and the KV cache", section "dynamic vs static scale";
+ * s = amax/448 and round(x/s): "FP8量化与长上下文推理" section 1.1.)
+ *
+ * Paged cache layout (the pages leave it open; this library fixes it)
+ * ------------------------------------------------------------------
+ * A cache is one byte array per layer and per K / V:
+ *     [num_pages][num_kv_heads][PB]   with PB = 16 * head_dim * e bytes,
+ * e = 1 for KVQ_FP8_E4M3 and 2 for KVQ_BF16 (little-endian bf16 bits).
+ * A page holds 16 consecutive positions of one sequence. Token position t of
+ * a sequence lives in page block_table[t / 16], row r = t % 16; a slot is
+ * page * 16 + r. Within the PB-byte block of (page, kv head) the element
+ * (row r, dim d) sits at byte
+ *   K:  ((d / CE) * 16 + r) * 16 + (d % CE) * e                 CE = 16 / e
+ *   V:  (d / DB) * 1024 + (r / 4) * 256 + (d % DB) * 4 * e + (r % 4) * e
+ *                                                                DB = 64 / e
+ * i.e. K is stored in 16-byte chunks of CE consecutive dims per row, chunk-
+ * major; V is stored in 1 KiB groups of DB dims, each holding 4 quads of rows
+ * with the 4 rows of a quad adjacent for every dim. Both make every 64-lane
+ * 16-byte load of the decode kernel one contiguous 1 KiB span.
+ * Example (fp8, head_dim 128): K (r=5, d=17) is at byte (1*16+5)*16+1 = 337;
+ * V (r=5, d=17) is at byte 0*1024 + 1*256 + 17*4 + 1 = 325.
+ */
+#ifndef KVFP8_H
+#define KVFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1,       /* null / misaligned pointer, negative size,
+                                     inconsistent shapes */
+  KVQ_ERR_UNSUPPORTED = -2,       /* head_dim not in {64,128,256}, page size
+                                     not 16, Hq % Hkv != 0, group > 16 */
+  KVQ_ERR_WORKSPACE_TOO_SMALL = -3,
+  KVQ_ERR_HIP = -4                /* a HIP runtime call or launch failed */
+};
+
+/* Cache element type of a layer. `auto` in the engine flags maps to bf16. */
+enum kvq_dtype { KVQ_BF16 = 0, KVQ_FP8_E4M3 = 1 };
+
+/* Scale granularity: one FP32 scale for the whole layer tensor, or one per KV
+ * head ("cooking-agi", section "how to enable it in the engine": per tensor
+ * or per attention head). K and V always have separate scale arrays. */
+enum kvq_scale_mode { KVQ_SCALE_PER_TENSOR = 0, KVQ_SCALE_PER_KV_HEAD = 1 };
+
+/* Output element type of the attention. */
+enum kvq_out_dtype { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 };
+
+/* Per-layer descriptor. */
+typedef struct kvq_layer_desc {
+  int32_t num_q_heads;     /* Hq */
+  int32_t num_kv_heads;    /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 16 */
+  int32_t head_dim;        /* D in {64, 128, 256} */
+  int32_t page_size;       /* must be 16 */
+  int32_t cache_dtype;     /* enum kvq_dtype */
+  int32_t scale_mode;      /* enum kvq_scale_mode; ignored for bf16 layers */
+  int32_t sliding_window;  /* W > 0: attend to the last W positions (the new
+                              token included); 0: full attention */
+  float sm_scale;          /* softmax scale; 0 means 1/sqrt(head_dim) */
+} kvq_layer_desc;
+
+/*
+ * kvq_kv_cache_write - store T new tokens' K and V into the paged caches.
+ *   k, v          device bf16 [T][Hkv][D]
+ *   slot_mapping  device int64 [T]; slot = page * 16 + row; slot < 0 skips the
+ *                 token; every slot must be < num_pages * 16 (not checked on
+ *                 the device: the host cannot read device memory without a
+ *                 sync). Two tokens with the same slot: which one wins is
+ *                 unspecified.
+ *   k_cache, v_cache  device byte arrays in the layout above, num_pages pages.
+ *   k_scale, v_scale  device fp32 [1] (per tensor) or [Hkv] (per KV head);
+ *                 ignored and may be NULL for bf16 layers, where the bf16 bits
+ *                 are copied unchanged.
+ * Only the bytes of the written (slot, head) rows change.
+ * For fp8 layers each element becomes E4M3_sat_RNE(fp32(x) / s_h) (above).
+ */
+int kvq_kv_cache_write(const kvq_layer_desc* desc, const void* k, const void* v,
+                       const int64_t* slot_mapping, int64_t num_tokens,
+                       void* k_cache, void* v_cache, int64_t num_pages,
+                       const float* k_scale, const float* v_scale, void* stream);
+
+/*
+ * kvq_decode_workspace_bytes - size of the FP32 split workspace that
+ * kvq_paged_decode_attention needs for this layer, batch size and longest
+ * context (host only, no device work). Writes the size to *bytes; it is 0
+ * when no split is needed. The partition plan depends only on these
+ * arguments and the current device's compute-unit count.
+ */
+int kvq_decode_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
+                               int32_t max_context_len, size_t* bytes);
+
+/*
+ * kvq_paged_decode_attention - one decode step of GQA attention over a paged
+ * cache. Query head i attends with KV head i / G (consecutive query heads
+ * share a KV head). For sequence b with L = context_lens[b] (the positions
+ * already written, the new token included) it attends to positions
+ * [lo, L), lo = max(0, L - W) when sliding_window W > 0, else 0:
+ *     z_t = sm_scale * sum_d q[d] * kh[t][d],  p = softmax(z),
+ *     out[d] = sum_t p_t * vh[t][d]
+ * where kh = decode(code) * k_scale[h] and vh = decode(code) * v_scale[h] for
+ * fp8 layers, and the bf16 values for bf16 layers. L == 0 gives zeros.
+ *   out           device [B][Hq][D], fp32 or bf16 per out_dtype
+ *   q             device bf16 [B][Hq][D]
+ *   k_cache, v_cache  as written by kvq_kv_cache_write; num_pages pages
+ *   block_tables  device int32 [B][max_pages_per_seq]; entries for the
+ *                 attended pages must be in [0, num_pages)
+ *   context_lens  device int32 [B]; each in [0, max_context_len] and
+ *                 ceil(L/16) <= max_pages_per_seq (not checked on the device)
+ *   max_context_len  host int, an upper bound of every context_lens[b]; it
+ *                 sizes the partition plan and must match the value given to
+ *                 kvq_decode_workspace_bytes
+ *   k_scale, v_scale  as for kvq_kv_cache_write
+ *   workspace     device scratch of at least the bytes reported by
+ *                 kvq_decode_workspace_bytes (may be NULL when that is 0);
+ *                 clobbered. Calls that share a workspace must be ordered on
+ *                 one stream.
+ */
+int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out,
+                               int32_t out_dtype, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               int64_t num_pages, const int32_t* block_tables,
+                               int32_t max_pages_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_context_len, const float* k_scale,
+                               const float* v_scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_kv_scale_from_amax - static scale calibration of one layer tensor:
+ * s = fp32(amax) / 448 over x, per KV head or over the whole tensor per
+ * desc->scale_mode ("FP8量化与长上下文推理" section 1.1: scale = max_abs/448;
+ * "cooking-agi", section "dynamic vs static scale": the largest value lands
+ * on 448). amax == 0 gives s = 1 (a zero scale cannot quantise anything);
+ * a NaN anywhere in the reduced values gives NaN.
+ *   x          device bf16 [T][Hkv][D]
+ *   scale_out  device fp32 [1] or [Hkv]
+ */
+int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x,
+                           int64_t num_tokens, float* scale_out, void* stream);
+
+/*
+ * kvq_e4m3_quantize - the cache write's conversion on a flat array:
+ * out[i] = E4M3_sat_RNE(x[i] / *scale). x device fp32 [n], scale device fp32
+ * [1], out device uint8 [n]. For quantising data outside the cache layout
+ * with exactly the cache's codec.
+ */
+int kvq_e4m3_quantize(const float* x, int64_t n, const float* scale,
+                      uint8_t* out, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* kvq_status_string(int32_t status);
+
+/*
+ * Profiling aid (not thread-safe): between kvq_profile_begin and
+ * kvq_profile_end the library records a HIP event pair around every launch of
+ * the split-decode kernel (up to max_launches of them) on the stream of that
+ * launch. kvq_profile_end synchronises those events and returns the summed
+ * kernel time in milliseconds and the number of launches recorded.
+ */
+int kvq_profile_begin(int32_t max_launches);
+int kvq_profile_end(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVFP8_H */
