@@ -1,0 +1,391 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the FP8 e4m3 paged KV cache on one MI355X.
+
+A step is one decode step of a layer stack: for every layer, write the new
+token's K/V into the paged cache (kv_cache_write) and run GQA decode attention
+over the cache (split + reduce kernels). Inputs are synthetic, seeded and
+resident in HBM before timing; the layer stack is large enough (>= 1 GiB of
+cache) that the 256 MB Infinity Cache cannot serve it.
+
+Default run (about a minute of GPU time):
+  * headline: Llama-3.1-8B-shaped layer (32 q / 8 KV heads, head_dim 128),
+    batch 1, context 131072, fp8 e4m3 cache with per-KV-head scales, 32
+    layers per step -> value = KV GB/s of the whole step;
+  * sweep over contexts 1k..128k for the fp8 and the bf16 cache with a linear
+    fit us/layer = slope * context + intercept (the ITL fit of "State of FP8
+    KV cache and attention quantization in vLLM", section "Single-request
+    benchmark"), the fp8/bf16 slope ratio and the break-even context;
+  * roofline of the split kernel from HIP events around its launches;
+  * the float64 CPU oracle timed on the host as a reported baseline.
+
+Prints one JSON line (rank 0, N = 1).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+GIB = 1 << 30
+
+WORKLOADS = {
+    # name: (B, Hq, Hkv, D, default context, layers of the model)
+    "llama8b": dict(B=1, Hq=32, Hkv=8, D=128, ctx=131072, layers=32,
+                    desc="Llama-3.1-8B-shaped decode layer (32 q / 8 KV heads, head_dim 128), batch 1"),
+    "batched": dict(B=8, Hq=32, Hkv=8, D=128, ctx=None, layers=32,
+                    desc="8 sequences of 18k-22k positions, 8B layer shape, shuffled page pool"),
+    "llama70b": dict(B=1, Hq=64, Hkv=8, D=128, ctx=131072, layers=80,
+                     desc="Llama-3.1-70B-shaped decode layer (64 q / 8 KV heads, head_dim 128), batch 1"),
+    "hd256": dict(B=1, Hq=8, Hkv=2, D=256, ctx=65536, layers=32,
+                  desc="head_dim 256 layer (8 q / 2 KV heads), batch 1"),
+    "gptoss": dict(B=1, Hq=64, Hkv=8, D=64, ctx=32768, layers=24,
+                   desc="gpt-oss-20b-like hybrid: full fp8 layers and sliding-window-128 bf16 layers"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class LayerStack:
+    """NL layers of one shape, each with its own caches, filled with seeded
+    synthetic K/V up to position L-1; a step writes position L-1 and attends
+    over L positions."""
+
+    def __init__(self, kv, torch, B, Hq, Hkv, D, lens, NL, cache_dtype="fp8_e4m3",
+                 window=0, shuffle=False, spare_frac=0.0, seed=0, dtypes=None):
+        self.kv, self.torch = kv, torch
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
+        self.lens = [int(x) for x in lens]
+        self.NL = NL
+        self.max_len = max(self.lens)
+        dtypes = dtypes or [cache_dtype] * NL
+        windows = window if isinstance(window, list) else [window] * NL
+        self.descs = [kv.layer_desc(Hq, Hkv, D, dtypes[i], "per_kv_head", windows[i])
+                      for i in range(NL)]
+        import numpy as np
+        need = [(L + 15) // 16 for L in self.lens]
+        total = sum(need)
+        num_pages = total + int(math.ceil(total * spare_frac))
+        ids = np.arange(num_pages, dtype=np.int32)
+        if shuffle:
+            ids = np.random.default_rng(seed + 99).permutation(ids).astype(np.int32)
+        mp = max(need)
+        bt = np.zeros((B, mp), dtype=np.int32)
+        at = 0
+        for b, n in enumerate(need):
+            bt[b, :n] = ids[at:at + n]
+            at += n
+        self.num_pages = num_pages
+        self.block_tables = torch.from_numpy(bt).to(dev)
+        self.context_lens = torch.tensor(self.lens, dtype=torch.int32, device=dev)
+        # slots of every position (all sequences), and of the newest ones
+        slots, newest = [], []
+        for b, L in enumerate(self.lens):
+            pos = np.arange(L, dtype=np.int64)
+            s = bt[b, pos // 16].astype(np.int64) * 16 + pos % 16
+            slots.append(s[:-1])
+            newest.append(s[-1])
+        self.fill_slots = torch.from_numpy(np.concatenate(slots)).to(dev)
+        self.new_slots = torch.tensor(newest, dtype=torch.int64, device=dev)
+        gen = torch.Generator(device=dev)
+        self.layers = []
+        T = int(self.fill_slots.numel())
+        for li in range(NL):
+            d = self.descs[li]
+            gen.manual_seed(seed * 1000 + li)
+            kc = torch.empty(kv.cache_shape(d, num_pages), dtype=torch.uint8, device=dev)
+            vc = torch.empty_like(kc)
+            k_all = torch.randn((T + B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+            v_all = torch.randn((T + B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+            if d.fp8:
+                ks = torch.empty(Hkv, dtype=torch.float32, device=dev)
+                vs = torch.empty(Hkv, dtype=torch.float32, device=dev)
+                kv.kv_scale_from_amax(d, k_all, ks)
+                kv.kv_scale_from_amax(d, v_all, vs)
+            else:
+                ks = vs = None
+            kv.kv_cache_write(d, k_all[:T], v_all[:T], self.fill_slots, kc, vc, ks, vs)
+            k_new = k_all[T:].contiguous()
+            v_new = v_all[T:].contiguous()
+            q = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+            ws = kv.alloc_workspace(d, B, self.max_len)
+            self.layers.append(dict(desc=d, kc=kc, vc=vc, ks=ks, vs=vs, k_new=k_new,
+                                    v_new=v_new, q=q, out=out, ws=ws))
+            del k_all, v_all
+        torch.cuda.synchronize()
+
+    def step(self):
+        kv = self.kv
+        for ly in self.layers:
+            d = ly["desc"]
+            kv.kv_cache_write(d, ly["k_new"], ly["v_new"], self.new_slots, ly["kc"], ly["vc"],
+                              ly["ks"], ly["vs"])
+            kv.paged_decode_attention(d, ly["out"], ly["q"], ly["kc"], ly["vc"],
+                                      self.block_tables, self.context_lens, self.max_len,
+                                      ly["ks"], ly["vs"], ly["ws"])
+
+    # ---- algorithmic byte model (per layer) -------------------------------
+    def attended(self, desc):
+        W = desc.sliding_window
+        return [min(L, W) if W > 0 else L for L in self.lens]
+
+    def kv_bytes(self, desc):
+        return sum(self.attended(desc)) * self.Hkv * self.D * 2 * desc.elem_bytes
+
+    def split_bytes(self, desc):
+        """Bytes the split kernel must read: K/V rows, q, block-table
+        entries, scales."""
+        n = self.attended(desc)
+        bt = sum((x + 15) // 16 + 1 for x in n) * 4
+        sc = 2 * self.Hkv * 4 if desc.fp8 else 0
+        return self.kv_bytes(desc) + self.B * self.Hq * self.D * 2 + bt + sc
+
+    def step_bytes(self, desc):
+        """Whole layer step: attention (K/V, q, out, block table, scales) plus
+        the cache write of the new tokens (bf16 in, cache rows out)."""
+        write = self.B * self.Hkv * self.D * 2 * (2 + desc.elem_bytes)
+        return self.split_bytes(desc) + self.B * self.Hq * self.D * 4 + write
+
+    def total_step_bytes(self):
+        return sum(self.step_bytes(ly["desc"]) for ly in self.layers)
+
+    def total_kv_bytes(self):
+        return sum(self.kv_bytes(ly["desc"]) for ly in self.layers)
+
+
+def time_steps(torch, kv, stack, steps, warmup, profile=True):
+    for _ in range(warmup):
+        stack.step()
+    torch.cuda.synchronize()
+    if profile:
+        kv.profile_begin(steps * stack.NL)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        stack.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    split_ms, n = kv.profile_end() if profile else (0.0, 0)
+    return ms, (split_ms / n if n else None), n
+
+
+def layers_for(bytes_per_layer, lo=8, hi=512, target=2 * GIB):
+    return int(min(hi, max(lo, math.ceil(target / max(bytes_per_layer, 1)))))
+
+
+def fit(xs, ys):
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    sxy = sum((x - mx) * (y - my) for x, y in zip(xs, ys))
+    slope = sxy / sxx
+    return slope, my - slope * mx
+
+
+def sweep(torch, kv, w, contexts, steps, warmup):
+    rows = []
+    for dt in ("fp8_e4m3", "bf16"):
+        e = 1 if dt.startswith("fp8") else 2
+        for ctx in contexts:
+            per_layer = ctx * w["Hkv"] * w["D"] * 2 * e
+            NL = layers_for(per_layer)
+            st = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, dt, seed=ctx)
+            ms, split_ms, _ = time_steps(torch, kv, st, steps, warmup)
+            us_layer = ms * 1e3 / NL
+            gbs = st.total_kv_bytes() / (ms * 1e-3) / 1e9
+            rows.append(dict(cache=dt, context=ctx, layers=NL, us_per_layer=round(us_layer, 3),
+                             kv_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+                             split_us=round(split_ms * 1e3, 3) if split_ms else None))
+            log(f"sweep {dt:8s} ctx={ctx:6d} layers={NL:3d} {us_layer:8.2f} us/layer "
+                f"{gbs:7.1f} GB/s split={rows[-1]['split_us']} us")
+            del st
+            torch.cuda.empty_cache()
+    fits = {}
+    for dt in ("fp8_e4m3", "bf16"):
+        pts = [(r["context"], r["us_per_layer"]) for r in rows
+               if r["cache"] == dt and r["context"] >= 8192]
+        if len(pts) >= 2:
+            s, b = fit([p[0] for p in pts], [p[1] for p in pts])
+            fits[dt] = dict(slope_us_per_token=s, intercept_us=b)
+    out = dict(points=rows, fit_range="8192..%d" % max(contexts))
+    if "fp8_e4m3" in fits and "bf16" in fits:
+        f, bb = fits["fp8_e4m3"], fits["bf16"]
+        out["fits"] = fits
+        out["slope_ratio_fp8_over_bf16"] = f["slope_us_per_token"] / bb["slope_us_per_token"]
+        ds = bb["slope_us_per_token"] - f["slope_us_per_token"]
+        out["break_even_context"] = ((f["intercept_us"] - bb["intercept_us"]) / ds
+                                     if ds > 0 else None)
+    return out
+
+
+def cpu_baseline(w, ctx, min_seconds=10.0):
+    """The float64 oracle on the headline layer (all heads, full context),
+    repeated until at least min_seconds of wall time."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = min(16, os.cpu_count() or 1)
+    os.environ["ORACLE_THREADS"] = str(threads)
+    case = synth.decode_case(synth.LLAMA8B, w["Hq"], w["Hkv"], w["D"], [ctx])
+    kc = synth.poisoned_cache(case.num_pages, w["Hkv"], w["D"], True)
+    vc = kc.copy()
+    ks = oracle.scale_from_amax(case.k_new, True)
+    vs = oracle.scale_from_amax(case.v_new, True)
+    oracle.kv_cache_write(kc, vc, case.k_new, case.v_new, case.slots, oracle.FP8, True, ks, vs)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(case.q, kc, vc, case.block_tables, case.lens, w["Hkv"], oracle.FP8,
+                         True, 0, 0.0, ks, vs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 50:
+            break
+    kv_bytes = ctx * w["Hkv"] * w["D"] * 2
+    gbs = kv_bytes * reps / el / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{w['desc']}, context {ctx}, fp8 per-KV-head, all {w['Hq']} query "
+                       f"heads, attention only, {reps} repetitions in {el:.1f} s "
+                       f"({el / reps * 1e3:.0f} ms per layer step)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--context", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--cache", default="fp8_e4m3", choices=["fp8_e4m3", "bf16"])
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=10)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_kv_cache_write_amd as kv
+    if not os.path.exists(kv.LIB_PATH):
+        from fp8_kv_cache_write_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_calibration:
+        src = torch.empty(GIB, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes=GIB, launches=3)))
+        return
+
+    w = WORKLOADS[args.workload]
+    ctx = args.context or w["ctx"]
+    NL = args.layers or w["layers"]
+    torch.manual_seed(0)
+
+    # ---- headline --------------------------------------------------------
+    if args.workload == "batched":
+        import synth
+        lens = [int(x) for x in synth.batched_lens()]
+        stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], lens, NL, args.cache,
+                           shuffle=True, spare_frac=0.1, seed=3)
+        ctx_desc = f"lengths {min(lens)}..{max(lens)} (sum {sum(lens)})"
+    elif args.workload == "gptoss":
+        dts = ["fp8_e4m3" if i % 2 == 0 else "bf16" for i in range(NL)]
+        wins = [0 if i % 2 == 0 else 128 for i in range(NL)]
+        stack = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, seed=5,
+                           dtypes=dts, window=wins)
+        ctx_desc = f"context {ctx}; {NL // 2} full fp8 layers + {NL - NL // 2} SW-128 bf16 layers"
+    else:
+        stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], [ctx], NL, args.cache,
+                           seed=1)
+        ctx_desc = f"context {ctx}"
+    log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}")
+    ms, split_ms, nsplit = time_steps(torch, kv, stack, args.steps, args.warmup)
+    step_bytes = stack.total_step_bytes()
+    value = step_bytes / (ms * 1e-3) / 1e9
+    kv_gbs = stack.total_kv_bytes() / (ms * 1e-3) / 1e9
+    d0 = stack.layers[0]["desc"]
+    split_bytes = stack.split_bytes(d0)
+    achieved = split_bytes / (split_ms * 1e-3) / 1e9 if split_ms else None
+    log(f"headline: {ms:.3f} ms/step, {ms * 1e3 / NL:.2f} us/layer, {value:.1f} GB/s "
+        f"(KV {kv_gbs:.1f} GB/s), split kernel {split_ms * 1e3 if split_ms else 0:.2f} us "
+        f"-> {achieved or 0:.1f} GB/s")
+
+    result = {
+        "metric": "decode-attn µs/step & KV GB/s (% HBM peak) vs context; fp8/bf16 slope",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 cache, bf16 MFMA on exact e4m3 values, fp32 accumulation"
+                 if args.cache.startswith("fp8") else "bf16 cache, fp32 accumulation",
+        "data": "synthetic (seeded normal K/V/q)",
+        "config": {
+            "workload": f"{w['desc']}, {ctx_desc}, {args.cache} cache with per-KV-head scales, "
+                        f"{NL} layers per step (kv_cache_write of the new token + paged decode "
+                        f"attention per layer)",
+            "batch": w["B"], "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": w["D"],
+            "page_size": 16, "layers_per_step": NL, "parallelism": "single GPU",
+        },
+        "us_per_layer_step": round(ms * 1e3 / NL, 3),
+        "kv_gbs": round(kv_gbs, 2),
+        "kv_frac_of_hbm_peak": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_split_kernel",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+            "traffic": None,
+            "launch_us": round(split_ms * 1e3, 3) if split_ms else None,
+            "launches_timed": nsplit,
+            "algorithmic_bytes_per_launch": split_bytes,
+        },
+    }
+    del stack
+    torch.cuda.empty_cache()
+
+    if not args.no_sweep and args.workload == "llama8b":
+        contexts = [1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
+        result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)...")
+        result["cpu_baseline"] = cpu_baseline(WORKLOADS["llama8b"], 131072)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

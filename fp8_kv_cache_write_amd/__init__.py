@@ -1,0 +1,246 @@
+"""Python binding of libkvfp8 (include/kvfp8.h): FP8 e4m3 paged KV-cache write
+and GQA paged decode attention on MI355X (gfx950).
+
+Argument marshalling only: every function checks that the tensors are what
+the C ABI expects (device, dtype, contiguity, shape), passes their device
+pointers and the current HIP stream, and raises Kvfp8Error on a non-zero
+status. All computation runs in the library's HIP kernels; there is no
+fallback. The library must have been built (``python -m
+fp8_kv_cache_write_amd.build`` or ``__graft_entry__.build()``).
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvfp8.so")
+
+# enums of kvfp8.h
+BF16, FP8_E4M3 = 0, 1
+PER_TENSOR, PER_KV_HEAD = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+PAGE_SIZE = 16
+
+_DTYPES = {"bf16": BF16, "auto": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
+_SCALES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD}
+
+
+class Kvfp8Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("cache_dtype", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("sliding_window", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+    @property
+    def fp8(self):
+        return self.cache_dtype == FP8_E4M3
+
+    @property
+    def elem_bytes(self):
+        return 1 if self.fp8 else 2
+
+    @property
+    def page_bytes(self):
+        """Bytes of one (page, kv head) block."""
+        return PAGE_SIZE * self.head_dim * self.elem_bytes
+
+
+def layer_desc(num_q_heads, num_kv_heads, head_dim, cache_dtype="fp8_e4m3",
+               scale_mode="per_kv_head", sliding_window=0, sm_scale=0.0):
+    """Descriptor of one attention layer. cache_dtype: "fp8_e4m3"/"fp8" or
+    "bf16"/"auto"; scale_mode: "per_tensor" or "per_kv_head"."""
+    return LayerDesc(int(num_q_heads), int(num_kv_heads), int(head_dim), PAGE_SIZE,
+                     _DTYPES[cache_dtype] if isinstance(cache_dtype, str) else int(cache_dtype),
+                     _SCALES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode),
+                     int(sliding_window), float(sm_scale))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkvfp8.so. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m "
+                "fp8_kv_cache_write_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        dp = ctypes.POINTER(LayerDesc)
+        L.kvq_kv_cache_write.argtypes = [dp, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp]
+        L.kvq_decode_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
+        L.kvq_paged_decode_attention.argtypes = [dp, vp, i32, vp, vp, vp, i64, vp, i32, vp,
+                                                 i32, i32, vp, vp, vp, sz, vp]
+        L.kvq_kv_scale_from_amax.argtypes = [dp, vp, i64, vp, vp]
+        L.kvq_e4m3_quantize.argtypes = [vp, i64, vp, vp, vp]
+        L.kvq_status_string.argtypes = [i32]
+        L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_profile_begin.argtypes = [i32]
+        L.kvq_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+        for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes",
+                  "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
+                  "kvq_e4m3_quantize", "kvq_profile_begin", "kvq_profile_end"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().kvq_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Kvfp8Error(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, device=True):
+    import torch
+    if t is None:
+        return
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def cache_shape(desc, num_pages):
+    """Shape of one K or V cache tensor (uint8): [num_pages, Hkv, page_bytes]."""
+    return (int(num_pages), desc.num_kv_heads, desc.page_bytes)
+
+
+def kv_cache_write(desc, k, v, slot_mapping, k_cache, v_cache, k_scale=None,
+                   v_scale=None, stream=None):
+    """Quantise (fp8) or copy (bf16) T new tokens into the paged caches.
+    k, v: bf16 [T, Hkv, D]; slot_mapping: int64 [T]; caches: uint8
+    [P, Hkv, page_bytes]; scales: float32 [1] or [Hkv] (fp8 layers)."""
+    import torch
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    _need(slot_mapping, "slot_mapping", torch.int64)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache")
+    _need(k_scale, "k_scale", torch.float32)
+    _need(v_scale, "v_scale", torch.float32)
+    T = k.shape[0]
+    if tuple(k.shape) != (T, desc.num_kv_heads, desc.head_dim) or v.shape != k.shape:
+        raise ValueError("k, v must be [T, Hkv, D]")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have T entries")
+    num_pages = k_cache.numel() // (desc.num_kv_heads * desc.page_bytes) if k_cache.numel() else 0
+    if k_cache.numel() * k_cache.element_size() != num_pages * desc.num_kv_heads * desc.page_bytes \
+            or v_cache.numel() * v_cache.element_size() != k_cache.numel() * k_cache.element_size():
+        raise ValueError("caches must be [P, Hkv, page_bytes] bytes")
+    _check("kvq_kv_cache_write", lib().kvq_kv_cache_write(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
+        _ptr(v_cache), num_pages, _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def decode_workspace_bytes(desc, num_seqs, max_context_len):
+    n = ctypes.c_size_t(0)
+    _check("kvq_decode_workspace_bytes", lib().kvq_decode_workspace_bytes(
+        ctypes.byref(desc), int(num_seqs), int(max_context_len), ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_workspace(desc, num_seqs, max_context_len, device="cuda"):
+    """A uint8 device tensor big enough for one decode call (None if 0)."""
+    import torch
+    n = decode_workspace_bytes(desc, num_seqs, max_context_len)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def paged_decode_attention(desc, out, q, k_cache, v_cache, block_tables,
+                           context_lens, max_context_len, k_scale=None,
+                           v_scale=None, workspace=None, stream=None):
+    """out: float32 or bf16 [B, Hq, D]; q: bf16 [B, Hq, D]; block_tables:
+    int32 [B, max_pages]; context_lens: int32 [B]; max_context_len: host int
+    bound of context_lens (sizes the split plan)."""
+    import torch
+    _need(out, "out")
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache")
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32)
+    _need(k_scale, "k_scale", torch.float32)
+    _need(v_scale, "v_scale", torch.float32)
+    _need(workspace, "workspace")
+    if out.dtype == torch.float32:
+        out_dtype = OUT_F32
+    elif out.dtype == torch.bfloat16:
+        out_dtype = OUT_BF16
+    else:
+        raise ValueError("out must be float32 or bfloat16")
+    B = q.shape[0]
+    if tuple(q.shape) != (B, desc.num_q_heads, desc.head_dim) or out.shape != q.shape:
+        raise ValueError("q, out must be [B, Hq, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_pages], context_lens [B]")
+    num_pages = k_cache.numel() * k_cache.element_size() // (desc.num_kv_heads * desc.page_bytes)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("kvq_paged_decode_attention", lib().kvq_paged_decode_attention(
+        ctypes.byref(desc), _ptr(out), out_dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        num_pages, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
+        int(max_context_len), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def kv_scale_from_amax(desc, x, scale_out, stream=None):
+    """scale_out[h] = amax(|x[:, h, :]|) / 448 (or one scale over all heads
+    for per-tensor layers). x: bf16 [T, Hkv, D]; scale_out: float32."""
+    import torch
+    _need(x, "x", torch.bfloat16)
+    _need(scale_out, "scale_out", torch.float32)
+    if x.dim() != 3 or x.shape[1] != desc.num_kv_heads or x.shape[2] != desc.head_dim:
+        raise ValueError("x must be [T, Hkv, D]")
+    want = desc.num_kv_heads if desc.scale_mode == PER_KV_HEAD else 1
+    if scale_out.numel() != want:
+        raise ValueError(f"scale_out must have {want} entries")
+    _check("kvq_kv_scale_from_amax", lib().kvq_kv_scale_from_amax(
+        ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(scale_out), _stream(stream)))
+
+
+def e4m3_quantize(x, scale, out, stream=None):
+    """out[i] = e4m3_sat_rne(x[i] / scale[0]); x float32, out uint8."""
+    import torch
+    _need(x, "x", torch.float32)
+    _need(scale, "scale", torch.float32)
+    _need(out, "out", torch.uint8)
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
+    _check("kvq_e4m3_quantize", lib().kvq_e4m3_quantize(
+        _ptr(x), x.numel(), _ptr(scale), _ptr(out), _stream(stream)))
+
+
+def profile_begin(max_launches):
+    _check("kvq_profile_begin", lib().kvq_profile_begin(int(max_launches)))
+
+
+def profile_end():
+    """(summed split-kernel milliseconds, launches recorded)."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    _check("kvq_profile_end", lib().kvq_profile_end(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, int(n.value)

@@ -1,0 +1,289 @@
+// api.cpp - the C ABI of include/kvfp8.h: argument checks (host only, before
+// any launch), the split-context partition plan, and the launches.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "../../include/kvfp8.h"
+#include "launch.hpp"
+
+using namespace kvfp8;
+
+namespace {
+
+constexpr int kMaxGroup = 8;
+constexpr int kMaxPagesPerWave = 64;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_desc(const kvq_layer_desc* d) {
+  if (!d) return KVQ_ERR_INVALID_ARG;
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
+  if (d->cache_dtype != KVQ_BF16 && d->cache_dtype != KVQ_FP8_E4M3) return KVQ_ERR_INVALID_ARG;
+  if (d->scale_mode != KVQ_SCALE_PER_TENSOR && d->scale_mode != KVQ_SCALE_PER_KV_HEAD)
+    return KVQ_ERR_INVALID_ARG;
+  if (d->sliding_window < 0) return KVQ_ERR_INVALID_ARG;
+  if (!(d->sm_scale >= 0.0f) || !isfinite(d->sm_scale)) return KVQ_ERR_INVALID_ARG;
+  if (d->page_size != 16) return KVQ_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (d->num_q_heads % d->num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads > kMaxGroup) return KVQ_ERR_UNSUPPORTED;
+  if (d->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+// Compute units of the current device, queried once per device.
+int cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+struct Plan {
+  int pages_per_wave;
+  int num_parts;
+  size_t off_l, off_o, bytes;  // workspace layout (bytes)
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Split-context plan. Pages of one (sequence, KV head) are cut into
+// partitions of kSplitWaves * pages_per_wave pages; each partition is one
+// work-group, each wave streams pages_per_wave pages. pages_per_wave aims at
+// about 16 waves per compute unit over the whole grid; when one partition per
+// sequence is cheap enough (short contexts, sliding windows) the split kernel
+// writes the output itself and the reduce kernel is skipped.
+Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
+  const int W = d->sliding_window;
+  int64_t pages_max = ((int64_t)max_context_len + 15) / 16;
+  if (W > 0) pages_max = std::min<int64_t>(pages_max, ((int64_t)W + 15) / 16 + 1);
+  if (pages_max < 1) pages_max = 1;
+  const int64_t total = (int64_t)std::max(num_seqs, 1) * d->num_kv_heads * pages_max;
+  const int64_t target_waves = (int64_t)cu_count() * 16;
+  int64_t ppw = (total + target_waves - 1) / target_waves;
+  ppw = std::max<int64_t>(ppw, 2);
+  ppw = (ppw + 1) / 2 * 2;
+  ppw = std::min<int64_t>(ppw, kMaxPagesPerWave);
+  int64_t direct_ppw = (pages_max + kSplitWaves - 1) / kSplitWaves;
+  direct_ppw = (direct_ppw + 1) / 2 * 2;
+  if (direct_ppw <= std::max<int64_t>(ppw, 8)) ppw = direct_ppw;
+  // KVFP8_PAGES_PER_WAVE=n (2..64) overrides the choice (tuning sweeps).
+  if (const char* env = getenv("KVFP8_PAGES_PER_WAVE")) {
+    const long n = strtol(env, nullptr, 10);
+    if (n >= 1 && n <= kMaxPagesPerWave) ppw = n;
+  }
+  Plan p;
+  p.pages_per_wave = (int)ppw;
+  p.num_parts = (int)((pages_max + kSplitWaves * ppw - 1) / (kSplitWaves * ppw));
+  if (p.num_parts <= 1) {
+    p.num_parts = 1;
+    p.off_l = p.off_o = p.bytes = 0;
+    return p;
+  }
+  const size_t rows = (size_t)num_seqs * d->num_q_heads * p.num_parts;
+  p.off_l = round_up(rows * sizeof(float), 256);
+  p.off_o = p.off_l + round_up(rows * sizeof(float), 256);
+  p.bytes = p.off_o + round_up(rows * d->head_dim * sizeof(float), 256);
+  return p;
+}
+
+// Profiling hook (see kvq_profile_begin).
+struct Profiler {
+  bool on = false;
+  int max = 0;
+  std::vector<hipEvent_t> ev;
+  int used = 0;
+} g_prof;
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(int32_t status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int kvq_kv_cache_write(const kvq_layer_desc* desc, const void* k, const void* v,
+                       const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                       void* v_cache, int64_t num_pages, const float* k_scale,
+                       const float* v_scale, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (num_tokens < 0 || num_pages < 0) return KVQ_ERR_INVALID_ARG;
+  if (num_tokens == 0) return KVQ_OK;
+  if (num_pages == 0) return KVQ_ERR_INVALID_ARG;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return KVQ_ERR_INVALID_ARG;
+  const bool fp8 = desc->cache_dtype == KVQ_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return KVQ_ERR_INVALID_ARG;
+  const int64_t threads = num_tokens * desc->num_kv_heads * (desc->head_dim / 16);
+  if ((threads + 255) / 256 > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
+  hipError_t e = launch_kv_cache_write(
+      fp8, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slot_mapping,
+      num_tokens, desc->num_kv_heads, desc->head_dim, static_cast<uint8_t*>(k_cache),
+      static_cast<uint8_t*>(v_cache), num_pages, k_scale, v_scale,
+      desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_decode_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
+                               int32_t max_context_len, size_t* bytes) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!bytes || num_seqs < 0 || max_context_len < 0) return KVQ_ERR_INVALID_ARG;
+  *bytes = make_plan(desc, num_seqs, max_context_len).bytes;
+  return KVQ_OK;
+}
+
+int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out, int32_t out_dtype,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               int64_t num_pages, const int32_t* block_tables,
+                               int32_t max_pages_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t max_context_len,
+                               const float* k_scale, const float* v_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16) return KVQ_ERR_INVALID_ARG;
+  if (num_seqs < 0 || max_context_len < 0 || num_pages < 0 || max_pages_per_seq < 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (num_seqs == 0) return KVQ_OK;
+  if (num_seqs > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (((int64_t)max_context_len + 15) / 16 > max_pages_per_seq) return KVQ_ERR_INVALID_ARG;
+  if (max_context_len > 0 && num_pages == 0) return KVQ_ERR_INVALID_ARG;
+  if (!out || !q || !context_lens || !aligned(out, 16) || !aligned(q, 16) ||
+      !aligned(context_lens, 4))
+    return KVQ_ERR_INVALID_ARG;
+  if (max_pages_per_seq > 0 && (!block_tables || !aligned(block_tables, 4)))
+    return KVQ_ERR_INVALID_ARG;
+  if (max_context_len > 0 && (!k_cache || !v_cache || !aligned(k_cache, 16) || !aligned(v_cache, 16)))
+    return KVQ_ERR_INVALID_ARG;
+  const bool fp8 = desc->cache_dtype == KVQ_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return KVQ_ERR_INVALID_ARG;
+  const Plan plan = make_plan(desc, num_seqs, max_context_len);
+  if (plan.bytes > 0) {
+    if (workspace_bytes < plan.bytes) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned(workspace, 256)) return KVQ_ERR_INVALID_ARG;
+  }
+  DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint8_t*>(k_cache);
+  p.v_cache = static_cast<const uint8_t*>(v_cache);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_pages = num_pages;
+  p.k_scale = fp8 ? k_scale : nullptr;
+  p.v_scale = fp8 ? v_scale : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_m = plan.bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_l = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  p.ws_o = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_o) : nullptr;
+  p.out = out;
+  p.num_q_heads = desc->num_q_heads;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.group = desc->num_q_heads / desc->num_kv_heads;
+  p.max_pages_per_seq = max_pages_per_seq;
+  p.window = desc->sliding_window;
+  p.pages_per_wave = plan.pages_per_wave;
+  p.num_parts = plan.num_parts;
+  p.scale_per_head = desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0;
+  p.out_bf16 = out_dtype == KVQ_OUT_BF16 ? 1 : 0;
+  p.direct = plan.num_parts == 1 ? 1 : 0;
+  const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
+                                         : 1.0f / sqrtf((float)desc->head_dim);
+  p.sm_scale_log2 = sm * 1.4426950408889634f;
+
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_prof.on && g_prof.used < g_prof.max) {
+    e0 = g_prof.ev[2 * g_prof.used];
+    e1 = g_prof.ev[2 * g_prof.used + 1];
+    g_prof.used++;
+  }
+  hipError_t e = launch_paged_decode(p, desc->head_dim, fp8, num_seqs,
+                                     static_cast<hipStream_t>(stream), e0, e1);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x, int64_t num_tokens,
+                           float* scale_out, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (num_tokens < 0 || !x || !scale_out || !aligned(x, 16) || !aligned(scale_out, 4))
+    return KVQ_ERR_INVALID_ARG;
+  hipError_t e = launch_scale_from_amax(
+      static_cast<const uint16_t*>(x), num_tokens, desc->num_kv_heads, desc->head_dim,
+      desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0, scale_out,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_e4m3_quantize(const float* x, int64_t n, const float* scale, uint8_t* out,
+                      void* stream) {
+  if (n < 0) return KVQ_ERR_INVALID_ARG;
+  if (n == 0) return KVQ_OK;
+  if (!x || !scale || !out || !aligned(x, 16) || !aligned(out, 4) || !aligned(scale, 4))
+    return KVQ_ERR_INVALID_ARG;
+  hipError_t e = launch_quantize(x, n, scale, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_profile_begin(int32_t max_launches) {
+  if (max_launches <= 0) return KVQ_ERR_INVALID_ARG;
+  if ((int)g_prof.ev.size() < 2 * max_launches) {
+    while ((int)g_prof.ev.size() < 2 * max_launches) {
+      hipEvent_t ev;
+      if (hipEventCreate(&ev) != hipSuccess) return KVQ_ERR_HIP;
+      g_prof.ev.push_back(ev);
+    }
+  }
+  g_prof.max = max_launches;
+  g_prof.used = 0;
+  g_prof.on = true;
+  return KVQ_OK;
+}
+
+int kvq_profile_end(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return KVQ_ERR_INVALID_ARG;
+  g_prof.on = false;
+  double sum = 0.0;
+  for (int i = 0; i < g_prof.used; ++i) {
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) return KVQ_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
+      return KVQ_ERR_HIP;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = g_prof.used;
+  g_prof.used = 0;
+  return KVQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// device_common.hpp - gfx950 device helpers shared by the kvfp8 kernels:
+// vector types, the paged-cache layout, the e4m3 encoder and the exact
+// e4m3 -> bf16 expansion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp8 {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPage = 16;     // positions per page
+constexpr int kWave = 64;     // CDNA wavefront
+
+// ---------------------------------------------------------------------------
+// Paged layout of one (page, kv head) block, e = element bytes (1 fp8, 2 bf16).
+// K: 16-byte chunks of CE = 16/e consecutive dims of one row, chunk-major:
+//      byte((r, d)) = ((d / CE) * 16 + r) * 16 + (d % CE) * e
+// V: 1 KiB groups of DB = 64/e dims; inside a group 4 quads of rows, each
+//    holding, for every dim, its 4 rows side by side:
+//      byte((r, d)) = (d / DB) * 1024 + (r / 4) * 256 + (d % DB) * 4e + (r % 4) * e
+// With these, lane l of a wave loading 16 bytes at 1024 * i + 16 * l gets
+//   K: row l % 16, dims of chunk 4i + l / 16;
+//   V: rows 4 * (l/16) .. +3, dims DB*i + (16/(4e)) * (l % 16) .. (4 or 2 dims)
+// which is exactly what one lane feeds to a 16x16x32 MFMA (see the decode
+// kernel), and every load instruction reads one contiguous 1 KiB span.
+// ---------------------------------------------------------------------------
+template <int E>
+__device__ __forceinline__ uint32_t k_byte(int r, int d) {
+  constexpr int CE = 16 / E;
+  return ((uint32_t)(d / CE) * 16u + (uint32_t)r) * 16u + (uint32_t)(d % CE) * E;
+}
+template <int E>
+__device__ __forceinline__ uint32_t v_byte(int r, int d) {
+  constexpr int DB = 64 / E;
+  return (uint32_t)(d / DB) * 1024u + (uint32_t)(r / 4) * 256u +
+         (uint32_t)(d % DB) * (4u * E) + (uint32_t)(r % 4) * E;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> e4m3 (OCP), saturating, round to nearest even.
+// |y| >= 448 (and +-Inf) -> +-448; NaN -> 0x7F with the sign of y; the sign
+// of zero is kept. Normal range: y = 2^E * f with f in [1, 2); f * 8 is
+// rounded to an integer in [8, 16] by rintf (ties to even) and a result of 16
+// moves to the next binade. Below 2^-6 the representable values are the
+// multiples of 2^-9, so y * 2^9 is rounded directly. All scalings are by
+// powers of two and exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_encode_sat(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  uint32_t mag;
+  if (!(a == a)) {
+    mag = 0x7Fu;                                   // NaN
+  } else if (a >= 448.0f) {
+    mag = 0x7Eu;                                   // saturate (Inf too)
+  } else if (a < 0.015625f) {                      // 2^-6
+    mag = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 9));   // 0..8
+  } else {
+    int ex = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -6 .. 8
+    uint32_t m8 = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - ex)); // 8..16
+    if (m8 == 16u) { m8 = 8u; ex += 1; }
+    mag = ((uint32_t)(ex + 7) << 3) | (m8 - 8u);   // ex + 7 in 1..15
+    if (mag > 0x7Eu) mag = 0x7Eu;                  // 448 < a < 448 rounds up
+  }
+  return sign | mag;
+}
+
+// ---------------------------------------------------------------------------
+// e4m3 -> bf16, exact (every e4m3 value, subnormals included, is a bf16
+// value). gfx950 converts two codes of a dword per instruction; the scale
+// operand 1.0 leaves the values unchanged. NaN codes give NaN.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16x2(uint32_t w, bool high_pair) {
+  return high_pair ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                   : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+
+__device__ __forceinline__ bf16x4 e4m3x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo = e4m3x2_to_bf16x2(w, false);
+  bf16x2 hi = e4m3x2_to_bf16x2(w, true);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+}
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  bf16x4 a = e4m3x4_to_bf16x4(w0);
+  bf16x4 b = e4m3x4_to_bf16x4(w1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 bits_to_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x4 bits_to_bf16x4(uint32_t a, uint32_t b) {
+  uint2 t = make_uint2(a, b);
+  return __builtin_bit_cast(bf16x4, t);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+}  // namespace kvfp8

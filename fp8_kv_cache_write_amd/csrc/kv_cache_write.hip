@@ -1,0 +1,208 @@
+// kv_cache_write.hip - quantise new tokens' K/V into the paged cache (gfx950),
+// plus the static amax/448 scale calibration and the flat e4m3 quantiser.
+//
+// The write is the cache-write kernel of "State of FP8 KV cache and attention
+// quantization in vLLM" (section "Kernel and vLLM improvements", paragraph
+// "Per-head scales": one FP32 scale per KV head instead of a scalar); the
+// conversion is "FP8量化与长上下文推理" section 1.1 (q = round(x / s)) with the
+// saturating mode of "cooking-agi: FP8 and the KV cache" (section "dynamic vs
+// static scale").
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace kvfp8 {
+
+// One thread per (token, kv head, 16-dim chunk). It reads 16 bf16 of K and of
+// V (two 16-byte loads each) and writes
+//   fp8 : K as one 16-byte store (one layout chunk), V as 16 byte stores
+//         (the V layout interleaves 4 rows per dim, so a row's dims are 4 bytes
+//         apart);
+//   bf16: K as two 16-byte stores, V as 16 two-byte stores.
+template <bool FP8>
+__global__ __launch_bounds__(256) void kv_cache_write_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ slots, int64_t num_tokens, int num_kv_heads,
+    int head_dim, uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    int64_t num_pages, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, int scale_per_head) {
+  const int chunks = head_dim / 16;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = num_tokens * num_kv_heads * chunks;
+  if (gid >= total) return;
+  const int c = (int)(gid % chunks);
+  const int64_t th = gid / chunks;
+  const int h = (int)(th % num_kv_heads);
+  const int64_t t = th / num_kv_heads;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_pages * kPage) return;   // skipped / outside the pool
+  const int64_t page = slot / kPage;
+  const int r = (int)(slot % kPage);
+
+  const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)c * 16;
+  const uint4* ks = reinterpret_cast<const uint4*>(k + src);
+  const uint4* vs = reinterpret_cast<const uint4*>(v + src);
+  uint4 kx[2] = {ks[0], ks[1]};
+  uint4 vx[2] = {vs[0], vs[1]};
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(kx);
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(vx);
+
+  constexpr int E = FP8 ? 1 : 2;
+  const int64_t pb = (int64_t)kPage * head_dim * E;
+  uint8_t* kb = k_cache + (page * num_kv_heads + h) * pb;
+  uint8_t* vb = v_cache + (page * num_kv_heads + h) * pb;
+  const int d0 = c * 16;
+
+  if constexpr (FP8) {
+    const float sk = k_scale[scale_per_head ? h : 0];
+    const float sv = v_scale[scale_per_head ? h : 0];
+    uint32_t kq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int e = j * 4 + b;
+        const uint32_t bits = (kw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+        w |= e4m3_encode_sat(bf16_bits_to_f32(bits) / sk) << (8 * b);
+      }
+      kq[j] = w;
+    }
+    // 16 consecutive dims of one row form exactly one K chunk.
+    *reinterpret_cast<uint4*>(kb + k_byte<1>(r, d0)) =
+        make_uint4(kq[0], kq[1], kq[2], kq[3]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t bits = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+      vb[v_byte<1>(r, d0 + e)] =
+          (uint8_t)e4m3_encode_sat(bf16_bits_to_f32(bits) / sv);
+    }
+  } else {
+    // bf16 layers keep the bits: the skip-layer path.
+    *reinterpret_cast<uint4*>(kb + k_byte<2>(r, d0)) = kx[0];
+    *reinterpret_cast<uint4*>(kb + k_byte<2>(r, d0 + 8)) = kx[1];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t bits = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+      *reinterpret_cast<uint16_t*>(vb + v_byte<2>(r, d0 + e)) = (uint16_t)bits;
+    }
+  }
+}
+
+// Static scale calibration: s = fp32(amax) / 448 over one KV head (or over
+// every head). One work-group per output scale; threads stride over the
+// tensor in 16-byte loads. NaN anywhere gives NaN, amax == 0 gives 1.
+__global__ __launch_bounds__(1024) void scale_from_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t num_tokens, int num_kv_heads,
+    int head_dim, int per_head, float* __restrict__ scale_out) {
+  const int h_out = blockIdx.x;
+  const int chunks = head_dim / 8;                 // 8 bf16 per 16 bytes
+  const int heads_here = per_head ? 1 : num_kv_heads;
+  const int64_t per_token = (int64_t)heads_here * chunks;
+  const int64_t total = num_tokens * per_token;
+  float amax = 0.0f;
+  bool nan = false;
+  for (int64_t i = threadIdx.x; i < total; i += blockDim.x) {
+    const int64_t t = i / per_token;
+    const int64_t rem = i % per_token;
+    const int h = per_head ? h_out : (int)(rem / chunks);
+    const int c = (int)(rem % chunks);
+    const uint4 w = *reinterpret_cast<const uint4*>(
+        x + (t * num_kv_heads + h) * head_dim + c * 8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = fabsf(bf16_bits_to_f32((ws[j / 2] >> (16 * (j % 2))) & 0xFFFFu));
+      nan |= !(f == f);
+      amax = f > amax ? f : amax;
+    }
+  }
+  __shared__ float red[1024 / kWave];
+  __shared__ int rnan[1024 / kWave];
+  for (int off = kWave / 2; off > 0; off /= 2) {
+    const float o = __shfl_xor(amax, off);
+    amax = o > amax ? o : amax;
+  }
+  const int any_nan = __any(nan) ? 1 : 0;
+  const int wid = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) {
+    red[wid] = amax;
+    rnan[wid] = any_nan;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.0f;
+    int n = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+      m = red[w] > m ? red[w] : m;
+      n |= rnan[w];
+    }
+    float s;
+    if (n) s = __builtin_nanf("");
+    else if (m == 0.0f) s = 1.0f;
+    else s = m / 448.0f;
+    scale_out[h_out] = s;
+  }
+}
+
+// Flat quantiser: out[i] = e4m3(x[i] / s), 4 elements per thread.
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const float* __restrict__ x, int64_t n, const float* __restrict__ scale,
+    uint8_t* __restrict__ out) {
+  const float s = scale[0];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 4 < n;
+       i += stride) {
+    const int64_t base = i * 4;
+    if (base + 4 <= n) {
+      const float4 f = *reinterpret_cast<const float4*>(x + base);
+      const uint32_t w = e4m3_encode_sat(f.x / s) | (e4m3_encode_sat(f.y / s) << 8) |
+                         (e4m3_encode_sat(f.z / s) << 16) |
+                         (e4m3_encode_sat(f.w / s) << 24);
+      *reinterpret_cast<uint32_t*>(out + base) = w;
+    } else {
+      for (int64_t j = base; j < n; ++j) out[j] = (uint8_t)e4m3_encode_sat(x[j] / s);
+    }
+  }
+}
+
+hipError_t launch_kv_cache_write(bool fp8, const uint16_t* k, const uint16_t* v,
+                                 const int64_t* slots, int64_t num_tokens,
+                                 int num_kv_heads, int head_dim, uint8_t* k_cache,
+                                 uint8_t* v_cache, int64_t num_pages,
+                                 const float* k_scale, const float* v_scale,
+                                 int scale_per_head, hipStream_t stream) {
+  const int64_t total = num_tokens * num_kv_heads * (head_dim / 16);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  if (fp8)
+    hipLaunchKernelGGL(kv_cache_write_kernel<true>, dim3((unsigned)blocks), dim3(256),
+                       0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
+                       k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
+  else
+    hipLaunchKernelGGL(kv_cache_write_kernel<false>, dim3((unsigned)blocks), dim3(256),
+                       0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
+                       k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_from_amax(const uint16_t* x, int64_t num_tokens,
+                                  int num_kv_heads, int head_dim, int per_head,
+                                  float* scale_out, hipStream_t stream) {
+  const int blocks = per_head ? num_kv_heads : 1;
+  hipLaunchKernelGGL(scale_from_amax_kernel, dim3(blocks), dim3(1024), 0, stream, x,
+                     num_tokens, num_kv_heads, head_dim, per_head, scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* x, int64_t n, const float* scale,
+                           uint8_t* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  int64_t groups = (n + 3) / 4;
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     x, n, scale, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvfp8

@@ -1,0 +1,58 @@
+// launch.hpp - internal interface between the C ABI (api.cpp) and the
+// kernels. Not installed; the public interface is include/kvfp8.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp8 {
+
+hipError_t launch_kv_cache_write(bool fp8, const uint16_t* k, const uint16_t* v,
+                                 const int64_t* slots, int64_t num_tokens,
+                                 int num_kv_heads, int head_dim, uint8_t* k_cache,
+                                 uint8_t* v_cache, int64_t num_pages,
+                                 const float* k_scale, const float* v_scale,
+                                 int scale_per_head, hipStream_t stream);
+
+hipError_t launch_scale_from_amax(const uint16_t* x, int64_t num_tokens,
+                                  int num_kv_heads, int head_dim, int per_head,
+                                  float* scale_out, hipStream_t stream);
+
+hipError_t launch_quantize(const float* x, int64_t n, const float* scale,
+                           uint8_t* out, hipStream_t stream);
+
+// Everything the split-decode and reduce kernels read; passed by value.
+struct DecodeParams {
+  const uint16_t* q;             // bf16 [B][Hq][D]
+  const uint8_t* k_cache;        // [P][Hkv][PB]
+  const uint8_t* v_cache;
+  const int32_t* block_tables;   // [B][max_pages_per_seq]
+  const int32_t* context_lens;   // [B]
+  int64_t num_pages;             // pool size: page ids outside [0, num_pages) read as empty
+  const float* k_scale;          // [1] or [Hkv]; unused for bf16
+  const float* v_scale;
+  float* ws_m;                   // [B][Hq][num_parts]   (log2 domain)
+  float* ws_l;                   // [B][Hq][num_parts]
+  float* ws_o;                   // [B][Hq][num_parts][D]
+  void* out;                     // [B][Hq][D] f32 or bf16
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                     // G = Hq / Hkv, <= 8
+  int max_pages_per_seq;
+  int window;                    // 0 = full
+  int pages_per_wave;            // <= 64
+  int num_parts;                 // partitions allocated per (b, q head)
+  int scale_per_head;
+  int out_bf16;
+  int direct;                    // num_parts == 1: the split kernel finishes
+  float sm_scale_log2;           // sm_scale * log2(e)
+};
+
+// Waves per work-group of the split kernel.
+constexpr int kSplitWaves = 4;
+
+hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,
+                               int num_seqs, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after);
+
+}  // namespace kvfp8

@@ -111,10 +111,9 @@ typedef struct kvq_layer_desc {
 /*
  * kvq_kv_cache_write - store T new tokens' K and V into the paged caches.
  *   k, v          device bf16 [T][Hkv][D]
- *   slot_mapping  device int64 [T]; slot = page * 16 + row; slot < 0 skips the
- *                 token; every slot must be < num_pages * 16 (not checked on
- *                 the device: the host cannot read device memory without a
- *                 sync). Two tokens with the same slot: which one wins is
+ *   slot_mapping  device int64 [T]; slot = page * 16 + row; a slot < 0 or
+ *                 >= num_pages * 16 skips the token (checked on the device).
+ *                 Two tokens with the same slot: which one wins is
  *                 unspecified.
  *   k_cache, v_cache  device byte arrays in the layout above, num_pages pages.
  *   k_scale, v_scale  device fp32 [1] (per tensor) or [Hkv] (per KV head);
@@ -152,9 +151,14 @@ int kvq_decode_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
  *   q             device bf16 [B][Hq][D]
  *   k_cache, v_cache  as written by kvq_kv_cache_write; num_pages pages
  *   block_tables  device int32 [B][max_pages_per_seq]; entries for the
- *                 attended pages must be in [0, num_pages)
- *   context_lens  device int32 [B]; each in [0, max_context_len] and
- *                 ceil(L/16) <= max_pages_per_seq (not checked on the device)
+ *                 attended pages should be in [0, num_pages): an entry
+ *                 outside it reads as an empty page (its positions are
+ *                 skipped) and is never dereferenced
+ *   context_lens  device int32 [B]; each should be in [0, max_context_len].
+ *                 On the device a length is cut to max_pages_per_seq * 16 and
+ *                 to the partitions planned for max_context_len, so a larger
+ *                 value gives a truncated result, never an access out of
+ *                 bounds
  *   max_context_len  host int, an upper bound of every context_lens[b]; it
  *                 sizes the partition plan and must match the value given to
  *                 kvq_decode_workspace_bytes

@@ -68,6 +68,11 @@ def lib():
                                          ctypes.c_int, ctypes.c_int, _u16p,
                                          _u16p, _i64p, ctypes.c_int64, _u8p,
                                          _u8p, ctypes.c_int64, _f32p, _f32p]
+        L.orc_kv_cache_write_mt.argtypes = [ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, _u16p,
+                                            _u16p, _i64p, ctypes.c_int64, _u8p,
+                                            _u8p, ctypes.c_int64, _f32p, _f32p,
+                                            ctypes.c_int]
         L.orc_softmax_weighted_sum.argtypes = [_f64p, _f64p, ctypes.c_int64,
                                                ctypes.c_int, _f64p]
         att = [ctypes.c_int] * 7 + [ctypes.c_double, _u16p, _u8p, _u8p, _i32p,
@@ -155,7 +160,7 @@ def page_bytes(head_dim: int, dtype: int) -> int:
 # ----------------------------------------------------------- cache write ---
 def kv_cache_write(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
                    v: np.ndarray, slots: np.ndarray, dtype: int, per_head: bool,
-                   k_scale=None, v_scale=None):
+                   k_scale=None, v_scale=None, nthreads=None):
     """In place on uint8 caches [P][H][PB]. k, v: uint16 bf16 bits [T][H][D]."""
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
@@ -166,10 +171,11 @@ def kv_cache_write(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
     num_pages = k_cache.shape[0]
     ks = np.ascontiguousarray(k_scale if k_scale is not None else [1.0], dtype=np.float32)
     vs = np.ascontiguousarray(v_scale if v_scale is not None else [1.0], dtype=np.float32)
-    lib().orc_kv_cache_write(H, D, dtype, int(per_head), _ptr(k, _u16p),
-                             _ptr(v, _u16p), _ptr(slots, _i64p), T,
-                             _ptr(k_cache, _u8p), _ptr(v_cache, _u8p), num_pages,
-                             _ptr(ks, _f32p), _ptr(vs, _f32p))
+    lib().orc_kv_cache_write_mt(H, D, dtype, int(per_head), _ptr(k, _u16p),
+                                _ptr(v, _u16p), _ptr(slots, _i64p), T,
+                                _ptr(k_cache, _u8p), _ptr(v_cache, _u8p),
+                                num_pages, _ptr(ks, _f32p), _ptr(vs, _f32p),
+                                _threads(nthreads))
 
 
 # -------------------------------------------------------------- attention --

@@ -328,6 +328,47 @@ void orc_kv_cache_write(int H, int D, int dtype, int per_head,
   }
 }
 
+/* Threaded cache write: tokens are split across threads; each token is
+ * written exactly as orc_kv_cache_write writes it. Tokens sharing a slot
+ * must not be split across threads (callers pass distinct slots). */
+typedef struct {
+  int H, D, dtype, per_head;
+  const uint16_t *k, *v;
+  const int64_t* slots;
+  int64_t lo, hi;
+  uint8_t *kc, *vc;
+  int64_t num_pages;
+  const float *ks, *vs;
+} wjob;
+
+static void* write_worker(void* p) {
+  wjob* j = (wjob*)p;
+  int64_t off = j->lo * j->H * j->D;
+  orc_kv_cache_write(j->H, j->D, j->dtype, j->per_head, j->k + off, j->v + off,
+                     j->slots + j->lo, j->hi - j->lo, j->kc, j->vc, j->num_pages,
+                     j->ks, j->vs);
+  return NULL;
+}
+
+void orc_kv_cache_write_mt(int H, int D, int dtype, int per_head,
+                           const uint16_t* k, const uint16_t* v,
+                           const int64_t* slots, int64_t T, uint8_t* kc,
+                           uint8_t* vc, int64_t num_pages, const float* ks,
+                           const float* vs, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (T < 4096) nthreads = 1;
+  pthread_t th[256];
+  wjob jobs[256];
+  for (int i = 0; i < nthreads; ++i) {
+    wjob w = {H, D, dtype, per_head, k, v, slots, T * i / nthreads,
+              T * (i + 1) / nthreads, kc, vc, num_pages, ks, vs};
+    jobs[i] = w;
+    pthread_create(&th[i], NULL, write_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
 /* Dequantised element (float64) of the K or V cache. */
 static double cache_value(const uint8_t* cache, int is_v, int64_t page, int H,
                           int h, int r, int d, int D, int dtype, double scale) {

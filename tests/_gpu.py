@@ -1,0 +1,138 @@
+"""Helpers shared by the GPU parity tests: run one decode layer through the
+HIP library (C ABI via the Python binding) and through the oracle on the same
+seeded inputs."""
+
+import numpy as np
+import torch
+
+import fp8_kv_cache_write_amd as kv
+import oracle
+import synth
+
+FP8, BF16 = oracle.FP8, oracle.BF16
+GATE_MAX_ABS = 1e-2      # attention gate (max-abs, unit-scale inputs)
+GATE_MEAN_ABS = 1e-3     # attention gate (mean-abs)
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def bf16_dev(bits):
+    """uint16 bf16 bit patterns -> bf16 device tensor (same bits)."""
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).to(dev()).view(torch.bfloat16)
+
+
+def i32_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+
+
+def i64_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(dev())
+
+
+def u8_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev())
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+class GpuLayer:
+    """One layer on the GPU: poisoned caches, scales calibrated by the
+    library, every position of the case written by the library."""
+
+    def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
+                 scales=None):
+        self.case = case
+        self.fp8 = fp8
+        self.desc = kv.layer_desc(case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                  "fp8_e4m3" if fp8 else "bf16",
+                                  "per_kv_head" if per_head else "per_tensor",
+                                  window, sm_scale)
+        self.k_new = bf16_dev(case.k_new)
+        self.v_new = bf16_dev(case.v_new)
+        self.slots = i64_dev(case.slots)
+        pc = synth.poisoned_cache(case.num_pages, case.num_kv_heads, case.head_dim, fp8)
+        self.k_cache = u8_dev(pc)
+        self.v_cache = u8_dev(pc)
+        n = case.num_kv_heads if per_head else 1
+        if fp8:
+            if scales is None:
+                self.k_scale = torch.empty(n, dtype=torch.float32, device=dev())
+                self.v_scale = torch.empty(n, dtype=torch.float32, device=dev())
+                kv.kv_scale_from_amax(self.desc, self.k_new, self.k_scale)
+                kv.kv_scale_from_amax(self.desc, self.v_new, self.v_scale)
+            else:
+                self.k_scale = torch.tensor(scales[0], dtype=torch.float32, device=dev())
+                self.v_scale = torch.tensor(scales[1], dtype=torch.float32, device=dev())
+        else:
+            self.k_scale = self.v_scale = None
+        kv.kv_cache_write(self.desc, self.k_new, self.v_new, self.slots, self.k_cache,
+                          self.v_cache, self.k_scale, self.v_scale)
+        self.q = bf16_dev(case.q)
+        self.block_tables = i32_dev(case.block_tables)
+        self.context_lens = i32_dev(case.lens)
+
+    def attend(self, out_dtype=torch.float32, block_tables=None, q=None):
+        c = self.case
+        out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=out_dtype,
+                          device=dev())
+        ws = kv.alloc_workspace(self.desc, c.num_seqs, c.max_context_len)
+        kv.paged_decode_attention(self.desc, out, self.q if q is None else q,
+                                  self.k_cache, self.v_cache,
+                                  self.block_tables if block_tables is None else block_tables,
+                                  self.context_lens, c.max_context_len, self.k_scale,
+                                  self.v_scale, ws)
+        torch.cuda.synchronize()
+        return out
+
+    def scales_host(self):
+        if not self.fp8:
+            return None, None
+        return host(self.k_scale), host(self.v_scale)
+
+
+class OracleLayer:
+    """The same layer through the oracle (its own scales, its own caches)."""
+
+    def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
+                 scales=None):
+        self.case, self.fp8, self.per_head = case, fp8, per_head
+        self.window, self.sm_scale = window, sm_scale
+        self.k_cache = synth.poisoned_cache(case.num_pages, case.num_kv_heads,
+                                            case.head_dim, fp8)
+        self.v_cache = self.k_cache.copy()
+        if fp8:
+            if scales is None:
+                self.ks = oracle.scale_from_amax(case.k_new, per_head)
+                self.vs = oracle.scale_from_amax(case.v_new, per_head)
+            else:
+                self.ks = np.asarray(scales[0], np.float32)
+                self.vs = np.asarray(scales[1], np.float32)
+        else:
+            self.ks = self.vs = None
+        oracle.kv_cache_write(self.k_cache, self.v_cache, case.k_new, case.v_new,
+                              case.slots, FP8 if fp8 else BF16, per_head, self.ks,
+                              self.vs)
+
+    def attend(self):
+        c = self.case
+        return oracle.attention(c.q, self.k_cache, self.v_cache, c.block_tables, c.lens,
+                                c.num_kv_heads, FP8 if self.fp8 else BF16, self.per_head,
+                                self.window, self.sm_scale, self.ks, self.vs)
+
+
+def errors(gpu_out, ref):
+    g = host(gpu_out.float()).astype(np.float64)
+    d = np.abs(g - ref)
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def unquantised_reference(case, window=0, sm_scale=0.0):
+    """Attention over the bf16 inputs themselves (no quantisation): the
+    reference for reporting the quantisation error."""
+    o = OracleLayer(case, fp8=False, window=window, sm_scale=sm_scale)
+    return o.attend()

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+entry point include/kvfp8.h declares, and rejects bad arguments with the
+documented status before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_kv_cache_write_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfp8.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kv.LIB_PATH):
+        from fp8_kv_cache_write_amd import build
+        build.build()
+    return kv.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("kvq_kv_cache_write", "kvq_paged_decode_attention",
+              "kvq_decode_workspace_bytes", "kvq_kv_scale_from_amax",
+              "kvq_e4m3_quantize", "kvq_status_string"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    assert kv.status_string(OK) == "ok"
+    assert "workspace" in kv.status_string(WS_SMALL)
+    assert kv.status_string(12345) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x100004)    # 4-byte aligned only
+
+
+def write(L, desc, k=FAKE, v=FAKE, slots=FAKE, T=4, kc=FAKE, vc=FAKE, P=8,
+          ks=FAKE, vs=FAKE):
+    return L.kvq_kv_cache_write(ctypes.byref(desc), k, v, slots, T, kc, vc, P, ks, vs,
+                                None)
+
+
+def attend(L, desc, out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, P=8, bt=FAKE, mp=8,
+           lens=FAKE, B=1, maxlen=100, ks=FAKE, vs=FAKE, ws=FAKE, wsb=1 << 30,
+           out_dtype=0):
+    return L.kvq_paged_decode_attention(ctypes.byref(desc), out, out_dtype, q, kc, vc, P,
+                                        bt, mp, lens, B, maxlen, ks, vs, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(head_dim=512), UNSUPPORTED),
+    (dict(num_q_heads=30, num_kv_heads=8), UNSUPPORTED),
+    (dict(num_q_heads=64, num_kv_heads=4), UNSUPPORTED),   # group 16 > 8
+    (dict(num_q_heads=0), INVALID),
+    (dict(sliding_window=-1), INVALID),
+    (dict(sm_scale=-1.0), INVALID),
+])
+def test_descriptor_checks(L, kw, status):
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128)
+    base.update(kw)
+    d = kv.layer_desc(**base)
+    assert write(L, d) == status
+    assert attend(L, d) == status
+    n = ctypes.c_size_t()
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 1, 100, ctypes.byref(n)) == status
+
+
+def test_page_size_must_be_16(L):
+    d = kv.layer_desc(32, 8, 128)
+    d.page_size = 32
+    assert write(L, d) == UNSUPPORTED
+
+
+def test_write_argument_checks(L):
+    d = kv.layer_desc(32, 8, 128)
+    assert write(L, d, k=None) == INVALID
+    assert write(L, d, slots=None) == INVALID
+    assert write(L, d, kc=FAKE_ODD) == INVALID
+    assert write(L, d, ks=None) == INVALID           # fp8 layers need scales
+    assert write(L, d, T=-1) == INVALID
+    assert write(L, d, T=0, k=None) == OK            # nothing to do, nothing launched
+    b = kv.layer_desc(32, 8, 128, cache_dtype="bf16")
+    assert write(L, b, T=0, ks=None, vs=None) == OK
+
+
+def test_attention_argument_checks(L):
+    d = kv.layer_desc(32, 8, 128)
+    assert attend(L, d, q=None) == INVALID
+    assert attend(L, d, out=FAKE_ODD) == INVALID
+    assert attend(L, d, mp=6, maxlen=100) == INVALID     # 100 positions need 7 pages
+    assert attend(L, d, out_dtype=7) == INVALID
+    assert attend(L, d, ks=None) == INVALID
+    assert attend(L, d, B=0) == OK
+
+
+def test_workspace_checks(L):
+    d = kv.layer_desc(32, 8, 128)
+    need = kv.decode_workspace_bytes(d, 1, 131072)
+    assert need > 0
+    mp = 131072 // 16
+    assert attend(L, d, maxlen=131072, mp=mp, wsb=need - 1) == WS_SMALL
+    assert attend(L, d, maxlen=131072, mp=mp, ws=None, wsb=need) == INVALID
+
+
+def test_workspace_plan():
+    d = kv.layer_desc(32, 8, 128)
+    # short contexts and sliding windows finish in the split kernel
+    assert kv.decode_workspace_bytes(d, 1, 256) == 0
+    sw = kv.layer_desc(64, 8, 64, cache_dtype="bf16", sliding_window=128)
+    assert kv.decode_workspace_bytes(sw, 1, 32768) == 0
+    # long contexts split: one (m, l, o[D]) float row per partition and head
+    sizes = [kv.decode_workspace_bytes(d, 1, n) for n in (8192, 32768, 131072)]
+    assert sizes[0] <= sizes[1] <= sizes[2]
+    assert sizes[2] >= 32 * 2 * (128 + 2) * 4
+    # partials stay a small fraction of the KV bytes they summarise
+    assert sizes[2] < 0.02 * (2 * 131072 * 8 * 128)
+
+
+def test_no_oracle_in_the_product():
+    pkg = os.path.join(ROOT, "fp8_kv_cache_write_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "liboracle" not in text, f
+                assert "orc_" not in text, f
