@@ -165,6 +165,8 @@ class LayerStack:
 
 
 def time_steps(torch, kv, stack, steps, warmup, profile=True):
+    """Eager steps: mean ms per step, and (with profile) the split kernel's
+    mean duration from the library's kernel-timestamped HIP events."""
     for _ in range(warmup):
         stack.step()
     torch.cuda.synchronize()
@@ -181,6 +183,62 @@ def time_steps(torch, kv, stack, steps, warmup, profile=True):
     ms = e0.elapsed_time(e1) / steps
     split_ms, n = kv.profile_end() if profile else (0.0, 0)
     return ms, (split_ms / n if n else None), n
+
+
+def time_steps_graph(torch, stack, steps, warmup):
+    """The step captured once as a HIP graph, replayed: mean ms per step.
+    The replayed outputs are checked against the eager step's."""
+    stack.step()
+    torch.cuda.synchronize()
+    ref = [ly["out"].clone() for ly in stack.layers]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stack.step()
+    for _ in range(max(warmup, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    for ly, r in zip(stack.layers, ref):
+        if not torch.equal(ly["out"], r):
+            raise RuntimeError("graph replay differs from the eager step")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / steps
+
+
+KERNEL_SOURCES = ["fp8_kv_cache_write_amd/csrc/paged_decode.hip",
+                  "fp8_kv_cache_write_amd/csrc/device_common.hpp",
+                  "fp8_kv_cache_write_amd/csrc/launch.hpp",
+                  "fp8_kv_cache_write_amd/csrc/api.cpp"]
+TRAFFIC_PROFILE = "profiles/paged_decode_split_llama8b_128k_fp8_traffic.json"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_key):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 PMC
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's readings), or
+    None when it was taken on other kernel sources or another workload."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload_key:
+        return None
+    return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
 
 def layers_for(bytes_per_layer, lo=8, hi=512, target=2 * GIB):
@@ -204,7 +262,8 @@ def sweep(torch, kv, w, contexts, steps, warmup):
             per_layer = ctx * w["Hkv"] * w["D"] * 2 * e
             NL = layers_for(per_layer)
             st = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, dt, seed=ctx)
-            ms, split_ms, _ = time_steps(torch, kv, st, steps, warmup)
+            ms = time_steps_graph(torch, st, steps, warmup)
+            _, split_ms, _ = time_steps(torch, kv, st, 2, 1)
             us_layer = ms * 1e3 / NL
             gbs = st.total_kv_bytes() / (ms * 1e-3) / 1e9
             rows.append(dict(cache=dt, context=ctx, layers=NL, us_per_layer=round(us_layer, 3),
@@ -327,14 +386,17 @@ def main():
                            seed=1)
         ctx_desc = f"context {ctx}"
     log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}")
-    ms, split_ms, nsplit = time_steps(torch, kv, stack, args.steps, args.warmup)
+    # the timed region: K steps, each one replay of the captured decode step
+    ms = time_steps_graph(torch, stack, args.steps, args.warmup)
+    # eager steps with the split kernel's launches timed by the library
+    ms_eager, split_ms, nsplit = time_steps(torch, kv, stack, args.steps, args.warmup)
     step_bytes = stack.total_step_bytes()
     value = step_bytes / (ms * 1e-3) / 1e9
     kv_gbs = stack.total_kv_bytes() / (ms * 1e-3) / 1e9
     d0 = stack.layers[0]["desc"]
     split_bytes = stack.split_bytes(d0)
     achieved = split_bytes / (split_ms * 1e-3) / 1e9 if split_ms else None
-    log(f"headline: {ms:.3f} ms/step, {ms * 1e3 / NL:.2f} us/layer, {value:.1f} GB/s "
+    log(f"headline: {ms:.3f} ms/step (graph; eager {ms_eager:.3f}), {ms * 1e3 / NL:.2f} us/layer, {value:.1f} GB/s "
         f"(KV {kv_gbs:.1f} GB/s), split kernel {split_ms * 1e3 if split_ms else 0:.2f} us "
         f"-> {achieved or 0:.1f} GB/s")
 
@@ -359,6 +421,8 @@ def main():
             "batch": w["B"], "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": w["D"],
             "page_size": 16, "layers_per_step": NL, "parallelism": "single GPU",
         },
+        "timing": "each step is one replay of the decode step captured as a HIP graph",
+        "ms_per_step_eager": round(ms_eager, 5),
         "us_per_layer_step": round(ms * 1e3 / NL, 3),
         "kv_gbs": round(kv_gbs, 2),
         "kv_frac_of_hbm_peak": round(kv_gbs / HBM_PEAK_GBS, 4),
@@ -369,9 +433,12 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-            "traffic": None,
+            "traffic": measured_traffic(f"{args.workload}:{ctx}:{args.cache}:{NL}")
+            if args.workload == "llama8b" else None,
             "launch_us": round(split_ms * 1e3, 3) if split_ms else None,
             "launches_timed": nsplit,
+            "timed_with": "kernel-timestamped HIP event pairs around every split-kernel launch "
+                          "of the eager steps (kvq_profile_begin/end)",
             "algorithmic_bytes_per_launch": split_bytes,
         },
     }

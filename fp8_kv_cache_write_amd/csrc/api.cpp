@@ -65,8 +65,10 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Split-context plan. Pages of one (sequence, KV head) are cut into
 // partitions of kSplitWaves * pages_per_wave pages; each partition is one
-// work-group, each wave streams pages_per_wave pages. pages_per_wave aims at
-// about 16 waves per compute unit over the whole grid; when one partition per
+// work-group, each wave streams pages_per_wave pages. Measured on MI355X,
+// long runs per wave beat many concurrent waves: pages_per_wave is the power
+// of two that gives about one wave per SIMD for fp8 (about two for bf16,
+// whose pages are twice as large), in [2, 64]. When one partition per
 // sequence is cheap enough (short contexts, sliding windows) the split kernel
 // writes the output itself and the reduce kernel is skipped.
 Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
@@ -75,15 +77,15 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
   if (W > 0) pages_max = std::min<int64_t>(pages_max, ((int64_t)W + 15) / 16 + 1);
   if (pages_max < 1) pages_max = 1;
   const int64_t total = (int64_t)std::max(num_seqs, 1) * d->num_kv_heads * pages_max;
-  const int64_t target_waves = (int64_t)cu_count() * 16;
-  int64_t ppw = (total + target_waves - 1) / target_waves;
-  ppw = std::max<int64_t>(ppw, 2);
-  ppw = (ppw + 1) / 2 * 2;
-  ppw = std::min<int64_t>(ppw, kMaxPagesPerWave);
+  const int64_t waves_per_cu = d->cache_dtype == KVQ_FP8_E4M3 ? 4 : 8;
+  const int64_t target_waves = (int64_t)cu_count() * waves_per_cu;
+  const int64_t want = (total + target_waves - 1) / target_waves;
+  int64_t ppw = 2;
+  while (ppw < want && ppw < kMaxPagesPerWave) ppw *= 2;
   int64_t direct_ppw = (pages_max + kSplitWaves - 1) / kSplitWaves;
   direct_ppw = (direct_ppw + 1) / 2 * 2;
   if (direct_ppw <= std::max<int64_t>(ppw, 8)) ppw = direct_ppw;
-  // KVFP8_PAGES_PER_WAVE=n (2..64) overrides the choice (tuning sweeps).
+  // KVFP8_PAGES_PER_WAVE=n (1..64) overrides the choice (tuning sweeps).
   if (const char* env = getenv("KVFP8_PAGES_PER_WAVE")) {
     const long n = strtol(env, nullptr, 10);
     if (n >= 1 && n <= kMaxPagesPerWave) ppw = n;

@@ -24,7 +24,10 @@
 //    running accumulator after the online-softmax rescale (level 2);
 //  * the waves of a work-group merge their (m, l, o) through LDS; the reduce
 //    kernel merges partitions in FP32 and applies the V head scale.
+#include <hip/hip_ext.h>
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -68,7 +71,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   return r;
 }
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, int TP, int RING>
 __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const DecodeParams p) {
   constexpr int E = FP8 ? 1 : 2;
@@ -146,39 +149,36 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 #pragma unroll
   for (int i = 0; i < NBLK; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // A tile is TP pages (an even number: the P*V MFMA contracts 32 positions,
+  // two pages). Missing pages (past the run, an odd tail) and invalid ids
+  // load pool page 0 instead: their positions are masked, so the values never
+  // matter, and the registers never hold uninitialised data.
   struct Tile {
-    uint4 k[2][NI];
-    uint4 v[2][NI];
+    uint4 k[TP][NI];
+    uint4 v[TP][NI];
   };
 
   auto load_tile = [&](int t, Tile& tl) {
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const int idx = 2 * t + pg;
-      if (idx < npages && !((bad_pages >> idx) & 1ull)) {
-        const int pid = __builtin_amdgcn_readlane(my_page, idx);
-        const uint4* kp = reinterpret_cast<const uint4*>(kbase + (int64_t)pid * page_stride);
-        const uint4* vp = reinterpret_cast<const uint4*>(vbase + (int64_t)pid * page_stride);
+    for (int pg = 0; pg < TP; ++pg) {
+      const int idx = TP * t + pg;
+      const bool ok = idx < npages && !((bad_pages >> idx) & 1ull);
+      const int pid = ok ? __builtin_amdgcn_readlane(my_page, idx) : 0;
+      const uint4* kp = reinterpret_cast<const uint4*>(kbase + (int64_t)pid * page_stride);
+      const uint4* vp = reinterpret_cast<const uint4*>(vbase + (int64_t)pid * page_stride);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          tl.k[pg][i] = kp[i * kWave + lane];
-          tl.v[pg][i] = vp[i * kWave + lane];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          tl.k[pg][i] = make_uint4(0u, 0u, 0u, 0u);
-          tl.v[pg][i] = make_uint4(0u, 0u, 0u, 0u);
-        }
+      for (int i = 0; i < NI; ++i) {
+        tl.k[pg][i] = kp[i * kWave + lane];
+        tl.v[pg][i] = vp[i * kWave + lane];
       }
     }
   };
 
   auto compute_tile = [&](int t, const Tile& tl) {
-    // ---- logits: S^T[row 4qd+e][col c] for both pages of the tile --------
-    f32x4 s2[2];
+    // ---- logits: S^T[row 4qd+e][col c] for every page of the tile --------
+    float x[TP][4];
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
+    for (int pg = 0; pg < TP; ++pg) {
       f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
@@ -191,118 +191,135 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         }
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[s], sacc, 0, 0, 0);
       }
-      s2[pg] = sacc;
-    }
-    float x[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = s2[0][e] * c_log2;
-      x[4 + e] = s2[1][e] * c_log2;
+      for (int e = 0; e < 4; ++e) x[pg][e] = sacc[e] * c_log2;
     }
-    // ---- masking: positions outside [lo, L) or past this wave's run ------
-    const int pos0 = (wbeg + 2 * t) * kPage;          // first position of page A
-    const bool has_a = !((bad_pages >> (2 * t)) & 1ull);
-    const bool has_b = 2 * t + 1 < npages && !((bad_pages >> (2 * t + 1)) & 1ull);
-    const bool need_mask = (pos0 < pr.lo) || (pos0 + 2 * kPage > pr.L) || !has_b || !has_a;
-    uint32_t vkeep = 0xFFu;                             // bit j: operand element j valid
+    // ---- masking: positions outside [lo, L), past the run, invalid pages --
+    const int pos0 = (wbeg + TP * t) * kPage;           // first position of the tile
+    bool any_missing = false;
+#pragma unroll
+    for (int pg = 0; pg < TP; ++pg) {
+      const int idx = TP * t + pg;
+      any_missing |= idx >= npages || ((bad_pages >> idx) & 1ull);
+    }
+    const bool need_mask = (pos0 < pr.lo) || (pos0 + TP * kPage > pr.L) || any_missing;
+    uint32_t vkeep = 0xFFFFFFFFu;                        // bit 4*pg+e: row 4qd+e of page pg
     if (need_mask) {
       vkeep = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ta = pos0 + 4 * qd + e;
-        const int tb = ta + kPage;
-        const bool va = has_a && ta >= pr.lo && ta < pr.L;
-        const bool vb = has_b && tb >= pr.lo && tb < pr.L;
-        if (!va) x[e] = -INFINITY;
-        if (!vb) x[4 + e] = -INFINITY;
-        vkeep |= (va ? 1u : 0u) << e;
-        vkeep |= (vb ? 1u : 0u) << (4 + e);
+      for (int pg = 0; pg < TP; ++pg) {
+        const int idx = TP * t + pg;
+        const bool page_ok = idx < npages && !((bad_pages >> idx) & 1ull);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pos = pos0 + pg * kPage + 4 * qd + e;
+          const bool ok = page_ok && pos >= pr.lo && pos < pr.L;
+          if (!ok) x[pg][e] = -INFINITY;
+          vkeep |= (ok ? 1u : 0u) << (4 * pg + e);
+        }
       }
     }
     if (g < 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = -INFINITY;
+      for (int pg = 0; pg < TP; ++pg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[pg][e] = -INFINITY;
     }
     // ---- online softmax (log2 domain) -------------------------------------
-    float tmax = x[0];
+    float tmax = x[0][0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, x[j]);
+    for (int pg = 0; pg < TP; ++pg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[pg][e]);
     tmax = wave_max_col(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float pe[8];
     float psum = 0.0f;
+    bf16x8 pop[TP / 2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pe[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
-      psum += pe[j];
+    for (int pg = 0; pg < TP; ++pg) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(x[pg][e] - m_use);
+        psum += pe;
+        // P as bf16: the high part in the query columns, the rounding
+        // residue in the duplicate columns.
+        const __bf16 hi = (__bf16)pe;
+        pop[pg / 2][4 * (pg % 2) + e] = lo_col ? (__bf16)(pe - (float)hi) : hi;
+      }
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // P as bf16: high part in the query columns, the rounding residue in
-    // the duplicate columns.
-    bf16x8 pop;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 hi = (__bf16)pe[j];
-      pop[j] = lo_col ? (__bf16)(pe[j] - (float)hi) : hi;
-    }
-    // V operand element mask for the boundary tiles (poison rows -> 0).
-    uint4 vmask = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
-    if (need_mask) {
-      uint32_t mw[4];
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2)
-        mw[k2] = (((vkeep >> (2 * k2)) & 1u) ? 0x0000FFFFu : 0u) |
-                 (((vkeep >> (2 * k2 + 1)) & 1u) ? 0xFFFF0000u : 0u);
-      vmask = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-    }
-    // ---- P*V: one k=32 MFMA per 16-dim block, then fold into acc ----------
+    // ---- P*V: TP/2 chained k=32 MFMAs per 16-dim block (level 1, FP32),
+    // folded into the running accumulator after the rescale (level 2) -------
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
-      uint4 vb;
-      if constexpr (FP8) {
-        const int i = blk / 4, ep = blk % 4;
-        const uint4 wa = tl.v[0][i], wb = tl.v[1][i];
-        const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
-        const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
-        vb = __builtin_bit_cast(uint4, cat(e4m3x4_to_bf16x4(da), e4m3x4_to_bf16x4(db)));
-      } else {
-        const int i = blk / 2, ep = blk % 2;
-        const uint4 wa = tl.v[0][i], wb = tl.v[1][i];
-        vb = ep == 0 ? make_uint4(wa.x, wa.y, wb.x, wb.y) : make_uint4(wa.z, wa.w, wb.z, wb.w);
+      f32x4 part_o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int pp = 0; pp < TP / 2; ++pp) {
+        uint4 vb;
+        if constexpr (FP8) {
+          const int i = blk / 4, ep = blk % 4;
+          const uint4 wa = tl.v[2 * pp][i], wb = tl.v[2 * pp + 1][i];
+          const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
+          const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
+          vb = __builtin_bit_cast(uint4, cat(e4m3x4_to_bf16x4(da), e4m3x4_to_bf16x4(db)));
+        } else {
+          const int i = blk / 2, ep = blk % 2;
+          const uint4 wa = tl.v[2 * pp][i], wb = tl.v[2 * pp + 1][i];
+          vb = ep == 0 ? make_uint4(wa.x, wa.y, wb.x, wb.y) : make_uint4(wa.z, wa.w, wb.z, wb.w);
+        }
+        if (need_mask) {
+          // zero the bf16 values of masked rows (poison codes are NaN)
+          const uint32_t kk = vkeep >> (8 * pp);
+          uint32_t mw[4];
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2)
+            mw[k2] = (((kk >> (2 * k2)) & 1u) ? 0x0000FFFFu : 0u) |
+                     (((kk >> (2 * k2 + 1)) & 1u) ? 0xFFFF0000u : 0u);
+          vb.x &= mw[0]; vb.y &= mw[1]; vb.z &= mw[2]; vb.w &= mw[3];
+        }
+        part_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vb), pop[pp], part_o,
+                                                         0, 0, 0);
       }
-      if (need_mask) {
-        vb.x &= vmask.x; vb.y &= vmask.y; vb.z &= vmask.z; vb.w &= vmask.w;
-      }
-      const f32x4 part_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          bits_to_bf16x8(vb), pop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[blk][e] = acc[blk][e] * alpha + part_o[e];
     }
   };
 
-  const int ntiles = (npages + 1) / 2;
-  // Two register buffers (the next tile's loads in flight while the current
-  // one is computed) when a tile is at most 32 VGPRs; larger tiles (bf16
-  // D >= 128, fp8 D = 256) use one buffer to stay clear of spills.
-  constexpr bool kDoubleBuffer = NI * 2 * 2 * 4 <= 32;
-  Tile ta, tb;
-  if constexpr (kDoubleBuffer) {
-    if (ntiles > 0) load_tile(0, ta);
-    for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) load_tile(t + 1, tb);
-      compute_tile(t, ta);
+  const int ntiles = (npages + TP - 1) / TP;
+  // Register ring of RING tiles: RING - 1 tiles are in flight while one is
+  // computed.
+  if constexpr (RING == 3) {
+    Tile t0, t1, t2;
+    if (ntiles > 0) load_tile(0, t0);
+    if (ntiles > 1) load_tile(1, t1);
+    for (int t = 0; t < ntiles; t += 3) {
+      if (t + 2 < ntiles) load_tile(t + 2, t2);
+      compute_tile(t, t0);
       if (t + 1 >= ntiles) break;
-      if (t + 2 < ntiles) load_tile(t + 2, ta);
-      compute_tile(t + 1, tb);
+      if (t + 3 < ntiles) load_tile(t + 3, t0);
+      compute_tile(t + 1, t1);
+      if (t + 2 >= ntiles) break;
+      if (t + 4 < ntiles) load_tile(t + 4, t1);
+      compute_tile(t + 2, t2);
+    }
+  } else if constexpr (RING == 2) {
+    Tile t0, t1;
+    if (ntiles > 0) load_tile(0, t0);
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) load_tile(t + 1, t1);
+      compute_tile(t, t0);
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) load_tile(t + 2, t0);
+      compute_tile(t + 1, t1);
     }
   } else {
-    (void)tb;
+    Tile t0;
     for (int t = 0; t < ntiles; ++t) {
-      load_tile(t, ta);
-      compute_tile(t, ta);
+      load_tile(t, t0);
+      compute_tile(t, t0);
     }
   }
 
@@ -368,13 +385,34 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 
 // Merge the partitions of one (sequence, query head):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = s_v * sum_j w_j o_j / sum_j w_j l_j
-// One thread per head dimension.
+// kReduceThreads threads: the maxima, weights and the normaliser are reduced
+// over partitions cooperatively; the weighted sum of the partial outputs runs
+// as (dim, partition group) pairs so that every partial row is read once, in
+// parallel, and the groups are added through LDS.
+constexpr int kReduceThreads = 512;
+constexpr int kReduceWeightsLds = 4096;   // partitions whose weight is cached in LDS
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+  for (int off = kWave / 2; off > 0; off /= 2) {
+    const float o = __shfl_xor(v, off);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  __syncthreads();                       // red[] may still be read by a previous call
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x / kWave); ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
+__global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(
     const DecodeParams p, int part_pages) {
+  constexpr int NG = kReduceThreads / D;  // partition groups
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const int h = hq / p.group;
   const PartitionRange pr = partition_range(p, b, part_pages);
   const int np = pr.num_parts_b;
@@ -383,54 +421,98 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(
   const float* ls = p.ws_l + row * p.num_parts;
   const float* os = p.ws_o + row * p.num_parts * D;
 
-  float M = -INFINITY;
-  for (int j = 0; j < np; ++j) M = fmaxf(M, ms[j]);
-  float o = 0.0f, l = 0.0f;
-  if (M != -INFINITY) {
-    int j = 0;
-    for (; j + 4 <= np; j += 4) {
-      float w[4], ov[4], lv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        w[u] = __builtin_amdgcn_exp2f(ms[j + u] - M);
-        ov[u] = os[(int64_t)(j + u) * D + d];
-        lv[u] = ls[j + u];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        o += w[u] * ov[u];
-        l += w[u] * lv[u];
-      }
-    }
-    for (; j < np; ++j) {
-      const float w = __builtin_amdgcn_exp2f(ms[j] - M);
-      o += w * os[(int64_t)j * D + d];
-      l += w * ls[j];
-    }
+  __shared__ float red[kReduceThreads / kWave];
+  __shared__ float w_s[kReduceWeightsLds];
+  __shared__ float o_s[NG][D];
+
+  float m = -INFINITY;
+  for (int j = tid; j < np; j += kReduceThreads) m = fmaxf(m, ms[j]);
+  const float M = block_reduce(m, true, red);
+  float lsum = 0.0f;
+  for (int j = tid; j < np; j += kReduceThreads) {
+    const float w = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[j] - M);
+    if (j < kReduceWeightsLds) w_s[j] = w;
+    lsum += w * ls[j];
   }
-  const float vs = p.v_scale ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
-  const float r = l > 0.0f ? o / l * vs : 0.0f;
-  if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
-  else reinterpret_cast<float*>(p.out)[row * D + d] = r;
+  const float L = block_reduce(lsum, false, red);   // its barriers publish w_s
+
+  const int d = tid % D, grp = tid / D;
+  float acc = 0.0f;
+  int j = grp;
+  for (; j + 3 * NG < np; j += 4 * NG) {
+    float w[4], o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int jj = j + u * NG;
+      w[u] = jj < kReduceWeightsLds ? w_s[jj] : __builtin_amdgcn_exp2f(ms[jj] - M);
+      o[u] = os[(int64_t)jj * D + d];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += w[u] * o[u];
+  }
+  for (; j < np; j += NG) {
+    const float w = j < kReduceWeightsLds ? w_s[j] : __builtin_amdgcn_exp2f(ms[j] - M);
+    acc += w * os[(int64_t)j * D + d];
+  }
+  o_s[grp][d] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    float o = 0.0f;
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) o += o_s[g2][d];
+    const float vs = p.v_scale ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
+    const float r = L > 0.0f ? o / L * vs : 0.0f;
+    if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
+    else reinterpret_cast<float*>(p.out)[row * D + d] = r;
+  }
 }
 
-template <int D, bool FP8>
-static hipError_t launch_typed(const DecodeParams& p, int num_seqs, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after) {
+template <int D, bool FP8, int TP, int RING>
+static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_t stream,
+                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NW = kSplitWaves;
   const dim3 grid((unsigned)p.num_parts, (unsigned)p.num_kv_heads, (unsigned)num_seqs);
-  if (ev_before) (void)hipEventRecord(ev_before, stream);
-  hipLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW>), grid, dim3(NW * kWave), 0,
-                     stream, p);
+  if (ev_before && ev_after) {
+    // the events take the kernel's own start and end timestamps
+    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING>), grid,
+                          dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
+  } else {
+    hipLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING>), grid,
+                       dim3(NW * kWave), 0, stream, p);
+  }
   hipError_t err = hipGetLastError();
-  if (ev_after) (void)hipEventRecord(ev_after, stream);
   if (err != hipSuccess || p.direct) return err;
   DecodeParams pr = p;
   if (!FP8) pr.v_scale = nullptr;
   hipLaunchKernelGGL((paged_decode_reduce_kernel<D>),
-                     dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(D), 0, stream,
-                     pr, NW * p.pages_per_wave);
+                     dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(kReduceThreads), 0,
+                     stream, pr, NW * p.pages_per_wave);
   return hipGetLastError();
+}
+
+// Tile shape of the split kernel: TP pages per tile, RING register buffers.
+// Default: 2-page tiles with one tile in flight (fp8 D <= 128, bf16 D = 64;
+// the fastest shape measured on MI355X at 32k-128k), one buffer for the large
+// tiles of bf16 D >= 128 and fp8 D = 256. KVFP8_SPLIT_VARIANT=TPxRING (2x1,
+// 2x2, 2x3, 4x1, 4x2) overrides it for tuning sweeps.
+template <int D, bool FP8>
+static hipError_t launch_typed(const DecodeParams& p, int num_seqs, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after) {
+  int tp = 2, ring = (FP8 ? D <= 128 : D <= 64) ? 2 : 1;
+  if (const char* env = getenv("KVFP8_SPLIT_VARIANT")) {
+    int a = 0, c = 0;
+    if (sscanf(env, "%dx%d", &a, &c) == 2) { tp = a; ring = c; }
+  }
+#define KVFP8_VARIANT(TP_, RING_)                                                    \
+  if (tp == TP_ && ring == RING_)                                                    \
+    return launch_variant<D, FP8, TP_, RING_>(p, num_seqs, stream, ev_before, ev_after);
+  KVFP8_VARIANT(2, 1)
+  KVFP8_VARIANT(2, 2)
+  KVFP8_VARIANT(2, 3)
+  KVFP8_VARIANT(4, 1)
+  KVFP8_VARIANT(4, 2)
+#undef KVFP8_VARIANT
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,

@@ -377,3 +377,28 @@ def test_full_gptoss_hybrid_32k():
     gs = GpuLayer(case, fp8=False, window=128)
     os_ = OracleLayer(case, fp8=False, window=128)
     check_attention(gs, os_, "gptoss-sw128-bf16-32k")
+
+
+VARIANTS = ["2x1", "2x2", "2x3", "4x1", "4x2"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_attention_every_tile_variant(variant, monkeypatch):
+    # every compiled (pages per tile x register ring) shape of the split
+    # kernel, on ragged lengths, a window and both cache dtypes
+    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+    for D, fp8, window, lens in ((128, True, 0, [1000, 37, 1]), (64, True, 50, [700, 129]),
+                                 (128, False, 0, [515, 64]), (256, True, 0, [333]),
+                                 (256, False, 21, [300, 16])):
+        if D == 256 and variant in ("2x3", "4x2"):
+            continue                   # these shapes spill at head_dim 256
+        label = f"variant {variant} D={D} fp8={fp8} window={window}"
+        say(label)
+        case = synth.decode_case(80, 4 * (D // 64), D // 64, D, lens, shuffle=True,
+                                 spare_frac=0.2)
+        g = GpuLayer(case, fp8=fp8, window=window)
+        o = OracleLayer(case, fp8=fp8, window=window)
+        check_attention(g, o, label)
+        monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", "3")
+        check_attention(g, o, label + " ppw=3")
+        monkeypatch.delenv("KVFP8_PAGES_PER_WAVE")
