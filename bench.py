@@ -60,8 +60,9 @@ class LayerStack:
     over L positions."""
 
     def __init__(self, kv, torch, B, Hq, Hkv, D, lens, NL, cache_dtype="fp8_e4m3",
-                 window=0, shuffle=False, spare_frac=0.0, seed=0, dtypes=None):
+                 window=0, shuffle=False, spare_frac=0.0, seed=0, dtypes=None, path="fused"):
         self.kv, self.torch = kv, torch
+        self.path = path
         dev = torch.device("cuda:0")
         self.dev = dev
         self.B, self.Hq, self.Hkv, self.D = B, Hq, Hkv, D
@@ -126,14 +127,23 @@ class LayerStack:
         torch.cuda.synchronize()
 
     def step(self):
+        """One decode step of every layer: the new token's cache write, then
+        the attention. path "fused": one kvq_decode_step call per layer (the
+        split kernel does the write); "separate": kvq_kv_cache_write then
+        kvq_paged_decode_attention."""
         kv = self.kv
         for ly in self.layers:
             d = ly["desc"]
-            kv.kv_cache_write(d, ly["k_new"], ly["v_new"], self.new_slots, ly["kc"], ly["vc"],
-                              ly["ks"], ly["vs"])
-            kv.paged_decode_attention(d, ly["out"], ly["q"], ly["kc"], ly["vc"],
-                                      self.block_tables, self.context_lens, self.max_len,
-                                      ly["ks"], ly["vs"], ly["ws"])
+            if self.path == "fused":
+                kv.decode_step(d, ly["k_new"], ly["v_new"], ly["kc"], ly["vc"], ly["out"], ly["q"],
+                               self.block_tables, self.context_lens, self.max_len, ly["ks"],
+                               ly["vs"], ly["ws"])
+            else:
+                kv.kv_cache_write(d, ly["k_new"], ly["v_new"], self.new_slots, ly["kc"],
+                                  ly["vc"], ly["ks"], ly["vs"])
+                kv.paged_decode_attention(d, ly["out"], ly["q"], ly["kc"], ly["vc"],
+                                          self.block_tables, self.context_lens, self.max_len,
+                                          ly["ks"], ly["vs"], ly["ws"])
 
     # ---- algorithmic byte model (per layer) -------------------------------
     def attended(self, desc):
@@ -151,11 +161,14 @@ class LayerStack:
         sc = 2 * self.Hkv * 4 if desc.fp8 else 0
         return self.kv_bytes(desc) + self.B * self.Hq * self.D * 2 + bt + sc
 
+    def write_bytes(self, desc):
+        """The cache write of the new tokens: bf16 K/V in, cache rows out."""
+        return self.B * self.Hkv * self.D * 2 * (2 + desc.elem_bytes)
+
     def step_bytes(self, desc):
         """Whole layer step: attention (K/V, q, out, block table, scales) plus
-        the cache write of the new tokens (bf16 in, cache rows out)."""
-        write = self.B * self.Hkv * self.D * 2 * (2 + desc.elem_bytes)
-        return self.split_bytes(desc) + self.B * self.Hq * self.D * 4 + write
+        the cache write of the new tokens."""
+        return self.split_bytes(desc) + self.B * self.Hq * self.D * 4 + self.write_bytes(desc)
 
     def total_step_bytes(self):
         return sum(self.step_bytes(ly["desc"]) for ly in self.layers)
@@ -330,6 +343,8 @@ def main():
     ap.add_argument("--context", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cache", default="fp8_e4m3", choices=["fp8_e4m3", "bf16"])
+    ap.add_argument("--path", default="fused", choices=["fused", "separate"],
+                    help="fused: kvq_decode_step per layer; separate: write + attention calls")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=10)
@@ -373,30 +388,36 @@ def main():
         import synth
         lens = [int(x) for x in synth.batched_lens()]
         stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], lens, NL, args.cache,
-                           shuffle=True, spare_frac=0.1, seed=3)
+                           shuffle=True, spare_frac=0.1, seed=3, path=args.path)
         ctx_desc = f"lengths {min(lens)}..{max(lens)} (sum {sum(lens)})"
     elif args.workload == "gptoss":
         dts = ["fp8_e4m3" if i % 2 == 0 else "bf16" for i in range(NL)]
         wins = [0 if i % 2 == 0 else 128 for i in range(NL)]
         stack = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, seed=5,
-                           dtypes=dts, window=wins)
+                           dtypes=dts, window=wins, path=args.path)
         ctx_desc = f"context {ctx}; {NL // 2} full fp8 layers + {NL - NL // 2} SW-128 bf16 layers"
     else:
         stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], [ctx], NL, args.cache,
-                           seed=1)
+                           seed=1, path=args.path)
         ctx_desc = f"context {ctx}"
     log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}")
     # the timed region: K steps, each one replay of the captured decode step
     ms = time_steps_graph(torch, stack, args.steps, args.warmup)
     # eager steps with the split kernel's launches timed by the library
     ms_eager, split_ms, nsplit = time_steps(torch, kv, stack, args.steps, args.warmup)
+    # the other path, for comparison (graph-replayed too)
+    other = "separate" if args.path == "fused" else "fused"
+    stack.path = other
+    ms_other = time_steps_graph(torch, stack, args.steps, args.warmup)
+    stack.path = args.path
     step_bytes = stack.total_step_bytes()
     value = step_bytes / (ms * 1e-3) / 1e9
     kv_gbs = stack.total_kv_bytes() / (ms * 1e-3) / 1e9
     d0 = stack.layers[0]["desc"]
-    split_bytes = stack.split_bytes(d0)
+    split_bytes = stack.split_bytes(d0) + (stack.write_bytes(d0) if args.path == "fused" else 0)
     achieved = split_bytes / (split_ms * 1e-3) / 1e9 if split_ms else None
-    log(f"headline: {ms:.3f} ms/step (graph; eager {ms_eager:.3f}), {ms * 1e3 / NL:.2f} us/layer, {value:.1f} GB/s "
+    log(f"headline ({args.path}): {ms:.3f} ms/step (graph; eager {ms_eager:.3f}; {other} path "
+        f"{ms_other:.3f}), {ms * 1e3 / NL:.2f} us/layer, {value:.1f} GB/s "
         f"(KV {kv_gbs:.1f} GB/s), split kernel {split_ms * 1e3 if split_ms else 0:.2f} us "
         f"-> {achieved or 0:.1f} GB/s")
 
@@ -416,13 +437,16 @@ def main():
         "data": "synthetic (seeded normal K/V/q)",
         "config": {
             "workload": f"{w['desc']}, {ctx_desc}, {args.cache} cache with per-KV-head scales, "
-                        f"{NL} layers per step (kv_cache_write of the new token + paged decode "
-                        f"attention per layer)",
+                        f"{NL} layers per step (per layer: the new token's cache write + paged "
+                        f"decode attention, " + ("one kvq_decode_step call" if args.path == "fused"
+                        else "kvq_kv_cache_write + kvq_paged_decode_attention") + ")",
+            "path": args.path,
             "batch": w["B"], "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": w["D"],
             "page_size": 16, "layers_per_step": NL, "parallelism": "single GPU",
         },
         "timing": "each step is one replay of the decode step captured as a HIP graph",
         "ms_per_step_eager": round(ms_eager, 5),
+        f"ms_per_step_{other}_path": round(ms_other, 5),
         "us_per_layer_step": round(ms * 1e3 / NL, 3),
         "kv_gbs": round(kv_gbs, 2),
         "kv_frac_of_hbm_peak": round(kv_gbs / HBM_PEAK_GBS, 4),
@@ -433,7 +457,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-            "traffic": measured_traffic(f"{args.workload}:{ctx}:{args.cache}:{NL}")
+            "traffic": measured_traffic(f"{args.workload}:{ctx}:{args.cache}:{NL}:{args.path}")
             if args.workload == "llama8b" else None,
             "launch_us": round(split_ms * 1e3, 3) if split_ms else None,
             "launches_timed": nsplit,

@@ -79,13 +79,15 @@ def lib():
         L.kvq_decode_workspace_bytes.argtypes = [dp, i32, i32, ctypes.POINTER(sz)]
         L.kvq_paged_decode_attention.argtypes = [dp, vp, i32, vp, vp, vp, i64, vp, i32, vp,
                                                  i32, i32, vp, vp, vp, sz, vp]
+        L.kvq_decode_step.argtypes = [dp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, vp, i32,
+                                      i32, vp, vp, vp, sz, vp]
         L.kvq_kv_scale_from_amax.argtypes = [dp, vp, i64, vp, vp]
         L.kvq_e4m3_quantize.argtypes = [vp, i64, vp, vp, vp]
         L.kvq_status_string.argtypes = [i32]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_profile_begin.argtypes = [i32]
         L.kvq_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
-        for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes",
+        for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes", "kvq_decode_step",
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
                   "kvq_e4m3_quantize", "kvq_profile_begin", "kvq_profile_end"):
             getattr(L, f).restype = ctypes.c_int
@@ -171,12 +173,8 @@ def alloc_workspace(desc, num_seqs, max_context_len, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def paged_decode_attention(desc, out, q, k_cache, v_cache, block_tables,
-                           context_lens, max_context_len, k_scale=None,
-                           v_scale=None, workspace=None, stream=None):
-    """out: float32 or bf16 [B, Hq, D]; q: bf16 [B, Hq, D]; block_tables:
-    int32 [B, max_pages]; context_lens: int32 [B]; max_context_len: host int
-    bound of context_lens (sizes the split plan)."""
+def _decode_checks(desc, out, q, k_cache, v_cache, block_tables, context_lens, k_scale,
+                   v_scale, workspace):
     import torch
     _need(out, "out")
     _need(q, "q", torch.bfloat16)
@@ -200,11 +198,43 @@ def paged_decode_attention(desc, out, q, k_cache, v_cache, block_tables,
         raise ValueError("block_tables must be [B, max_pages], context_lens [B]")
     num_pages = k_cache.numel() * k_cache.element_size() // (desc.num_kv_heads * desc.page_bytes)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return out_dtype, num_pages, ws_bytes
+
+
+def paged_decode_attention(desc, out, q, k_cache, v_cache, block_tables,
+                           context_lens, max_context_len, k_scale=None,
+                           v_scale=None, workspace=None, stream=None):
+    """out: float32 or bf16 [B, Hq, D]; q: bf16 [B, Hq, D]; block_tables:
+    int32 [B, max_pages]; context_lens: int32 [B]; max_context_len: host int
+    bound of context_lens (sizes the split plan)."""
+    out_dtype, num_pages, ws_bytes = _decode_checks(desc, out, q, k_cache, v_cache, block_tables,
+                                                    context_lens, k_scale, v_scale, workspace)
     _check("kvq_paged_decode_attention", lib().kvq_paged_decode_attention(
         ctypes.byref(desc), _ptr(out), out_dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache),
-        num_pages, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
+        num_pages, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0],
         int(max_context_len), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def decode_step(desc, k_new, v_new, k_cache, v_cache, out, q, block_tables,
+                context_lens, max_context_len, k_scale=None, v_scale=None,
+                workspace=None, stream=None):
+    """Write every sequence's newest token (k_new, v_new: bf16 [B, Hkv, D],
+    position context_lens[b] - 1) and attend, in one call: the same results
+    as kv_cache_write followed by paged_decode_attention."""
+    import torch
+    _need(k_new, "k_new", torch.bfloat16)
+    _need(v_new, "v_new", torch.bfloat16)
+    B = q.shape[0]
+    if tuple(k_new.shape) != (B, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new, v_new must be [B, Hkv, D]")
+    out_dtype, num_pages, ws_bytes = _decode_checks(desc, out, q, k_cache, v_cache, block_tables,
+                                                    context_lens, k_scale, v_scale, workspace)
+    _check("kvq_decode_step", lib().kvq_decode_step(
+        ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), num_pages,
+        _ptr(out), out_dtype, _ptr(q), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, int(max_context_len), _ptr(k_scale), _ptr(v_scale),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def kv_scale_from_amax(desc, x, scale_out, stream=None):

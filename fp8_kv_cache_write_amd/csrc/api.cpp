@@ -66,9 +66,10 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Split-context plan. Pages of one (sequence, KV head) are cut into
 // partitions of kSplitWaves * pages_per_wave pages; each partition is one
 // work-group, each wave streams pages_per_wave pages. Measured on MI355X,
-// long runs per wave beat many concurrent waves: pages_per_wave is the power
-// of two that gives about one wave per SIMD for fp8 (about two for bf16,
-// whose pages are twice as large), in [2, 64]. When one partition per
+// long runs per wave beat many concurrent waves, and all waves should be
+// resident at once: pages_per_wave (even, in [2, 64]) divides the pages so
+// that there are about 1.5 waves per SIMD for fp8 (about two for bf16, whose
+// pages are twice as large). When one partition per
 // sequence is cheap enough (short contexts, sliding windows) the split kernel
 // writes the output itself and the reduce kernel is skipped.
 Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
@@ -77,11 +78,10 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
   if (W > 0) pages_max = std::min<int64_t>(pages_max, ((int64_t)W + 15) / 16 + 1);
   if (pages_max < 1) pages_max = 1;
   const int64_t total = (int64_t)std::max(num_seqs, 1) * d->num_kv_heads * pages_max;
-  const int64_t waves_per_cu = d->cache_dtype == KVQ_FP8_E4M3 ? 4 : 8;
+  const int64_t waves_per_cu = d->cache_dtype == KVQ_FP8_E4M3 ? 6 : 8;
   const int64_t target_waves = (int64_t)cu_count() * waves_per_cu;
-  const int64_t want = (total + target_waves - 1) / target_waves;
-  int64_t ppw = 2;
-  while (ppw < want && ppw < kMaxPagesPerWave) ppw *= 2;
+  int64_t ppw = (total + target_waves - 1) / target_waves;
+  ppw = std::min<int64_t>(std::max<int64_t>((ppw + 1) / 2 * 2, 2), kMaxPagesPerWave);
   int64_t direct_ppw = (pages_max + kSplitWaves - 1) / kSplitWaves;
   direct_ppw = (direct_ppw + 1) / 2 * 2;
   if (direct_ppw <= std::max<int64_t>(ppw, 8)) ppw = direct_ppw;
@@ -163,13 +163,17 @@ int kvq_decode_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
   return KVQ_OK;
 }
 
-int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out, int32_t out_dtype,
-                               const void* q, const void* k_cache, const void* v_cache,
-                               int64_t num_pages, const int32_t* block_tables,
-                               int32_t max_pages_per_seq, const int32_t* context_lens,
-                               int32_t num_seqs, int32_t max_context_len,
-                               const float* k_scale, const float* v_scale, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared by the attention call and the fused decode step: host checks, the
+// plan, the launch.
+int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, const void* q,
+                  const void* k_cache, const void* v_cache, int64_t num_pages,
+                  const int32_t* block_tables, int32_t max_pages_per_seq,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                  const float* k_scale, const float* v_scale, void* workspace,
+                  size_t workspace_bytes, const void* k_new, const void* v_new, bool fused,
+                  void* stream) {
   int st = check_desc(desc);
   if (st) return st;
   if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16) return KVQ_ERR_INVALID_ARG;
@@ -184,7 +188,10 @@ int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out, int32_t ou
     return KVQ_ERR_INVALID_ARG;
   if (max_pages_per_seq > 0 && (!block_tables || !aligned(block_tables, 4)))
     return KVQ_ERR_INVALID_ARG;
-  if (max_context_len > 0 && (!k_cache || !v_cache || !aligned(k_cache, 16) || !aligned(v_cache, 16)))
+  if ((max_context_len > 0 || fused) &&
+      (!k_cache || !v_cache || !aligned(k_cache, 16) || !aligned(v_cache, 16)))
+    return KVQ_ERR_INVALID_ARG;
+  if (fused && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
     return KVQ_ERR_INVALID_ARG;
   const bool fp8 = desc->cache_dtype == KVQ_FP8_E4M3;
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
@@ -208,6 +215,8 @@ int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out, int32_t ou
   p.ws_l = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
   p.ws_o = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_o) : nullptr;
   p.out = out;
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
   p.num_q_heads = desc->num_q_heads;
   p.num_kv_heads = desc->num_kv_heads;
   p.group = desc->num_q_heads / desc->num_kv_heads;
@@ -228,9 +237,34 @@ int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out, int32_t ou
     e1 = g_prof.ev[2 * g_prof.used + 1];
     g_prof.used++;
   }
-  hipError_t e = launch_paged_decode(p, desc->head_dim, fp8, num_seqs,
+  hipError_t e = launch_paged_decode(p, desc->head_dim, fp8, num_seqs, fused,
                                      static_cast<hipStream_t>(stream), e0, e1);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out, int32_t out_dtype,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               int64_t num_pages, const int32_t* block_tables,
+                               int32_t max_pages_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t max_context_len,
+                               const float* k_scale, const float* v_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return decode_common(desc, out, out_dtype, q, k_cache, v_cache, num_pages, block_tables,
+                       max_pages_per_seq, context_lens, num_seqs, max_context_len, k_scale,
+                       v_scale, workspace, workspace_bytes, nullptr, nullptr, false, stream);
+}
+
+int kvq_decode_step(const kvq_layer_desc* desc, const void* k_new, const void* v_new,
+                    void* k_cache, void* v_cache, int64_t num_pages, void* out,
+                    int32_t out_dtype, const void* q, const int32_t* block_tables,
+                    int32_t max_pages_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_context_len, const float* k_scale, const float* v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(desc, out, out_dtype, q, k_cache, v_cache, num_pages, block_tables,
+                       max_pages_per_seq, context_lens, num_seqs, max_context_len, k_scale,
+                       v_scale, workspace, workspace_bytes, k_new, v_new, true, stream);
 }
 
 int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x, int64_t num_tokens,

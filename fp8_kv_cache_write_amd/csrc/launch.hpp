@@ -35,6 +35,8 @@ struct DecodeParams {
   float* ws_l;                   // [B][Hq][num_parts]
   float* ws_o;                   // [B][Hq][num_parts][D]
   void* out;                     // [B][Hq][D] f32 or bf16
+  const uint16_t* k_new;         // fused decode step only: bf16 [B][Hkv][D] of the
+  const uint16_t* v_new;         //   token at position L-1 of every sequence
   int num_q_heads;
   int num_kv_heads;
   int group;                     // G = Hq / Hkv, <= 8
@@ -51,8 +53,10 @@ struct DecodeParams {
 // Waves per work-group of the split kernel.
 constexpr int kSplitWaves = 4;
 
+// fused = true: the split kernel also writes k_new / v_new into the caches at
+// position L-1 of every sequence (p.k_cache / p.v_cache must be writable).
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,
-                               int num_seqs, hipStream_t stream,
+                               int num_seqs, bool fused, hipStream_t stream,
                                hipEvent_t ev_before, hipEvent_t ev_after);
 
 }  // namespace kvfp8

@@ -34,6 +34,14 @@
 
 namespace kvfp8 {
 
+// K/V pages are read exactly once per step: non-temporal loads keep them
+// from displacing other lines in the caches (measured on MI355X: bf16 pages
+// 97 -> 87 us, fp8 54 -> 52 us at 131072 positions).
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
+}
+
 __device__ __forceinline__ float wave_max_col(float x) {
   // lanes c, c+16, c+32, c+48 hold the same MFMA column
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -71,7 +79,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   return r;
 }
 
-template <int D, bool FP8, int NW, int TP, int RING>
+template <int D, bool FP8, int NW, int TP, int RING, bool FUSED>
 __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const DecodeParams p) {
   constexpr int E = FP8 ? 1 : 2;
@@ -143,6 +151,81 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
   const float c_log2 = ks * p.sm_scale_log2;
 
+  // ---- fused decode step: the cache write of position L-1 -----------------
+  // Exactly one wave streams the page that holds the newest position of this
+  // (sequence, KV head). That wave quantises the new K and V rows (the same
+  // arithmetic as the cache-write kernel), stores them into the cache and
+  // keeps the stored bytes in LDS; when it reaches that page it patches them
+  // into its tile registers. No other wave reads that page, so no ordering
+  // across waves is needed, and the page load never has to observe the store.
+  __shared__ __align__(16) uint8_t new_rows[FUSED ? 2 * D * E : 16];
+  int t_new = -1, pg_new = 0, r_new = 0;
+  int idx_new = -1;
+  if constexpr (FUSED) {
+    const int pos = pr.L - 1;
+    const int pn = pos >= 0 ? pos / kPage : -1;
+    if (pn >= wbeg && pn < wend && !((bad_pages >> (pn - wbeg)) & 1ull)) {
+      idx_new = pn - wbeg;
+      t_new = idx_new / TP;
+      pg_new = idx_new % TP;
+      r_new = pos % kPage;
+    }
+  }
+  // The owning wave issues the loads of the new rows before its first tiles'
+  // loads (lane j < D/8 holds dims 8j..8j+7 of K and of V) and quantises,
+  // stores and stages them right after: memory operations retire in order,
+  // so waiting for the rows does not wait for the tiles, and the conversion
+  // overlaps their latency.
+  uint4 kx_new = make_uint4(0u, 0u, 0u, 0u), vx_new = make_uint4(0u, 0u, 0u, 0u);
+  auto fused_prefetch = [&]() {
+    if constexpr (FUSED) {
+      if (t_new < 0 || lane >= D / 8) return;
+      const int64_t src = ((int64_t)b * p.num_kv_heads + h) * D + 8 * lane;
+      kx_new = *reinterpret_cast<const uint4*>(p.k_new + src);
+      vx_new = *reinterpret_cast<const uint4*>(p.v_new + src);
+    }
+  };
+  auto fused_commit = [&]() {
+    if constexpr (FUSED) {
+      const int pid = __builtin_amdgcn_readlane(my_page, idx_new);
+      uint8_t* kblk = const_cast<uint8_t*>(p.k_cache) + ((int64_t)pid * p.num_kv_heads + h) * PB;
+      uint8_t* vblk = const_cast<uint8_t*>(p.v_cache) + ((int64_t)pid * p.num_kv_heads + h) * PB;
+      const int j = lane;
+      if (j < D / 8) {
+        const uint4 kx = kx_new, vx = vx_new;
+        if constexpr (FP8) {
+          const float sk = p.k_scale[p.scale_per_head ? h : 0];
+          const float sv = p.v_scale[p.scale_per_head ? h : 0];
+          const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w};
+          const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+          uint32_t kq[2] = {0u, 0u}, vq[2] = {0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t kb = (kw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+            const uint32_t vb = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+            kq[e / 4] |= e4m3_encode_sat(bf16_bits_to_f32(kb) / sk) << (8 * (e % 4));
+            vq[e / 4] |= e4m3_encode_sat(bf16_bits_to_f32(vb) / sv) << (8 * (e % 4));
+          }
+          *reinterpret_cast<uint2*>(new_rows + 8 * j) = make_uint2(kq[0], kq[1]);
+          *reinterpret_cast<uint2*>(new_rows + D + 8 * j) = make_uint2(vq[0], vq[1]);
+          *reinterpret_cast<uint2*>(kblk + k_byte<1>(r_new, 8 * j)) = make_uint2(kq[0], kq[1]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vblk[v_byte<1>(r_new, 8 * j + e)] = (uint8_t)(vq[e / 4] >> (8 * (e % 4)));
+        } else {
+          *reinterpret_cast<uint4*>(new_rows + 16 * j) = kx;
+          *reinterpret_cast<uint4*>(new_rows + 2 * D + 16 * j) = vx;
+          *reinterpret_cast<uint4*>(kblk + k_byte<2>(r_new, 8 * j)) = kx;
+          const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<uint16_t*>(vblk + v_byte<2>(r_new, 8 * j + e)) =
+                (uint16_t)(vw[e / 2] >> (16 * (e % 2)));
+        }
+      }
+    }
+  };
+
   float m_run = -INFINITY;
   float l_run = 0.0f;
   f32x4 acc[NBLK];
@@ -168,8 +251,50 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       const uint4* vp = reinterpret_cast<const uint4*>(vbase + (int64_t)pid * page_stride);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        tl.k[pg][i] = kp[i * kWave + lane];
-        tl.v[pg][i] = vp[i * kWave + lane];
+        tl.k[pg][i] = load_stream(kp + i * kWave + lane);
+        tl.v[pg][i] = load_stream(vp + i * kWave + lane);
+      }
+    }
+  };
+
+  // Replace row r_new of page pg_new in the tile registers by the bytes
+  // stored for the newest position (fused decode step).
+  auto patch_tile = [&](Tile& tl) {
+    const uint8_t* kr = new_rows;
+    const uint8_t* vr = new_rows + D * E;
+#pragma unroll
+    for (int pg = 0; pg < TP; ++pg) {
+      if (pg != pg_new) continue;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        // K: lane (qd, c) holds row c, 16-byte chunk 4i + qd of the row
+        if (c == r_new) tl.k[pg][i] = *reinterpret_cast<const uint4*>(kr + 16 * (4 * i + qd));
+        // V: lane (qd, c) holds rows 4qd..4qd+3 of 16/(4E) dims
+        if (qd == r_new / 4) {
+          uint4 w = tl.v[pg][i];
+          if constexpr (FP8) {
+            const uint32_t nv = *reinterpret_cast<const uint32_t*>(vr + 64 * i + 4 * c);
+            const int sh = 8 * (r_new % 4);
+            const uint32_t m = ~(0xFFu << sh);
+            w.x = (w.x & m) | (((nv >> 0) & 0xFFu) << sh);
+            w.y = (w.y & m) | (((nv >> 8) & 0xFFu) << sh);
+            w.z = (w.z & m) | (((nv >> 16) & 0xFFu) << sh);
+            w.w = (w.w & m) | (((nv >> 24) & 0xFFu) << sh);
+          } else {
+            const uint32_t nv = *reinterpret_cast<const uint32_t*>(vr + 2 * (32 * i + 2 * c));
+            const int sh = 16 * (r_new % 2);
+            const uint32_t m = ~(0xFFFFu << sh);
+            const uint32_t d0 = nv & 0xFFFFu, d1 = nv >> 16;
+            if ((r_new % 4) < 2) {
+              w.x = (w.x & m) | (d0 << sh);
+              w.z = (w.z & m) | (d1 << sh);
+            } else {
+              w.y = (w.y & m) | (d0 << sh);
+              w.w = (w.w & m) | (d1 << sh);
+            }
+          }
+          tl.v[pg][i] = w;
+        }
       }
     }
   };
@@ -293,32 +418,45 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   // computed.
   if constexpr (RING == 3) {
     Tile t0, t1, t2;
+    fused_prefetch();
     if (ntiles > 0) load_tile(0, t0);
     if (ntiles > 1) load_tile(1, t1);
+    if (t_new >= 0) fused_commit();
     for (int t = 0; t < ntiles; t += 3) {
       if (t + 2 < ntiles) load_tile(t + 2, t2);
+      if (FUSED && t == t_new) patch_tile(t0);
       compute_tile(t, t0);
       if (t + 1 >= ntiles) break;
       if (t + 3 < ntiles) load_tile(t + 3, t0);
+      if (FUSED && t + 1 == t_new) patch_tile(t1);
       compute_tile(t + 1, t1);
       if (t + 2 >= ntiles) break;
       if (t + 4 < ntiles) load_tile(t + 4, t1);
+      if (FUSED && t + 2 == t_new) patch_tile(t2);
       compute_tile(t + 2, t2);
     }
   } else if constexpr (RING == 2) {
     Tile t0, t1;
+    fused_prefetch();
     if (ntiles > 0) load_tile(0, t0);
+    if (t_new >= 0) fused_commit();
     for (int t = 0; t < ntiles; t += 2) {
       if (t + 1 < ntiles) load_tile(t + 1, t1);
+      if (FUSED && t == t_new) patch_tile(t0);
       compute_tile(t, t0);
       if (t + 1 >= ntiles) break;
       if (t + 2 < ntiles) load_tile(t + 2, t0);
+      if (FUSED && t + 1 == t_new) patch_tile(t1);
       compute_tile(t + 1, t1);
     }
   } else {
     Tile t0;
+    fused_prefetch();
+    if (ntiles > 0) load_tile(0, t0);
+    if (t_new >= 0) fused_commit();
     for (int t = 0; t < ntiles; ++t) {
-      load_tile(t, t0);
+      if (t > 0) load_tile(t, t0);
+      if (FUSED && t == t_new) patch_tile(t0);
       compute_tile(t, t0);
     }
   }
@@ -385,12 +523,15 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 
 // Merge the partitions of one (sequence, query head):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = s_v * sum_j w_j o_j / sum_j w_j l_j
-// kReduceThreads threads: the maxima, weights and the normaliser are reduced
-// over partitions cooperatively; the weighted sum of the partial outputs runs
-// as (dim, partition group) pairs so that every partial row is read once, in
-// parallel, and the groups are added through LDS.
+// kReduceThreads threads, as (dim d, partition group) pairs. Every global load
+// is issued up front - each thread's first kReducePer partial outputs into
+// registers, the m and l rows into LDS - so the kernel costs one memory round
+// trip plus two block reductions; partitions past the first
+// kReduceThreads / D * kReducePer (very long contexts) are read in a second
+// loop.
 constexpr int kReduceThreads = 512;
-constexpr int kReduceWeightsLds = 4096;   // partitions whose weight is cached in LDS
+constexpr int kReducePer = 8;             // partial outputs per thread held in registers
+constexpr int kReduceLds = 4096;          // partitions whose m/l (then weight) sit in LDS
 
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
   for (int off = kWave / 2; off > 0; off /= 2) {
@@ -422,38 +563,47 @@ __global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(
   const float* os = p.ws_o + row * p.num_parts * D;
 
   __shared__ float red[kReduceThreads / kWave];
-  __shared__ float w_s[kReduceWeightsLds];
+  __shared__ float m_s[kReduceLds];       // m_j, then the weight w_j
+  __shared__ float l_s[kReduceLds];
   __shared__ float o_s[NG][D];
 
+  const int d = tid % D, grp = tid / D;
+  // ---- every load first -----------------------------------------------------
+  float ov[kReducePer];
+#pragma unroll
+  for (int u = 0; u < kReducePer; ++u) {
+    const int jj = grp + u * NG;
+    ov[u] = jj < np ? os[(int64_t)jj * D + d] : 0.0f;
+  }
+  for (int jj = tid; jj < np && jj < kReduceLds; jj += kReduceThreads) {
+    m_s[jj] = ms[jj];
+    l_s[jj] = ls[jj];
+  }
+  // ---- M, weights, normaliser (each thread touches the LDS entries it wrote)
   float m = -INFINITY;
-  for (int j = tid; j < np; j += kReduceThreads) m = fmaxf(m, ms[j]);
+  for (int jj = tid; jj < np; jj += kReduceThreads)
+    m = fmaxf(m, jj < kReduceLds ? m_s[jj] : ms[jj]);
   const float M = block_reduce(m, true, red);
   float lsum = 0.0f;
-  for (int j = tid; j < np; j += kReduceThreads) {
-    const float w = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[j] - M);
-    if (j < kReduceWeightsLds) w_s[j] = w;
-    lsum += w * ls[j];
+  for (int jj = tid; jj < np; jj += kReduceThreads) {
+    const float mj = jj < kReduceLds ? m_s[jj] : ms[jj];
+    const float lj = jj < kReduceLds ? l_s[jj] : ls[jj];
+    const float w = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
+    if (jj < kReduceLds) m_s[jj] = w;
+    lsum += w * lj;
   }
-  const float L = block_reduce(lsum, false, red);   // its barriers publish w_s
-
-  const int d = tid % D, grp = tid / D;
+  const float L = block_reduce(lsum, false, red);   // its barriers publish the weights
+  auto weight = [&](int jj) {
+    return jj < kReduceLds ? m_s[jj] : __builtin_amdgcn_exp2f(ms[jj] - M);
+  };
+  // ---- weighted sum of the partial outputs ---------------------------------
   float acc = 0.0f;
-  int j = grp;
-  for (; j + 3 * NG < np; j += 4 * NG) {
-    float w[4], o[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int jj = j + u * NG;
-      w[u] = jj < kReduceWeightsLds ? w_s[jj] : __builtin_amdgcn_exp2f(ms[jj] - M);
-      o[u] = os[(int64_t)jj * D + d];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc += w[u] * o[u];
+  for (int u = 0; u < kReducePer; ++u) {
+    const int jj = grp + u * NG;
+    if (jj < np) acc += weight(jj) * ov[u];
   }
-  for (; j < np; j += NG) {
-    const float w = j < kReduceWeightsLds ? w_s[j] : __builtin_amdgcn_exp2f(ms[j] - M);
-    acc += w * os[(int64_t)j * D + d];
-  }
+  for (int jj = grp + kReducePer * NG; jj < np; jj += NG) acc += weight(jj) * os[(int64_t)jj * D + d];
   o_s[grp][d] = acc;
   __syncthreads();
   if (grp == 0) {
@@ -467,17 +617,17 @@ __global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(
   }
 }
 
-template <int D, bool FP8, int TP, int RING>
+template <int D, bool FP8, int TP, int RING, bool FUSED>
 static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_t stream,
                                  hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NW = kSplitWaves;
   const dim3 grid((unsigned)p.num_parts, (unsigned)p.num_kv_heads, (unsigned)num_seqs);
   if (ev_before && ev_after) {
     // the events take the kernel's own start and end timestamps
-    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING>), grid,
+    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, FUSED>), grid,
                           dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING>), grid,
+    hipLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, FUSED>), grid,
                        dim3(NW * kWave), 0, stream, p);
   }
   hipError_t err = hipGetLastError();
@@ -491,21 +641,26 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
 }
 
 // Tile shape of the split kernel: TP pages per tile, RING register buffers.
-// Default: 2-page tiles with one tile in flight (fp8 D <= 128, bf16 D = 64;
-// the fastest shape measured on MI355X at 32k-128k), one buffer for the large
-// tiles of bf16 D >= 128 and fp8 D = 256. KVFP8_SPLIT_VARIANT=TPxRING (2x1,
-// 2x2, 2x3, 4x1, 4x2) overrides it for tuning sweeps.
+// Default 2x1: 2-page tiles, loaded and computed one at a time, which keeps
+// the register count low enough for 3 waves per SIMD; with about 1.5 waves
+// per SIMD it was the fastest shape measured on MI355X for the 8B layer at
+// 131072 positions (70.5 % of peak) and for 8 ragged sequences of ~20k
+// (71.4 %), ahead of the prefetching shapes. KVFP8_SPLIT_VARIANT=TPxRING
+// (2x1, 2x2, 2x3, 4x1, 4x2) overrides it for tuning sweeps.
 template <int D, bool FP8>
-static hipError_t launch_typed(const DecodeParams& p, int num_seqs, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after) {
-  int tp = 2, ring = (FP8 ? D <= 128 : D <= 64) ? 2 : 1;
+static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused,
+                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+  int tp = 2, ring = 1;
   if (const char* env = getenv("KVFP8_SPLIT_VARIANT")) {
     int a = 0, c = 0;
     if (sscanf(env, "%dx%d", &a, &c) == 2) { tp = a; ring = c; }
   }
-#define KVFP8_VARIANT(TP_, RING_)                                                    \
-  if (tp == TP_ && ring == RING_)                                                    \
-    return launch_variant<D, FP8, TP_, RING_>(p, num_seqs, stream, ev_before, ev_after);
+#define KVFP8_VARIANT(TP_, RING_)                                                       \
+  if (tp == TP_ && ring == RING_)                                                       \
+    return fused ? launch_variant<D, FP8, TP_, RING_, true>(p, num_seqs, stream, ev_before,   \
+                                                             ev_after)                       \
+                 : launch_variant<D, FP8, TP_, RING_, false>(p, num_seqs, stream, ev_before,  \
+                                                              ev_after);
   KVFP8_VARIANT(2, 1)
   KVFP8_VARIANT(2, 2)
   KVFP8_VARIANT(2, 3)
@@ -516,18 +671,18 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, hipStream_t 
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,
-                               int num_seqs, hipStream_t stream, hipEvent_t ev_before,
-                               hipEvent_t ev_after) {
+                               int num_seqs, bool fused, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after) {
   switch (head_dim) {
     case 64:
-      return fp8 ? launch_typed<64, true>(p, num_seqs, stream, ev_before, ev_after)
-                 : launch_typed<64, false>(p, num_seqs, stream, ev_before, ev_after);
+      return fp8 ? launch_typed<64, true>(p, num_seqs, fused, stream, ev_before, ev_after)
+                 : launch_typed<64, false>(p, num_seqs, fused, stream, ev_before, ev_after);
     case 128:
-      return fp8 ? launch_typed<128, true>(p, num_seqs, stream, ev_before, ev_after)
-                 : launch_typed<128, false>(p, num_seqs, stream, ev_before, ev_after);
+      return fp8 ? launch_typed<128, true>(p, num_seqs, fused, stream, ev_before, ev_after)
+                 : launch_typed<128, false>(p, num_seqs, fused, stream, ev_before, ev_after);
     case 256:
-      return fp8 ? launch_typed<256, true>(p, num_seqs, stream, ev_before, ev_after)
-                 : launch_typed<256, false>(p, num_seqs, stream, ev_before, ev_after);
+      return fp8 ? launch_typed<256, true>(p, num_seqs, fused, stream, ev_before, ev_after)
+                 : launch_typed<256, false>(p, num_seqs, fused, stream, ev_before, ev_after);
     default:
       return hipErrorInvalidValue;
   }

@@ -79,7 +79,7 @@ enum kvq_status {
   KVQ_ERR_INVALID_ARG = -1,       /* null / misaligned pointer, negative size,
                                      inconsistent shapes */
   KVQ_ERR_UNSUPPORTED = -2,       /* head_dim not in {64,128,256}, page size
-                                     not 16, Hq % Hkv != 0, group > 16 */
+                                     not 16, Hq % Hkv != 0, group > 8 */
   KVQ_ERR_WORKSPACE_TOO_SMALL = -3,
   KVQ_ERR_HIP = -4                /* a HIP runtime call or launch failed */
 };
@@ -98,7 +98,7 @@ enum kvq_out_dtype { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 };
 /* Per-layer descriptor. */
 typedef struct kvq_layer_desc {
   int32_t num_q_heads;     /* Hq */
-  int32_t num_kv_heads;    /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 16 */
+  int32_t num_kv_heads;    /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 8 */
   int32_t head_dim;        /* D in {64, 128, 256} */
   int32_t page_size;       /* must be 16 */
   int32_t cache_dtype;     /* enum kvq_dtype */
@@ -177,6 +177,31 @@ int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out,
                                int32_t max_context_len, const float* k_scale,
                                const float* v_scale, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_decode_step - one decode step of a layer in one call: the cache write
+ * of every sequence's newest token followed by the attention, i.e. exactly
+ *     kvq_kv_cache_write(k_new, v_new, slot of position L-1 of each sequence)
+ *     kvq_paged_decode_attention(...)
+ * with L = context_lens[b] (the new token included; sequences with L == 0
+ * write nothing). The slot is block_tables[b][(L-1)/16] * 16 + (L-1) % 16;
+ * an entry outside [0, num_pages) writes nothing. The split kernel does the
+ * write itself (the one wave that streams that page quantises the row,
+ * stores it and uses the stored bytes), which saves the separate write
+ * kernel and its dependency on the decode path of a step. Same results, bit
+ * for bit, as the two calls.
+ *   k_new, v_new  device bf16 [B][Hkv][D]
+ *   k_cache, v_cache  writable caches (layout above)
+ *   all other arguments as for kvq_paged_decode_attention
+ */
+int kvq_decode_step(const kvq_layer_desc* desc, const void* k_new,
+                    const void* v_new, void* k_cache, void* v_cache,
+                    int64_t num_pages, void* out, int32_t out_dtype,
+                    const void* q, const int32_t* block_tables,
+                    int32_t max_pages_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t max_context_len,
+                    const float* k_scale, const float* v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kvq_kv_scale_from_amax - static scale calibration of one layer tensor:

@@ -402,3 +402,105 @@ def test_attention_every_tile_variant(variant, monkeypatch):
         monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", "3")
         check_attention(g, o, label + " ppw=3")
         monkeypatch.delenv("KVFP8_PAGES_PER_WAVE")
+
+
+# ------------------------------------------------------ fused decode step ---
+def split_newest(case):
+    """(case holding every position but each sequence's newest, rows of the
+    newest positions in case order)."""
+    import copy
+    ends = np.cumsum(case.lens.astype(np.int64))
+    newest = [int(e) - 1 for e, L in zip(ends, case.lens) if L > 0]
+    keep = np.ones(case.slots.size, bool)
+    keep[newest] = False
+    pre = copy.copy(case)
+    pre.k_new, pre.v_new, pre.slots = case.k_new[keep], case.v_new[keep], case.slots[keep]
+    return pre
+
+
+def newest_rows(case):
+    """bf16 [B][Hkv][D] of every sequence's newest position (zeros when the
+    sequence is empty)."""
+    B, H, D = case.num_seqs, case.num_kv_heads, case.head_dim
+    k = np.zeros((B, H, D), np.uint16)
+    v = np.zeros((B, H, D), np.uint16)
+    ends = np.cumsum(case.lens.astype(np.int64))
+    for b, (e, L) in enumerate(zip(ends, case.lens)):
+        if L > 0:
+            k[b], v[b] = case.k_new[e - 1], case.v_new[e - 1]
+    return k, v
+
+
+def run_decode_step(g, case, knew, vnew, out_dtype=torch.float32):
+    out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=out_dtype,
+                      device=dev())
+    ws = kv.alloc_workspace(g.desc, case.num_seqs, case.max_context_len)
+    kv.decode_step(g.desc, bf16_dev(knew), bf16_dev(vnew), g.k_cache, g.v_cache, out, g.q,
+                   i32_dev(case.block_tables), i32_dev(case.lens), case.max_context_len,
+                   g.k_scale, g.v_scale, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+DECODE_STEP_CASES = [
+    # (label, Hq, Hkv, D, lens, fp8, window)
+    ("d128-fp8", 32, 8, 128, [1000, 4099, 1, 0, 17], True, 0),
+    ("d128-bf16", 32, 8, 128, [513, 16, 33], False, 0),
+    ("d64-fp8-window", 16, 2, 64, [700, 129, 3], True, 100),
+    ("d64-bf16-sw128", 64, 8, 64, [3001, 100], False, 128),
+    ("d256-fp8", 8, 2, 256, [777, 31], True, 0),
+    ("d256-bf16", 8, 2, 256, [300, 15], False, 21),
+    ("g8-fp8", 64, 8, 128, [2050, 48], True, 0),
+]
+
+
+@pytest.mark.parametrize("label,Hq,Hkv,D,lens,fp8,window", DECODE_STEP_CASES,
+                         ids=[c[0] for c in DECODE_STEP_CASES])
+def test_decode_step_equals_write_then_attend(label, Hq, Hkv, D, lens, fp8, window):
+    say(f"decode step {label}")
+    case = synth.decode_case(90, Hq, Hkv, D, lens, shuffle=True, spare_frac=0.2)
+    pre = split_newest(case)
+    knew, vnew = newest_rows(case)
+    # scales from the whole layer (both sides calibrate on all positions)
+    o = OracleLayer(case, fp8=fp8, window=window)
+    ref_gpu = GpuLayer(case, fp8=fp8, window=window)       # the two-call path
+    sc = ref_gpu.scales_host() if fp8 else None
+    if fp8:
+        assert np.array_equal(sc[0], o.ks) and np.array_equal(sc[1], o.vs)
+    g = GpuLayer(pre, fp8=fp8, window=window, scales=sc)
+    g.case = case
+    g.q = bf16_dev(case.q)
+    out = run_decode_step(g, case, knew, vnew)
+    assert np.array_equal(host(g.k_cache), o.k_cache), label
+    assert np.array_equal(host(g.v_cache), o.v_cache), label
+    two_call = ref_gpu.attend()
+    assert np.array_equal(host(out), host(two_call)), label
+    ref = o.attend()
+    mx, mean = errors(out, ref)
+    say(f"[{label}] max_abs={mx:.3e} mean_abs={mean:.3e}")
+    assert mx <= GATE_MAX_ABS and mean <= GATE_MEAN_ABS and mx <= tight_bound(ref)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_decode_step_every_tile_variant(variant, monkeypatch):
+    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+    for ppw in ("auto", "1", "3"):
+        if ppw == "auto":
+            monkeypatch.delenv("KVFP8_PAGES_PER_WAVE", raising=False)
+        else:
+            monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
+        for D, fp8 in ((128, True), (64, False)):
+            label = f"decode step variant={variant} ppw={ppw} D={D} fp8={fp8}"
+            say(label)
+            case = synth.decode_case(91, 4 * (D // 64), D // 64, D, [333, 32, 1], shuffle=True,
+                                     spare_frac=0.2)
+            pre = split_newest(case)
+            knew, vnew = newest_rows(case)
+            ref_gpu = GpuLayer(case, fp8=fp8)
+            g = GpuLayer(pre, fp8=fp8, scales=ref_gpu.scales_host() if fp8 else None)
+            g.q = bf16_dev(case.q)
+            out = run_decode_step(g, case, knew, vnew)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(g.k_cache), host(ref_gpu.k_cache)), label
+            assert np.array_equal(host(g.v_cache), host(ref_gpu.v_cache)), label
+            assert np.array_equal(host(out), host(ref_gpu.attend())), label
