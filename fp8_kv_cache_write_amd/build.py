@@ -19,6 +19,10 @@ FLAGS = [
     "-fno-fast-math", "-ffp-contract=fast-honor-pragmas",
     # Packed-FP32 instructions are kept out of generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the decode loop adds them into the
+    # FP32 running sum and rescales them with VALU code, which would
+    # otherwise copy them out of (and back into) accumulation registers.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 

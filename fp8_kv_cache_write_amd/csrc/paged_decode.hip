@@ -42,6 +42,21 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
 }
 
+// Max over the four lanes c, c+16, c+32, c+48 that hold one MFMA column,
+// with the gfx950 row swaps (VALU, no LDS round trip).
+__device__ __forceinline__ float col_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+constexpr float kLazyLog2 = 8.0f;   // running max raised only past +8 (P <= 256)
+constexpr int kFoldTiles = 4;       // level-1 P*V accumulation length in tiles
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float wave_max_col(float x) {
   // lanes c, c+16, c+32, c+48 hold the same MFMA column
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -55,6 +70,52 @@ __device__ __forceinline__ float wave_sum_col(float x) {
   return x;
 }
 
+// ---- LDS staging of K/V tiles -------------------------------------------------
+// With SLOTS > 0 every wave owns a ring of SLOTS tile buffers in LDS and
+// fills them with direct global->LDS loads (16 bytes per lane, 1 KiB per
+// wave instruction, written at lane * 16 of the destination), so SLOTS tiles
+// are in flight while the wave computes on the registers of the current one,
+// at the register cost of a single tile. The compiler's wait insertion
+// cannot tell the buffers apart and would wait for every outstanding load
+// before any LDS read, so the reads of a staged tile are written as one
+// instruction group that first waits for all but the loads issued after
+// that tile (vmcnt) and ends by waiting for its own LDS reads (lgkmcnt).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kAuxNonTemporal = 2;          // cache policy bit NT of the load
+// The LDS address of a direct-to-LDS load comes from M0; on MI355X rings
+// that reached past 64 KiB read back wrong data, so a ring stays below.
+constexpr int kMaxLdsRing = 64 * 1024;
+
+__device__ __forceinline__ void dma_1k(const uint8_t* src_wave_chunk, int lane, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(src_wave_chunk + 16 * lane), (lds_void_t*)lds_dst,
+                                   16, 0, kAuxNonTemporal);
+}
+
+// Four 1 KiB chunks at lds_addr + {0, 1, 2, 3} KiB (lds_addr includes lane*16),
+// after waiting until at most PENDING vector-memory operations are
+// outstanding.
+template <int PENDING>
+__device__ __forceinline__ void lds_read4(uint32_t lds_addr, uint4& a, uint4& b, uint4& c,
+                                          uint4& d) {
+  u32x4_t ra, rb, rc, rd;
+  asm volatile(
+      "s_waitcnt vmcnt(%4)\n\t"
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:1024\n\t"
+      "ds_read_b128 %2, %5 offset:2048\n\t"
+      "ds_read_b128 %3, %5 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(ra), "=v"(rb), "=v"(rc), "=v"(rd)
+      : "n"(PENDING), "v"(lds_addr)
+      : "memory");
+  a = __builtin_bit_cast(uint4, ra);
+  b = __builtin_bit_cast(uint4, rb);
+  c = __builtin_bit_cast(uint4, rc);
+  d = __builtin_bit_cast(uint4, rd);
+}
+
 struct PartitionRange {
   int L, lo, first_page, end_page, num_parts_b;
 };
@@ -65,7 +126,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
                                                           int b, int part_pages) {
   PartitionRange r;
   r.L = p.context_lens[b];
-  if (r.L < 0) r.L = 0;
+  if (r.L < 0 || p.num_pages <= 0) r.L = 0;         // no page can be valid without a pool
   r.lo = (p.window > 0 && r.L > p.window) ? r.L - p.window : 0;
   // Device-side values are never trusted to stay in bounds: positions past
   // the block-table row are ignored and partitions past the plan are dropped.
@@ -79,7 +140,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   return r;
 }
 
-template <int D, bool FP8, int NW, int TP, int RING, bool FUSED>
+template <int D, bool FP8, int NW, int TP, int RING, int SLOTS, bool FUSED>
 __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const DecodeParams p) {
   constexpr int E = FP8 ? 1 : 2;
@@ -90,7 +151,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   constexpr int GMAX = 8;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int part = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -99,30 +160,15 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const int c = lane & 15;              // MFMA column
   const int part_pages = NW * p.pages_per_wave;
 
-  const PartitionRange pr = partition_range(p, b, part_pages);
-  const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
-  if (part >= pr.num_parts_b) {
-    // Nothing to attend here. In direct mode the first partition still owns
-    // the output rows (empty context -> zeros).
-    if (p.direct && part == 0) {
-      for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
-        const int64_t o = ((int64_t)b * p.num_q_heads + h * G + i / D) * D + i % D;
-        if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[o] = (__bf16)0.0f;
-        else reinterpret_cast<float*>(p.out)[o] = 0.0f;
-      }
-    }
-    return;
-  }
-
-  const int wbeg = pr.first_page + part * part_pages + wave * p.pages_per_wave;
-  const int wend = min(wbeg + p.pages_per_wave, pr.end_page);
-  const int npages = wend > wbeg ? wend - wbeg : 0;
-
   // Column c < G: query c (high half of P); G <= c < 2G: query c - G (low
   // half of P); other columns idle.
   const int g = c < G ? c : (c < 2 * G ? c - G : -1);
   const bool lo_col = (c >= G) && (c < 2 * G);
 
+  // Loads that do not depend on the context length go out before it is
+  // known, so a work-group waits for one memory round trip, not two, before
+  // its first page loads: the query operands and, for full attention (where
+  // the run of pages starts at a fixed place), this wave's block-table slice.
   // q k^T B operand: lane (qd, c) holds query g's dims of K-slice s, in the
   // same order the K loads deliver them.
   bf16x8 qop[NK];
@@ -137,18 +183,81 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       qop[s] = bits_to_bf16x8(w);
     }
   }
-
-  // Page ids of this wave's run, one per lane.
+  const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
+  const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
+  const int32_t* bt_row = p.block_tables + (int64_t)b * p.max_pages_per_seq;
   int my_page = -1;
-  if (lane < npages)
-    my_page = p.block_tables[(int64_t)b * p.max_pages_per_seq + wbeg + lane];
+  if (p.window == 0) {
+    const int idx = part * part_pages + wave * p.pages_per_wave + lane;
+    if (lane < p.pages_per_wave && idx < p.max_pages_per_seq) my_page = bt_row[idx];
+  }
+
+  const PartitionRange pr = partition_range(p, b, part_pages);
+  if (part >= pr.num_parts_b) {
+    // Nothing to attend here. In direct mode the first partition still owns
+    // the output rows (empty context -> zeros).
+    if (p.direct && part == 0) {
+      for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+        const int64_t o = ((int64_t)b * p.num_q_heads + h * G + i / D) * D + i % D;
+        if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[o] = (__bf16)0.0f;
+        else reinterpret_cast<float*>(p.out)[o] = 0.0f;
+      }
+    }
+    return;
+  }
+
+  // This wave's run of pages. A partial (last) partition spreads its pages
+  // evenly over the work-group's waves, so its waves - among them the one
+  // holding the newest position - finish early instead of two running full.
+  const int part_start = pr.first_page + part * part_pages;
+  const int part_end = min(part_start + part_pages, pr.end_page);
+  int ppw = p.pages_per_wave;
+  if (part_end - part_start < part_pages)
+    ppw = min(ppw, (((part_end - part_start) + NW - 1) / NW + 1) & ~1);
+  const int wbeg = part_start + wave * ppw;
+  const int wend = min(wbeg + ppw, part_end);
+  const int npages = wend > wbeg ? wend - wbeg : 0;
+
+  // Page ids of this wave's run, one per lane. The early read holds them
+  // when the run starts where it was guessed (full attention, full
+  // partition); a window or a partial partition reads them now.
+  if (p.window != 0 || ppw != p.pages_per_wave) {
+    my_page = -1;
+    if (lane < npages) my_page = bt_row[wbeg + lane];
+  } else if (lane >= npages) {
+    my_page = -1;
+  }
   if (my_page < 0 || (int64_t)my_page >= p.num_pages) my_page = -1;   // empty page
   const uint64_t bad_pages = __ballot(my_page < 0 && lane < npages);
+  // what a tile loads for page index idx: the page, or pool page 0 for a
+  // missing or invalid one (its positions are masked)
+  const int page_or0 = my_page < 0 ? 0 : my_page;
+
+  // Per-wave LDS region: the tile ring while streaming, then the wave's
+  // unnormalised output rows for the merge (written after the wave's last
+  // staged tile has been read, so no load is still landing there).
+  constexpr int TILE_BYTES = TP * 2 * PB;             // K and V of TP pages
+  constexpr int LPT = TP * 2 * NI;                    // 1 KiB loads per tile
+  constexpr int O_BYTES = GMAX * D * 4;
+  constexpr int REGION = (SLOTS * TILE_BYTES > O_BYTES) ? SLOTS * TILE_BYTES : O_BYTES;
+  static_assert(LPT % 4 == 0, "staged tiles are read in groups of four 1 KiB chunks");
+  static_assert(SLOTS == 0 || NW * REGION <= kMaxLdsRing,
+                "direct-to-LDS loads address the first 64 KiB only");
+  // One LDS block, so the ring starts at address 0: the per-wave regions,
+  // then the waves' m and l, then the staged new rows of the fused step.
+  constexpr int M_OFF = NW * REGION;
+  constexpr int L_OFF = M_OFF + NW * GMAX * 4;
+  constexpr int NEW_OFF = L_OFF + NW * GMAX * 4;
+  constexpr int SMEM_BYTES = NEW_OFF + (FUSED ? 2 * D * E : 16);
+  __shared__ __align__(16) uint8_t smem[SMEM_BYTES];
+  uint8_t* const my_region = smem + wave * REGION;
+  float (*const sm_m)[GMAX] = reinterpret_cast<float (*)[GMAX]>(smem + M_OFF);
+  float (*const sm_l)[GMAX] = reinterpret_cast<float (*)[GMAX]>(smem + L_OFF);
+  uint8_t* const new_rows = smem + NEW_OFF;
 
   const int64_t page_stride = (int64_t)p.num_kv_heads * PB;
   const uint8_t* kbase = p.k_cache + (int64_t)h * PB;
   const uint8_t* vbase = p.v_cache + (int64_t)h * PB;
-  const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
   const float c_log2 = ks * p.sm_scale_log2;
 
   // ---- fused decode step: the cache write of position L-1 -----------------
@@ -158,7 +267,6 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   // keeps the stored bytes in LDS; when it reaches that page it patches them
   // into its tile registers. No other wave reads that page, so no ordering
   // across waves is needed, and the page load never has to observe the store.
-  __shared__ __align__(16) uint8_t new_rows[FUSED ? 2 * D * E : 16];
   int t_new = -1, pg_new = 0, r_new = 0;
   int idx_new = -1;
   if constexpr (FUSED) {
@@ -172,17 +280,26 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     }
   }
   // The owning wave issues the loads of the new rows before its first tiles'
-  // loads (lane j < D/8 holds dims 8j..8j+7 of K and of V) and quantises,
-  // stores and stages them right after: memory operations retire in order,
-  // so waiting for the rows does not wait for the tiles, and the conversion
-  // overlaps their latency.
-  uint4 kx_new = make_uint4(0u, 0u, 0u, 0u), vx_new = make_uint4(0u, 0u, 0u, 0u);
+  // loads (lane j holds dims VPL*j .. VPL*j+VPL-1 of K and of V, so the whole
+  // wave shares the quantisation) and quantises, stores and stages them right
+  // after: memory operations retire in order, so waiting for the rows does
+  // not wait for the tiles, and the conversion overlaps their latency.
+  constexpr int VPL = D / kWave;
+  uint32_t kx_new[(VPL + 1) / 2] = {}, vx_new[(VPL + 1) / 2] = {};
   auto fused_prefetch = [&]() {
     if constexpr (FUSED) {
-      if (t_new < 0 || lane >= D / 8) return;
-      const int64_t src = ((int64_t)b * p.num_kv_heads + h) * D + 8 * lane;
-      kx_new = *reinterpret_cast<const uint4*>(p.k_new + src);
-      vx_new = *reinterpret_cast<const uint4*>(p.v_new + src);
+      if (t_new < 0) return;
+      const int64_t src = ((int64_t)b * p.num_kv_heads + h) * D + VPL * lane;
+      if constexpr (VPL == 1) {
+        kx_new[0] = p.k_new[src];
+        vx_new[0] = p.v_new[src];
+      } else {
+#pragma unroll
+        for (int i = 0; i < VPL / 2; ++i) {
+          kx_new[i] = reinterpret_cast<const uint32_t*>(p.k_new + src)[i];
+          vx_new[i] = reinterpret_cast<const uint32_t*>(p.v_new + src)[i];
+        }
+      }
     }
   };
   auto fused_commit = [&]() {
@@ -190,47 +307,63 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       const int pid = __builtin_amdgcn_readlane(my_page, idx_new);
       uint8_t* kblk = const_cast<uint8_t*>(p.k_cache) + ((int64_t)pid * p.num_kv_heads + h) * PB;
       uint8_t* vblk = const_cast<uint8_t*>(p.v_cache) + ((int64_t)pid * p.num_kv_heads + h) * PB;
-      const int j = lane;
-      if (j < D / 8) {
-        const uint4 kx = kx_new, vx = vx_new;
-        if constexpr (FP8) {
-          const float sk = p.k_scale[p.scale_per_head ? h : 0];
-          const float sv = p.v_scale[p.scale_per_head ? h : 0];
-          const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w};
-          const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
-          uint32_t kq[2] = {0u, 0u}, vq[2] = {0u, 0u};
+      const int d0 = VPL * lane;
+      uint16_t kb[VPL], vb[VPL];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t kb = (kw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-            const uint32_t vb = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-            kq[e / 4] |= e4m3_encode_sat(bf16_bits_to_f32(kb) / sk) << (8 * (e % 4));
-            vq[e / 4] |= e4m3_encode_sat(bf16_bits_to_f32(vb) / sv) << (8 * (e % 4));
-          }
-          *reinterpret_cast<uint2*>(new_rows + 8 * j) = make_uint2(kq[0], kq[1]);
-          *reinterpret_cast<uint2*>(new_rows + D + 8 * j) = make_uint2(vq[0], vq[1]);
-          *reinterpret_cast<uint2*>(kblk + k_byte<1>(r_new, 8 * j)) = make_uint2(kq[0], kq[1]);
+      for (int e = 0; e < VPL; ++e) {
+        kb[e] = (uint16_t)(kx_new[e / 2] >> (16 * (e % 2)));
+        vb[e] = (uint16_t)(vx_new[e / 2] >> (16 * (e % 2)));
+      }
+      if constexpr (FP8) {
+        const float sk = ks, sv = vs;
+        uint8_t kq[VPL], vq[VPL];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            vblk[v_byte<1>(r_new, 8 * j + e)] = (uint8_t)(vq[e / 4] >> (8 * (e % 4)));
-        } else {
-          *reinterpret_cast<uint4*>(new_rows + 16 * j) = kx;
-          *reinterpret_cast<uint4*>(new_rows + 2 * D + 16 * j) = vx;
-          *reinterpret_cast<uint4*>(kblk + k_byte<2>(r_new, 8 * j)) = kx;
-          const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
+        for (int e = 0; e < VPL; ++e) {
+          kq[e] = (uint8_t)e4m3_encode_sat(bf16_bits_to_f32(kb[e]) / sk);
+          vq[e] = (uint8_t)e4m3_encode_sat(bf16_bits_to_f32(vb[e]) / sv);
+        }
+        // K: the lane's dims are adjacent in one 16-byte chunk; V: 4 bytes apart
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<uint16_t*>(vblk + v_byte<2>(r_new, 8 * j + e)) =
-                (uint16_t)(vw[e / 2] >> (16 * (e % 2)));
+        for (int e = 0; e < VPL; ++e) {
+          new_rows[d0 + e] = kq[e];
+          new_rows[D + d0 + e] = vq[e];
+          kblk[k_byte<1>(r_new, d0 + e)] = kq[e];
+          vblk[v_byte<1>(r_new, d0 + e)] = vq[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) {
+          reinterpret_cast<uint16_t*>(new_rows)[d0 + e] = kb[e];
+          reinterpret_cast<uint16_t*>(new_rows)[D + d0 + e] = vb[e];
+          *reinterpret_cast<uint16_t*>(kblk + k_byte<2>(r_new, d0 + e)) = kb[e];
+          *reinterpret_cast<uint16_t*>(vblk + v_byte<2>(r_new, d0 + e)) = vb[e];
         }
       }
     }
   };
 
+  // Online softmax state per column (log2 domain). The running max is raised
+  // lazily - only when a tile's max exceeds it by more than kLazyLog2 - so
+  // most tiles need no rescale and P stays below 2^kLazyLog2. P*V is
+  // accumulated in two FP32 levels: the MFMA accumulator `lvl1` (level 1)
+  // takes up to kFoldTiles tiles, then is added into `acc` (level 2); a
+  // rescale folds first.
   float m_run = -INFINITY;
   float l_run = 0.0f;
-  f32x4 acc[NBLK];
+  f32x4 acc[NBLK], lvl1[NBLK];
 #pragma unroll
-  for (int i = 0; i < NBLK; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < NBLK; ++i) {
+    acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    lvl1[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  auto fold = [&]() {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] += lvl1[i][e];
+      lvl1[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
 
   // A tile is TP pages (an even number: the P*V MFMA contracts 32 positions,
   // two pages). Missing pages (past the run, an odd tail) and invalid ids
@@ -245,8 +378,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 #pragma unroll
     for (int pg = 0; pg < TP; ++pg) {
       const int idx = TP * t + pg;
-      const bool ok = idx < npages && !((bad_pages >> idx) & 1ull);
-      const int pid = ok ? __builtin_amdgcn_readlane(my_page, idx) : 0;
+      const int pid = __builtin_amdgcn_readlane(page_or0, idx & (kWave - 1));
       const uint4* kp = reinterpret_cast<const uint4*>(kbase + (int64_t)pid * page_stride);
       const uint4* vp = reinterpret_cast<const uint4*>(vbase + (int64_t)pid * page_stride);
 #pragma unroll
@@ -320,17 +452,17 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       for (int e = 0; e < 4; ++e) x[pg][e] = sacc[e] * c_log2;
     }
     // ---- masking: positions outside [lo, L), past the run, invalid pages --
+    // (wave-uniform decision; only boundary tiles take it)
     const int pos0 = (wbeg + TP * t) * kPage;           // first position of the tile
-    bool any_missing = false;
-#pragma unroll
-    for (int pg = 0; pg < TP; ++pg) {
-      const int idx = TP * t + pg;
-      any_missing |= idx >= npages || ((bad_pages >> idx) & 1ull);
-    }
+    const uint64_t tile_bits = ((1ull << TP) - 1ull) << (TP * t);
+    const uint64_t run_bits = npages >= 64 ? ~0ull : ((1ull << npages) - 1ull);
+    const bool any_missing = ((tile_bits & ~run_bits) | (tile_bits & bad_pages)) != 0ull;
     const bool need_mask = (pos0 < pr.lo) || (pos0 + TP * kPage > pr.L) || any_missing;
-    uint32_t vkeep = 0xFFFFFFFFu;                        // bit 4*pg+e: row 4qd+e of page pg
+    // masked V rows: per 32-position MFMA, AND masks for the four packed
+    // bf16 pairs of the operand (set, and used, only on boundary tiles)
+    uint32_t vmask[TP / 2][4];
     if (need_mask) {
-      vkeep = 0u;
+      uint32_t vkeep = 0u;                               // bit 4*pg+e: row 4qd+e of page pg
 #pragma unroll
       for (int pg = 0; pg < TP; ++pg) {
         const int idx = TP * t + pg;
@@ -343,44 +475,64 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
           vkeep |= (ok ? 1u : 0u) << (4 * pg + e);
         }
       }
-    }
-    if (g < 0) {
 #pragma unroll
-      for (int pg = 0; pg < TP; ++pg)
+      for (int pp = 0; pp < TP / 2; ++pp) {
+        const uint32_t kk = vkeep >> (8 * pp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[pg][e] = -INFINITY;
+        for (int k2 = 0; k2 < 4; ++k2)
+          vmask[pp][k2] = (((kk >> (2 * k2)) & 1u) ? 0x0000FFFFu : 0u) |
+                          (((kk >> (2 * k2 + 1)) & 1u) ? 0xFFFF0000u : 0u);
+      }
     }
-    // ---- online softmax (log2 domain) -------------------------------------
+    // ---- online softmax (log2 domain), lazy rescale -----------------------
     float tmax = x[0][0];
 #pragma unroll
     for (int pg = 0; pg < TP; ++pg)
 #pragma unroll
       for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[pg][e]);
-    tmax = wave_max_col(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.0f;
+    tmax = col_max(tmax);
+    const bool grow = tmax > m_run + kLazyLog2;          // -inf > -inf is false
+    if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+      fold();
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    float psum_pg[TP];
     bf16x8 pop[TP / 2];
 #pragma unroll
     for (int pg = 0; pg < TP; ++pg) {
+      float u[4], pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float pe = __builtin_amdgcn_exp2f(x[pg][e] - m_use);
-        psum += pe;
-        // P as bf16: the high part in the query columns, the rounding
-        // residue in the duplicate columns.
-        const __bf16 hi = (__bf16)pe;
-        pop[pg / 2][4 * (pg % 2) + e] = lo_col ? (__bf16)(pe - (float)hi) : hi;
+        pv[e] = pe;
+        // P = hi + lo: hi is pe truncated to bf16 (query columns), lo the
+        // exact residue, rounded to bf16 (duplicate columns)
+        const float hi = __uint_as_float(__float_as_uint(pe) & 0xFFFF0000u);
+        u[e] = lo_col ? pe - hi : hi;
+      }
+      psum_pg[pg] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const bf16x2 v2 = __builtin_convertvector((float2_t){u[e], u[e + 1]}, bf16x2);
+        pop[pg / 2][4 * (pg % 2) + e] = v2[0];
+        pop[pg / 2][4 * (pg % 2) + e + 1] = v2[1];
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // ---- P*V: TP/2 chained k=32 MFMAs per 16-dim block (level 1, FP32),
-    // folded into the running accumulator after the rescale (level 2) -------
+    float psum = psum_pg[0];
+#pragma unroll
+    for (int pg = 1; pg < TP; ++pg) psum += psum_pg[pg];
+    l_run += psum;
+    // ---- P*V: TP/2 chained k=32 MFMAs per 16-dim block into level 1 -------
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
-      f32x4 part_o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int pp = 0; pp < TP / 2; ++pp) {
         uint4 vb;
@@ -397,26 +549,78 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         }
         if (need_mask) {
           // zero the bf16 values of masked rows (poison codes are NaN)
-          const uint32_t kk = vkeep >> (8 * pp);
-          uint32_t mw[4];
-#pragma unroll
-          for (int k2 = 0; k2 < 4; ++k2)
-            mw[k2] = (((kk >> (2 * k2)) & 1u) ? 0x0000FFFFu : 0u) |
-                     (((kk >> (2 * k2 + 1)) & 1u) ? 0xFFFF0000u : 0u);
-          vb.x &= mw[0]; vb.y &= mw[1]; vb.z &= mw[2]; vb.w &= mw[3];
+          vb.x &= vmask[pp][0]; vb.y &= vmask[pp][1];
+          vb.z &= vmask[pp][2]; vb.w &= vmask[pp][3];
         }
-        part_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vb), pop[pp], part_o,
-                                                         0, 0, 0);
+        lvl1[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vb), pop[pp], lvl1[blk],
+                                                            0, 0, 0);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[blk][e] = acc[blk][e] * alpha + part_o[e];
     }
+    // ---- level 2: every kFoldTiles tiles ----------------------------------
+    if (t % kFoldTiles == kFoldTiles - 1) fold();
   };
 
   const int ntiles = (npages + TP - 1) / TP;
-  // Register ring of RING tiles: RING - 1 tiles are in flight while one is
-  // computed.
-  if constexpr (RING == 3) {
+  if constexpr (SLOTS > 0) {
+    // ---- LDS ring: tile t lives in slot t % SLOTS ------------------------------
+    // chunk q of a slot: page q / (2 NI), K (then V) chunk q % NI
+    auto stage_tile = [&](int t, int slot) {
+      uint8_t* dst = my_region + slot * TILE_BYTES;
+#pragma unroll
+      for (int pg = 0; pg < TP; ++pg) {
+        const int idx = TP * t + pg;
+        const int pid = __builtin_amdgcn_readlane(page_or0, idx & (kWave - 1));
+        const uint8_t* kp = kbase + (int64_t)pid * page_stride;
+        const uint8_t* vp = vbase + (int64_t)pid * page_stride;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          dma_1k(kp + 1024 * i, lane, dst + 1024 * (2 * NI * pg + i));
+          dma_1k(vp + 1024 * i, lane, dst + 1024 * (2 * NI * pg + NI + i));
+        }
+      }
+    };
+    // Reads slot `slot` into registers once at most `later` tiles issued after
+    // it are still outstanding.
+    auto read_tile = [&](int slot, int later, Tile& tl) {
+      const uint32_t base =
+          (uint32_t)(uintptr_t)(lds_void_t*)(my_region + slot * TILE_BYTES) + 16u * lane;
+      uint4 ch[LPT];
+#pragma unroll
+      for (int j = 0; j < LPT / 4; ++j) {
+        const uint32_t a = base + 4096u * j;
+        if (later >= 2 && SLOTS >= 3)
+          lds_read4<2 * LPT>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
+        else if (later >= 1 && SLOTS >= 2)
+          lds_read4<LPT>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
+        else
+          lds_read4<0>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
+      }
+#pragma unroll
+      for (int pg = 0; pg < TP; ++pg)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          tl.k[pg][i] = ch[2 * NI * pg + i];
+          tl.v[pg][i] = ch[2 * NI * pg + NI + i];
+        }
+    };
+    Tile t0;
+    fused_prefetch();
+#pragma unroll
+    for (int sl = 0; sl < SLOTS; ++sl)
+      if (sl < ntiles) stage_tile(sl, sl);
+    if (t_new >= 0) fused_commit();
+    for (int t = 0; t < ntiles; ++t) {
+      // tiles issued after tile t; the wave that stored the new rows waits
+      // for everything once (stores and loads share the counter)
+      int later = min(ntiles, t + SLOTS) - (t + 1);
+      if (FUSED && t == 0 && t_new >= 0) later = 0;
+      read_tile(t % SLOTS, later, t0);
+      if (t + SLOTS < ntiles) stage_tile(t + SLOTS, t % SLOTS);
+      if (FUSED && t == t_new) patch_tile(t0);
+      compute_tile(t, t0);
+    }
+  } else if constexpr (RING == 3) {
+    // ---- register ring of RING tiles: RING - 1 in flight while one is computed
     Tile t0, t1, t2;
     fused_prefetch();
     if (ntiles > 0) load_tile(0, t0);
@@ -461,6 +665,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     }
   }
 
+  fold();
   // ---- per-wave results: l over the row quads, lo columns into hi ----------
   l_run = wave_sum_col(l_run);
 #pragma unroll
@@ -468,9 +673,6 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[blk][e] += __shfl_down(acc[blk][e], G);
 
-  __shared__ float sm_o[NW][GMAX][D];
-  __shared__ float sm_m[NW][GMAX];
-  __shared__ float sm_l[NW][GMAX];
   if (c < G) {
     if (qd == 0) {
       sm_m[wave][c] = m_run;
@@ -483,7 +685,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         int d;
         if constexpr (FP8) d = 64 * (blk / 4) + 16 * qd + 4 * e + (blk % 4);
         else d = 32 * (blk / 2) + 8 * qd + 2 * e + (blk % 2);
-        sm_o[wave][c][d] = acc[blk][e];
+        reinterpret_cast<float*>(my_region)[c * D + d] = acc[blk][e];
       }
     }
   }
@@ -500,7 +702,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float wt = __builtin_amdgcn_exp2f(sm_m[w][gg] - M);
-        o += wt * sm_o[w][gg][d];
+        o += wt * reinterpret_cast<const float*>(smem + w * REGION)[gg * D + d];
         l += wt * sm_l[w][gg];
       }
     }
@@ -523,111 +725,94 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 
 // Merge the partitions of one (sequence, query head):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = s_v * sum_j w_j o_j / sum_j w_j l_j
-// kReduceThreads threads, as (dim d, partition group) pairs. Every global load
-// is issued up front - each thread's first kReducePer partial outputs into
-// registers, the m and l rows into LDS - so the kernel costs one memory round
-// trip plus two block reductions; partitions past the first
-// kReduceThreads / D * kReducePer (very long contexts) are read in a second
-// loop.
-constexpr int kReduceThreads = 512;
-constexpr int kReducePer = 8;             // partial outputs per thread held in registers
-constexpr int kReduceLds = 4096;          // partitions whose m/l (then weight) sit in LDS
+// Each wave owns 64 dims of one (sequence, query head) and needs no barrier:
+// lane j reads m_j and l_j, lane d reads the partial outputs o_j[d] of the
+// first 64 partitions, all issued before the first wait, so the kernel costs
+// one memory round trip, two wave reductions and an FMA per partition (the
+// weight of partition j comes from lane j through readlane). Partitions past
+// 64 (contexts beyond 64 partitions) are read in further 64-wide chunks.
+__device__ __forceinline__ float wave_max_all(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off /= 2) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
 
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
-  for (int off = kWave / 2; off > 0; off /= 2) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  __syncthreads();                       // red[] may still be read by a previous call
-  if (lane == 0) red[wid] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < (int)(blockDim.x / kWave); ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  return r;
+__device__ __forceinline__ float wave_sum_all(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off /= 2) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
 }
 
 template <int D>
-__global__ __launch_bounds__(kReduceThreads) void paged_decode_reduce_kernel(
-    const DecodeParams p, int part_pages) {
-  constexpr int NG = kReduceThreads / D;  // partition groups
+__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodeParams p,
+                                                                 int part_pages) {
+  const int lane = threadIdx.x % kWave;
+  const int d = threadIdx.x;              // D threads: wave w owns dims 64w..64w+63
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int tid = threadIdx.x;
   const int h = hq / p.group;
   const PartitionRange pr = partition_range(p, b, part_pages);
   const int np = pr.num_parts_b;
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
-  const float* ms = p.ws_m + row * p.num_parts;
-  const float* ls = p.ws_l + row * p.num_parts;
-  const float* os = p.ws_o + row * p.num_parts * D;
+  const float vs = p.v_scale ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
+  float r = 0.0f;
+  if (np > 0) {
+    const float* ms = p.ws_m + row * p.num_parts;
+    const float* ls = p.ws_l + row * p.num_parts;
+    const float* os = p.ws_o + row * p.num_parts * D + d;
 
-  __shared__ float red[kReduceThreads / kWave];
-  __shared__ float m_s[kReduceLds];       // m_j, then the weight w_j
-  __shared__ float l_s[kReduceLds];
-  __shared__ float o_s[NG][D];
+    // ---- every load of the first chunk up front (indexes clamped in range;
+    // partitions past np get weight 0) -----------------------------------------
+    float ov[kWave];
+#pragma unroll
+    for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(u, np - 1) * D];
+    const float m0 = lane < np ? ms[lane] : -INFINITY;
+    const float l0 = lane < np ? ls[lane] : 0.0f;
 
-  const int d = tid % D, grp = tid / D;
-  // ---- every load first -----------------------------------------------------
-  float ov[kReducePer];
+    // ---- M and the normaliser ---------------------------------------------------
+    float m = m0;
+    for (int j = kWave + lane; j < np; j += kWave) m = fmaxf(m, ms[j]);
+    const float M = wave_max_all(m);
+    const bool empty = (M == -INFINITY);
+    const float w0 = (lane < np && !empty) ? __builtin_amdgcn_exp2f(m0 - M) : 0.0f;
+    float lsum = w0 * l0;
+    for (int j = kWave + lane; j < np; j += kWave)
+      lsum += (empty ? 0.0f : __builtin_amdgcn_exp2f(ms[j] - M)) * ls[j];
+    const float L = wave_sum_all(lsum);
+
+    // ---- weighted sum of the partial outputs ------------------------------------
+    float acc = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kReducePer; ++u) {
-    const int jj = grp + u * NG;
-    ov[u] = jj < np ? os[(int64_t)jj * D + d] : 0.0f;
-  }
-  for (int jj = tid; jj < np && jj < kReduceLds; jj += kReduceThreads) {
-    m_s[jj] = ms[jj];
-    l_s[jj] = ls[jj];
-  }
-  // ---- M, weights, normaliser (each thread touches the LDS entries it wrote)
-  float m = -INFINITY;
-  for (int jj = tid; jj < np; jj += kReduceThreads)
-    m = fmaxf(m, jj < kReduceLds ? m_s[jj] : ms[jj]);
-  const float M = block_reduce(m, true, red);
-  float lsum = 0.0f;
-  for (int jj = tid; jj < np; jj += kReduceThreads) {
-    const float mj = jj < kReduceLds ? m_s[jj] : ms[jj];
-    const float lj = jj < kReduceLds ? l_s[jj] : ls[jj];
-    const float w = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
-    if (jj < kReduceLds) m_s[jj] = w;
-    lsum += w * lj;
-  }
-  const float L = block_reduce(lsum, false, red);   // its barriers publish the weights
-  auto weight = [&](int jj) {
-    return jj < kReduceLds ? m_s[jj] : __builtin_amdgcn_exp2f(ms[jj] - M);
-  };
-  // ---- weighted sum of the partial outputs ---------------------------------
-  float acc = 0.0f;
+    for (int u = 0; u < kWave; ++u) acc += lane_value(w0, u) * ov[u];
+    for (int base = kWave; base < np; base += kWave) {
+      const int j = base + lane;
+      const float wl = (j < np && !empty) ? __builtin_amdgcn_exp2f(ms[j] - M) : 0.0f;
 #pragma unroll
-  for (int u = 0; u < kReducePer; ++u) {
-    const int jj = grp + u * NG;
-    if (jj < np) acc += weight(jj) * ov[u];
-  }
-  for (int jj = grp + kReducePer * NG; jj < np; jj += NG) acc += weight(jj) * os[(int64_t)jj * D + d];
-  o_s[grp][d] = acc;
-  __syncthreads();
-  if (grp == 0) {
-    float o = 0.0f;
+      for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(base + u, np - 1) * D];
 #pragma unroll
-    for (int g2 = 0; g2 < NG; ++g2) o += o_s[g2][d];
-    const float vs = p.v_scale ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
-    const float r = L > 0.0f ? o / L * vs : 0.0f;
-    if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
-    else reinterpret_cast<float*>(p.out)[row * D + d] = r;
+      for (int u = 0; u < kWave; ++u) acc += lane_value(wl, u) * ov[u];
+    }
+    r = L > 0.0f ? acc / L * vs : 0.0f;
   }
+  if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
+  else reinterpret_cast<float*>(p.out)[row * D + d] = r;
 }
 
-template <int D, bool FP8, int TP, int RING, bool FUSED>
+template <int D, bool FP8, int TP, int RING, int SLOTS, bool FUSED>
 static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_t stream,
                                  hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NW = kSplitWaves;
   const dim3 grid((unsigned)p.num_parts, (unsigned)p.num_kv_heads, (unsigned)num_seqs);
   if (ev_before && ev_after) {
     // the events take the kernel's own start and end timestamps
-    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, FUSED>), grid,
+    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, SLOTS, FUSED>), grid,
                           dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, FUSED>), grid,
+    hipLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, SLOTS, FUSED>), grid,
                        dim3(NW * kWave), 0, stream, p);
   }
   hipError_t err = hipGetLastError();
@@ -635,38 +820,54 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
   DecodeParams pr = p;
   if (!FP8) pr.v_scale = nullptr;
   hipLaunchKernelGGL((paged_decode_reduce_kernel<D>),
-                     dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(kReduceThreads), 0,
+                     dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(D), 0,
                      stream, pr, NW * p.pages_per_wave);
   return hipGetLastError();
 }
 
-// Tile shape of the split kernel: TP pages per tile, RING register buffers.
-// Default 2x1: 2-page tiles, loaded and computed one at a time, which keeps
-// the register count low enough for 3 waves per SIMD; with about 1.5 waves
-// per SIMD it was the fastest shape measured on MI355X for the 8B layer at
-// 131072 positions (70.5 % of peak) and for 8 ragged sequences of ~20k
-// (71.4 %), ahead of the prefetching shapes. KVFP8_SPLIT_VARIANT=TPxRING
-// (2x1, 2x2, 2x3, 4x1, 4x2) overrides it for tuning sweeps.
+// Tile shape of the split kernel: TP pages per tile, RING register buffers,
+// SLOTS LDS buffers (SLOTS > 0: LDS-staged loads, one register tile).
+// Default 2x1: 2-page tiles, loaded and computed one at a time.
+// KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 2x3, 4x1, 4x2,
+// 2x1s1, 2x1s2, 2x1s3, 4x1s1) overrides it for tuning sweeps; a shape whose
+// LDS ring would pass 64 KiB is rejected.
+template <int D, bool FP8, int TP, int RING, int SLOTS>
+static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused,
+                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+  constexpr int E = FP8 ? 1 : 2;
+  if constexpr (kSplitWaves * SLOTS * TP * 2 * kPage * D * E > kMaxLdsRing) {
+    return hipErrorInvalidValue;
+  } else {
+    return fused ? launch_variant<D, FP8, TP, RING, SLOTS, true>(p, num_seqs, stream, ev_before,
+                                                                  ev_after)
+                 : launch_variant<D, FP8, TP, RING, SLOTS, false>(p, num_seqs, stream, ev_before,
+                                                                   ev_after);
+  }
+}
+
 template <int D, bool FP8>
 static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
-  int tp = 2, ring = 1;
+  int tp = 2, ring = 1, slots = 0;
   if (const char* env = getenv("KVFP8_SPLIT_VARIANT")) {
-    int a = 0, c = 0;
-    if (sscanf(env, "%dx%d", &a, &c) == 2) { tp = a; ring = c; }
+    int a = 0, c = 0, sl = 0;
+    const int n = sscanf(env, "%dx%ds%d", &a, &c, &sl);
+    if (n >= 2) { tp = a; ring = c; slots = n == 3 ? sl : 0; }
   }
-#define KVFP8_VARIANT(TP_, RING_)                                                       \
-  if (tp == TP_ && ring == RING_)                                                       \
-    return fused ? launch_variant<D, FP8, TP_, RING_, true>(p, num_seqs, stream, ev_before,   \
-                                                             ev_after)                       \
-                 : launch_variant<D, FP8, TP_, RING_, false>(p, num_seqs, stream, ev_before,  \
-                                                              ev_after);
-  KVFP8_VARIANT(2, 1)
-  KVFP8_VARIANT(2, 2)
-  KVFP8_VARIANT(2, 3)
-  KVFP8_VARIANT(4, 1)
-  KVFP8_VARIANT(4, 2)
-#undef KVFP8_VARIANT
+#define KVFP8_SHAPE(TP_, RING_, SLOTS_)                                                 \
+  if (tp == TP_ && ring == RING_ && slots == SLOTS_)                                    \
+    return launch_shape<D, FP8, TP_, RING_, SLOTS_>(p, num_seqs, fused, stream, ev_before, \
+                                                    ev_after);
+  KVFP8_SHAPE(2, 1, 0)
+  KVFP8_SHAPE(2, 2, 0)
+  KVFP8_SHAPE(2, 3, 0)
+  KVFP8_SHAPE(4, 1, 0)
+  KVFP8_SHAPE(4, 2, 0)
+  KVFP8_SHAPE(2, 1, 1)
+  KVFP8_SHAPE(2, 1, 2)
+  KVFP8_SHAPE(2, 1, 3)
+  KVFP8_SHAPE(4, 1, 1)
+#undef KVFP8_SHAPE
   return hipErrorInvalidValue;
 }
 

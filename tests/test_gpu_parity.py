@@ -379,7 +379,16 @@ def test_full_gptoss_hybrid_32k():
     check_attention(gs, os_, "gptoss-sw128-bf16-32k")
 
 
-VARIANTS = ["2x1", "2x2", "2x3", "4x1", "4x2"]
+VARIANTS = ["2x1", "2x2", "2x3", "4x1", "4x2", "2x1s1", "2x1s2", "2x1s3", "4x1s1"]
+
+
+def shape_fits(variant, D, fp8):
+    """Whether a split-kernel shape (TPxRING[sSLOTS]) is offered for this
+    head dim and cache dtype: the LDS ring of 4 waves must stay within the
+    first 64 KiB of LDS (direct-to-LDS loads)."""
+    tp = int(variant.split("x")[0])
+    slots = int(variant.split("s")[1]) if "s" in variant else 0
+    return 4 * slots * tp * 2 * 16 * D * (1 if fp8 else 2) <= 64 * 1024
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -392,6 +401,8 @@ def test_attention_every_tile_variant(variant, monkeypatch):
                                  (256, False, 21, [300, 16])):
         if D == 256 and variant in ("2x3", "4x2"):
             continue                   # these shapes spill at head_dim 256
+        if not shape_fits(variant, D, fp8):
+            continue
         label = f"variant {variant} D={D} fp8={fp8} window={window}"
         say(label)
         case = synth.decode_case(80, 4 * (D // 64), D // 64, D, lens, shuffle=True,
@@ -490,6 +501,8 @@ def test_decode_step_every_tile_variant(variant, monkeypatch):
         else:
             monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
         for D, fp8 in ((128, True), (64, False)):
+            if not shape_fits(variant, D, fp8):
+                continue
             label = f"decode step variant={variant} ppw={ppw} D={D} fp8={fp8}"
             say(label)
             case = synth.decode_case(91, 4 * (D // 64), D // 64, D, [333, 32, 1], shuffle=True,
