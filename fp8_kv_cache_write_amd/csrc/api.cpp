@@ -58,6 +58,7 @@ int cu_count() {
 struct Plan {
   int pages_per_wave;
   int num_parts;
+  int slots;                   // split-kernel shape: LDS-staged tiles (1) or registers (0)
   size_t off_l, off_o, bytes;  // workspace layout (bytes)
 };
 
@@ -65,33 +66,65 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Split-context plan. Pages of one (sequence, KV head) are cut into
 // partitions of kSplitWaves * pages_per_wave pages; each partition is one
-// work-group, each wave streams pages_per_wave pages. Measured on MI355X,
-// long runs per wave beat many concurrent waves, and all waves should be
-// resident at once: pages_per_wave (even, in [2, 64]) divides the pages so
-// that there are about 1.5 waves per SIMD for fp8 (about two for bf16, whose
-// pages are twice as large). When one partition per
+// work-group of kSplitWaves waves, each wave streams pages_per_wave pages.
+//
+// Measured on MI355X: the kernel is fastest when every compute unit gets the
+// same number of work-groups and each wave streams a long run. The plan
+// tries k = 1..4 work-groups per compute unit: for each, the shortest even
+// run (<= 64 pages) that fits the longest sequence into k * CUs work-groups,
+// costed as k * run (pages each CU streams) with a small penalty per extra
+// co-resident work-group (measured: two work-groups of 32 pages per CU take
+// ~3.5 % longer than one of 64). One work-group per CU (one wave per SIMD)
+// uses the LDS-staged tile shape, so a wave keeps its next tile in flight
+// while it computes; more use the register shape. When one partition per
 // sequence is cheap enough (short contexts, sliding windows) the split kernel
 // writes the output itself and the reduce kernel is skipped.
+constexpr double kCoResidentPenalty = 0.035;
+
 Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
   const int W = d->sliding_window;
   int64_t pages_max = ((int64_t)max_context_len + 15) / 16;
   if (W > 0) pages_max = std::min<int64_t>(pages_max, ((int64_t)W + 15) / 16 + 1);
   if (pages_max < 1) pages_max = 1;
-  const int64_t total = (int64_t)std::max(num_seqs, 1) * d->num_kv_heads * pages_max;
-  const int64_t waves_per_cu = d->cache_dtype == KVQ_FP8_E4M3 ? 6 : 8;
-  const int64_t target_waves = (int64_t)cu_count() * waves_per_cu;
-  int64_t ppw = (total + target_waves - 1) / target_waves;
-  ppw = std::min<int64_t>(std::max<int64_t>((ppw + 1) / 2 * 2, 2), kMaxPagesPerWave);
+  const int64_t units = (int64_t)std::max(num_seqs, 1) * d->num_kv_heads;
+  const int64_t cus = cu_count();
+  auto even_run = [](int64_t n) { return std::max<int64_t>((n + 1) / 2 * 2, 2); };
+  int64_t ppw = 0;
+  int k_best = 0;
+  double best = 0.0;
+  for (int k = 1; k <= 4; ++k) {
+    const int64_t parts_cap = k * cus / units;
+    if (parts_cap < 1) continue;
+    const int64_t run =
+        even_run((pages_max + kSplitWaves * parts_cap - 1) / (kSplitWaves * parts_cap));
+    if (run > kMaxPagesPerWave) continue;
+    const double cost = (double)k * (double)run * (1.0 + kCoResidentPenalty * (k - 1));
+    if (k_best == 0 || cost < best) {
+      best = cost;
+      ppw = run;
+      k_best = k;
+    }
+  }
+  if (k_best == 0)   // many sequences, or very long ones: full-length runs
+    ppw = std::min<int64_t>(even_run((pages_max + kSplitWaves - 1) / kSplitWaves),
+                            kMaxPagesPerWave);
+  const int64_t page_block = 16LL * d->head_dim * (d->cache_dtype == KVQ_FP8_E4M3 ? 1 : 2);
+  const bool ring_fits = kSplitWaves * 2 * 2 * page_block <= 64 * 1024;
+  int slots = (k_best == 1 && ring_fits) ? 1 : 0;
   int64_t direct_ppw = (pages_max + kSplitWaves - 1) / kSplitWaves;
   direct_ppw = (direct_ppw + 1) / 2 * 2;
-  if (direct_ppw <= std::max<int64_t>(ppw, 8)) ppw = direct_ppw;
-  // KVFP8_PAGES_PER_WAVE=n (1..64) overrides the choice (tuning sweeps).
+  if (direct_ppw <= std::max<int64_t>(ppw, 8)) {
+    ppw = direct_ppw;
+    slots = 0;
+  }
+  // KVFP8_PAGES_PER_WAVE=n (1..64) overrides the run length (tuning sweeps).
   if (const char* env = getenv("KVFP8_PAGES_PER_WAVE")) {
     const long n = strtol(env, nullptr, 10);
     if (n >= 1 && n <= kMaxPagesPerWave) ppw = n;
   }
   Plan p;
   p.pages_per_wave = (int)ppw;
+  p.slots = slots;
   p.num_parts = (int)((pages_max + kSplitWaves * ppw - 1) / (kSplitWaves * ppw));
   if (p.num_parts <= 1) {
     p.num_parts = 1;
@@ -237,7 +270,7 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
     e1 = g_prof.ev[2 * g_prof.used + 1];
     g_prof.used++;
   }
-  hipError_t e = launch_paged_decode(p, desc->head_dim, fp8, num_seqs, fused,
+  hipError_t e = launch_paged_decode(p, desc->head_dim, fp8, num_seqs, fused, plan.slots,
                                      static_cast<hipStream_t>(stream), e0, e1);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

@@ -55,8 +55,9 @@ constexpr int kSplitWaves = 4;
 
 // fused = true: the split kernel also writes k_new / v_new into the caches at
 // position L-1 of every sequence (p.k_cache / p.v_cache must be writable).
+// slots: split-kernel tile shape, 1 = LDS-staged tiles, 0 = register tiles.
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,
-                               int num_seqs, bool fused, hipStream_t stream,
+                               int num_seqs, bool fused, int slots, hipStream_t stream,
                                hipEvent_t ev_before, hipEvent_t ev_after);
 
 }  // namespace kvfp8

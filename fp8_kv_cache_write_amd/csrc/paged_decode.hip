@@ -619,27 +619,8 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       if (FUSED && t == t_new) patch_tile(t0);
       compute_tile(t, t0);
     }
-  } else if constexpr (RING == 3) {
-    // ---- register ring of RING tiles: RING - 1 in flight while one is computed
-    Tile t0, t1, t2;
-    fused_prefetch();
-    if (ntiles > 0) load_tile(0, t0);
-    if (ntiles > 1) load_tile(1, t1);
-    if (t_new >= 0) fused_commit();
-    for (int t = 0; t < ntiles; t += 3) {
-      if (t + 2 < ntiles) load_tile(t + 2, t2);
-      if (FUSED && t == t_new) patch_tile(t0);
-      compute_tile(t, t0);
-      if (t + 1 >= ntiles) break;
-      if (t + 3 < ntiles) load_tile(t + 3, t0);
-      if (FUSED && t + 1 == t_new) patch_tile(t1);
-      compute_tile(t + 1, t1);
-      if (t + 2 >= ntiles) break;
-      if (t + 4 < ntiles) load_tile(t + 4, t1);
-      if (FUSED && t + 2 == t_new) patch_tile(t2);
-      compute_tile(t + 2, t2);
-    }
   } else if constexpr (RING == 2) {
+    // ---- register ring of two tiles: one in flight while one is computed
     Tile t0, t1;
     fused_prefetch();
     if (ntiles > 0) load_tile(0, t0);
@@ -827,10 +808,11 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
 
 // Tile shape of the split kernel: TP pages per tile, RING register buffers,
 // SLOTS LDS buffers (SLOTS > 0: LDS-staged loads, one register tile).
-// Default 2x1: 2-page tiles, loaded and computed one at a time.
-// KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 2x3, 4x1, 4x2,
-// 2x1s1, 2x1s2, 2x1s3, 4x1s1) overrides it for tuning sweeps; a shape whose
-// LDS ring would pass 64 KiB is rejected.
+// The plan picks 2x1 (2-page tiles, loaded and computed one at a time) or
+// 2x1s1 (the same with the next tile staged in LDS).
+// KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 4x1, 2x1s1, 2x1s2,
+// 4x1s1) overrides it for tuning sweeps; a shape whose LDS ring would pass
+// 64 KiB is rejected.
 template <int D, bool FP8, int TP, int RING, int SLOTS>
 static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
@@ -846,9 +828,9 @@ static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused,
 }
 
 template <int D, bool FP8>
-static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused,
+static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, int plan_slots,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
-  int tp = 2, ring = 1, slots = 0;
+  int tp = 2, ring = 1, slots = plan_slots;
   if (const char* env = getenv("KVFP8_SPLIT_VARIANT")) {
     int a = 0, c = 0, sl = 0;
     const int n = sscanf(env, "%dx%ds%d", &a, &c, &sl);
@@ -860,30 +842,29 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused,
                                                     ev_after);
   KVFP8_SHAPE(2, 1, 0)
   KVFP8_SHAPE(2, 2, 0)
-  KVFP8_SHAPE(2, 3, 0)
   KVFP8_SHAPE(4, 1, 0)
-  KVFP8_SHAPE(4, 2, 0)
   KVFP8_SHAPE(2, 1, 1)
   KVFP8_SHAPE(2, 1, 2)
-  KVFP8_SHAPE(2, 1, 3)
   KVFP8_SHAPE(4, 1, 1)
 #undef KVFP8_SHAPE
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,
-                               int num_seqs, bool fused, hipStream_t stream,
+                               int num_seqs, bool fused, int slots, hipStream_t stream,
                                hipEvent_t ev_before, hipEvent_t ev_after) {
   switch (head_dim) {
     case 64:
-      return fp8 ? launch_typed<64, true>(p, num_seqs, fused, stream, ev_before, ev_after)
-                 : launch_typed<64, false>(p, num_seqs, fused, stream, ev_before, ev_after);
+      return fp8 ? launch_typed<64, true>(p, num_seqs, fused, slots, stream, ev_before, ev_after)
+                 : launch_typed<64, false>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
     case 128:
-      return fp8 ? launch_typed<128, true>(p, num_seqs, fused, stream, ev_before, ev_after)
-                 : launch_typed<128, false>(p, num_seqs, fused, stream, ev_before, ev_after);
+      return fp8 ? launch_typed<128, true>(p, num_seqs, fused, slots, stream, ev_before, ev_after)
+                 : launch_typed<128, false>(p, num_seqs, fused, slots, stream, ev_before,
+                                            ev_after);
     case 256:
-      return fp8 ? launch_typed<256, true>(p, num_seqs, fused, stream, ev_before, ev_after)
-                 : launch_typed<256, false>(p, num_seqs, fused, stream, ev_before, ev_after);
+      return fp8 ? launch_typed<256, true>(p, num_seqs, fused, slots, stream, ev_before, ev_after)
+                 : launch_typed<256, false>(p, num_seqs, fused, slots, stream, ev_before,
+                                            ev_after);
     default:
       return hipErrorInvalidValue;
   }

@@ -379,7 +379,7 @@ def test_full_gptoss_hybrid_32k():
     check_attention(gs, os_, "gptoss-sw128-bf16-32k")
 
 
-VARIANTS = ["2x1", "2x2", "2x3", "4x1", "4x2", "2x1s1", "2x1s2", "2x1s3", "4x1s1"]
+VARIANTS = ["2x1", "2x2", "4x1", "2x1s1", "2x1s2", "4x1s1"]
 
 
 def shape_fits(variant, D, fp8):
@@ -399,8 +399,6 @@ def test_attention_every_tile_variant(variant, monkeypatch):
     for D, fp8, window, lens in ((128, True, 0, [1000, 37, 1]), (64, True, 50, [700, 129]),
                                  (128, False, 0, [515, 64]), (256, True, 0, [333]),
                                  (256, False, 21, [300, 16])):
-        if D == 256 and variant in ("2x3", "4x2"):
-            continue                   # these shapes spill at head_dim 256
         if not shape_fits(variant, D, fp8):
             continue
         label = f"variant {variant} D={D} fp8={fp8} window={window}"
