@@ -195,13 +195,21 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const PartitionRange pr = partition_range(p, b, part_pages);
   if (part >= pr.num_parts_b) {
     // Nothing to attend here. In direct mode the first partition still owns
-    // the output rows (empty context -> zeros).
-    if (p.direct && part == 0) {
-      for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
-        const int64_t o = ((int64_t)b * p.num_q_heads + h * G + i / D) * D + i % D;
-        if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[o] = (__bf16)0.0f;
-        else reinterpret_cast<float*>(p.out)[o] = 0.0f;
+    // the output rows (empty context -> zeros); otherwise the partition's
+    // slots get an empty partial (m = -inf, l = 0; o is never read), so the
+    // reduce kernel can merge every planned partition without the length.
+    if (p.direct) {
+      if (part == 0) {
+        for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+          const int64_t o = ((int64_t)b * p.num_q_heads + h * G + i / D) * D + i % D;
+          if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[o] = (__bf16)0.0f;
+          else reinterpret_cast<float*>(p.out)[o] = 0.0f;
+        }
       }
+    } else if ((int)threadIdx.x < G) {
+      const int64_t slot = ((int64_t)b * p.num_q_heads + h * G + threadIdx.x) * p.num_parts + part;
+      p.ws_m[slot] = -INFINITY;
+      p.ws_l[slot] = 0.0f;
     }
     return;
   }
@@ -706,12 +714,14 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 
 // Merge the partitions of one (sequence, query head):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = s_v * sum_j w_j o_j / sum_j w_j l_j
-// Each wave owns 64 dims of one (sequence, query head) and needs no barrier:
-// lane j reads m_j and l_j, lane d reads the partial outputs o_j[d] of the
-// first 64 partitions, all issued before the first wait, so the kernel costs
-// one memory round trip, two wave reductions and an FMA per partition (the
-// weight of partition j comes from lane j through readlane). Partitions past
-// 64 (contexts beyond 64 partitions) are read in further 64-wide chunks.
+// over every planned partition: the split kernel leaves an empty partial
+// (m = -inf, l = 0) in the slots of partitions a sequence does not reach, so
+// the merge needs neither the context length nor a second round trip. Each
+// wave owns 64 dims of one (sequence, query head) and needs no barrier: lane
+// j reads m_j and l_j, lane d the partial outputs o_j[d] of the first 64
+// partitions, all issued before the first wait; the weight of partition j
+// comes from lane j through readlane, and a partition of weight 0 is skipped
+// (its o was never written). Partitions past 64 are read in further chunks.
 __device__ __forceinline__ float wave_max_all(float x) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off /= 2) x = fmaxf(x, __shfl_xor(x, off));
@@ -729,56 +739,57 @@ __device__ __forceinline__ float lane_value(float x, int j) {
 }
 
 template <int D>
-__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodeParams p,
-                                                                 int part_pages) {
+__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodeParams p) {
   const int lane = threadIdx.x % kWave;
   const int d = threadIdx.x;              // D threads: wave w owns dims 64w..64w+63
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int h = hq / p.group;
-  const PartitionRange pr = partition_range(p, b, part_pages);
-  const int np = pr.num_parts_b;
+  const int np = p.num_parts;
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
+  const float* ms = p.ws_m + row * np;
+  const float* ls = p.ws_l + row * np;
+  const float* os = p.ws_o + row * np * D + d;
   const float vs = p.v_scale ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
-  float r = 0.0f;
-  if (np > 0) {
-    const float* ms = p.ws_m + row * p.num_parts;
-    const float* ls = p.ws_l + row * p.num_parts;
-    const float* os = p.ws_o + row * p.num_parts * D + d;
 
-    // ---- every load of the first chunk up front (indexes clamped in range;
-    // partitions past np get weight 0) -----------------------------------------
-    float ov[kWave];
+  // ---- every load of the first chunk up front (indexes clamped in range) ----
+  float ov[kWave];
 #pragma unroll
-    for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(u, np - 1) * D];
-    const float m0 = lane < np ? ms[lane] : -INFINITY;
-    const float l0 = lane < np ? ls[lane] : 0.0f;
+  for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(u, np - 1) * D];
+  const float m0 = lane < np ? ms[lane] : -INFINITY;
+  const float l0 = lane < np ? ls[lane] : 0.0f;
 
-    // ---- M and the normaliser ---------------------------------------------------
-    float m = m0;
-    for (int j = kWave + lane; j < np; j += kWave) m = fmaxf(m, ms[j]);
-    const float M = wave_max_all(m);
-    const bool empty = (M == -INFINITY);
-    const float w0 = (lane < np && !empty) ? __builtin_amdgcn_exp2f(m0 - M) : 0.0f;
-    float lsum = w0 * l0;
-    for (int j = kWave + lane; j < np; j += kWave)
-      lsum += (empty ? 0.0f : __builtin_amdgcn_exp2f(ms[j] - M)) * ls[j];
-    const float L = wave_sum_all(lsum);
+  // ---- M and the normaliser ---------------------------------------------------
+  float m = m0;
+  for (int j = kWave + lane; j < np; j += kWave) m = fmaxf(m, ms[j]);
+  const float M = wave_max_all(m);
+  const bool empty = (M == -INFINITY);
+  const float w0 = empty ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);   // 0 for m0 = -inf
+  float lsum = w0 * l0;
+  for (int j = kWave + lane; j < np; j += kWave)
+    lsum += (empty ? 0.0f : __builtin_amdgcn_exp2f(ms[j] - M)) * ls[j];
+  const float L = wave_sum_all(lsum);
 
-    // ---- weighted sum of the partial outputs ------------------------------------
-    float acc = 0.0f;
+  // ---- weighted sum of the partial outputs (4 independent chains) -------------
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < kWave; ++u) acc += lane_value(w0, u) * ov[u];
-    for (int base = kWave; base < np; base += kWave) {
-      const int j = base + lane;
-      const float wl = (j < np && !empty) ? __builtin_amdgcn_exp2f(ms[j] - M) : 0.0f;
-#pragma unroll
-      for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(base + u, np - 1) * D];
-#pragma unroll
-      for (int u = 0; u < kWave; ++u) acc += lane_value(wl, u) * ov[u];
-    }
-    r = L > 0.0f ? acc / L * vs : 0.0f;
+  for (int u = 0; u < kWave; ++u) {
+    const float wu = lane_value(w0, u);
+    acc[u % 4] += wu != 0.0f ? wu * ov[u] : 0.0f;
   }
+  for (int base = kWave; base < np; base += kWave) {
+    const int j = base + lane;
+    const float wl = (j < np && !empty) ? __builtin_amdgcn_exp2f(ms[j] - M) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(base + u, np - 1) * D];
+#pragma unroll
+    for (int u = 0; u < kWave; ++u) {
+      const float wu = lane_value(wl, u);
+      acc[u % 4] += wu != 0.0f ? wu * ov[u] : 0.0f;
+    }
+  }
+  const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  const float r = L > 0.0f ? o / L * vs : 0.0f;
   if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
   else reinterpret_cast<float*>(p.out)[row * D + d] = r;
 }
@@ -802,7 +813,7 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
   if (!FP8) pr.v_scale = nullptr;
   hipLaunchKernelGGL((paged_decode_reduce_kernel<D>),
                      dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(D), 0,
-                     stream, pr, NW * p.pages_per_wave);
+                     stream, pr);
   return hipGetLastError();
 }
 
