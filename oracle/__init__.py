@@ -1,4 +1,5 @@
-"""CPU oracle for the FP8 e4m3 paged KV cache and GQA paged decode attention.
+"""CPU oracle for the FP8 (e4m3, e5m2) paged KV cache and GQA paged decode
+attention.
 
 TEST INFRASTRUCTURE. Only tests/, the smoke check in __graft_entry__ and the
 CPU-baseline leg of bench.py import this package. The product path (the HIP
@@ -27,7 +28,8 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _u64p = ctypes.POINTER(ctypes.c_uint64)
 
-FP8 = 1
+FP8 = 1          # e4m3
+E5M2 = 2
 BF16 = 0
 
 
@@ -48,6 +50,25 @@ def lib():
         L.orc_e4m3_encode_scan.argtypes = [ctypes.c_float]
         L.orc_e4m3_encode_bits.restype = ctypes.c_uint8
         L.orc_e4m3_encode_bits.argtypes = [ctypes.c_uint32]
+        L.orc_e5m2_decode.restype = ctypes.c_double
+        L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_decode_all.argtypes = [_f64p]
+        L.orc_e5m2_encode.restype = ctypes.c_uint8
+        L.orc_e5m2_encode.argtypes = [ctypes.c_float]
+        L.orc_e5m2_encode_scan.restype = ctypes.c_uint8
+        L.orc_e5m2_encode_scan.argtypes = [ctypes.c_float]
+        L.orc_e5m2_encode_bits.restype = ctypes.c_uint8
+        L.orc_e5m2_encode_bits.argtypes = [ctypes.c_uint32]
+        L.orc_sweep_encoders_e5m2.restype = ctypes.c_uint64
+        L.orc_sweep_encoders_e5m2.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
+                                              ctypes.c_int, _u64p]
+        L.orc_quantize_fmt.restype = ctypes.c_uint8
+        L.orc_quantize_fmt.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_float]
+        L.orc_quantize_fmt_array_mt.argtypes = [ctypes.c_int, _f32p, ctypes.c_int64,
+                                                ctypes.c_float, _u8p, ctypes.c_int]
+        L.orc_scale_from_amax_fmt.argtypes = [_u16p, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              _f32p]
         L.orc_sweep_encoders.restype = ctypes.c_uint64
         L.orc_sweep_encoders.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
                                          ctypes.c_int, _u64p]
@@ -112,35 +133,57 @@ def e4m3_encode_bits(u: int) -> int:
     return int(lib().orc_e4m3_encode_bits(ctypes.c_uint32(u)))
 
 
-def sweep_encoders(lo=0, hi=1 << 32, nthreads=None):
-    """Compare the table encoder with the bit-field encoder on every 32-bit
-    pattern in [lo, hi). Returns (mismatches, first mismatching pattern)."""
+def sweep_encoders(lo=0, hi=1 << 32, nthreads=None, fmt=FP8):
+    """Compare the table encoder with the bit-field encoder of one format
+    (FP8 = e4m3, E5M2) on every 32-bit pattern in [lo, hi). Returns
+    (mismatches, first mismatching pattern)."""
     first = ctypes.c_uint64(0)
-    bad = lib().orc_sweep_encoders(lo, hi, _threads(nthreads), ctypes.byref(first))
+    fn = lib().orc_sweep_encoders_e5m2 if fmt == E5M2 else lib().orc_sweep_encoders
+    bad = fn(lo, hi, _threads(nthreads), ctypes.byref(first))
     return int(bad), int(first.value)
 
 
-def quantize(x_f32: np.ndarray, scale: float, nthreads=None) -> np.ndarray:
-    """E4M3_sat_RNE(x / scale) element by element (fp32 division)."""
+def e5m2_decode_all() -> np.ndarray:
+    out = np.zeros(256, dtype=np.float64)
+    lib().orc_e5m2_decode_all(_ptr(out, _f64p))
+    return out
+
+
+def e5m2_encode(y: float) -> int:
+    return int(lib().orc_e5m2_encode(ctypes.c_float(y)))
+
+
+def e5m2_encode_scan(y: float) -> int:
+    return int(lib().orc_e5m2_encode_scan(ctypes.c_float(y)))
+
+
+def e5m2_encode_bits(u: int) -> int:
+    return int(lib().orc_e5m2_encode_bits(ctypes.c_uint32(u)))
+
+
+def quantize(x_f32: np.ndarray, scale: float, nthreads=None, fmt=FP8) -> np.ndarray:
+    """FMT_sat_RNE(x / scale) element by element (fp32 division); fmt FP8 is
+    e4m3, E5M2 is e5m2."""
     x = np.ascontiguousarray(x_f32, dtype=np.float32).ravel()
     out = np.empty(x.size, dtype=np.uint8)
-    lib().orc_quantize_f32_array_mt(_ptr(x, _f32p), x.size, ctypes.c_float(scale),
+    lib().orc_quantize_fmt_array_mt(int(fmt), _ptr(x, _f32p), x.size, ctypes.c_float(scale),
                                     _ptr(out, _u8p), _threads(nthreads))
     return out.reshape(np.shape(x_f32))
 
 
-def quantize_one(x: float, scale: float) -> int:
-    return int(lib().orc_quantize_f32(ctypes.c_float(x), ctypes.c_float(scale)))
+def quantize_one(x: float, scale: float, fmt=FP8) -> int:
+    return int(lib().orc_quantize_fmt(int(fmt), ctypes.c_float(x), ctypes.c_float(scale)))
 
 
 # ---------------------------------------------------------------- scales ---
-def scale_from_amax(x_bf16: np.ndarray, per_head: bool) -> np.ndarray:
-    """x_bf16: uint16 [T][H][D]. Returns float32 [H] or [1]."""
+def scale_from_amax(x_bf16: np.ndarray, per_head: bool, fmt=FP8) -> np.ndarray:
+    """x_bf16: uint16 [T][H][D]. Returns float32 [H] or [1]: amax / 448 (e4m3)
+    or amax / 57344 (e5m2)."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     T, H, D = x.shape
     out = np.zeros(H if per_head else 1, dtype=np.float32)
-    lib().orc_scale_from_amax(_ptr(x, _u16p), T, H, D, int(per_head),
-                              _ptr(out, _f32p))
+    lib().orc_scale_from_amax_fmt(_ptr(x, _u16p), T, H, D, int(per_head), int(fmt),
+                                  _ptr(out, _f32p))
     return out
 
 
@@ -154,7 +197,7 @@ def v_offset(r, d, elem_bytes):
 
 
 def page_bytes(head_dim: int, dtype: int) -> int:
-    return 16 * head_dim * (1 if dtype == FP8 else 2)
+    return 16 * head_dim * (2 if dtype == BF16 else 1)
 
 
 # ----------------------------------------------------------- cache write ---

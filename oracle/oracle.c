@@ -1,6 +1,6 @@
 /*
  * oracle.c - plain, slow, float64 CPU oracle for the FP8 e4m3 paged KV cache
- * and GQA paged decode attention.
+ * (and E5M2) and GQA paged decode attention.
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg load this library. The product (the HIP library and its
@@ -14,8 +14,14 @@
  *    it in the engine" (smallest subnormal 2^-9). Exponent bias 7, no
  *    infinities and the single NaN mantissa pattern are the OCP definition
  *    the latter page refers to.
+ *  - E5M2 format (1 sign, 5 exponent, 2 mantissa bits, range about +-57344):
+ *    "FP8量化与长上下文推理" section 1 (format table); offered as a KV-cache
+ *    dtype (fp8_e5m2) in "cooking-agi", section "how to enable it in the
+ *    engine". Exponent bias 15, infinities (S.11111.00) and NaNs
+ *    (S.11111.xx, xx != 0) are the OCP definition.
  *  - Saturating conversion (overflow clamps to the largest finite value):
- *    "cooking-agi", section "dynamic vs static scale".
+ *    "cooking-agi", section "dynamic vs static scale"; applied to both
+ *    formats (E5M2 infinities saturate too, like E4M3's).
  *  - Symmetric scaled quantisation q = round(x / s), dequantisation q * s,
  *    s = max_abs / 448: "FP8量化与长上下文推理" section 1.1.
  *  - Cache write into pages with a scalar or per-KV-head scale: "State of FP8
@@ -199,6 +205,153 @@ uint64_t orc_sweep_encoders(uint64_t lo, uint64_t hi, int nthreads,
 }
 
 /* ------------------------------------------------------------------------ */
+/* E5M2 decode: the OCP definition written out.                              */
+/* ------------------------------------------------------------------------ */
+double orc_e5m2_decode(uint8_t c) {
+  int s = c >> 7;
+  int e = (c >> 2) & 31;
+  int m = c & 3;
+  double mag;
+  if (e == 31) {
+    if (m != 0) return NAN;                        /* S.11111.xx */
+    mag = INFINITY;                                /* S.11111.00 */
+  } else if (e == 0) {
+    mag = ldexp((double)m, -16);                   /* m/4 * 2^(1-15) */
+  } else {
+    mag = ldexp((double)(4 + m), e - 17);          /* (1+m/4) * 2^(e-15) */
+  }
+  return s ? -mag : mag;
+}
+
+void orc_e5m2_decode_all(double* out256) {
+  for (int c = 0; c < 256; ++c) out256[c] = orc_e5m2_decode((uint8_t)c);
+}
+
+/* E5M2 encode, saturating, round-to-nearest-even: nearest of the 124
+ * non-negative finite values (codes 0x00..0x7B, increasing with the code),
+ * an exact midpoint to the even code; |y| >= 57344 and Inf give 0x7B, NaN
+ * gives 0x7F with the sign of y. */
+static double g_table5[124];
+static pthread_once_t g_table5_once = PTHREAD_ONCE_INIT;
+
+static void build_table5(void) {
+  for (int c = 0; c < 124; ++c) g_table5[c] = orc_e5m2_decode((uint8_t)c);
+}
+
+uint8_t orc_e5m2_encode(float y) {
+  pthread_once(&g_table5_once, build_table5);
+  uint32_t sign = f32_bits(y) >> 31;
+  if (isnan(y)) return (uint8_t)(0x7F | (sign << 7));
+  double a = fabs((double)y);
+  int code;
+  if (a >= g_table5[123]) {
+    code = 123;                                    /* saturate, Inf too */
+  } else {
+    int lo = 0, hi = 123;                          /* g_table5[lo] <= a < g_table5[hi] */
+    while (hi - lo > 1) {
+      int mid = (lo + hi) / 2;
+      if (g_table5[mid] <= a) lo = mid; else hi = mid;
+    }
+    double below = g_table5[lo], above = g_table5[hi];
+    double mid = 0.5 * (below + above);            /* exact in double */
+    if (a < mid) code = lo;
+    else if (a > mid) code = hi;
+    else code = (lo % 2 == 0) ? lo : hi;
+  }
+  return (uint8_t)(code | (sign << 7));
+}
+
+/* The same definition by a linear scan (samples only). */
+uint8_t orc_e5m2_encode_scan(float y) {
+  pthread_once(&g_table5_once, build_table5);
+  uint32_t sign = f32_bits(y) >> 31;
+  if (isnan(y)) return (uint8_t)(0x7F | (sign << 7));
+  double a = fabs((double)y);
+  if (a > g_table5[123]) a = g_table5[123];
+  int best = 0;
+  double best_d = fabs(a - g_table5[0]);
+  for (int c = 1; c < 124; ++c) {
+    double d = fabs(a - g_table5[c]);
+    if (d < best_d || (d == best_d && (c % 2 == 0))) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(best | (sign << 7));
+}
+
+/* A second, independent E5M2 encoder on the fp32 bit fields (pins the
+ * table encoder over all 2^32 inputs). */
+uint8_t orc_e5m2_encode_bits(uint32_t u) {
+  uint32_t sign = (u >> 31) << 7;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return (uint8_t)(sign | 0x7F);         /* NaN */
+  if (a >= 0x47600000u) return (uint8_t)(sign | 0x7B);        /* >= 57344, Inf */
+  uint32_t E = a >> 23;
+  if (E >= 113) {                                              /* >= 2^-14 */
+    /* Keep 2 of the 23 mantissa bits with RNE on the integer E:M, then move
+     * the exponent bias from 127 to 15. */
+    uint32_t keep = a >> 21;
+    uint32_t rem = a & 0x1FFFFFu;
+    if (rem > 0x100000u || (rem == 0x100000u && (keep & 1u))) keep += 1;
+    return (uint8_t)(sign | (keep - (112u << 2)));
+  }
+  if (E == 0) return (uint8_t)sign;                            /* fp32 subnormal */
+  /* Below 2^-14: multiples of 2^-16. k = RNE(value * 2^16), value * 2^16 =
+   * (2^23 + M) * 2^(E - 134). k = 4 is the smallest normal, code 0x04. */
+  uint32_t mant = (1u << 23) | (a & 0x7FFFFFu);
+  uint32_t shift = 134u - E;                                   /* >= 22 */
+  if (shift >= 32) return (uint8_t)sign;
+  uint32_t k = mant >> shift;
+  uint32_t r = mant & ((1u << shift) - 1u);
+  uint32_t half = 1u << (shift - 1);
+  if (r > half || (r == half && (k & 1u))) k += 1;
+  return (uint8_t)(sign | k);
+}
+
+typedef struct {
+  uint64_t lo, hi, bad, first;
+} sweep5_job;
+
+static void* sweep5_worker(void* p) {
+  sweep5_job* j = (sweep5_job*)p;
+  j->bad = 0;
+  j->first = UINT64_MAX;
+  for (uint64_t u = j->lo; u < j->hi; ++u) {
+    float f;
+    uint32_t b = (uint32_t)u;
+    memcpy(&f, &b, 4);
+    if (orc_e5m2_encode(f) != orc_e5m2_encode_bits(b)) {
+      if (j->bad == 0) j->first = u;
+      j->bad++;
+    }
+  }
+  return NULL;
+}
+
+uint64_t orc_sweep_encoders_e5m2(uint64_t lo, uint64_t hi, int nthreads,
+                                 uint64_t* first_bad) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  sweep5_job jobs[256];
+  uint64_t n = hi - lo;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i].lo = lo + n * (uint64_t)i / (uint64_t)nthreads;
+    jobs[i].hi = lo + n * (uint64_t)(i + 1) / (uint64_t)nthreads;
+    pthread_create(&th[i], NULL, sweep5_worker, &jobs[i]);
+  }
+  uint64_t bad = 0, first = UINT64_MAX;
+  for (int i = 0; i < nthreads; ++i) {
+    pthread_join(th[i], NULL);
+    bad += jobs[i].bad;
+    if (jobs[i].first < first) first = jobs[i].first;
+  }
+  if (first_bad) *first_bad = first;
+  return bad;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Quantisation: code = E4M3_sat_RNE( fp32(x) / s ), fp32 IEEE division.     */
 /* ------------------------------------------------------------------------ */
 static float bf16_to_f32(uint16_t h) {
@@ -213,6 +366,12 @@ uint8_t orc_quantize_f32(float x, float s) {
   return orc_e4m3_encode(y);
 }
 
+/* The same quantisation into either format: fmt 1 = E4M3, 2 = E5M2. */
+uint8_t orc_quantize_fmt(int fmt, float x, float s) {
+  volatile float y = x / s;
+  return fmt == 2 ? orc_e5m2_encode(y) : orc_e4m3_encode(y);
+}
+
 void orc_quantize_f32_array(const float* x, int64_t n, float s, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_quantize_f32(x[i], s);
 }
@@ -222,16 +381,17 @@ typedef struct {
   const float* x;
   int64_t lo, hi;
   float s;
+  int fmt;
   uint8_t* out;
 } qjob;
 
 static void* quant_worker(void* p) {
   qjob* j = (qjob*)p;
-  for (int64_t i = j->lo; i < j->hi; ++i) j->out[i] = orc_quantize_f32(j->x[i], j->s);
+  for (int64_t i = j->lo; i < j->hi; ++i) j->out[i] = orc_quantize_fmt(j->fmt, j->x[i], j->s);
   return NULL;
 }
 
-void orc_quantize_f32_array_mt(const float* x, int64_t n, float s, uint8_t* out,
+void orc_quantize_fmt_array_mt(int fmt, const float* x, int64_t n, float s, uint8_t* out,
                                int nthreads) {
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
@@ -242,17 +402,26 @@ void orc_quantize_f32_array_mt(const float* x, int64_t n, float s, uint8_t* out,
     jobs[i].lo = n * (int64_t)i / nthreads;
     jobs[i].hi = n * (int64_t)(i + 1) / nthreads;
     jobs[i].s = s;
+    jobs[i].fmt = fmt;
     jobs[i].out = out;
     pthread_create(&th[i], NULL, quant_worker, &jobs[i]);
   }
   for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
 }
 
+void orc_quantize_f32_array_mt(const float* x, int64_t n, float s, uint8_t* out,
+                               int nthreads) {
+  orc_quantize_fmt_array_mt(1, x, n, s, out, nthreads);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scale calibration: s = fp32(amax) / 448 over one KV head (or the tensor). */
 /* ------------------------------------------------------------------------ */
-void orc_scale_from_amax(const uint16_t* x, int64_t T, int H, int D,
-                         int per_head, float* out) {
+/* s = fp32(amax) / fmax, fmax = 448 (E4M3, fmt 1) or 57344 (E5M2, fmt 2):
+ * the largest value lands on the format's largest finite value. */
+void orc_scale_from_amax_fmt(const uint16_t* x, int64_t T, int H, int D,
+                             int per_head, int fmt, float* out) {
+  const float fmax = fmt == 2 ? 57344.0f : 448.0f;
   int nout = per_head ? H : 1;
   for (int o = 0; o < nout; ++o) {
     double amax = 0.0;
@@ -270,9 +439,14 @@ void orc_scale_from_amax(const uint16_t* x, int64_t T, int H, int D,
     else if (amax == 0.0) out[o] = 1.0f;
     else {
       volatile float a = (float)amax;              /* exact: a bf16 value or Inf */
-      out[o] = a / 448.0f;
+      out[o] = a / fmax;
     }
   }
+}
+
+void orc_scale_from_amax(const uint16_t* x, int64_t T, int H, int D,
+                         int per_head, float* out) {
+  orc_scale_from_amax_fmt(x, T, H, D, per_head, 1, out);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -291,14 +465,14 @@ int64_t orc_v_offset(int r, int d, int e) {
          (int64_t)(d % db) * 4 * e + (int64_t)(r % 4) * e;
 }
 
-/* Cache write. k, v: bf16 bits [T][H][D]. dtype 1 = fp8 e4m3, 0 = bf16.
- * Scales are read at index h when per_head, else index 0. */
+/* Cache write. k, v: bf16 bits [T][H][D]. dtype 1 = fp8 e4m3, 2 = fp8 e5m2,
+ * 0 = bf16. Scales are read at index h when per_head, else index 0. */
 void orc_kv_cache_write(int H, int D, int dtype, int per_head,
                         const uint16_t* k, const uint16_t* v,
                         const int64_t* slots, int64_t T, uint8_t* kc,
                         uint8_t* vc, int64_t num_pages, const float* ks,
                         const float* vs) {
-  int e = dtype == 1 ? 1 : 2;
+  int e = dtype == 0 ? 2 : 1;
   int64_t pb = 16LL * D * e;
   for (int64_t t = 0; t < T; ++t) {
     int64_t slot = slots[t];
@@ -312,10 +486,10 @@ void orc_kv_cache_write(int H, int D, int dtype, int per_head,
       for (int d = 0; d < D; ++d) {
         uint16_t kx = k[(t * H + h) * D + d];
         uint16_t vx = v[(t * H + h) * D + d];
-        if (dtype == 1) {
+        if (dtype != 0) {
           float sk = ks[per_head ? h : 0], sv = vs[per_head ? h : 0];
-          kb[orc_k_offset(r, d, 1)] = orc_quantize_f32(bf16_to_f32(kx), sk);
-          vb[orc_v_offset(r, d, 1)] = orc_quantize_f32(bf16_to_f32(vx), sv);
+          kb[orc_k_offset(r, d, 1)] = orc_quantize_fmt(dtype, bf16_to_f32(kx), sk);
+          vb[orc_v_offset(r, d, 1)] = orc_quantize_fmt(dtype, bf16_to_f32(vx), sv);
         } else {
           int64_t ko = orc_k_offset(r, d, 2), vo = orc_v_offset(r, d, 2);
           kb[ko] = (uint8_t)(kx & 0xFF);
@@ -372,11 +546,12 @@ void orc_kv_cache_write_mt(int H, int D, int dtype, int per_head,
 /* Dequantised element (float64) of the K or V cache. */
 static double cache_value(const uint8_t* cache, int is_v, int64_t page, int H,
                           int h, int r, int d, int D, int dtype, double scale) {
-  int e = dtype == 1 ? 1 : 2;
+  int e = dtype == 0 ? 2 : 1;
   int64_t pb = 16LL * D * e;
   const uint8_t* blk = cache + (page * H + h) * pb;
   int64_t off = is_v ? orc_v_offset(r, d, e) : orc_k_offset(r, d, e);
   if (dtype == 1) return orc_e4m3_decode(blk[off]) * scale;
+  if (dtype == 2) return orc_e5m2_decode(blk[off]) * scale;
   uint16_t bits = (uint16_t)(blk[off] | (blk[off + 1] << 8));
   return (double)bf16_to_f32(bits);
 }
@@ -427,8 +602,8 @@ static int64_t gather(const att_args* a, int b, int i, double* z, double* v) {
   int64_t L = a->lens[b];
   if (L <= 0) return 0;
   int64_t lo = (a->window > 0 && L > a->window) ? L - a->window : 0;
-  double ks = a->dtype == 1 ? (double)a->ks[a->per_head ? h : 0] : 1.0;
-  double vs = a->dtype == 1 ? (double)a->vs[a->per_head ? h : 0] : 1.0;
+  double ks = a->dtype != 0 ? (double)a->ks[a->per_head ? h : 0] : 1.0;
+  double vs = a->dtype != 0 ? (double)a->vs[a->per_head ? h : 0] : 1.0;
   const uint16_t* qi = a->q + ((int64_t)b * a->Hq + i) * a->D;
   for (int64_t t = lo; t < L; ++t) {
     int64_t page = a->bt[(int64_t)b * a->max_pages + t / 16];
