@@ -342,7 +342,7 @@ def main():
     ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS))
     ap.add_argument("--context", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--cache", default="fp8_e4m3", choices=["fp8_e4m3", "bf16"])
+    ap.add_argument("--cache", default="fp8_e4m3", choices=["fp8_e4m3", "fp8_e5m2", "bf16"])
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="fused: kvq_decode_step per layer; separate: write + attention calls")
     ap.add_argument("--no-sweep", action="store_true")
@@ -432,8 +432,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 cache, bf16 MFMA on exact e4m3 values, fp32 accumulation"
-                 if args.cache.startswith("fp8") else "bf16 cache, fp32 accumulation",
+        "dtype": (f"{args.cache} cache, bf16 MFMA on exact {args.cache[4:]} values, "
+                  "fp32 accumulation") if args.cache.startswith("fp8")
+                 else "bf16 cache, fp32 accumulation",
         "data": "synthetic (seeded normal K/V/q)",
         "config": {
             "workload": f"{w['desc']}, {ctx_desc}, {args.cache} cache with per-KV-head scales, "

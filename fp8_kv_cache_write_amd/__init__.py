@@ -16,12 +16,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvfp8.so")
 
 # enums of kvfp8.h
-BF16, FP8_E4M3 = 0, 1
+BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2
 PER_TENSOR, PER_KV_HEAD = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 PAGE_SIZE = 16
 
-_DTYPES = {"bf16": BF16, "auto": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
+_DTYPES = {"bf16": BF16, "auto": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3,
+           "fp8_e5m2": FP8_E5M2}
 _SCALES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD}
 
 
@@ -39,7 +40,7 @@ class LayerDesc(ctypes.Structure):
 
     @property
     def fp8(self):
-        return self.cache_dtype == FP8_E4M3
+        return self.cache_dtype in (FP8_E4M3, FP8_E5M2)
 
     @property
     def elem_bytes(self):
@@ -53,8 +54,8 @@ class LayerDesc(ctypes.Structure):
 
 def layer_desc(num_q_heads, num_kv_heads, head_dim, cache_dtype="fp8_e4m3",
                scale_mode="per_kv_head", sliding_window=0, sm_scale=0.0):
-    """Descriptor of one attention layer. cache_dtype: "fp8_e4m3"/"fp8" or
-    "bf16"/"auto"; scale_mode: "per_tensor" or "per_kv_head"."""
+    """Descriptor of one attention layer. cache_dtype: "fp8_e4m3"/"fp8",
+    "fp8_e5m2" or "bf16"/"auto"; scale_mode: "per_tensor" or "per_kv_head"."""
     return LayerDesc(int(num_q_heads), int(num_kv_heads), int(head_dim), PAGE_SIZE,
                      _DTYPES[cache_dtype] if isinstance(cache_dtype, str) else int(cache_dtype),
                      _SCALES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode),
@@ -83,13 +84,15 @@ def lib():
                                       i32, vp, vp, vp, sz, vp]
         L.kvq_kv_scale_from_amax.argtypes = [dp, vp, i64, vp, vp]
         L.kvq_e4m3_quantize.argtypes = [vp, i64, vp, vp, vp]
+        L.kvq_e5m2_quantize.argtypes = [vp, i64, vp, vp, vp]
         L.kvq_status_string.argtypes = [i32]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_profile_begin.argtypes = [i32]
         L.kvq_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
         for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes", "kvq_decode_step",
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
-                  "kvq_e4m3_quantize", "kvq_profile_begin", "kvq_profile_end"):
+                  "kvq_e4m3_quantize", "kvq_e5m2_quantize", "kvq_profile_begin",
+                  "kvq_profile_end"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -238,8 +241,9 @@ def decode_step(desc, k_new, v_new, k_cache, v_cache, out, q, block_tables,
 
 
 def kv_scale_from_amax(desc, x, scale_out, stream=None):
-    """scale_out[h] = amax(|x[:, h, :]|) / 448 (or one scale over all heads
-    for per-tensor layers). x: bf16 [T, Hkv, D]; scale_out: float32."""
+    """scale_out[h] = amax(|x[:, h, :]|) / 448 (57344 for an e5m2 layer), or
+    one scale over all heads for per-tensor layers. x: bf16 [T, Hkv, D];
+    scale_out: float32."""
     import torch
     _need(x, "x", torch.bfloat16)
     _need(scale_out, "scale_out", torch.float32)
@@ -252,16 +256,24 @@ def kv_scale_from_amax(desc, x, scale_out, stream=None):
         ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(scale_out), _stream(stream)))
 
 
-def e4m3_quantize(x, scale, out, stream=None):
-    """out[i] = e4m3_sat_rne(x[i] / scale[0]); x float32, out uint8."""
+def _quantize(fn, x, scale, out, stream):
     import torch
     _need(x, "x", torch.float32)
     _need(scale, "scale", torch.float32)
     _need(out, "out", torch.uint8)
     if out.numel() != x.numel():
         raise ValueError("out must have as many elements as x")
-    _check("kvq_e4m3_quantize", lib().kvq_e4m3_quantize(
-        _ptr(x), x.numel(), _ptr(scale), _ptr(out), _stream(stream)))
+    _check(fn, getattr(lib(), fn)(_ptr(x), x.numel(), _ptr(scale), _ptr(out), _stream(stream)))
+
+
+def e4m3_quantize(x, scale, out, stream=None):
+    """out[i] = e4m3_sat_rne(x[i] / scale[0]); x float32, out uint8."""
+    _quantize("kvq_e4m3_quantize", x, scale, out, stream)
+
+
+def e5m2_quantize(x, scale, out, stream=None):
+    """out[i] = e5m2_sat_rne(x[i] / scale[0]); x float32, out uint8."""
+    _quantize("kvq_e5m2_quantize", x, scale, out, stream)
 
 
 def profile_begin(max_launches):

@@ -24,7 +24,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_desc(const kvq_layer_desc* d) {
   if (!d) return KVQ_ERR_INVALID_ARG;
   if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
-  if (d->cache_dtype != KVQ_BF16 && d->cache_dtype != KVQ_FP8_E4M3) return KVQ_ERR_INVALID_ARG;
+  if (d->cache_dtype != KVQ_BF16 && d->cache_dtype != KVQ_FP8_E4M3 &&
+      d->cache_dtype != KVQ_FP8_E5M2)
+    return KVQ_ERR_INVALID_ARG;
   if (d->scale_mode != KVQ_SCALE_PER_TENSOR && d->scale_mode != KVQ_SCALE_PER_KV_HEAD)
     return KVQ_ERR_INVALID_ARG;
   if (d->sliding_window < 0) return KVQ_ERR_INVALID_ARG;
@@ -108,7 +110,7 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
   if (k_best == 0)   // many sequences, or very long ones: full-length runs
     ppw = std::min<int64_t>(even_run((pages_max + kSplitWaves - 1) / kSplitWaves),
                             kMaxPagesPerWave);
-  const int64_t page_block = 16LL * d->head_dim * (d->cache_dtype == KVQ_FP8_E4M3 ? 1 : 2);
+  const int64_t page_block = 16LL * d->head_dim * (d->cache_dtype == KVQ_BF16 ? 2 : 1);
   const bool ring_fits = kSplitWaves * 2 * 2 * page_block <= 64 * 1024;
   int slots = (k_best == 1 && ring_fits) ? 1 : 0;
   int64_t direct_ppw = (pages_max + kSplitWaves - 1) / kSplitWaves;
@@ -174,13 +176,13 @@ int kvq_kv_cache_write(const kvq_layer_desc* desc, const void* k, const void* v,
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(slot_mapping, 8))
     return KVQ_ERR_INVALID_ARG;
-  const bool fp8 = desc->cache_dtype == KVQ_FP8_E4M3;
+  const bool fp8 = desc->cache_dtype != KVQ_BF16;
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return KVQ_ERR_INVALID_ARG;
   const int64_t threads = num_tokens * desc->num_kv_heads * (desc->head_dim / 16);
   if ((threads + 255) / 256 > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
   hipError_t e = launch_kv_cache_write(
-      fp8, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slot_mapping,
+      (int)desc->cache_dtype, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slot_mapping,
       num_tokens, desc->num_kv_heads, desc->head_dim, static_cast<uint8_t*>(k_cache),
       static_cast<uint8_t*>(v_cache), num_pages, k_scale, v_scale,
       desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0, static_cast<hipStream_t>(stream));
@@ -226,7 +228,7 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
     return KVQ_ERR_INVALID_ARG;
   if (fused && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
     return KVQ_ERR_INVALID_ARG;
-  const bool fp8 = desc->cache_dtype == KVQ_FP8_E4M3;
+  const bool fp8 = desc->cache_dtype != KVQ_BF16;
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return KVQ_ERR_INVALID_ARG;
   const Plan plan = make_plan(desc, num_seqs, max_context_len);
@@ -270,7 +272,8 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
     e1 = g_prof.ev[2 * g_prof.used + 1];
     g_prof.used++;
   }
-  hipError_t e = launch_paged_decode(p, desc->head_dim, fp8, num_seqs, fused, plan.slots,
+  hipError_t e = launch_paged_decode(p, desc->head_dim, (int)desc->cache_dtype, num_seqs, fused,
+                                     plan.slots,
                                      static_cast<hipStream_t>(stream), e0, e1);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -306,21 +309,34 @@ int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x, int64_t nu
   if (st) return st;
   if (num_tokens < 0 || !x || !scale_out || !aligned(x, 16) || !aligned(scale_out, 4))
     return KVQ_ERR_INVALID_ARG;
+  const float fmax = desc->cache_dtype == KVQ_FP8_E5M2 ? 57344.0f : 448.0f;
   hipError_t e = launch_scale_from_amax(
       static_cast<const uint16_t*>(x), num_tokens, desc->num_kv_heads, desc->head_dim,
-      desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0, scale_out,
+      desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0, fmax, scale_out,
       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
-int kvq_e4m3_quantize(const float* x, int64_t n, const float* scale, uint8_t* out,
-                      void* stream) {
+namespace {
+int quantize_common(int fmt, const float* x, int64_t n, const float* scale, uint8_t* out,
+                    void* stream) {
   if (n < 0) return KVQ_ERR_INVALID_ARG;
   if (n == 0) return KVQ_OK;
   if (!x || !scale || !out || !aligned(x, 16) || !aligned(out, 4) || !aligned(scale, 4))
     return KVQ_ERR_INVALID_ARG;
-  hipError_t e = launch_quantize(x, n, scale, out, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_quantize(fmt, x, n, scale, out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+}  // namespace
+
+int kvq_e4m3_quantize(const float* x, int64_t n, const float* scale, uint8_t* out,
+                      void* stream) {
+  return quantize_common(KVQ_FP8_E4M3, x, n, scale, out, stream);
+}
+
+int kvq_e5m2_quantize(const float* x, int64_t n, const float* scale, uint8_t* out,
+                      void* stream) {
+  return quantize_common(KVQ_FP8_E5M2, x, n, scale, out, stream);
 }
 
 int kvq_profile_begin(int32_t max_launches) {

@@ -1,6 +1,6 @@
 // device_common.hpp - gfx950 device helpers shared by the kvfp8 kernels:
-// vector types, the paged-cache layout, the e4m3 encoder and the exact
-// e4m3 -> bf16 expansion.
+// vector types, the paged-cache layout, the e4m3 and e5m2 encoders and the
+// exact fp8 -> bf16 expansions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,6 +15,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPage = 16;     // positions per page
 constexpr int kWave = 64;     // CDNA wavefront
+
+// Cache element formats (the values of the C ABI's kvq_dtype).
+constexpr int kFmtBf16 = 0;
+constexpr int kFmtE4M3 = 1;
+constexpr int kFmtE5M2 = 2;
 
 // ---------------------------------------------------------------------------
 // Paged layout of one (page, kv head) block, e = element bytes (1 fp8, 2 bf16).
@@ -79,6 +84,39 @@ __device__ __forceinline__ uint32_t e4m3_encode_sat(float y) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32 -> e5m2 (OCP), saturating, round to nearest even: the same scheme with
+// 2 mantissa bits and bias 15. |y| >= 57344 (and +-Inf) -> +-57344 (0x7B,
+// saturation as for e4m3); NaN -> 0x7F with the sign of y; below 2^-14 the
+// representable values are the multiples of 2^-16.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e5m2_encode_sat(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  uint32_t mag;
+  if (!(a == a)) {
+    mag = 0x7Fu;                                   // NaN
+  } else if (a >= 57344.0f) {
+    mag = 0x7Bu;                                   // saturate (Inf too)
+  } else if (a < 6.103515625e-05f) {               // 2^-14
+    mag = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 16));  // 0..4
+  } else {
+    int ex = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -14 .. 15
+    uint32_t m4 = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 2 - ex)); // 4..8
+    if (m4 == 8u) { m4 = 4u; ex += 1; }
+    mag = ((uint32_t)(ex + 15) << 2) | (m4 - 4u);  // ex + 15 in 1..30
+    if (mag > 0x7Bu) mag = 0x7Bu;
+  }
+  return sign | mag;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_encode_sat(float y) {
+  if constexpr (FMT == kFmtE5M2) return e5m2_encode_sat(y);
+  else return e4m3_encode_sat(y);
+}
+
+// ---------------------------------------------------------------------------
 // e4m3 -> bf16, exact (every e4m3 value, subnormals included, is a bf16
 // value). gfx950 converts two codes of a dword per instruction; the scale
 // operand 1.0 leaves the values unchanged. NaN codes give NaN.
@@ -97,6 +135,34 @@ __device__ __forceinline__ bf16x4 e4m3x4_to_bf16x4(uint32_t w) {
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   bf16x4 a = e4m3x4_to_bf16x4(w0);
   bf16x4 b = e4m3x4_to_bf16x4(w1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// e5m2 -> bf16, exact likewise (bf16 has the wider exponent; e5m2 infinities
+// and NaNs stay infinities and NaNs).
+__device__ __forceinline__ bf16x2 e5m2x2_to_bf16x2(uint32_t w, bool high_pair) {
+  return high_pair ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)
+                   : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
+}
+
+// Four / eight codes of either fp8 format to bf16.
+template <int FMT>
+__device__ __forceinline__ bf16x4 fp8x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo, hi;
+  if constexpr (FMT == kFmtE5M2) {
+    lo = e5m2x2_to_bf16x2(w, false);
+    hi = e5m2x2_to_bf16x2(w, true);
+  } else {
+    lo = e4m3x2_to_bf16x2(w, false);
+    hi = e4m3x2_to_bf16x2(w, true);
+  }
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+}
+
+template <int FMT>
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  bf16x4 a = fp8x4_to_bf16x4<FMT>(w0);
+  bf16x4 b = fp8x4_to_bf16x4<FMT>(w1);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 

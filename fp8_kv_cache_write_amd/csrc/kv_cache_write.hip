@@ -1,12 +1,14 @@
 // kv_cache_write.hip - quantise new tokens' K/V into the paged cache (gfx950),
-// plus the static amax/448 scale calibration and the flat e4m3 quantiser.
+// plus the static amax/fmax scale calibration and the flat fp8 quantiser, for
+// the e4m3 and e5m2 formats.
 //
 // The write is the cache-write kernel of "State of FP8 KV cache and attention
 // quantization in vLLM" (section "Kernel and vLLM improvements", paragraph
 // "Per-head scales": one FP32 scale per KV head instead of a scalar); the
 // conversion is "FP8量化与长上下文推理" section 1.1 (q = round(x / s)) with the
 // saturating mode of "cooking-agi: FP8 and the KV cache" (section "dynamic vs
-// static scale").
+// static scale"); e5m2 is the same page's second fp8 cache dtype (section "how
+// to enable it in the engine").
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -18,7 +20,7 @@ namespace kvfp8 {
 //         (the V layout interleaves 4 rows per dim, so a row's dims are 4 bytes
 //         apart);
 //   bf16: K as two 16-byte stores, V as 16 two-byte stores.
-template <bool FP8>
+template <int FMT>
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ slots, int64_t num_tokens, int num_kv_heads,
@@ -46,6 +48,7 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   const uint32_t* kw = reinterpret_cast<const uint32_t*>(kx);
   const uint32_t* vw = reinterpret_cast<const uint32_t*>(vx);
 
+  constexpr bool FP8 = FMT != kFmtBf16;
   constexpr int E = FP8 ? 1 : 2;
   const int64_t pb = (int64_t)kPage * head_dim * E;
   uint8_t* kb = k_cache + (page * num_kv_heads + h) * pb;
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
       for (int b = 0; b < 4; ++b) {
         const int e = j * 4 + b;
         const uint32_t bits = (kw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-        w |= e4m3_encode_sat(bf16_bits_to_f32(bits) / sk) << (8 * b);
+        w |= fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sk) << (8 * b);
       }
       kq[j] = w;
     }
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     for (int e = 0; e < 16; ++e) {
       const uint32_t bits = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
       vb[v_byte<1>(r, d0 + e)] =
-          (uint8_t)e4m3_encode_sat(bf16_bits_to_f32(bits) / sv);
+          (uint8_t)fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sv);
     }
   } else {
     // bf16 layers keep the bits: the skip-layer path.
@@ -88,12 +91,13 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   }
 }
 
-// Static scale calibration: s = fp32(amax) / 448 over one KV head (or over
-// every head). One work-group per output scale; threads stride over the
-// tensor in 16-byte loads. NaN anywhere gives NaN, amax == 0 gives 1.
+// Static scale calibration: s = fp32(amax) / fmax over one KV head (or over
+// every head); fmax = 448 (e4m3) or 57344 (e5m2). One work-group per output
+// scale; threads stride over the tensor in 16-byte loads. NaN anywhere gives
+// NaN, amax == 0 gives 1.
 __global__ __launch_bounds__(1024) void scale_from_amax_kernel(
     const uint16_t* __restrict__ x, int64_t num_tokens, int num_kv_heads,
-    int head_dim, int per_head, float* __restrict__ scale_out) {
+    int head_dim, int per_head, float fmax, float* __restrict__ scale_out) {
   const int h_out = blockIdx.x;
   const int chunks = head_dim / 8;                 // 8 bf16 per 16 bytes
   const int heads_here = per_head ? 1 : num_kv_heads;
@@ -139,12 +143,13 @@ __global__ __launch_bounds__(1024) void scale_from_amax_kernel(
     float s;
     if (n) s = __builtin_nanf("");
     else if (m == 0.0f) s = 1.0f;
-    else s = m / 448.0f;
+    else s = m / fmax;
     scale_out[h_out] = s;
   }
 }
 
-// Flat quantiser: out[i] = e4m3(x[i] / s), 4 elements per thread.
+// Flat quantiser: out[i] = fp8(x[i] / s), 4 elements per thread.
+template <int FMT>
 __global__ __launch_bounds__(256) void quantize_kernel(
     const float* __restrict__ x, int64_t n, const float* __restrict__ scale,
     uint8_t* __restrict__ out) {
@@ -155,17 +160,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const int64_t base = i * 4;
     if (base + 4 <= n) {
       const float4 f = *reinterpret_cast<const float4*>(x + base);
-      const uint32_t w = e4m3_encode_sat(f.x / s) | (e4m3_encode_sat(f.y / s) << 8) |
-                         (e4m3_encode_sat(f.z / s) << 16) |
-                         (e4m3_encode_sat(f.w / s) << 24);
+      const uint32_t w = fp8_encode_sat<FMT>(f.x / s) | (fp8_encode_sat<FMT>(f.y / s) << 8) |
+                         (fp8_encode_sat<FMT>(f.z / s) << 16) |
+                         (fp8_encode_sat<FMT>(f.w / s) << 24);
       *reinterpret_cast<uint32_t*>(out + base) = w;
     } else {
-      for (int64_t j = base; j < n; ++j) out[j] = (uint8_t)e4m3_encode_sat(x[j] / s);
+      for (int64_t j = base; j < n; ++j) out[j] = (uint8_t)fp8_encode_sat<FMT>(x[j] / s);
     }
   }
 }
 
-hipError_t launch_kv_cache_write(bool fp8, const uint16_t* k, const uint16_t* v,
+hipError_t launch_kv_cache_write(int fmt, const uint16_t* k, const uint16_t* v,
                                  const int64_t* slots, int64_t num_tokens,
                                  int num_kv_heads, int head_dim, uint8_t* k_cache,
                                  uint8_t* v_cache, int64_t num_pages,
@@ -174,34 +179,44 @@ hipError_t launch_kv_cache_write(bool fp8, const uint16_t* k, const uint16_t* v,
   const int64_t total = num_tokens * num_kv_heads * (head_dim / 16);
   if (total == 0) return hipSuccess;
   const int64_t blocks = (total + 255) / 256;
-  if (fp8)
-    hipLaunchKernelGGL(kv_cache_write_kernel<true>, dim3((unsigned)blocks), dim3(256),
+  if (fmt == kFmtE4M3)
+    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtE4M3>, dim3((unsigned)blocks), dim3(256),
+                       0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
+                       k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
+  else if (fmt == kFmtE5M2)
+    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtE5M2>, dim3((unsigned)blocks), dim3(256),
+                       0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
+                       k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
+  else if (fmt == kFmtBf16)
+    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtBf16>, dim3((unsigned)blocks), dim3(256),
                        0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
                        k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
   else
-    hipLaunchKernelGGL(kv_cache_write_kernel<false>, dim3((unsigned)blocks), dim3(256),
-                       0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
-                       k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_scale_from_amax(const uint16_t* x, int64_t num_tokens,
                                   int num_kv_heads, int head_dim, int per_head,
-                                  float* scale_out, hipStream_t stream) {
+                                  float fmax, float* scale_out, hipStream_t stream) {
   const int blocks = per_head ? num_kv_heads : 1;
   hipLaunchKernelGGL(scale_from_amax_kernel, dim3(blocks), dim3(1024), 0, stream, x,
-                     num_tokens, num_kv_heads, head_dim, per_head, scale_out);
+                     num_tokens, num_kv_heads, head_dim, per_head, fmax, scale_out);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const float* x, int64_t n, const float* scale,
+hipError_t launch_quantize(int fmt, const float* x, int64_t n, const float* scale,
                            uint8_t* out, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   int64_t groups = (n + 3) / 4;
   int64_t blocks = (groups + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     x, n, scale, out);
+  if (fmt == kFmtE5M2)
+    hipLaunchKernelGGL(quantize_kernel<kFmtE5M2>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       x, n, scale, out);
+  else
+    hipLaunchKernelGGL(quantize_kernel<kFmtE4M3>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       x, n, scale, out);
   return hipGetLastError();
 }
 

@@ -7,18 +7,20 @@
 
 namespace kvfp8 {
 
-hipError_t launch_kv_cache_write(bool fp8, const uint16_t* k, const uint16_t* v,
+// fmt (here and below): cache element format, 0 = bf16, 1 = e4m3, 2 = e5m2.
+hipError_t launch_kv_cache_write(int fmt, const uint16_t* k, const uint16_t* v,
                                  const int64_t* slots, int64_t num_tokens,
                                  int num_kv_heads, int head_dim, uint8_t* k_cache,
                                  uint8_t* v_cache, int64_t num_pages,
                                  const float* k_scale, const float* v_scale,
                                  int scale_per_head, hipStream_t stream);
 
+// s = fp32(amax) / fmax (448 for e4m3, 57344 for e5m2).
 hipError_t launch_scale_from_amax(const uint16_t* x, int64_t num_tokens,
                                   int num_kv_heads, int head_dim, int per_head,
-                                  float* scale_out, hipStream_t stream);
+                                  float fmax, float* scale_out, hipStream_t stream);
 
-hipError_t launch_quantize(const float* x, int64_t n, const float* scale,
+hipError_t launch_quantize(int fmt, const float* x, int64_t n, const float* scale,
                            uint8_t* out, hipStream_t stream);
 
 // Everything the split-decode and reduce kernels read; passed by value.
@@ -56,8 +58,9 @@ constexpr int kSplitWaves = 4;
 // fused = true: the split kernel also writes k_new / v_new into the caches at
 // position L-1 of every sequence (p.k_cache / p.v_cache must be writable).
 // slots: split-kernel tile shape, 1 = LDS-staged tiles, 0 = register tiles.
-hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,
-                               int num_seqs, bool fused, int slots, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after);
+// fmt: cache element format, kFmtBf16 / kFmtE4M3 / kFmtE5M2 (device_common.hpp).
+hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
+                               bool fused, int slots, hipStream_t stream, hipEvent_t ev_before,
+                               hipEvent_t ev_after);
 
 }  // namespace kvfp8

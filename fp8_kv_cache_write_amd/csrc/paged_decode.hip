@@ -1,4 +1,4 @@
-// paged_decode.hip - GQA decode attention over the paged FP8 e4m3 (or bf16)
+// paged_decode.hip - GQA decode attention over the paged FP8 (e4m3 or e5m2) or bf16
 // KV cache on gfx950: a split kernel over context partitions and an FP32
 // reduce kernel that merges the partitions.
 //
@@ -140,9 +140,10 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   return r;
 }
 
-template <int D, bool FP8, int NW, int TP, int RING, int SLOTS, bool FUSED>
+template <int D, int FMT, int NW, int TP, int RING, int SLOTS, bool FUSED>
 __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const DecodeParams p) {
+  constexpr bool FP8 = FMT != kFmtBf16;
   constexpr int E = FP8 ? 1 : 2;
   constexpr int PB = kPage * D * E;     // bytes of one (page, head) block
   constexpr int NI = PB / 1024;         // 1 KiB wave loads per page per tensor
@@ -327,8 +328,8 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         uint8_t kq[VPL], vq[VPL];
 #pragma unroll
         for (int e = 0; e < VPL; ++e) {
-          kq[e] = (uint8_t)e4m3_encode_sat(bf16_bits_to_f32(kb[e]) / sk);
-          vq[e] = (uint8_t)e4m3_encode_sat(bf16_bits_to_f32(vb[e]) / sv);
+          kq[e] = (uint8_t)fp8_encode_sat<FMT>(bf16_bits_to_f32(kb[e]) / sk);
+          vq[e] = (uint8_t)fp8_encode_sat<FMT>(bf16_bits_to_f32(vb[e]) / sv);
         }
         // K: the lane's dims are adjacent in one 16-byte chunk; V: 4 bytes apart
 #pragma unroll
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         bf16x8 kop;
         if constexpr (FP8) {
           const uint4 w = tl.k[pg][s / 2];
-          kop = (s % 2 == 0) ? e4m3x8_to_bf16x8(w.x, w.y) : e4m3x8_to_bf16x8(w.z, w.w);
+          kop = (s % 2 == 0) ? fp8x8_to_bf16x8<FMT>(w.x, w.y) : fp8x8_to_bf16x8<FMT>(w.z, w.w);
         } else {
           kop = bits_to_bf16x8(tl.k[pg][s]);
         }
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
           const uint4 wa = tl.v[2 * pp][i], wb = tl.v[2 * pp + 1][i];
           const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
           const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
-          vb = __builtin_bit_cast(uint4, cat(e4m3x4_to_bf16x4(da), e4m3x4_to_bf16x4(db)));
+          vb = __builtin_bit_cast(uint4, cat(fp8x4_to_bf16x4<FMT>(da), fp8x4_to_bf16x4<FMT>(db)));
         } else {
           const int i = blk / 2, ep = blk % 2;
           const uint4 wa = tl.v[2 * pp][i], wb = tl.v[2 * pp + 1][i];
@@ -794,23 +795,23 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodePara
   else reinterpret_cast<float*>(p.out)[row * D + d] = r;
 }
 
-template <int D, bool FP8, int TP, int RING, int SLOTS, bool FUSED>
+template <int D, int FMT, int TP, int RING, int SLOTS, bool FUSED>
 static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_t stream,
                                  hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NW = kSplitWaves;
   const dim3 grid((unsigned)p.num_parts, (unsigned)p.num_kv_heads, (unsigned)num_seqs);
   if (ev_before && ev_after) {
     // the events take the kernel's own start and end timestamps
-    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, SLOTS, FUSED>), grid,
+    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED>), grid,
                           dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_decode_split_kernel<D, FP8, NW, TP, RING, SLOTS, FUSED>), grid,
+    hipLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED>), grid,
                        dim3(NW * kWave), 0, stream, p);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.direct) return err;
   DecodeParams pr = p;
-  if (!FP8) pr.v_scale = nullptr;
+  if (FMT == kFmtBf16) pr.v_scale = nullptr;
   hipLaunchKernelGGL((paged_decode_reduce_kernel<D>),
                      dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(D), 0,
                      stream, pr);
@@ -824,21 +825,21 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
 // KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 4x1, 2x1s1, 2x1s2,
 // 4x1s1) overrides it for tuning sweeps; a shape whose LDS ring would pass
 // 64 KiB is rejected.
-template <int D, bool FP8, int TP, int RING, int SLOTS>
+template <int D, int FMT, int TP, int RING, int SLOTS>
 static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
-  constexpr int E = FP8 ? 1 : 2;
+  constexpr int E = FMT == kFmtBf16 ? 2 : 1;
   if constexpr (kSplitWaves * SLOTS * TP * 2 * kPage * D * E > kMaxLdsRing) {
     return hipErrorInvalidValue;
   } else {
-    return fused ? launch_variant<D, FP8, TP, RING, SLOTS, true>(p, num_seqs, stream, ev_before,
+    return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true>(p, num_seqs, stream, ev_before,
                                                                   ev_after)
-                 : launch_variant<D, FP8, TP, RING, SLOTS, false>(p, num_seqs, stream, ev_before,
+                 : launch_variant<D, FMT, TP, RING, SLOTS, false>(p, num_seqs, stream, ev_before,
                                                                    ev_after);
   }
 }
 
-template <int D, bool FP8>
+template <int D, int FMT>
 static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, int plan_slots,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
   int tp = 2, ring = 1, slots = plan_slots;
@@ -849,7 +850,7 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, 
   }
 #define KVFP8_SHAPE(TP_, RING_, SLOTS_)                                                 \
   if (tp == TP_ && ring == RING_ && slots == SLOTS_)                                    \
-    return launch_shape<D, FP8, TP_, RING_, SLOTS_>(p, num_seqs, fused, stream, ev_before, \
+    return launch_shape<D, FMT, TP_, RING_, SLOTS_>(p, num_seqs, fused, stream, ev_before, \
                                                     ev_after);
   KVFP8_SHAPE(2, 1, 0)
   KVFP8_SHAPE(2, 2, 0)
@@ -861,23 +862,29 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, bool fp8,
-                               int num_seqs, bool fused, int slots, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after) {
-  switch (head_dim) {
-    case 64:
-      return fp8 ? launch_typed<64, true>(p, num_seqs, fused, slots, stream, ev_before, ev_after)
-                 : launch_typed<64, false>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
-    case 128:
-      return fp8 ? launch_typed<128, true>(p, num_seqs, fused, slots, stream, ev_before, ev_after)
-                 : launch_typed<128, false>(p, num_seqs, fused, slots, stream, ev_before,
-                                            ev_after);
-    case 256:
-      return fp8 ? launch_typed<256, true>(p, num_seqs, fused, slots, stream, ev_before, ev_after)
-                 : launch_typed<256, false>(p, num_seqs, fused, slots, stream, ev_before,
-                                            ev_after);
+template <int D>
+static hipError_t launch_dim(const DecodeParams& p, int fmt, int num_seqs, bool fused, int slots,
+                             hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+  switch (fmt) {
+    case kFmtBf16:
+      return launch_typed<D, kFmtBf16>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
+    case kFmtE4M3:
+      return launch_typed<D, kFmtE4M3>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
+    case kFmtE5M2:
+      return launch_typed<D, kFmtE5M2>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
     default:
       return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
+                               bool fused, int slots, hipStream_t stream, hipEvent_t ev_before,
+                               hipEvent_t ev_after) {
+  switch (head_dim) {
+    case 64: return launch_dim<64>(p, fmt, num_seqs, fused, slots, stream, ev_before, ev_after);
+    case 128: return launch_dim<128>(p, fmt, num_seqs, fused, slots, stream, ev_before, ev_after);
+    case 256: return launch_dim<256>(p, fmt, num_seqs, fused, slots, stream, ev_before, ev_after);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -1,5 +1,6 @@
 /*
- * kvfp8.h - C ABI of the MI355X (gfx950) FP8 e4m3 paged KV-cache library.
+ * kvfp8.h - C ABI of the MI355X (gfx950) FP8 (e4m3, e5m2) paged KV-cache
+ * library.
  *
  * Two operations make up one decode step of an attention layer:
  *
@@ -44,11 +45,21 @@
  * mode: "cooking-agi: FP8 and the KV cache", section "dynamic vs static scale";
  * s = amax/448 and round(x/s): "FP8量化与长上下文推理" section 1.1.)
  *
+ * E5M2 (OCP FP8), the second fp8 cache dtype (fp8_e5m2: "cooking-agi",
+ * section "how to enable it in the engine"; format: "FP8量化与长上下文推理"
+ * section 1 table): 1 sign, 5 exponent (bias 15), 2 mantissa bits; largest
+ * finite magnitude 57344, smallest subnormal 2^-16, infinities S.11111.00,
+ * NaNs S.11111.xx. The same rule with E5M2 in place of E4M3: saturation of
+ * finite and infinite overflow to +-57344 (0x7B / 0xFB), NaN to 0x7F|sign,
+ * and the calibrated scale is s = amax / 57344. Stored infinities (which the
+ * write never produces) read back as NaN in the attention output.
+ *
  * Paged cache layout (the pages leave it open; this library fixes it)
  * ------------------------------------------------------------------
  * A cache is one byte array per layer and per K / V:
  *     [num_pages][num_kv_heads][PB]   with PB = 16 * head_dim * e bytes,
- * e = 1 for KVQ_FP8_E4M3 and 2 for KVQ_BF16 (little-endian bf16 bits).
+ * e = 1 for KVQ_FP8_E4M3 and KVQ_FP8_E5M2, 2 for KVQ_BF16 (little-endian bf16
+ * bits).
  * A page holds 16 consecutive positions of one sequence. Token position t of
  * a sequence lives in page block_table[t / 16], row r = t % 16; a slot is
  * page * 16 + r. Within the PB-byte block of (page, kv head) the element
@@ -85,7 +96,7 @@ enum kvq_status {
 };
 
 /* Cache element type of a layer. `auto` in the engine flags maps to bf16. */
-enum kvq_dtype { KVQ_BF16 = 0, KVQ_FP8_E4M3 = 1 };
+enum kvq_dtype { KVQ_BF16 = 0, KVQ_FP8_E4M3 = 1, KVQ_FP8_E5M2 = 2 };
 
 /* Scale granularity: one FP32 scale for the whole layer tensor, or one per KV
  * head ("cooking-agi", section "how to enable it in the engine": per tensor
@@ -120,7 +131,8 @@ typedef struct kvq_layer_desc {
  *                 ignored and may be NULL for bf16 layers, where the bf16 bits
  *                 are copied unchanged.
  * Only the bytes of the written (slot, head) rows change.
- * For fp8 layers each element becomes E4M3_sat_RNE(fp32(x) / s_h) (above).
+ * For fp8 layers each element becomes E4M3_sat_RNE(fp32(x) / s_h), or
+ * E5M2_sat_RNE(fp32(x) / s_h) for an e5m2 layer (above).
  */
 int kvq_kv_cache_write(const kvq_layer_desc* desc, const void* k, const void* v,
                        const int64_t* slot_mapping, int64_t num_tokens,
@@ -208,8 +220,9 @@ int kvq_decode_step(const kvq_layer_desc* desc, const void* k_new,
  * s = fp32(amax) / 448 over x, per KV head or over the whole tensor per
  * desc->scale_mode ("FP8量化与长上下文推理" section 1.1: scale = max_abs/448;
  * "cooking-agi", section "dynamic vs static scale": the largest value lands
- * on 448). amax == 0 gives s = 1 (a zero scale cannot quantise anything);
- * a NaN anywhere in the reduced values gives NaN.
+ * on 448). For an e5m2 layer the divisor is 57344, the e5m2 maximum, so the
+ * largest value lands there. amax == 0 gives s = 1 (a zero scale cannot
+ * quantise anything); a NaN anywhere in the reduced values gives NaN.
  *   x          device bf16 [T][Hkv][D]
  *   scale_out  device fp32 [1] or [Hkv]
  */
@@ -223,6 +236,13 @@ int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x,
  * with exactly the cache's codec.
  */
 int kvq_e4m3_quantize(const float* x, int64_t n, const float* scale,
+                      uint8_t* out, void* stream);
+
+/*
+ * kvq_e5m2_quantize - the same for the e5m2 cache dtype:
+ * out[i] = E5M2_sat_RNE(x[i] / *scale), arguments as for kvq_e4m3_quantize.
+ */
+int kvq_e5m2_quantize(const float* x, int64_t n, const float* scale,
                       uint8_t* out, void* stream);
 
 /* Human-readable text of a status code (static storage). */

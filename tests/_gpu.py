@@ -9,7 +9,13 @@ import fp8_kv_cache_write_amd as kv
 import oracle
 import synth
 
-FP8, BF16 = oracle.FP8, oracle.BF16
+FP8, BF16, E5M2 = oracle.FP8, oracle.BF16, oracle.E5M2
+_ORACLE_FMT = {"fp8_e4m3": FP8, "fp8_e5m2": E5M2, "bf16": BF16}
+
+
+def cache_fmt(fp8, fmt):
+    """The cache dtype name: fmt if given, else e4m3 (fp8) or bf16."""
+    return fmt if fmt is not None else ("fp8_e4m3" if fp8 else "bf16")
 GATE_MAX_ABS = 1e-2      # attention gate (max-abs, unit-scale inputs)
 GATE_MEAN_ABS = 1e-3     # attention gate (mean-abs)
 
@@ -45,11 +51,11 @@ class GpuLayer:
     library, every position of the case written by the library."""
 
     def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
-                 scales=None):
+                 scales=None, fmt=None):
         self.case = case
-        self.fp8 = fp8
-        self.desc = kv.layer_desc(case.num_q_heads, case.num_kv_heads, case.head_dim,
-                                  "fp8_e4m3" if fp8 else "bf16",
+        fmt = cache_fmt(fp8, fmt)
+        self.fp8 = fp8 = fmt != "bf16"
+        self.desc = kv.layer_desc(case.num_q_heads, case.num_kv_heads, case.head_dim, fmt,
                                   "per_kv_head" if per_head else "per_tensor",
                                   window, sm_scale)
         self.k_new = bf16_dev(case.k_new)
@@ -99,7 +105,10 @@ class OracleLayer:
     """The same layer through the oracle (its own scales, its own caches)."""
 
     def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
-                 scales=None):
+                 scales=None, fmt=None):
+        fmt = cache_fmt(fp8, fmt)
+        self.fmt = _ORACLE_FMT[fmt]
+        fp8 = fmt != "bf16"
         self.case, self.fp8, self.per_head = case, fp8, per_head
         self.window, self.sm_scale = window, sm_scale
         self.k_cache = synth.poisoned_cache(case.num_pages, case.num_kv_heads,
@@ -107,21 +116,20 @@ class OracleLayer:
         self.v_cache = self.k_cache.copy()
         if fp8:
             if scales is None:
-                self.ks = oracle.scale_from_amax(case.k_new, per_head)
-                self.vs = oracle.scale_from_amax(case.v_new, per_head)
+                self.ks = oracle.scale_from_amax(case.k_new, per_head, fmt=self.fmt)
+                self.vs = oracle.scale_from_amax(case.v_new, per_head, fmt=self.fmt)
             else:
                 self.ks = np.asarray(scales[0], np.float32)
                 self.vs = np.asarray(scales[1], np.float32)
         else:
             self.ks = self.vs = None
         oracle.kv_cache_write(self.k_cache, self.v_cache, case.k_new, case.v_new,
-                              case.slots, FP8 if fp8 else BF16, per_head, self.ks,
-                              self.vs)
+                              case.slots, self.fmt, per_head, self.ks, self.vs)
 
     def attend(self):
         c = self.case
         return oracle.attention(c.q, self.k_cache, self.v_cache, c.block_tables, c.lens,
-                                c.num_kv_heads, FP8 if self.fp8 else BF16, self.per_head,
+                                c.num_kv_heads, self.fmt, self.per_head,
                                 self.window, self.sm_scale, self.ks, self.vs)
 
 
