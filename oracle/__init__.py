@@ -102,6 +102,7 @@ def lib():
         L.orc_attention_split.argtypes = att + [ctypes.c_int, ctypes.c_int]
         L.orc_attention_lowprec.argtypes = att + [ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int]
+        L.orc_attention_fp8attn.argtypes = att + [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -281,4 +282,17 @@ def attention_lowprec(q, k_cache, v_cache, block_tables, context_lens,
                                    window, sm_scale, k_scale, v_scale)
     lib().orc_attention_lowprec(*args, int(acc_bits), int(acc_tile),
                                 _threads(nthreads))
+    return out
+
+
+def attention_fp8attn(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
+                      dtype, per_head=True, window=0, sm_scale=0.0, k_scale=None,
+                      v_scale=None, nthreads=None) -> np.ndarray:
+    """All-FP8 attention: q quantised to e4m3 per row (s = amax / 448), the
+    probabilities quantised to e4m3 per aligned 32-position block relative
+    to the block's largest logit; float64 elsewhere. [B][Hq][D]."""
+    args, out, _keep = _att_common(q, k_cache, v_cache, block_tables,
+                                   context_lens, num_kv_heads, dtype, per_head,
+                                   window, sm_scale, k_scale, v_scale)
+    lib().orc_attention_fp8attn(*args, _threads(nthreads))
     return out

@@ -573,6 +573,8 @@ typedef struct {
   int part_tokens;
   /* reduced-precision accumulation variant */
   int acc_bits, acc_tile;
+  /* all-FP8 attention variant: q quantised to e4m3 in gather */
+  int q8;
 } att_args;
 
 /* Softmax-weighted sum over n positions: out[d] = sum_t p_t v[t][d] / sum p,
@@ -605,13 +607,26 @@ static int64_t gather(const att_args* a, int b, int i, double* z, double* v) {
   double ks = a->dtype != 0 ? (double)a->ks[a->per_head ? h : 0] : 1.0;
   double vs = a->dtype != 0 ? (double)a->vs[a->per_head ? h : 0] : 1.0;
   const uint16_t* qi = a->q + ((int64_t)b * a->Hq + i) * a->D;
+  /* the query as the attention reads it: its bf16 values, or (all-FP8
+   * variant) their e4m3 codes times the row's scale */
+  double qv[512];
+  if (a->q8) {
+    float sq = 0.0f;
+    uint16_t qrow[1][1][512];
+    for (int d = 0; d < a->D; ++d) qrow[0][0][d] = qi[d];
+    orc_scale_from_amax_fmt(&qrow[0][0][0], 1, 1, a->D, 1, 1, &sq);
+    for (int d = 0; d < a->D; ++d)
+      qv[d] = orc_e4m3_decode(orc_quantize_f32(bf16_to_f32(qi[d]), sq)) * (double)sq;
+  } else {
+    for (int d = 0; d < a->D; ++d) qv[d] = (double)bf16_to_f32(qi[d]);
+  }
   for (int64_t t = lo; t < L; ++t) {
     int64_t page = a->bt[(int64_t)b * a->max_pages + t / 16];
     int r = (int)(t % 16);
     double dot = 0.0;
     for (int d = 0; d < a->D; ++d) {
       double kh = cache_value(a->kc, 0, page, a->Hkv, h, r, d, a->D, a->dtype, ks);
-      dot += (double)bf16_to_f32(qi[d]) * kh;
+      dot += qv[d] * kh;
       v[(t - lo) * a->D + d] =
           cache_value(a->vc, 1, page, a->Hkv, h, r, d, a->D, a->dtype, vs);
     }
@@ -713,6 +728,53 @@ static void lowprec_sum(const double* z, const double* v, int64_t n, int D,
   free(tacc);
 }
 
+/* All-FP8 attention (the FP8 ScoreV product): the attended positions fall
+ * into aligned blocks of 32 (block j holds positions 32j .. 32j+31). In
+ * block j, with M_j the largest logit of its attended positions,
+ *   p~_t = E4M3_sat_RNE( fp32(exp(z_t - M_j)) )        (the quantised P)
+ *   S_j  = sum_t p~_t v_t,   L_j = sum_t exp(z_t - M_j)   (P unquantised)
+ * and with M = max_j M_j:  out = sum_j e^(M_j-M) S_j / sum_j e^(M_j-M) L_j.
+ * lo is the first attended position (the window start), z and v are indexed
+ * from it. */
+static void fp8attn_sum(const double* z, const double* v, int64_t n, int64_t lo,
+                        int D, double* out) {
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (n <= 0) return;
+  int64_t j0 = lo / 32, j1 = (lo + n - 1) / 32;
+  int64_t nb = j1 - j0 + 1;
+  double* mb = (double*)malloc(sizeof(double) * nb);
+  double* lb = (double*)malloc(sizeof(double) * nb);
+  double* sb = (double*)calloc((size_t)nb * D, sizeof(double));
+  for (int64_t j = 0; j < nb; ++j) {
+    int64_t t0 = (j0 + j) * 32 - lo, t1 = t0 + 32;
+    if (t0 < 0) t0 = 0;
+    if (t1 > n) t1 = n;
+    mb[j] = -INFINITY;
+    for (int64_t t = t0; t < t1; ++t)
+      if (z[t] > mb[j]) mb[j] = z[t];
+    lb[j] = 0.0;
+    for (int64_t t = t0; t < t1; ++t) {
+      double e = exp(z[t] - mb[j]);
+      lb[j] += e;
+      double pq = orc_e4m3_decode(orc_e4m3_encode((float)e));
+      for (int d = 0; d < D; ++d) sb[j * D + d] += pq * v[t * D + d];
+    }
+  }
+  double M = -INFINITY;
+  for (int64_t j = 0; j < nb; ++j)
+    if (mb[j] > M) M = mb[j];
+  double Lam = 0.0;
+  for (int64_t j = 0; j < nb; ++j) {
+    double w = exp(mb[j] - M);
+    Lam += w * lb[j];
+    for (int d = 0; d < D; ++d) out[d] += w * sb[j * D + d];
+  }
+  for (int d = 0; d < D; ++d) out[d] /= Lam;
+  free(mb);
+  free(lb);
+  free(sb);
+}
+
 static void* att_worker(void* p) {
   att_job* j = (att_job*)p;
   const att_args* a = j->a;
@@ -725,7 +787,11 @@ static void* att_worker(void* p) {
     int b = idx / a->Hq, i = idx % a->Hq;
     double* out = a->out + (int64_t)idx * a->D;
     int64_t n = gather(a, b, i, z, v);
-    if (j->mode == 0)
+    int64_t L = a->lens[b];
+    int64_t lo = (a->window > 0 && L > a->window) ? L - a->window : 0;
+    if (j->mode == 3)
+      fp8attn_sum(z, v, n, lo, a->D, out);
+    else if (j->mode == 0)
       orc_softmax_weighted_sum(z, v, n, a->D, out);
     else if (j->mode == 1)
       split_merge(z, v, n, a->D, a->part_tokens, out);
@@ -764,7 +830,7 @@ static void fill_args(att_args* a, int B, int Hq, int Hkv, int D, int dtype,
   a->sm_scale = sm_scale > 0.0 ? sm_scale : 1.0 / sqrt((double)D);
   a->q = q; a->kc = kc; a->vc = vc; a->bt = bt; a->max_pages = max_pages;
   a->lens = lens; a->ks = ks; a->vs = vs; a->out = out;
-  a->part_tokens = 0; a->acc_bits = 0; a->acc_tile = 0;
+  a->part_tokens = 0; a->acc_bits = 0; a->acc_tile = 0; a->q8 = 0;
 }
 
 /* out: float64 [B][Hq][D]. sm_scale <= 0 means 1/sqrt(D). */
@@ -805,4 +871,23 @@ void orc_attention_lowprec(int B, int Hq, int Hkv, int D, int dtype,
   a.acc_bits = acc_bits;
   a.acc_tile = acc_tile;
   run_attention(&a, 2, nthreads);
+}
+
+/* All-FP8 attention: q quantised to e4m3 per (sequence, query head) with
+ * s_q = fp32(amax |q row|) / 448, the QK^T product on those codes and the
+ * cache codes, and P quantised per aligned 32-position block (fp8attn_sum).
+ * Sources: "State of FP8 KV cache and attention quantization in vLLM"
+ * (introduction: the whole attention, QK and ScoreV, in FP8 e4m3; section
+ * on fixes: query quantisation fused ahead of the kernel); the scale rule
+ * and the block reference are this library's reading. */
+void orc_attention_fp8attn(int B, int Hq, int Hkv, int D, int dtype, int per_head,
+                           int window, double sm_scale, const uint16_t* q,
+                           const uint8_t* kc, const uint8_t* vc, const int32_t* bt,
+                           int max_pages, const int32_t* lens, const float* ks,
+                           const float* vs, double* out, int nthreads) {
+  att_args a;
+  fill_args(&a, B, Hq, Hkv, D, dtype, per_head, window, sm_scale, q, kc, vc, bt,
+            max_pages, lens, ks, vs, out);
+  a.q8 = 1;
+  run_attention(&a, 3, nthreads);
 }
