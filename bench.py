@@ -60,7 +60,8 @@ class LayerStack:
     over L positions."""
 
     def __init__(self, kv, torch, B, Hq, Hkv, D, lens, NL, cache_dtype="fp8_e4m3",
-                 window=0, shuffle=False, spare_frac=0.0, seed=0, dtypes=None, path="fused"):
+                 window=0, shuffle=False, spare_frac=0.0, seed=0, dtypes=None, path="fused",
+                 attn="bf16"):
         self.kv, self.torch = kv, torch
         self.path = path
         dev = torch.device("cuda:0")
@@ -71,7 +72,8 @@ class LayerStack:
         self.max_len = max(self.lens)
         dtypes = dtypes or [cache_dtype] * NL
         windows = window if isinstance(window, list) else [window] * NL
-        self.descs = [kv.layer_desc(Hq, Hkv, D, dtypes[i], "per_kv_head", windows[i])
+        self.descs = [kv.layer_desc(Hq, Hkv, D, dtypes[i], "per_kv_head", windows[i],
+                                    attn=attn if dtypes[i] != "bf16" else "bf16")
                       for i in range(NL)]
         import numpy as np
         need = [(L + 15) // 16 for L in self.lens]
@@ -343,6 +345,9 @@ def main():
     ap.add_argument("--context", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--cache", default="fp8_e4m3", choices=["fp8_e4m3", "fp8_e5m2", "bf16"])
+    ap.add_argument("--attn", default="bf16", choices=["bf16", "fp8"],
+                    help="attention arithmetic: bf16 MFMA on exact cache codes, or the "
+                         "all-FP8 mode (e4m3 q and P, fp8 MFMA)")
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="fused: kvq_decode_step per layer; separate: write + attention calls")
     ap.add_argument("--no-sweep", action="store_true")
@@ -388,19 +393,19 @@ def main():
         import synth
         lens = [int(x) for x in synth.batched_lens()]
         stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], lens, NL, args.cache,
-                           shuffle=True, spare_frac=0.1, seed=3, path=args.path)
+                           shuffle=True, spare_frac=0.1, seed=3, path=args.path, attn=args.attn)
         ctx_desc = f"lengths {min(lens)}..{max(lens)} (sum {sum(lens)})"
     elif args.workload == "gptoss":
         dts = ["fp8_e4m3" if i % 2 == 0 else "bf16" for i in range(NL)]
         wins = [0 if i % 2 == 0 else 128 for i in range(NL)]
         stack = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, seed=5,
-                           dtypes=dts, window=wins, path=args.path)
+                           dtypes=dts, window=wins, path=args.path, attn=args.attn)
         ctx_desc = f"context {ctx}; {NL // 2} full fp8 layers + {NL - NL // 2} SW-128 bf16 layers"
     else:
         stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], [ctx], NL, args.cache,
-                           seed=1, path=args.path)
+                           seed=1, path=args.path, attn=args.attn)
         ctx_desc = f"context {ctx}"
-    log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}")
+    log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}, attention {args.attn}")
     # the timed region: K steps, each one replay of the captured decode step
     ms = time_steps_graph(torch, stack, args.steps, args.warmup)
     # eager steps with the split kernel's launches timed by the library
@@ -432,9 +437,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (f"{args.cache} cache, bf16 MFMA on exact {args.cache[4:]} values, "
-                  "fp32 accumulation") if args.cache.startswith("fp8")
-                 else "bf16 cache, fp32 accumulation",
+        "dtype": ((f"{args.cache} cache, e4m3 q and P on fp8 MFMA, fp32 accumulation"
+                   if args.attn == "fp8" else
+                   f"{args.cache} cache, bf16 MFMA on exact {args.cache[4:]} values, "
+                   "fp32 accumulation") if args.cache.startswith("fp8")
+                  else "bf16 cache, fp32 accumulation"),
         "data": "synthetic (seeded normal K/V/q)",
         "config": {
             "workload": f"{w['desc']}, {ctx_desc}, {args.cache} cache with per-KV-head scales, "
@@ -442,6 +449,7 @@ def main():
                         f"decode attention, " + ("one kvq_decode_step call" if args.path == "fused"
                         else "kvq_kv_cache_write + kvq_paged_decode_attention") + ")",
             "path": args.path,
+            "attention": args.attn,
             "batch": w["B"], "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": w["D"],
             "page_size": 16, "layers_per_step": NL, "parallelism": "single GPU",
         },
@@ -459,7 +467,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
             "traffic": measured_traffic(f"{args.workload}:{ctx}:{args.cache}:{NL}:{args.path}")
-            if args.workload == "llama8b" else None,
+            if args.workload == "llama8b" and args.attn == "bf16" else None,
             "launch_us": round(split_ms * 1e3, 3) if split_ms else None,
             "launches_timed": nsplit,
             "timed_with": "kernel-timestamped HIP event pairs around every split-kernel launch "

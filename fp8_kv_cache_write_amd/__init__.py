@@ -18,12 +18,14 @@ LIB_PATH = os.path.join(_HERE, "libkvfp8.so")
 # enums of kvfp8.h
 BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2
 PER_TENSOR, PER_KV_HEAD = 0, 1
+ATTN_BF16, ATTN_FP8 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 PAGE_SIZE = 16
 
 _DTYPES = {"bf16": BF16, "auto": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3,
            "fp8_e5m2": FP8_E5M2}
 _SCALES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD}
+_ATTN = {"bf16": ATTN_BF16, "fp8": ATTN_FP8}
 
 
 class Kvfp8Error(RuntimeError):
@@ -36,7 +38,8 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("cache_dtype", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
-                ("sliding_window", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+                ("sliding_window", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("attn_dtype", ctypes.c_int32)]
 
     @property
     def fp8(self):
@@ -53,13 +56,16 @@ class LayerDesc(ctypes.Structure):
 
 
 def layer_desc(num_q_heads, num_kv_heads, head_dim, cache_dtype="fp8_e4m3",
-               scale_mode="per_kv_head", sliding_window=0, sm_scale=0.0):
+               scale_mode="per_kv_head", sliding_window=0, sm_scale=0.0, attn="bf16"):
     """Descriptor of one attention layer. cache_dtype: "fp8_e4m3"/"fp8",
-    "fp8_e5m2" or "bf16"/"auto"; scale_mode: "per_tensor" or "per_kv_head"."""
+    "fp8_e5m2" or "bf16"/"auto"; scale_mode: "per_tensor" or "per_kv_head";
+    attn: "bf16" (exact cache codes, bf16 MFMA) or "fp8" (e4m3 q and P, fp8
+    MFMA)."""
     return LayerDesc(int(num_q_heads), int(num_kv_heads), int(head_dim), PAGE_SIZE,
                      _DTYPES[cache_dtype] if isinstance(cache_dtype, str) else int(cache_dtype),
                      _SCALES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode),
-                     int(sliding_window), float(sm_scale))
+                     int(sliding_window), float(sm_scale),
+                     _ATTN[attn] if isinstance(attn, str) else int(attn))
 
 
 _lib = None

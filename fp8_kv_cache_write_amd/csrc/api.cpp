@@ -16,7 +16,8 @@ using namespace kvfp8;
 
 namespace {
 
-constexpr int kMaxGroup = 8;
+constexpr int kMaxGroup = 8;        // bf16-MFMA attention (P carried as hi + lo)
+constexpr int kMaxGroupFp8 = 16;    // all-FP8 attention
 constexpr int kMaxPagesPerWave = 64;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -34,7 +35,11 @@ int check_desc(const kvq_layer_desc* d) {
   if (d->page_size != 16) return KVQ_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (d->num_q_heads % d->num_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
-  if (d->num_q_heads / d->num_kv_heads > kMaxGroup) return KVQ_ERR_UNSUPPORTED;
+  if (d->attn_dtype != KVQ_ATTN_BF16 && d->attn_dtype != KVQ_ATTN_FP8) return KVQ_ERR_INVALID_ARG;
+  if (d->attn_dtype == KVQ_ATTN_FP8 && d->cache_dtype == KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads >
+      (d->attn_dtype == KVQ_ATTN_FP8 ? kMaxGroupFp8 : kMaxGroup))
+    return KVQ_ERR_UNSUPPORTED;
   if (d->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
@@ -85,8 +90,11 @@ constexpr double kCoResidentPenalty = 0.035;
 
 Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
   const int W = d->sliding_window;
+  const bool att8 = d->attn_dtype == KVQ_ATTN_FP8;
   int64_t pages_max = ((int64_t)max_context_len + 15) / 16;
-  if (W > 0) pages_max = std::min<int64_t>(pages_max, ((int64_t)W + 15) / 16 + 1);
+  // a window's first page; the all-FP8 mode starts on an even page (tiles on
+  // aligned 32-position blocks), one more
+  if (W > 0) pages_max = std::min<int64_t>(pages_max, ((int64_t)W + 15) / 16 + 1 + (att8 ? 1 : 0));
   if (pages_max < 1) pages_max = 1;
   const int64_t units = (int64_t)std::max(num_seqs, 1) * d->num_kv_heads;
   const int64_t cus = cu_count();
@@ -124,6 +132,7 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
     const long n = strtol(env, nullptr, 10);
     if (n >= 1 && n <= kMaxPagesPerWave) ppw = n;
   }
+  if (att8) ppw = (ppw + 1) / 2 * 2;   // runs of whole 32-position blocks
   Plan p;
   p.pages_per_wave = (int)ppw;
   p.slots = slots;
@@ -273,7 +282,7 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
     g_prof.used++;
   }
   hipError_t e = launch_paged_decode(p, desc->head_dim, (int)desc->cache_dtype, num_seqs, fused,
-                                     plan.slots,
+                                     plan.slots, desc->attn_dtype == KVQ_ATTN_FP8,
                                      static_cast<hipStream_t>(stream), e0, e1);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

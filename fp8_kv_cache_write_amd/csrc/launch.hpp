@@ -41,7 +41,7 @@ struct DecodeParams {
   const uint16_t* v_new;         //   token at position L-1 of every sequence
   int num_q_heads;
   int num_kv_heads;
-  int group;                     // G = Hq / Hkv, <= 8
+  int group;                     // G = Hq / Hkv, <= 8 (<= 16 in the all-FP8 mode)
   int max_pages_per_seq;
   int window;                    // 0 = full
   int pages_per_wave;            // <= 64
@@ -59,8 +59,9 @@ constexpr int kSplitWaves = 4;
 // position L-1 of every sequence (p.k_cache / p.v_cache must be writable).
 // slots: split-kernel tile shape, 1 = LDS-staged tiles, 0 = register tiles.
 // fmt: cache element format, kFmtBf16 / kFmtE4M3 / kFmtE5M2 (device_common.hpp).
+// att8: all-FP8 attention (e4m3 Q and P, fp8 MFMA); fp8 caches only.
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
-                               bool fused, int slots, hipStream_t stream, hipEvent_t ev_before,
-                               hipEvent_t ev_after);
+                               bool fused, int slots, bool att8, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after);
 
 }  // namespace kvfp8

@@ -123,7 +123,8 @@ struct PartitionRange {
 // The partitions of one sequence: pages [first_page, end_page) cover the
 // attended positions [lo, L); partition j holds part_pages pages of them.
 __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
-                                                          int b, int part_pages) {
+                                                          int b, int part_pages,
+                                                          bool even_pages) {
   PartitionRange r;
   r.L = p.context_lens[b];
   if (r.L < 0 || p.num_pages <= 0) r.L = 0;         // no page can be valid without a pool
@@ -133,6 +134,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   if (r.L > p.max_pages_per_seq * kPage) r.L = p.max_pages_per_seq * kPage;
   if (r.lo > r.L) r.lo = r.L;
   r.first_page = r.lo / kPage;
+  if (even_pages) r.first_page &= ~1;   // tiles on aligned 32-position blocks
   r.end_page = (r.L + kPage - 1) / kPage;
   const int n = r.end_page - r.first_page;
   r.num_parts_b = n > 0 ? (n + part_pages - 1) / part_pages : 0;
@@ -140,7 +142,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   return r;
 }
 
-template <int D, int FMT, int NW, int TP, int RING, int SLOTS, bool FUSED>
+template <int D, int FMT, int NW, int TP, int RING, int SLOTS, bool FUSED, bool ATT8>
 __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const DecodeParams p) {
   constexpr bool FP8 = FMT != kFmtBf16;
@@ -149,7 +151,8 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   constexpr int NI = PB / 1024;         // 1 KiB wave loads per page per tensor
   constexpr int NK = D / 32;            // q k^T MFMAs per page
   constexpr int NBLK = D / 16;          // P*V output blocks of 16 dims
-  constexpr int GMAX = 8;
+  constexpr int GMAX = ATT8 ? 16 : 8;   // query columns: G (+ G low halves of P)
+  static_assert(!ATT8 || FP8, "the all-FP8 mode reads fp8 caches");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -162,9 +165,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const int part_pages = NW * p.pages_per_wave;
 
   // Column c < G: query c (high half of P); G <= c < 2G: query c - G (low
-  // half of P); other columns idle.
-  const int g = c < G ? c : (c < 2 * G ? c - G : -1);
-  const bool lo_col = (c >= G) && (c < 2 * G);
+  // half of P); other columns idle. The all-FP8 mode has no low halves
+  // (P is e4m3 on purpose) and takes up to 16 queries.
+  const int g = c < G ? c : ((!ATT8 && c < 2 * G) ? c - G : -1);
+  const bool lo_col = !ATT8 && (c >= G) && (c < 2 * G);
 
   // Loads that do not depend on the context length go out before it is
   // known, so a work-group waits for one memory round trip, not two, before
@@ -184,6 +188,28 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       qop[s] = bits_to_bf16x8(w);
     }
   }
+  // All-FP8 mode: the query row as e4m3 codes with s_q = amax / 448 (the
+  // 4 lanes of a column hold the whole row), packed as 8-byte MFMA operands
+  // in the same order.
+  uint64_t qop8[ATT8 ? NK : 1];
+  float q_scale = 1.0f;
+  if constexpr (ATT8) {
+    float am = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NK; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf((float)qop[s][j]));
+    am = col_max(am);
+    q_scale = am == 0.0f ? 1.0f : am / 448.0f;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      uint64_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        w |= (uint64_t)e4m3_encode_sat((float)qop[s][j] / q_scale) << (8 * j);
+      qop8[s] = w;
+    }
+  }
   const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
   const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
   const int32_t* bt_row = p.block_tables + (int64_t)b * p.max_pages_per_seq;
@@ -193,7 +219,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     if (lane < p.pages_per_wave && idx < p.max_pages_per_seq) my_page = bt_row[idx];
   }
 
-  const PartitionRange pr = partition_range(p, b, part_pages);
+  const PartitionRange pr = partition_range(p, b, part_pages, ATT8);
   if (part >= pr.num_parts_b) {
     // Nothing to attend here. In direct mode the first partition still owns
     // the output rows (empty context -> zeros); otherwise the partition's
@@ -267,7 +293,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const int64_t page_stride = (int64_t)p.num_kv_heads * PB;
   const uint8_t* kbase = p.k_cache + (int64_t)h * PB;
   const uint8_t* vbase = p.v_cache + (int64_t)h * PB;
-  const float c_log2 = ks * p.sm_scale_log2;
+  const float c_log2 = q_scale * ks * p.sm_scale_log2;
 
   // ---- fused decode step: the cache write of position L-1 -----------------
   // Exactly one wave streams the page that holds the newest position of this
@@ -448,6 +474,17 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
+        if constexpr (ATT8) {
+          // the K codes themselves are the operand (fp8 x fp8 MFMA)
+          const uint4 w = tl.k[pg][s / 2];
+          const long kop8 = (long)((s % 2 == 0) ? (((uint64_t)w.y << 32) | w.x)
+                                                : (((uint64_t)w.w << 32) | w.z));
+          if constexpr (FMT == kFmtE5M2)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(kop8, (long)qop8[s], sacc, 0, 0, 0);
+          else
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(kop8, (long)qop8[s], sacc, 0, 0, 0);
+          continue;
+        }
         bf16x8 kop;
         if constexpr (FP8) {
           const uint4 w = tl.k[pg][s / 2];
@@ -470,6 +507,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     // masked V rows: per 32-position MFMA, AND masks for the four packed
     // bf16 pairs of the operand (set, and used, only on boundary tiles)
     uint32_t vmask[TP / 2][4];
+    uint32_t vmask8[TP];                                 // all-FP8 mode: byte masks per page
     if (need_mask) {
       uint32_t vkeep = 0u;                               // bit 4*pg+e: row 4qd+e of page pg
 #pragma unroll
@@ -484,13 +522,23 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
           vkeep |= (ok ? 1u : 0u) << (4 * pg + e);
         }
       }
+      if constexpr (ATT8) {
 #pragma unroll
-      for (int pp = 0; pp < TP / 2; ++pp) {
-        const uint32_t kk = vkeep >> (8 * pp);
+        for (int pg = 0; pg < TP; ++pg) {
+          uint32_t m8 = 0u;
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2)
-          vmask[pp][k2] = (((kk >> (2 * k2)) & 1u) ? 0x0000FFFFu : 0u) |
-                          (((kk >> (2 * k2 + 1)) & 1u) ? 0xFFFF0000u : 0u);
+          for (int e = 0; e < 4; ++e) m8 |= ((vkeep >> (4 * pg + e)) & 1u) ? (0xFFu << (8 * e)) : 0u;
+          vmask8[pg] = m8;
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < TP / 2; ++pp) {
+          const uint32_t kk = vkeep >> (8 * pp);
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2)
+            vmask[pp][k2] = (((kk >> (2 * k2)) & 1u) ? 0x0000FFFFu : 0u) |
+                            (((kk >> (2 * k2 + 1)) & 1u) ? 0xFFFF0000u : 0u);
+        }
       }
     }
     // ---- online softmax (log2 domain), lazy rescale -----------------------
@@ -502,7 +550,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     tmax = col_max(tmax);
     const bool grow = tmax > m_run + kLazyLog2;          // -inf > -inf is false
     if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
-      fold();
+      if constexpr (!ATT8) fold();
       const float m_new = grow ? tmax : m_run;
       const float alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
@@ -513,6 +561,53 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    if constexpr (ATT8) {
+      // ---- all-FP8 P*V: P of this 32-position block quantised to e4m3
+      // relative to the block's own max (tmax), the fp8 MFMA product rescaled
+      // by 2^(tmax - m) into the FP32 running sum (level 2, every tile) ------
+      const bool live = tmax != -INFINITY;
+      const float mb = live ? tmax : 0.0f;
+      const float fb = live ? __builtin_amdgcn_exp2f(tmax - m_use) : 0.0f;
+      float ps = 0.0f;
+      uint32_t pw[TP];
+#pragma unroll
+      for (int pg = 0; pg < TP; ++pg) {
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(x[pg][e] - mb);
+        ps += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+        // e4m3 codes, round to nearest even (the hardware conversion agrees
+        // with the cache codec on every input in [0, 1])
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pe[0], pe[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pe[2], pe[3], w, true);
+        pw[pg] = (uint32_t)w;
+      }
+      l_run += fb * ps;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        f32x4 tpv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int pp = 0; pp < TP / 2; ++pp) {
+          const int i = blk / 4, ep = blk % 4;
+          const uint4 wa = tl.v[2 * pp][i], wb = tl.v[2 * pp + 1][i];
+          uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
+          uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
+          if (need_mask) {
+            da &= vmask8[2 * pp];
+            db &= vmask8[2 * pp + 1];
+          }
+          const long vop = (long)(((uint64_t)db << 32) | da);
+          const long pop8 = (long)(((uint64_t)pw[2 * pp + 1] << 32) | pw[2 * pp]);
+          if constexpr (FMT == kFmtE5M2)
+            tpv = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(vop, pop8, tpv, 0, 0, 0);
+          else
+            tpv = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop8, tpv, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[blk][e] += fb * tpv[e];
+      }
+      return;
+    }
     float psum_pg[TP];
     bf16x8 pop[TP / 2];
 #pragma unroll
@@ -655,13 +750,15 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     }
   }
 
-  fold();
+  if constexpr (!ATT8) fold();
   // ---- per-wave results: l over the row quads, lo columns into hi ----------
   l_run = wave_sum_col(l_run);
+  if constexpr (!ATT8) {
 #pragma unroll
-  for (int blk = 0; blk < NBLK; ++blk)
+    for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[blk][e] += __shfl_down(acc[blk][e], G);
+      for (int e = 0; e < 4; ++e) acc[blk][e] += __shfl_down(acc[blk][e], G);
+  }
 
   if (c < G) {
     if (qd == 0) {
@@ -795,18 +892,18 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodePara
   else reinterpret_cast<float*>(p.out)[row * D + d] = r;
 }
 
-template <int D, int FMT, int TP, int RING, int SLOTS, bool FUSED>
+template <int D, int FMT, int TP, int RING, int SLOTS, bool FUSED, bool ATT8>
 static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_t stream,
                                  hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NW = kSplitWaves;
   const dim3 grid((unsigned)p.num_parts, (unsigned)p.num_kv_heads, (unsigned)num_seqs);
   if (ev_before && ev_after) {
     // the events take the kernel's own start and end timestamps
-    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED>), grid,
-                          dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
+    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8>),
+                          grid, dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED>), grid,
-                       dim3(NW * kWave), 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8>),
+                       grid, dim3(NW * kWave), 0, stream, p);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.direct) return err;
@@ -824,24 +921,36 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
 // 2x1s1 (the same with the next tile staged in LDS).
 // KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 4x1, 2x1s1, 2x1s2,
 // 4x1s1) overrides it for tuning sweeps; a shape whose LDS ring would pass
-// 64 KiB is rejected.
+// 64 KiB is rejected. The all-FP8 mode (att8) is built for the two planned
+// shapes only.
 template <int D, int FMT, int TP, int RING, int SLOTS>
-static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused,
+static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused, bool att8,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int E = FMT == kFmtBf16 ? 2 : 1;
   if constexpr (kSplitWaves * SLOTS * TP * 2 * kPage * D * E > kMaxLdsRing) {
     return hipErrorInvalidValue;
   } else {
-    return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true>(p, num_seqs, stream, ev_before,
-                                                                  ev_after)
-                 : launch_variant<D, FMT, TP, RING, SLOTS, false>(p, num_seqs, stream, ev_before,
-                                                                   ev_after);
+    if (att8) {
+      if constexpr (FMT != kFmtBf16 && TP == 2 && RING == 1 && SLOTS <= 1) {
+        return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, true>(
+                           p, num_seqs, stream, ev_before, ev_after)
+                     : launch_variant<D, FMT, TP, RING, SLOTS, false, true>(
+                           p, num_seqs, stream, ev_before, ev_after);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
+    return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, false>(p, num_seqs, stream,
+                                                                         ev_before, ev_after)
+                 : launch_variant<D, FMT, TP, RING, SLOTS, false, false>(p, num_seqs, stream,
+                                                                          ev_before, ev_after);
   }
 }
 
 template <int D, int FMT>
 static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, int plan_slots,
-                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+                               bool att8, hipStream_t stream, hipEvent_t ev_before,
+                               hipEvent_t ev_after) {
   int tp = 2, ring = 1, slots = plan_slots;
   if (const char* env = getenv("KVFP8_SPLIT_VARIANT")) {
     int a = 0, c = 0, sl = 0;
@@ -850,8 +959,8 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, 
   }
 #define KVFP8_SHAPE(TP_, RING_, SLOTS_)                                                 \
   if (tp == TP_ && ring == RING_ && slots == SLOTS_)                                    \
-    return launch_shape<D, FMT, TP_, RING_, SLOTS_>(p, num_seqs, fused, stream, ev_before, \
-                                                    ev_after);
+    return launch_shape<D, FMT, TP_, RING_, SLOTS_>(p, num_seqs, fused, att8, stream,   \
+                                                    ev_before, ev_after);
   KVFP8_SHAPE(2, 1, 0)
   KVFP8_SHAPE(2, 2, 0)
   KVFP8_SHAPE(4, 1, 0)
@@ -864,27 +973,35 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, 
 
 template <int D>
 static hipError_t launch_dim(const DecodeParams& p, int fmt, int num_seqs, bool fused, int slots,
-                             hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+                             bool att8, hipStream_t stream, hipEvent_t ev_before,
+                             hipEvent_t ev_after) {
   switch (fmt) {
     case kFmtBf16:
-      return launch_typed<D, kFmtBf16>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
+      return launch_typed<D, kFmtBf16>(p, num_seqs, fused, slots, att8, stream, ev_before,
+                                       ev_after);
     case kFmtE4M3:
-      return launch_typed<D, kFmtE4M3>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
+      return launch_typed<D, kFmtE4M3>(p, num_seqs, fused, slots, att8, stream, ev_before,
+                                       ev_after);
     case kFmtE5M2:
-      return launch_typed<D, kFmtE5M2>(p, num_seqs, fused, slots, stream, ev_before, ev_after);
+      return launch_typed<D, kFmtE5M2>(p, num_seqs, fused, slots, att8, stream, ev_before,
+                                       ev_after);
     default:
       return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
-                               bool fused, int slots, hipStream_t stream, hipEvent_t ev_before,
-                               hipEvent_t ev_after) {
+                               bool fused, int slots, bool att8, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after) {
   switch (head_dim) {
-    case 64: return launch_dim<64>(p, fmt, num_seqs, fused, slots, stream, ev_before, ev_after);
-    case 128: return launch_dim<128>(p, fmt, num_seqs, fused, slots, stream, ev_before, ev_after);
-    case 256: return launch_dim<256>(p, fmt, num_seqs, fused, slots, stream, ev_before, ev_after);
-    default: return hipErrorInvalidValue;
+    case 64:
+      return launch_dim<64>(p, fmt, num_seqs, fused, slots, att8, stream, ev_before, ev_after);
+    case 128:
+      return launch_dim<128>(p, fmt, num_seqs, fused, slots, att8, stream, ev_before, ev_after);
+    case 256:
+      return launch_dim<256>(p, fmt, num_seqs, fused, slots, att8, stream, ev_before, ev_after);
+    default:
+      return hipErrorInvalidValue;
   }
 }
 

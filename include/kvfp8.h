@@ -90,7 +90,8 @@ enum kvq_status {
   KVQ_ERR_INVALID_ARG = -1,       /* null / misaligned pointer, negative size,
                                      inconsistent shapes */
   KVQ_ERR_UNSUPPORTED = -2,       /* head_dim not in {64,128,256}, page size
-                                     not 16, Hq % Hkv != 0, group > 8 */
+                                     not 16, Hq % Hkv != 0, group > 8 (> 16
+                                     with KVQ_ATTN_FP8) */
   KVQ_ERR_WORKSPACE_TOO_SMALL = -3,
   KVQ_ERR_HIP = -4                /* a HIP runtime call or launch failed */
 };
@@ -106,6 +107,25 @@ enum kvq_scale_mode { KVQ_SCALE_PER_TENSOR = 0, KVQ_SCALE_PER_KV_HEAD = 1 };
 /* Output element type of the attention. */
 enum kvq_out_dtype { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 };
 
+/*
+ * Arithmetic of the attention over an fp8 cache.
+ *   KVQ_ATTN_BF16  the cache codes expand exactly to bf16 and q stays bf16;
+ *                  q k^T has exact products, P is carried to about 2^-16
+ *                  (bf16 high part + bf16 residue). Group size G <= 8.
+ *   KVQ_ATTN_FP8   the whole attention in FP8 e4m3 ("State of FP8 KV cache
+ *                  and attention quantization in vLLM", introduction: QK and
+ *                  ScoreV products in FP8): each query row is quantised to
+ *                  e4m3 with s_q = amax|q_row| / 448 in the kernel, q k^T
+ *                  runs on the codes (fp8 MFMA), and the probabilities of
+ *                  every aligned 32-position block (positions 32j .. 32j+31)
+ *                  are quantised to e4m3 relative to the block's largest
+ *                  logit for the P*V product; each block's product is
+ *                  rescaled into the FP32 sum, and the softmax normaliser
+ *                  sums the unquantised probabilities. G <= 16. fp8 caches
+ *                  only (a bf16 layer gives KVQ_ERR_UNSUPPORTED).
+ */
+enum kvq_attn_dtype { KVQ_ATTN_BF16 = 0, KVQ_ATTN_FP8 = 1 };
+
 /* Per-layer descriptor. */
 typedef struct kvq_layer_desc {
   int32_t num_q_heads;     /* Hq */
@@ -117,6 +137,7 @@ typedef struct kvq_layer_desc {
   int32_t sliding_window;  /* W > 0: attend to the last W positions (the new
                               token included); 0: full attention */
   float sm_scale;          /* softmax scale; 0 means 1/sqrt(head_dim) */
+  int32_t attn_dtype;      /* enum kvq_attn_dtype; 0 (bf16 arithmetic) by default */
 } kvq_layer_desc;
 
 /*

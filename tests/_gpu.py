@@ -51,13 +51,13 @@ class GpuLayer:
     library, every position of the case written by the library."""
 
     def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
-                 scales=None, fmt=None):
+                 scales=None, fmt=None, attn="bf16"):
         self.case = case
         fmt = cache_fmt(fp8, fmt)
         self.fp8 = fp8 = fmt != "bf16"
         self.desc = kv.layer_desc(case.num_q_heads, case.num_kv_heads, case.head_dim, fmt,
                                   "per_kv_head" if per_head else "per_tensor",
-                                  window, sm_scale)
+                                  window, sm_scale, attn)
         self.k_new = bf16_dev(case.k_new)
         self.v_new = bf16_dev(case.v_new)
         self.slots = i64_dev(case.slots)
@@ -105,9 +105,10 @@ class OracleLayer:
     """The same layer through the oracle (its own scales, its own caches)."""
 
     def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
-                 scales=None, fmt=None):
+                 scales=None, fmt=None, attn="bf16"):
         fmt = cache_fmt(fp8, fmt)
         self.fmt = _ORACLE_FMT[fmt]
+        self.attn = attn
         fp8 = fmt != "bf16"
         self.case, self.fp8, self.per_head = case, fp8, per_head
         self.window, self.sm_scale = window, sm_scale
@@ -128,9 +129,9 @@ class OracleLayer:
 
     def attend(self):
         c = self.case
-        return oracle.attention(c.q, self.k_cache, self.v_cache, c.block_tables, c.lens,
-                                c.num_kv_heads, self.fmt, self.per_head,
-                                self.window, self.sm_scale, self.ks, self.vs)
+        fn = oracle.attention_fp8attn if self.attn == "fp8" else oracle.attention
+        return fn(c.q, self.k_cache, self.v_cache, c.block_tables, c.lens, c.num_kv_heads,
+                  self.fmt, self.per_head, self.window, self.sm_scale, self.ks, self.vs)
 
 
 def errors(gpu_out, ref):

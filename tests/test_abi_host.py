@@ -144,3 +144,21 @@ def test_no_oracle_in_the_product():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text, f
                 assert "orc_" not in text, f
+
+
+def test_fp8_attention_mode_checks():
+    # the all-FP8 mode reads fp8 caches only and takes groups up to 16;
+    # the bf16-arithmetic mode stops at 8
+    with pytest.raises(kv.Kvfp8Error):
+        kv.decode_workspace_bytes(kv.layer_desc(32, 8, 128, "bf16", attn="fp8"), 1, 1024)
+    assert kv.decode_workspace_bytes(kv.layer_desc(64, 4, 128, attn="fp8"), 1, 4096) >= 0
+    assert kv.decode_workspace_bytes(kv.layer_desc(64, 4, 128, "fp8_e5m2", attn="fp8"), 1,
+                                     4096) >= 0
+    with pytest.raises(kv.Kvfp8Error):
+        kv.decode_workspace_bytes(kv.layer_desc(64, 4, 128, attn="bf16"), 1, 1024)
+    with pytest.raises(kv.Kvfp8Error):
+        kv.decode_workspace_bytes(kv.layer_desc(128, 4, 128, attn="fp8"), 1, 1024)
+    bad = kv.layer_desc(32, 8, 128)
+    bad.attn_dtype = 7
+    with pytest.raises(kv.Kvfp8Error):
+        kv.decode_workspace_bytes(bad, 1, 1024)
