@@ -190,26 +190,65 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   }
   // All-FP8 mode: the query row as e4m3 codes with s_q = amax / 448 (the
   // 4 lanes of a column hold the whole row), packed as 8-byte MFMA operands
-  // in the same order.
+  // in the same order. Run once the first tile's loads are in flight, so it
+  // overlaps their latency.
+  //   The codes are those of the IEEE quotient x / s_q. With r = 1 / s_q
+  // (correctly rounded), q0 = x r, e = fma(-q0, s_q, x), fma(e, r, q0) is
+  // that quotient by Markstein's theorem when nothing underflows; checked
+  // exhaustively over every bf16 amax and every bf16 x with |x| <= amax, the
+  // e4m3 codes of the two agree for all s_q >= 2^-100 (and the quotients
+  // themselves wherever they reach 2^-12). A row with a smaller or non-finite
+  // scale takes the division. The hardware conversion (round to nearest
+  // even) gives the saturating encoder's codes on [-448, 448] and just
+  // beyond, where the quotients lie (checked for every fp32 value there).
   uint64_t qop8[ATT8 ? NK : 1];
   float q_scale = 1.0f;
-  if constexpr (ATT8) {
-    float am = 0.0f;
+  auto quantize_q = [&]() {
+    if constexpr (ATT8) {
+      float am = 0.0f;
+      uint32_t mag = 0u;                               // largest |x| bits: NaN > Inf > finite
 #pragma unroll
-    for (int s = 0; s < NK; ++s)
+      for (int s = 0; s < NK; ++s) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf((float)qop[s][j]));
-    am = col_max(am);
-    q_scale = am == 0.0f ? 1.0f : am / 448.0f;
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf((float)qop[s][j]));
+        const uint4 w = __builtin_bit_cast(uint4, qop[s]);
+        const uint32_t m4 = max(max(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
+                                max(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
+        mag = max(mag, max(m4 & 0xFFFFu, m4 >> 16));
+      }
+      am = col_max(am);
+      q_scale = am == 0.0f ? 1.0f : am / 448.0f;
+      // a NaN element takes the division path too (the encoders' NaN codes differ)
+      const bool fast = q_scale >= 0x1p-100f && q_scale <= 0x1p+120f && mag <= 0x7F80u;
+      if (__builtin_amdgcn_ballot_w64(!fast) == 0ull) {
+        const float r = 1.0f / q_scale;
 #pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      uint64_t w = 0;
+        for (int s = 0; s < NK; ++s) {
+          float qq[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        w |= (uint64_t)e4m3_encode_sat((float)qop[s][j] / q_scale) << (8 * j);
-      qop8[s] = w;
+          for (int j = 0; j < 8; ++j) {
+            const float x = (float)qop[s][j];
+            const float q0 = x * r;
+            qq[j] = __builtin_fmaf(__builtin_fmaf(-q0, q_scale, x), r, q0);
+          }
+          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(qq[0], qq[1], 0, false);
+          lo = __builtin_amdgcn_cvt_pk_fp8_f32(qq[2], qq[3], lo, true);
+          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(qq[4], qq[5], 0, false);
+          hi = __builtin_amdgcn_cvt_pk_fp8_f32(qq[6], qq[7], hi, true);
+          qop8[s] = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          uint64_t w = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            w |= (uint64_t)e4m3_encode_sat((float)qop[s][j] / q_scale) << (8 * j);
+          qop8[s] = w;
+        }
+      }
     }
-  }
+  };
   const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
   const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
   const int32_t* bt_row = p.block_tables + (int64_t)b * p.max_pages_per_seq;
@@ -293,7 +332,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const int64_t page_stride = (int64_t)p.num_kv_heads * PB;
   const uint8_t* kbase = p.k_cache + (int64_t)h * PB;
   const uint8_t* vbase = p.v_cache + (int64_t)h * PB;
-  const float c_log2 = q_scale * ks * p.sm_scale_log2;
+  float c_log2 = ks * p.sm_scale_log2;              // times q_scale in the all-FP8 mode
 
   // ---- fused decode step: the cache write of position L-1 -----------------
   // Exactly one wave streams the page that holds the newest position of this
@@ -583,9 +622,12 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         pw[pg] = (uint32_t)w;
       }
       l_run += fb * ps;
+      // every block's product first, then the folds: the MFMAs issue back to
+      // back and each fold finds its result ready
+      f32x4 tpv[NBLK];
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk) {
-        f32x4 tpv = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        tpv[blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int pp = 0; pp < TP / 2; ++pp) {
           const int i = blk / 4, ep = blk % 4;
@@ -599,13 +641,15 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
           const long vop = (long)(((uint64_t)db << 32) | da);
           const long pop8 = (long)(((uint64_t)pw[2 * pp + 1] << 32) | pw[2 * pp]);
           if constexpr (FMT == kFmtE5M2)
-            tpv = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(vop, pop8, tpv, 0, 0, 0);
+            tpv[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(vop, pop8, tpv[blk], 0, 0, 0);
           else
-            tpv = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop8, tpv, 0, 0, 0);
+            tpv[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop8, tpv[blk], 0, 0, 0);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[blk][e] += fb * tpv[e];
       }
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[blk][e] += fb * tpv[blk][e];
       return;
     }
     float psum_pg[TP];
@@ -713,6 +757,8 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     for (int sl = 0; sl < SLOTS; ++sl)
       if (sl < ntiles) stage_tile(sl, sl);
     if (t_new >= 0) fused_commit();
+    quantize_q();
+    c_log2 *= q_scale;
     for (int t = 0; t < ntiles; ++t) {
       // tiles issued after tile t; the wave that stored the new rows waits
       // for everything once (stores and loads share the counter)
@@ -729,6 +775,8 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     fused_prefetch();
     if (ntiles > 0) load_tile(0, t0);
     if (t_new >= 0) fused_commit();
+    quantize_q();
+    c_log2 *= q_scale;
     for (int t = 0; t < ntiles; t += 2) {
       if (t + 1 < ntiles) load_tile(t + 1, t1);
       if (FUSED && t == t_new) patch_tile(t0);
@@ -743,6 +791,8 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     fused_prefetch();
     if (ntiles > 0) load_tile(0, t0);
     if (t_new >= 0) fused_commit();
+    quantize_q();
+    c_log2 *= q_scale;
     for (int t = 0; t < ntiles; ++t) {
       if (t > 0) load_tile(t, t0);
       if (FUSED && t == t_new) patch_tile(t0);
@@ -753,6 +803,9 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   if constexpr (!ATT8) fold();
   // ---- per-wave results: l over the row quads, lo columns into hi ----------
   l_run = wave_sum_col(l_run);
+  // A NaN logit (a NaN query element or cache code) leaves l NaN but may
+  // never raise the running max; carry it in m so the merges keep it.
+  if (l_run != l_run) m_run = __builtin_nanf("");
   if constexpr (!ATT8) {
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
@@ -782,10 +835,17 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
     const int gg = i / D, d = i % D;
     float M = -INFINITY;
+    bool nan_m = false;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][gg]);
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_m[w][gg];
+      nan_m |= mw != mw;
+      M = fmaxf(M, mw);
+    }
     float o = 0.0f, l = 0.0f;
-    if (M != -INFINITY) {
+    if (nan_m) {
+      M = o = l = __builtin_nanf("");
+    } else if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float wt = __builtin_amdgcn_exp2f(sm_m[w][gg] - M);
@@ -796,7 +856,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const int hq = h * G + gg;
     const int64_t row = (int64_t)b * p.num_q_heads + hq;
     if (p.direct) {
-      const float r = l > 0.0f ? o / l * vs : 0.0f;
+      const float r = (l > 0.0f || l != l) ? o / l * vs : 0.0f;   // NaN stays NaN
       if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
       else reinterpret_cast<float*>(p.out)[row * D + d] = r;
     } else {
@@ -859,7 +919,13 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodePara
 
   // ---- M and the normaliser ---------------------------------------------------
   float m = m0;
-  for (int j = kWave + lane; j < np; j += kWave) m = fmaxf(m, ms[j]);
+  bool nan_m = m0 != m0;                  // a NaN partial makes the row NaN
+  for (int j = kWave + lane; j < np; j += kWave) {
+    const float mj = ms[j];
+    nan_m |= mj != mj;
+    m = fmaxf(m, mj);
+  }
+  const bool any_nan = __builtin_amdgcn_ballot_w64(nan_m) != 0ull;
   const float M = wave_max_all(m);
   const bool empty = (M == -INFINITY);
   const float w0 = empty ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);   // 0 for m0 = -inf
@@ -887,7 +953,7 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodePara
     }
   }
   const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  const float r = L > 0.0f ? o / L * vs : 0.0f;
+  const float r = any_nan ? __builtin_nanf("") : (L > 0.0f ? o / L * vs : 0.0f);
   if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
   else reinterpret_cast<float*>(p.out)[row * D + d] = r;
 }

@@ -143,3 +143,39 @@ def test_fp8attn_decode_step_equals_write_then_attend(label, Hq, Hkv, D, lens, w
     mx, mean = errors(out, ref)
     scale = max(1.0, float(np.abs(ref).max()))
     assert mx <= GATE_MAX_ABS * scale and mean <= GATE_MEAN_ABS * scale, (label, mx, mean)
+
+
+@pytest.mark.parametrize("attn", ["fp8", "bf16"])
+def test_fp8attn_tiny_zero_and_nan_query_rows(attn):
+    # The kernel takes q / s_q by a reciprocal and one fma correction unless
+    # a column of the wave has s_q < 2^-100, a non-finite s_q or a NaN
+    # element; then the wave divides. Rows scaled by 2^-110 (exact in bf16)
+    # take that path: all of KV head 0's group, one head of KV head 1's
+    # (mixed wave). An all-zero row has s_q = 1 and attends uniformly.
+    # A NaN element makes its head's output NaN on both sides (in both
+    # attention modes: its running max never rises, so the merges must carry
+    # the NaN).
+    import dataclasses
+    Hq, Hkv, D = 32, 8, 128
+    case = synth.decode_case(61, Hq, Hkv, D, [1500, 77], shuffle=True, spare_frac=0.2)
+    qf = synth.bits_to_f32(case.q).copy()
+    G = Hq // Hkv
+    qf[:, 0:G] *= np.float32(2.0 ** -110)
+    qf[:, G] *= np.float32(2.0 ** -110)
+    qf[:, 2 * G] = 0.0
+    qf[1, 3 * G + 1, 5] = np.nan
+    q = synth.bf16_bits(qf)
+    assert np.array_equal(synth.bits_to_f32(q)[:, 0:G], qf[:, 0:G])   # scaling stayed exact
+    case = dataclasses.replace(case, q=q)
+    out = host(GpuLayer(case, attn=attn).attend())
+    ref = OracleLayer(case, attn=attn).attend()
+    nan_out = np.isnan(out)
+    assert np.array_equal(nan_out, np.isnan(ref)), (np.argwhere(nan_out.any(-1)).tolist(),
+                                                    np.argwhere(np.isnan(ref).any(-1)).tolist())
+    assert nan_out[1, 3 * G + 1].all() and nan_out.sum() == D
+    out[nan_out] = 0.0
+    ref = np.where(np.isnan(ref), 0.0, ref)
+    mx = float(np.abs(out.astype(np.float64) - ref).max())
+    mean = float(np.abs(out.astype(np.float64) - ref).mean())
+    say(f"[{attn} attention, tiny/zero/nan q] max_abs={mx:.3e} mean_abs={mean:.3e}")
+    assert mx <= GATE_MAX_ABS and mean <= GATE_MEAN_ABS
