@@ -94,6 +94,10 @@ def lib():
                                             _u16p, _i64p, ctypes.c_int64, _u8p,
                                             _u8p, ctypes.c_int64, _f32p, _f32p,
                                             ctypes.c_int]
+        L.orc_kv_cache_write_dyn_mt.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, _u16p, _u16p, _i64p,
+                                                ctypes.c_int64, _u8p, _u8p, ctypes.c_int64,
+                                                _f32p, _f32p, ctypes.c_int]
         L.orc_softmax_weighted_sum.argtypes = [_f64p, _f64p, ctypes.c_int64,
                                                ctypes.c_int, _f64p]
         att = [ctypes.c_int] * 7 + [ctypes.c_double, _u16p, _u8p, _u8p, _i32p,
@@ -222,6 +226,36 @@ def kv_cache_write(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
                                 _threads(nthreads))
 
 
+PER_TENSOR, PER_KV_HEAD, PER_TOKEN, PER_TOKEN_HEAD = 0, 1, 2, 3
+
+
+def scale_pools(num_pages: int, num_kv_heads: int):
+    """Zeroed K and V scale pools, float32 [P][H][16] (one scale per slot)."""
+    return (np.zeros((num_pages, num_kv_heads, 16), np.float32),
+            np.zeros((num_pages, num_kv_heads, 16), np.float32))
+
+
+def kv_cache_write_dyn(k_cache, v_cache, k, v, slots, dtype, mode, k_pool, v_pool,
+                       nthreads=None):
+    """Cache write with dynamic per-token scales (mode PER_TOKEN: one per
+    token over all heads; PER_TOKEN_HEAD: one per token and KV head). In
+    place on the uint8 caches [P][H][PB] and the float32 pools [P][H][16]."""
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    T, H, D = k.shape
+    assert mode in (PER_TOKEN, PER_TOKEN_HEAD) and H <= 64
+    for a in (k_cache, v_cache):
+        assert a.flags.c_contiguous and a.dtype == np.uint8
+    for a in (k_pool, v_pool):
+        assert a.flags.c_contiguous and a.dtype == np.float32 and a.shape == (k_cache.shape[0], H, 16)
+    lib().orc_kv_cache_write_dyn_mt(H, D, dtype, int(mode), _ptr(k, _u16p), _ptr(v, _u16p),
+                                    _ptr(slots, _i64p), T, _ptr(k_cache, _u8p),
+                                    _ptr(v_cache, _u8p), k_cache.shape[0],
+                                    _ptr(k_pool, _f32p), _ptr(v_pool, _f32p),
+                                    _threads(nthreads))
+
+
 # -------------------------------------------------------------- attention --
 def softmax_weighted_sum(z: np.ndarray, v: np.ndarray) -> np.ndarray:
     z = np.ascontiguousarray(z, dtype=np.float64)
@@ -255,7 +289,9 @@ def _att_common(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
 def attention(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads,
               dtype, per_head=True, window=0, sm_scale=0.0, k_scale=None,
               v_scale=None, nthreads=None) -> np.ndarray:
-    """float64 [B][Hq][D] decode attention over the paged caches."""
+    """float64 [B][Hq][D] decode attention over the paged caches. per_head
+    is the scale mode: False / PER_TENSOR, True / PER_KV_HEAD, or PER_TOKEN /
+    PER_TOKEN_HEAD with k_scale, v_scale the float32 [P][H][16] pools."""
     args, out, _keep = _att_common(q, k_cache, v_cache, block_tables,
                                    context_lens, num_kv_heads, dtype, per_head,
                                    window, sm_scale, k_scale, v_scale)

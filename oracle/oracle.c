@@ -543,6 +543,83 @@ void orc_kv_cache_write_mt(int H, int D, int dtype, int per_head,
   for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
 }
 
+/* Cache write with dynamic per-token scales ("FP8量化与长上下文推理" section
+ * 2.2: every new token gets its own scale; "cooking-agi", section "dynamic
+ * vs static scale": each token's largest magnitude lands on the format's
+ * largest value). mode 2: one scale per token over all H*D of its values;
+ * mode 3: one per (token, KV head) over D values; K and V separately. The
+ * scale follows the static calibration rule (orc_scale_from_amax_fmt: amax
+ * / fmax, 1 for an all-zero set, NaN if a NaN is present) and is stored for
+ * slot (page, r) of head h at pool[(page * H + h) * 16 + r]; the codes are
+ * then those of the static write with that scale. bf16 layers copy and
+ * leave the pools alone. */
+void orc_kv_cache_write_dyn(int H, int D, int dtype, int mode, const uint16_t* k,
+                            const uint16_t* v, const int64_t* slots, int64_t T,
+                            uint8_t* kc, uint8_t* vc, int64_t num_pages, float* ks_pool,
+                            float* vs_pool) {
+  float sk[64], sv[64];
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t slot = slots[t];
+    if (slot < 0 || slot / 16 >= num_pages) continue;
+    const uint16_t* kt = k + t * H * D;
+    const uint16_t* vt = v + t * H * D;
+    if (dtype != 0) {
+      orc_scale_from_amax_fmt(kt, 1, H, D, mode == 3, dtype, sk);
+      orc_scale_from_amax_fmt(vt, 1, H, D, mode == 3, dtype, sv);
+      if (mode != 3)
+        for (int h = 1; h < H; ++h) {
+          sk[h] = sk[0];
+          sv[h] = sv[0];
+        }
+      int64_t page = slot / 16;
+      int r = (int)(slot % 16);
+      for (int h = 0; h < H; ++h) {
+        ks_pool[(page * H + h) * 16 + r] = sk[h];
+        vs_pool[(page * H + h) * 16 + r] = sv[h];
+      }
+    }
+    orc_kv_cache_write(H, D, dtype, 1, kt, vt, &slots[t], 1, kc, vc, num_pages, sk, sv);
+  }
+}
+
+typedef struct {
+  int H, D, dtype, mode;
+  const uint16_t *k, *v;
+  const int64_t* slots;
+  int64_t lo, hi;
+  uint8_t *kc, *vc;
+  int64_t num_pages;
+  float *ks, *vs;
+} dwjob;
+
+static void* dyn_write_worker(void* p) {
+  dwjob* j = (dwjob*)p;
+  int64_t off = j->lo * j->H * j->D;
+  orc_kv_cache_write_dyn(j->H, j->D, j->dtype, j->mode, j->k + off, j->v + off,
+                         j->slots + j->lo, j->hi - j->lo, j->kc, j->vc, j->num_pages,
+                         j->ks, j->vs);
+  return NULL;
+}
+
+/* Threaded: tokens split across threads (callers pass distinct slots). */
+void orc_kv_cache_write_dyn_mt(int H, int D, int dtype, int mode, const uint16_t* k,
+                               const uint16_t* v, const int64_t* slots, int64_t T,
+                               uint8_t* kc, uint8_t* vc, int64_t num_pages, float* ks_pool,
+                               float* vs_pool, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (T < 4096) nthreads = 1;
+  pthread_t th[256];
+  dwjob jobs[256];
+  for (int i = 0; i < nthreads; ++i) {
+    dwjob w = {H, D, dtype, mode, k, v, slots, T * i / nthreads, T * (i + 1) / nthreads,
+               kc, vc, num_pages, ks_pool, vs_pool};
+    jobs[i] = w;
+    pthread_create(&th[i], NULL, dyn_write_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
 /* Dequantised element (float64) of the K or V cache. */
 static double cache_value(const uint8_t* cache, int is_v, int64_t page, int H,
                           int h, int r, int d, int D, int dtype, double scale) {
@@ -604,8 +681,9 @@ static int64_t gather(const att_args* a, int b, int i, double* z, double* v) {
   int64_t L = a->lens[b];
   if (L <= 0) return 0;
   int64_t lo = (a->window > 0 && L > a->window) ? L - a->window : 0;
-  double ks = a->dtype != 0 ? (double)a->ks[a->per_head ? h : 0] : 1.0;
-  double vs = a->dtype != 0 ? (double)a->vs[a->per_head ? h : 0] : 1.0;
+  /* per_head: 0 per tensor, 1 per KV head, 2 / 3 dynamic (per-slot pools) */
+  double ks = a->dtype != 0 && a->per_head < 2 ? (double)a->ks[a->per_head ? h : 0] : 1.0;
+  double vs = a->dtype != 0 && a->per_head < 2 ? (double)a->vs[a->per_head ? h : 0] : 1.0;
   const uint16_t* qi = a->q + ((int64_t)b * a->Hq + i) * a->D;
   /* the query as the attention reads it: its bf16 values, or (all-FP8
    * variant) their e4m3 codes times the row's scale */
@@ -623,6 +701,10 @@ static int64_t gather(const att_args* a, int b, int i, double* z, double* v) {
   for (int64_t t = lo; t < L; ++t) {
     int64_t page = a->bt[(int64_t)b * a->max_pages + t / 16];
     int r = (int)(t % 16);
+    if (a->dtype != 0 && a->per_head >= 2) {     /* dynamic: the slot's own scales */
+      ks = (double)a->ks[(page * a->Hkv + h) * 16 + r];
+      vs = (double)a->vs[(page * a->Hkv + h) * 16 + r];
+    }
     double dot = 0.0;
     for (int d = 0; d < a->D; ++d) {
       double kh = cache_value(a->kc, 0, page, a->Hkv, h, r, d, a->D, a->dtype, ks);

@@ -29,7 +29,7 @@ POISON_FP8 = 0x7F
 POISON_BF16 = 0x7FC0
 
 _STREAMS = {"q": 0, "k": 1, "v": 2, "lens": 3, "perm": 4, "outlier": 5,
-            "drift": 6, "heavy": 7, "new": 8, "extra": 9}
+            "drift": 6, "heavy": 7, "new": 8, "extra": 9, "spread": 10}
 
 
 def rng(workload: int, purpose: str) -> np.random.Generator:
@@ -121,7 +121,9 @@ def decode_case(workload: int, num_q_heads: int, num_kv_heads: int,
                 spare_frac: float = 0.0, values: str = "normal",
                 max_pages_per_seq: Optional[int] = None) -> DecodeCase:
     """values: "normal" (all N(0,1)), "tiny" (2 outlier channels x20 per KV
-    head in K and V) or "drift" (slow V mean drift and 64 heavy-tail rows)."""
+    head in K and V), "drift" (slow V mean drift and 64 heavy-tail rows) or
+    "spread" (every (token, KV head) row of K and of V scaled by 2^u, u an
+    integer drawn uniformly from -6..6: tokens of very different magnitude)."""
     lens = np.asarray(lens, dtype=np.int32)
     B, Hq, Hkv, D = len(lens), num_q_heads, num_kv_heads, head_dim
     T = int(lens.astype(np.int64).sum())
@@ -144,6 +146,10 @@ def decode_case(workload: int, num_q_heads: int, num_kv_heads: int,
         r = rng(workload, "heavy")
         heavy = r.choice(T, size=min(64, T), replace=False)
         v[heavy] *= 30.0
+    elif values == "spread":
+        r = rng(workload, "spread")
+        k *= np.exp2(r.integers(-6, 7, size=(T, Hkv, 1))).astype(np.float32)
+        v *= np.exp2(r.integers(-6, 7, size=(T, Hkv, 1))).astype(np.float32)
     elif values != "normal":
         raise ValueError(values)
     return DecodeCase(Hq, Hkv, D, lens, bf16_bits(q), bf16_bits(k), bf16_bits(v),
