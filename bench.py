@@ -61,7 +61,7 @@ class LayerStack:
 
     def __init__(self, kv, torch, B, Hq, Hkv, D, lens, NL, cache_dtype="fp8_e4m3",
                  window=0, shuffle=False, spare_frac=0.0, seed=0, dtypes=None, path="fused",
-                 attn="bf16"):
+                 attn="bf16", scales="per_kv_head"):
         self.kv, self.torch = kv, torch
         self.path = path
         dev = torch.device("cuda:0")
@@ -72,7 +72,7 @@ class LayerStack:
         self.max_len = max(self.lens)
         dtypes = dtypes or [cache_dtype] * NL
         windows = window if isinstance(window, list) else [window] * NL
-        self.descs = [kv.layer_desc(Hq, Hkv, D, dtypes[i], "per_kv_head", windows[i],
+        self.descs = [kv.layer_desc(Hq, Hkv, D, dtypes[i], scales, windows[i],
                                     attn=attn if dtypes[i] != "bf16" else "bf16")
                       for i in range(NL)]
         import numpy as np
@@ -110,14 +110,22 @@ class LayerStack:
             vc = torch.empty_like(kc)
             k_all = torch.randn((T + B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
             v_all = torch.randn((T + B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
-            if d.fp8:
-                ks = torch.empty(Hkv, dtype=torch.float32, device=dev)
-                vs = torch.empty(Hkv, dtype=torch.float32, device=dev)
-                kv.kv_scale_from_amax(d, k_all, ks)
-                kv.kv_scale_from_amax(d, v_all, vs)
+            if d.dynamic:
+                # dynamic per-token scales: pools beside the pages, set by the write
+                ks = torch.zeros(kv.scale_pool_shape(d, num_pages), dtype=torch.float32,
+                                 device=dev)
+                vs = torch.zeros_like(ks)
+                kv.kv_cache_write_dynamic(d, k_all[:T], v_all[:T], self.fill_slots, kc, vc, ks,
+                                          vs)
             else:
-                ks = vs = None
-            kv.kv_cache_write(d, k_all[:T], v_all[:T], self.fill_slots, kc, vc, ks, vs)
+                if d.fp8:
+                    ks = torch.empty(Hkv, dtype=torch.float32, device=dev)
+                    vs = torch.empty(Hkv, dtype=torch.float32, device=dev)
+                    kv.kv_scale_from_amax(d, k_all, ks)
+                    kv.kv_scale_from_amax(d, v_all, vs)
+                else:
+                    ks = vs = None
+                kv.kv_cache_write(d, k_all[:T], v_all[:T], self.fill_slots, kc, vc, ks, vs)
             k_new = k_all[T:].contiguous()
             v_new = v_all[T:].contiguous()
             q = torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
@@ -137,12 +145,14 @@ class LayerStack:
         for ly in self.layers:
             d = ly["desc"]
             if self.path == "fused":
-                kv.decode_step(d, ly["k_new"], ly["v_new"], ly["kc"], ly["vc"], ly["out"], ly["q"],
-                               self.block_tables, self.context_lens, self.max_len, ly["ks"],
-                               ly["vs"], ly["ws"])
+                step = kv.decode_step_dynamic if d.dynamic else kv.decode_step
+                step(d, ly["k_new"], ly["v_new"], ly["kc"], ly["vc"], ly["out"], ly["q"],
+                     self.block_tables, self.context_lens, self.max_len, ly["ks"], ly["vs"],
+                     ly["ws"])
             else:
-                kv.kv_cache_write(d, ly["k_new"], ly["v_new"], self.new_slots, ly["kc"],
-                                  ly["vc"], ly["ks"], ly["vs"])
+                write = kv.kv_cache_write_dynamic if d.dynamic else kv.kv_cache_write
+                write(d, ly["k_new"], ly["v_new"], self.new_slots, ly["kc"], ly["vc"], ly["ks"],
+                      ly["vs"])
                 kv.paged_decode_attention(d, ly["out"], ly["q"], ly["kc"], ly["vc"],
                                           self.block_tables, self.context_lens, self.max_len,
                                           ly["ks"], ly["vs"], ly["ws"])
@@ -160,12 +170,16 @@ class LayerStack:
         entries, scales."""
         n = self.attended(desc)
         bt = sum((x + 15) // 16 + 1 for x in n) * 4
-        sc = 2 * self.Hkv * 4 if desc.fp8 else 0
+        if desc.dynamic:      # a K and a V scale per attended position and KV head
+            sc = sum(n) * self.Hkv * 2 * 4
+        else:
+            sc = 2 * self.Hkv * 4 if desc.fp8 else 0
         return self.kv_bytes(desc) + self.B * self.Hq * self.D * 2 + bt + sc
 
     def write_bytes(self, desc):
         """The cache write of the new tokens: bf16 K/V in, cache rows out."""
-        return self.B * self.Hkv * self.D * 2 * (2 + desc.elem_bytes)
+        sc = self.B * self.Hkv * 2 * 4 if desc.dynamic else 0    # the new rows' scales
+        return self.B * self.Hkv * self.D * 2 * (2 + desc.elem_bytes) + sc
 
     def step_bytes(self, desc):
         """Whole layer step: attention (K/V, q, out, block table, scales) plus
@@ -177,6 +191,11 @@ class LayerStack:
 
     def total_kv_bytes(self):
         return sum(self.kv_bytes(ly["desc"]) for ly in self.layers)
+
+
+SCALE_TEXT = {"per_kv_head": "per-KV-head scales", "per_tensor": "per-tensor scales",
+              "per_token": "dynamic per-token scales",
+              "per_token_head": "dynamic per-token, per-KV-head scales"}
 
 
 def time_steps(torch, kv, stack, steps, warmup, profile=True):
@@ -348,6 +367,10 @@ def main():
     ap.add_argument("--attn", default="bf16", choices=["bf16", "fp8"],
                     help="attention arithmetic: bf16 MFMA on exact cache codes, or the "
                          "all-FP8 mode (e4m3 q and P, fp8 MFMA)")
+    ap.add_argument("--scales", default="per_kv_head",
+                    choices=["per_kv_head", "per_tensor", "per_token", "per_token_head"],
+                    help="static scales (per KV head, per tensor) or dynamic per-token scales "
+                         "(stored per slot beside the pages)")
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="fused: kvq_decode_step per layer; separate: write + attention calls")
     ap.add_argument("--no-sweep", action="store_true")
@@ -393,19 +416,22 @@ def main():
         import synth
         lens = [int(x) for x in synth.batched_lens()]
         stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], lens, NL, args.cache,
-                           shuffle=True, spare_frac=0.1, seed=3, path=args.path, attn=args.attn)
+                           shuffle=True, spare_frac=0.1, seed=3, path=args.path, attn=args.attn,
+                           scales=args.scales)
         ctx_desc = f"lengths {min(lens)}..{max(lens)} (sum {sum(lens)})"
     elif args.workload == "gptoss":
         dts = ["fp8_e4m3" if i % 2 == 0 else "bf16" for i in range(NL)]
         wins = [0 if i % 2 == 0 else 128 for i in range(NL)]
         stack = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, seed=5,
-                           dtypes=dts, window=wins, path=args.path, attn=args.attn)
+                           dtypes=dts, window=wins, path=args.path, attn=args.attn,
+                           scales=args.scales)
         ctx_desc = f"context {ctx}; {NL // 2} full fp8 layers + {NL - NL // 2} SW-128 bf16 layers"
     else:
         stack = LayerStack(kv, torch, w["B"], w["Hq"], w["Hkv"], w["D"], [ctx], NL, args.cache,
-                           seed=1, path=args.path, attn=args.attn)
+                           seed=1, path=args.path, attn=args.attn, scales=args.scales)
         ctx_desc = f"context {ctx}"
-    log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}, attention {args.attn}")
+    log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}, attention "
+        f"{args.attn}, scales {args.scales}")
     # the timed region: K steps, each one replay of the captured decode step
     ms = time_steps_graph(torch, stack, args.steps, args.warmup)
     # eager steps with the split kernel's launches timed by the library
@@ -444,12 +470,14 @@ def main():
                   else "bf16 cache, fp32 accumulation"),
         "data": "synthetic (seeded normal K/V/q)",
         "config": {
-            "workload": f"{w['desc']}, {ctx_desc}, {args.cache} cache with per-KV-head scales, "
+            "workload": f"{w['desc']}, {ctx_desc}, {args.cache} cache with "
+                        f"{SCALE_TEXT[args.scales]}, "
                         f"{NL} layers per step (per layer: the new token's cache write + paged "
                         f"decode attention, " + ("one kvq_decode_step call" if args.path == "fused"
                         else "kvq_kv_cache_write + kvq_paged_decode_attention") + ")",
             "path": args.path,
             "attention": args.attn,
+            "scales": args.scales,
             "batch": w["B"], "q_heads": w["Hq"], "kv_heads": w["Hkv"], "head_dim": w["D"],
             "page_size": 16, "layers_per_step": NL, "parallelism": "single GPU",
         },
@@ -467,7 +495,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
             "traffic": measured_traffic(f"{args.workload}:{ctx}:{args.cache}:{NL}:{args.path}")
-            if args.workload == "llama8b" and args.attn == "bf16" else None,
+            if args.workload == "llama8b" and args.attn == "bf16" and args.scales == "per_kv_head"
+            else None,
             "launch_us": round(split_ms * 1e3, 3) if split_ms else None,
             "launches_timed": nsplit,
             "timed_with": "kernel-timestamped HIP event pairs around every split-kernel launch "

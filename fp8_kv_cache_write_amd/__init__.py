@@ -17,14 +17,15 @@ LIB_PATH = os.path.join(_HERE, "libkvfp8.so")
 
 # enums of kvfp8.h
 BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2
-PER_TENSOR, PER_KV_HEAD = 0, 1
+PER_TENSOR, PER_KV_HEAD, PER_TOKEN, PER_TOKEN_HEAD = 0, 1, 2, 3
 ATTN_BF16, ATTN_FP8 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 PAGE_SIZE = 16
 
 _DTYPES = {"bf16": BF16, "auto": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3,
            "fp8_e5m2": FP8_E5M2}
-_SCALES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD}
+_SCALES = {"per_tensor": PER_TENSOR, "per_kv_head": PER_KV_HEAD, "per_token": PER_TOKEN,
+           "per_token_head": PER_TOKEN_HEAD}
 _ATTN = {"bf16": ATTN_BF16, "fp8": ATTN_FP8}
 
 
@@ -46,6 +47,11 @@ class LayerDesc(ctypes.Structure):
         return self.cache_dtype in (FP8_E4M3, FP8_E5M2)
 
     @property
+    def dynamic(self):
+        """fp8 layer with per-token scales (pools written by the write)."""
+        return self.fp8 and self.scale_mode in (PER_TOKEN, PER_TOKEN_HEAD)
+
+    @property
     def elem_bytes(self):
         return 1 if self.fp8 else 2
 
@@ -58,7 +64,8 @@ class LayerDesc(ctypes.Structure):
 def layer_desc(num_q_heads, num_kv_heads, head_dim, cache_dtype="fp8_e4m3",
                scale_mode="per_kv_head", sliding_window=0, sm_scale=0.0, attn="bf16"):
     """Descriptor of one attention layer. cache_dtype: "fp8_e4m3"/"fp8",
-    "fp8_e5m2" or "bf16"/"auto"; scale_mode: "per_tensor" or "per_kv_head";
+    "fp8_e5m2" or "bf16"/"auto"; scale_mode: "per_tensor", "per_kv_head"
+    (static) or "per_token", "per_token_head" (dynamic, see scale_pool_shape);
     attn: "bf16" (exact cache codes, bf16 MFMA) or "fp8" (e4m3 q and P, fp8
     MFMA)."""
     return LayerDesc(int(num_q_heads), int(num_kv_heads), int(head_dim), PAGE_SIZE,
@@ -88,6 +95,9 @@ def lib():
                                                  i32, i32, vp, vp, vp, sz, vp]
         L.kvq_decode_step.argtypes = [dp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, vp, i32,
                                       i32, vp, vp, vp, sz, vp]
+        L.kvq_kv_cache_write_dynamic.argtypes = [dp, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp]
+        L.kvq_decode_step_dynamic.argtypes = [dp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, vp,
+                                              i32, i32, vp, vp, vp, sz, vp]
         L.kvq_kv_scale_from_amax.argtypes = [dp, vp, i64, vp, vp]
         L.kvq_e4m3_quantize.argtypes = [vp, i64, vp, vp, vp]
         L.kvq_e5m2_quantize.argtypes = [vp, i64, vp, vp, vp]
@@ -98,7 +108,8 @@ def lib():
         for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes", "kvq_decode_step",
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
                   "kvq_e4m3_quantize", "kvq_e5m2_quantize", "kvq_profile_begin",
-                  "kvq_profile_end"):
+                  "kvq_profile_end", "kvq_kv_cache_write_dynamic",
+                  "kvq_decode_step_dynamic"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -166,6 +177,47 @@ def kv_cache_write(desc, k, v, slot_mapping, k_cache, v_cache, k_scale=None,
     _check("kvq_kv_cache_write", lib().kvq_kv_cache_write(
         ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
         _ptr(v_cache), num_pages, _ptr(k_scale), _ptr(v_scale), _stream(stream)))
+
+
+def scale_pool_shape(desc, num_pages):
+    """Shape of one K or V scale pool (float32) of a layer with dynamic
+    scales: [num_pages, Hkv, 16], one scale per slot and KV head."""
+    return (int(num_pages), desc.num_kv_heads, PAGE_SIZE)
+
+
+def _check_pools(desc, k_cache, k_scales, v_scales):
+    import torch
+    _need(k_scales, "k_scales", torch.float32)
+    _need(v_scales, "v_scales", torch.float32)
+    if desc.dynamic:
+        num_pages = k_cache.numel() * k_cache.element_size() // (desc.num_kv_heads *
+                                                                 desc.page_bytes)
+        for t in (k_scales, v_scales):
+            if t is None or tuple(t.shape) != scale_pool_shape(desc, num_pages):
+                raise ValueError("scale pools must be float32 [P, Hkv, 16]")
+
+
+def kv_cache_write_dynamic(desc, k, v, slot_mapping, k_cache, v_cache, k_scales, v_scales,
+                           stream=None):
+    """kv_cache_write for a layer with dynamic per-token scales: each token's
+    scales are computed from its values and stored into the pools
+    (float32 [P, Hkv, 16]) at its slot."""
+    import torch
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    _need(slot_mapping, "slot_mapping", torch.int64)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache")
+    _check_pools(desc, k_cache, k_scales, v_scales)
+    T = k.shape[0]
+    if tuple(k.shape) != (T, desc.num_kv_heads, desc.head_dim) or v.shape != k.shape:
+        raise ValueError("k, v must be [T, Hkv, D]")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have T entries")
+    num_pages = k_cache.numel() * k_cache.element_size() // (desc.num_kv_heads * desc.page_bytes)
+    _check("kvq_kv_cache_write_dynamic", lib().kvq_kv_cache_write_dynamic(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
+        _ptr(v_cache), num_pages, _ptr(k_scales), _ptr(v_scales), _stream(stream)))
 
 
 def decode_workspace_bytes(desc, num_seqs, max_context_len):
@@ -243,6 +295,28 @@ def decode_step(desc, k_new, v_new, k_cache, v_cache, out, q, block_tables,
         ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), num_pages,
         _ptr(out), out_dtype, _ptr(q), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, int(max_context_len), _ptr(k_scale), _ptr(v_scale),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decode_step_dynamic(desc, k_new, v_new, k_cache, v_cache, out, q, block_tables,
+                        context_lens, max_context_len, k_scales, v_scales, workspace=None,
+                        stream=None):
+    """decode_step for a layer with dynamic per-token scales: the new token's
+    scales go into the pools (float32 [P, Hkv, 16]), then every position is
+    attended with its own scales."""
+    import torch
+    _need(k_new, "k_new", torch.bfloat16)
+    _need(v_new, "v_new", torch.bfloat16)
+    B = q.shape[0]
+    if tuple(k_new.shape) != (B, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new, v_new must be [B, Hkv, D]")
+    _check_pools(desc, k_cache, k_scales, v_scales)
+    out_dtype, num_pages, ws_bytes = _decode_checks(desc, out, q, k_cache, v_cache, block_tables,
+                                                    context_lens, k_scales, v_scales, workspace)
+    _check("kvq_decode_step_dynamic", lib().kvq_decode_step_dynamic(
+        ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), num_pages,
+        _ptr(out), out_dtype, _ptr(q), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, int(max_context_len), _ptr(k_scales), _ptr(v_scales),
         _ptr(workspace), ws_bytes, _stream(stream)))
 
 

@@ -19,6 +19,7 @@ namespace {
 constexpr int kMaxGroup = 8;        // bf16-MFMA attention (P carried as hi + lo)
 constexpr int kMaxGroupFp8 = 16;    // all-FP8 attention
 constexpr int kMaxPagesPerWave = 64;
+constexpr int kMaxDynHeads = 256;   // dynamic scales: LDS per-head maxima of the write
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -28,7 +29,8 @@ int check_desc(const kvq_layer_desc* d) {
   if (d->cache_dtype != KVQ_BF16 && d->cache_dtype != KVQ_FP8_E4M3 &&
       d->cache_dtype != KVQ_FP8_E5M2)
     return KVQ_ERR_INVALID_ARG;
-  if (d->scale_mode != KVQ_SCALE_PER_TENSOR && d->scale_mode != KVQ_SCALE_PER_KV_HEAD)
+  if (d->scale_mode != KVQ_SCALE_PER_TENSOR && d->scale_mode != KVQ_SCALE_PER_KV_HEAD &&
+      d->scale_mode != KVQ_SCALE_PER_TOKEN && d->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD)
     return KVQ_ERR_INVALID_ARG;
   if (d->sliding_window < 0) return KVQ_ERR_INVALID_ARG;
   if (!(d->sm_scale >= 0.0f) || !isfinite(d->sm_scale)) return KVQ_ERR_INVALID_ARG;
@@ -41,7 +43,17 @@ int check_desc(const kvq_layer_desc* d) {
       (d->attn_dtype == KVQ_ATTN_FP8 ? kMaxGroupFp8 : kMaxGroup))
     return KVQ_ERR_UNSUPPORTED;
   if (d->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (d->cache_dtype != KVQ_BF16 && d->scale_mode >= KVQ_SCALE_PER_TOKEN) {
+    if (d->attn_dtype == KVQ_ATTN_FP8) return KVQ_ERR_UNSUPPORTED;
+    if (d->num_kv_heads > kMaxDynHeads) return KVQ_ERR_UNSUPPORTED;
+  }
   return KVQ_OK;
+}
+
+// An fp8 layer whose scales are per token (computed at write time, stored in
+// pools beside the pages).
+bool dynamic_scales(const kvq_layer_desc* d) {
+  return d->cache_dtype != KVQ_BF16 && d->scale_mode >= KVQ_SCALE_PER_TOKEN;
 }
 
 // Compute units of the current device, queried once per device.
@@ -119,7 +131,9 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
     ppw = std::min<int64_t>(even_run((pages_max + kSplitWaves - 1) / kSplitWaves),
                             kMaxPagesPerWave);
   const int64_t page_block = 16LL * d->head_dim * (d->cache_dtype == KVQ_BF16 ? 2 : 1);
-  const bool ring_fits = kSplitWaves * 2 * 2 * page_block <= 64 * 1024;
+  // a staged tile: K and V of two pages, with dynamic scales their 2 x 16 fp32 each
+  const int64_t tile_bytes = 2 * 2 * page_block + (dynamic_scales(d) ? 2 * 2 * 16 * 4 : 0);
+  const bool ring_fits = kSplitWaves * tile_bytes <= 64 * 1024;
   int slots = (k_best == 1 && ring_fits) ? 1 : 0;
   int64_t direct_ppw = (pages_max + kSplitWaves - 1) / kSplitWaves;
   direct_ppw = (direct_ppw + 1) / 2 * 2;
@@ -186,6 +200,7 @@ int kvq_kv_cache_write(const kvq_layer_desc* desc, const void* k, const void* v,
       !aligned(slot_mapping, 8))
     return KVQ_ERR_INVALID_ARG;
   const bool fp8 = desc->cache_dtype != KVQ_BF16;
+  if (dynamic_scales(desc)) return KVQ_ERR_INVALID_ARG;   // kvq_kv_cache_write_dynamic
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return KVQ_ERR_INVALID_ARG;
   const int64_t threads = num_tokens * desc->num_kv_heads * (desc->head_dim / 16);
@@ -195,6 +210,34 @@ int kvq_kv_cache_write(const kvq_layer_desc* desc, const void* k, const void* v,
       num_tokens, desc->num_kv_heads, desc->head_dim, static_cast<uint8_t*>(k_cache),
       static_cast<uint8_t*>(v_cache), num_pages, k_scale, v_scale,
       desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_kv_cache_write_dynamic(const kvq_layer_desc* desc, const void* k, const void* v,
+                               const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                               void* v_cache, int64_t num_pages, float* k_scales,
+                               float* v_scales, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->cache_dtype != KVQ_BF16 && !dynamic_scales(desc)) return KVQ_ERR_INVALID_ARG;
+  if (desc->cache_dtype == KVQ_BF16)     // bf16 layers copy; no scales
+    return kvq_kv_cache_write(desc, k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                              num_pages, nullptr, nullptr, stream);
+  if (num_tokens < 0 || num_pages < 0) return KVQ_ERR_INVALID_ARG;
+  if (num_tokens == 0) return KVQ_OK;
+  if (num_pages == 0) return KVQ_ERR_INVALID_ARG;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scales || !v_scales)
+    return KVQ_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8) || !aligned(k_scales, 16) || !aligned(v_scales, 16))
+    return KVQ_ERR_INVALID_ARG;
+  if (num_tokens > 0x7FFFFFFFLL) return KVQ_ERR_UNSUPPORTED;
+  hipError_t e = launch_kv_cache_write_dyn(
+      (int)desc->cache_dtype, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      slot_mapping, num_tokens, desc->num_kv_heads, desc->head_dim,
+      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), num_pages, k_scales,
+      v_scales, desc->scale_mode == KVQ_SCALE_PER_TOKEN ? 1 : 0,
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
@@ -238,7 +281,9 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
   if (fused && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
     return KVQ_ERR_INVALID_ARG;
   const bool fp8 = desc->cache_dtype != KVQ_BF16;
-  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+  const bool dyn = dynamic_scales(desc);
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, dyn ? 16 : 4) ||
+              !aligned(v_scale, dyn ? 16 : 4)))
     return KVQ_ERR_INVALID_ARG;
   const Plan plan = make_plan(desc, num_seqs, max_context_len);
   if (plan.bytes > 0) {
@@ -269,6 +314,7 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
   p.pages_per_wave = plan.pages_per_wave;
   p.num_parts = plan.num_parts;
   p.scale_per_head = desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0;
+  p.dyn_all_heads = desc->scale_mode == KVQ_SCALE_PER_TOKEN ? 1 : 0;
   p.out_bf16 = out_dtype == KVQ_OUT_BF16 ? 1 : 0;
   p.direct = plan.num_parts == 1 ? 1 : 0;
   const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
@@ -282,7 +328,7 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
     g_prof.used++;
   }
   hipError_t e = launch_paged_decode(p, desc->head_dim, (int)desc->cache_dtype, num_seqs, fused,
-                                     plan.slots, desc->attn_dtype == KVQ_ATTN_FP8,
+                                     plan.slots, desc->attn_dtype == KVQ_ATTN_FP8, dyn,
                                      static_cast<hipStream_t>(stream), e0, e1);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -307,9 +353,23 @@ int kvq_decode_step(const kvq_layer_desc* desc, const void* k_new, const void* v
                     int32_t max_pages_per_seq, const int32_t* context_lens, int32_t num_seqs,
                     int32_t max_context_len, const float* k_scale, const float* v_scale,
                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (desc && dynamic_scales(desc)) return KVQ_ERR_INVALID_ARG;   // kvq_decode_step_dynamic
   return decode_common(desc, out, out_dtype, q, k_cache, v_cache, num_pages, block_tables,
                        max_pages_per_seq, context_lens, num_seqs, max_context_len, k_scale,
                        v_scale, workspace, workspace_bytes, k_new, v_new, true, stream);
+}
+
+int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, int64_t num_pages, void* out,
+                            int32_t out_dtype, const void* q, const int32_t* block_tables,
+                            int32_t max_pages_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, float* k_scales,
+                            float* v_scales, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (desc && desc->cache_dtype != KVQ_BF16 && !dynamic_scales(desc)) return KVQ_ERR_INVALID_ARG;
+  return decode_common(desc, out, out_dtype, q, k_cache, v_cache, num_pages, block_tables,
+                       max_pages_per_seq, context_lens, num_seqs, max_context_len, k_scales,
+                       v_scales, workspace, workspace_bytes, k_new, v_new, true, stream);
 }
 
 int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x, int64_t num_tokens,
@@ -318,6 +378,7 @@ int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x, int64_t nu
   if (st) return st;
   if (num_tokens < 0 || !x || !scale_out || !aligned(x, 16) || !aligned(scale_out, 4))
     return KVQ_ERR_INVALID_ARG;
+  if (desc->scale_mode >= KVQ_SCALE_PER_TOKEN) return KVQ_ERR_INVALID_ARG;   // set by the write
   const float fmax = desc->cache_dtype == KVQ_FP8_E5M2 ? 57344.0f : 448.0f;
   hipError_t e = launch_scale_from_amax(
       static_cast<const uint16_t*>(x), num_tokens, desc->num_kv_heads, desc->head_dim,

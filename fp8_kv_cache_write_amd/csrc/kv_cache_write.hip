@@ -9,10 +9,39 @@
 // saturating mode of "cooking-agi: FP8 and the KV cache" (section "dynamic vs
 // static scale"); e5m2 is the same page's second fp8 cache dtype (section "how
 // to enable it in the engine").
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace kvfp8 {
+
+// Quantise 16 dims (d0 .. d0+15) of row r of K and of V and store them into
+// the (page, head) blocks kb, vb: K as one 16-byte store (one layout chunk),
+// V as 16 byte stores (the V layout interleaves 4 rows per dim).
+template <int FMT>
+__device__ __forceinline__ void store_chunk_fp8(uint8_t* kb, uint8_t* vb, int r, int d0,
+                                                const uint32_t* kw, const uint32_t* vw,
+                                                float sk, float sv) {
+  uint32_t kq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int e = j * 4 + b;
+      const uint32_t bits = (kw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+      w |= fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sk) << (8 * b);
+    }
+    kq[j] = w;
+  }
+  *reinterpret_cast<uint4*>(kb + k_byte<1>(r, d0)) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t bits = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+    vb[v_byte<1>(r, d0 + e)] = (uint8_t)fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sv);
+  }
+}
 
 // One thread per (token, kv head, 16-dim chunk). It reads 16 bf16 of K and of
 // V (two 16-byte loads each) and writes
@@ -56,29 +85,8 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   const int d0 = c * 16;
 
   if constexpr (FP8) {
-    const float sk = k_scale[scale_per_head ? h : 0];
-    const float sv = v_scale[scale_per_head ? h : 0];
-    uint32_t kq[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int e = j * 4 + b;
-        const uint32_t bits = (kw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-        w |= fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sk) << (8 * b);
-      }
-      kq[j] = w;
-    }
-    // 16 consecutive dims of one row form exactly one K chunk.
-    *reinterpret_cast<uint4*>(kb + k_byte<1>(r, d0)) =
-        make_uint4(kq[0], kq[1], kq[2], kq[3]);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t bits = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-      vb[v_byte<1>(r, d0 + e)] =
-          (uint8_t)fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sv);
-    }
+    store_chunk_fp8<FMT>(kb, vb, r, d0, kw, vw, k_scale[scale_per_head ? h : 0],
+                         v_scale[scale_per_head ? h : 0]);
   } else {
     // bf16 layers keep the bits: the skip-layer path.
     *reinterpret_cast<uint4*>(kb + k_byte<2>(r, d0)) = kx[0];
@@ -87,6 +95,73 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     for (int e = 0; e < 16; ++e) {
       const uint32_t bits = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
       *reinterpret_cast<uint16_t*>(vb + v_byte<2>(r, d0 + e)) = (uint16_t)bits;
+    }
+  }
+}
+
+// Largest |x| of 16 bf16 values (two 16-byte words each of K and V) as bf16
+// magnitude bits: the integer order of those bits is the order of the
+// magnitudes with NaN above Inf above every finite value.
+__device__ __forceinline__ uint32_t max_mag_bits(const uint32_t* w) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  return m;
+}
+
+// Cache write with dynamic per-token scales ("FP8量化与长上下文推理" section
+// 2.2: every new token gets its own scale): one work-group per token. Pass 1
+// takes the token's largest |x| of K and of V - over each KV head, or over
+// all of them (ALL_HEADS) - as an LDS integer max of magnitude bits; pass 2
+// sets s = amax / fmax (1 when amax is 0, NaN when a NaN is present: the
+// static calibration's rule), stores it beside the page for the slot
+// (pool[page][head][row]) and writes the codes as the static write does.
+constexpr int kMaxDynHeads = 256;
+template <int FMT, bool ALL_HEADS>
+__global__ __launch_bounds__(256) void kv_cache_write_dyn_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ slots, int num_kv_heads, int head_dim,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, int64_t num_pages,
+    float* __restrict__ k_pool, float* __restrict__ v_pool) {
+  constexpr float fmax = FMT == kFmtE5M2 ? 57344.0f : 448.0f;
+  const int64_t t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_pages * kPage) return;   // the whole work-group skips
+  const int64_t page = slot / kPage;
+  const int r = (int)(slot % kPage);
+  const int chunks = head_dim / 16;
+  const int items = num_kv_heads * chunks;
+  __shared__ uint32_t km[kMaxDynHeads], vm[kMaxDynHeads];
+  for (int i = threadIdx.x; i < num_kv_heads; i += blockDim.x) km[i] = vm[i] = 0u;
+  __syncthreads();
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int h = it / chunks;
+    const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)(it % chunks) * 16;
+    const uint4* ks = reinterpret_cast<const uint4*>(k + src);
+    const uint4* vs = reinterpret_cast<const uint4*>(v + src);
+    const uint4 kx[2] = {ks[0], ks[1]}, vx[2] = {vs[0], vs[1]};
+    atomicMax(&km[ALL_HEADS ? 0 : h], max_mag_bits(reinterpret_cast<const uint32_t*>(kx)));
+    atomicMax(&vm[ALL_HEADS ? 0 : h], max_mag_bits(reinterpret_cast<const uint32_t*>(vx)));
+  }
+  __syncthreads();
+  const int64_t pb = (int64_t)kPage * head_dim;
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    const int h = it / chunks, c = it % chunks;
+    const float ak = bf16_bits_to_f32(km[ALL_HEADS ? 0 : h]);
+    const float av = bf16_bits_to_f32(vm[ALL_HEADS ? 0 : h]);
+    const float sk = ak == 0.0f ? 1.0f : ak / fmax;
+    const float sv = av == 0.0f ? 1.0f : av / fmax;
+    const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)c * 16;
+    const uint4* ks = reinterpret_cast<const uint4*>(k + src);
+    const uint4* vs = reinterpret_cast<const uint4*>(v + src);
+    const uint4 kx[2] = {ks[0], ks[1]}, vx[2] = {vs[0], vs[1]};
+    store_chunk_fp8<FMT>(k_cache + (page * num_kv_heads + h) * pb,
+                         v_cache + (page * num_kv_heads + h) * pb, r, c * 16,
+                         reinterpret_cast<const uint32_t*>(kx),
+                         reinterpret_cast<const uint32_t*>(vx), sk, sv);
+    if (c == 0) {
+      k_pool[(page * num_kv_heads + h) * kPage + r] = sk;
+      v_pool[(page * num_kv_heads + h) * kPage + r] = sv;
     }
   }
 }
@@ -217,6 +292,30 @@ hipError_t launch_quantize(int fmt, const float* x, int64_t n, const float* scal
   else
     hipLaunchKernelGGL(quantize_kernel<kFmtE4M3>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        x, n, scale, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_cache_write_dyn(int fmt, const uint16_t* k, const uint16_t* v,
+                                     const int64_t* slots, int64_t num_tokens, int num_kv_heads,
+                                     int head_dim, uint8_t* k_cache, uint8_t* v_cache,
+                                     int64_t num_pages, float* k_pool, float* v_pool,
+                                     int all_heads, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  if (num_kv_heads > kMaxDynHeads || num_tokens > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const int items = num_kv_heads * (head_dim / 16);
+  const int threads = std::min(256, (items + kWave - 1) / kWave * kWave);
+  const dim3 grid((unsigned)num_tokens), block((unsigned)threads);
+#define KVFP8_DYN(F, A)                                                                      \
+  hipLaunchKernelGGL((kv_cache_write_dyn_kernel<F, A>), grid, block, 0, stream, k, v, slots, \
+                     num_kv_heads, head_dim, k_cache, v_cache, num_pages, k_pool, v_pool)
+  if (fmt == kFmtE4M3) {
+    if (all_heads) KVFP8_DYN(kFmtE4M3, true); else KVFP8_DYN(kFmtE4M3, false);
+  } else if (fmt == kFmtE5M2) {
+    if (all_heads) KVFP8_DYN(kFmtE5M2, true); else KVFP8_DYN(kFmtE5M2, false);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef KVFP8_DYN
   return hipGetLastError();
 }
 

@@ -31,8 +31,8 @@ struct DecodeParams {
   const int32_t* block_tables;   // [B][max_pages_per_seq]
   const int32_t* context_lens;   // [B]
   int64_t num_pages;             // pool size: page ids outside [0, num_pages) read as empty
-  const float* k_scale;          // [1] or [Hkv]; unused for bf16
-  const float* v_scale;
+  const float* k_scale;          // [1] or [Hkv]; dynamic scales: pools [P][Hkv][16]
+  const float* v_scale;          //   (written by the fused step); unused for bf16
   float* ws_m;                   // [B][Hq][num_parts]   (log2 domain)
   float* ws_l;                   // [B][Hq][num_parts]
   float* ws_o;                   // [B][Hq][num_parts][D]
@@ -47,6 +47,7 @@ struct DecodeParams {
   int pages_per_wave;            // <= 64
   int num_parts;                 // partitions allocated per (b, q head)
   int scale_per_head;
+  int dyn_all_heads;             // dynamic, one scale per token over all heads (fused step)
   int out_bf16;
   int direct;                    // num_parts == 1: the split kernel finishes
   float sm_scale_log2;           // sm_scale * log2(e)
@@ -60,8 +61,18 @@ constexpr int kSplitWaves = 4;
 // slots: split-kernel tile shape, 1 = LDS-staged tiles, 0 = register tiles.
 // fmt: cache element format, kFmtBf16 / kFmtE4M3 / kFmtE5M2 (device_common.hpp).
 // att8: all-FP8 attention (e4m3 Q and P, fp8 MFMA); fp8 caches only.
+// dyn: dynamic per-token scales (p.k_scale / p.v_scale are the pools); fp8
+// caches, bf16 arithmetic.
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
-                               bool fused, int slots, bool att8, hipStream_t stream,
+                               bool fused, int slots, bool att8, bool dyn, hipStream_t stream,
                                hipEvent_t ev_before, hipEvent_t ev_after);
+
+// Cache write with dynamic per-token scales: per token (all_heads = 1) or per
+// token and KV head, stored for each slot into the pools [P][Hkv][16].
+hipError_t launch_kv_cache_write_dyn(int fmt, const uint16_t* k, const uint16_t* v,
+                                     const int64_t* slots, int64_t num_tokens, int num_kv_heads,
+                                     int head_dim, uint8_t* k_cache, uint8_t* v_cache,
+                                     int64_t num_pages, float* k_pool, float* v_pool,
+                                     int all_heads, hipStream_t stream);
 
 }  // namespace kvfp8

@@ -116,6 +116,30 @@ __device__ __forceinline__ void lds_read4(uint32_t lds_addr, uint4& a, uint4& b,
   d = __builtin_bit_cast(uint4, rd);
 }
 
+// Four 16-byte LDS reads at lds_addr + {0, 64, 128, 192} once the loads that
+// filled them are known to be complete (no vector-memory wait).
+__device__ __forceinline__ void lds_read4_s64(uint32_t lds_addr, f32x4& a, f32x4& b, f32x4& c,
+                                              f32x4& d) {
+  u32x4_t ra, rb, rc, rd;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:64\n\t"
+      "ds_read_b128 %2, %4 offset:128\n\t"
+      "ds_read_b128 %3, %4 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(ra), "=v"(rb), "=v"(rc), "=v"(rd)
+      : "v"(lds_addr)
+      : "memory");
+  a = __builtin_bit_cast(f32x4, ra);
+  b = __builtin_bit_cast(f32x4, rb);
+  c = __builtin_bit_cast(f32x4, rc);
+  d = __builtin_bit_cast(f32x4, rd);
+}
+
+// Bytes of a staged tile's scales in dynamic-scale mode: per page 16 rows of
+// K scales and 16 of V scales (fp32).
+constexpr int kTileScaleBytesPerPage = 2 * kPage * 4;
+
 struct PartitionRange {
   int L, lo, first_page, end_page, num_parts_b;
 };
@@ -142,7 +166,7 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   return r;
 }
 
-template <int D, int FMT, int NW, int TP, int RING, int SLOTS, bool FUSED, bool ATT8>
+template <int D, int FMT, int NW, int TP, int RING, int SLOTS, bool FUSED, bool ATT8, bool DYN>
 __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const DecodeParams p) {
   constexpr bool FP8 = FMT != kFmtBf16;
@@ -153,6 +177,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   constexpr int NBLK = D / 16;          // P*V output blocks of 16 dims
   constexpr int GMAX = ATT8 ? 16 : 8;   // query columns: G (+ G low halves of P)
   static_assert(!ATT8 || FP8, "the all-FP8 mode reads fp8 caches");
+  static_assert(!DYN || (FP8 && !ATT8), "dynamic scales: fp8 caches, bf16 arithmetic");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -249,8 +274,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       }
     }
   };
-  const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
-  const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
+  // static scales: one per head or tensor; dynamic ones are per position
+  // (the pools p.k_scale / p.v_scale [page][head][row]), applied per row
+  const float ks = FP8 && !DYN ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
+  const float vs = FP8 && !DYN ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
   const int32_t* bt_row = p.block_tables + (int64_t)b * p.max_pages_per_seq;
   int my_page = -1;
   if (p.window == 0) {
@@ -310,8 +337,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   // Per-wave LDS region: the tile ring while streaming, then the wave's
   // unnormalised output rows for the merge (written after the wave's last
   // staged tile has been read, so no load is still landing there).
-  constexpr int TILE_BYTES = TP * 2 * PB;             // K and V of TP pages
+  constexpr int KV_BYTES = TP * 2 * PB;               // K and V of TP pages
+  constexpr int TILE_BYTES = KV_BYTES + (DYN ? TP * kTileScaleBytesPerPage : 0);
   constexpr int LPT = TP * 2 * NI;                    // 1 KiB loads per tile
+  constexpr int VPT = LPT + (DYN ? 1 : 0);            // vector-memory ops per staged tile
   constexpr int O_BYTES = GMAX * D * 4;
   constexpr int REGION = (SLOTS * TILE_BYTES > O_BYTES) ? SLOTS * TILE_BYTES : O_BYTES;
   static_assert(LPT % 4 == 0, "staged tiles are read in groups of four 1 KiB chunks");
@@ -376,6 +405,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       }
     }
   };
+  float sk_new = 1.0f, sv_new = 1.0f;   // dynamic scales of the new row
   auto fused_commit = [&]() {
     if constexpr (FUSED) {
       const int pid = __builtin_amdgcn_readlane(my_page, idx_new);
@@ -389,7 +419,60 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         vb[e] = (uint16_t)(vx_new[e / 2] >> (16 * (e % 2)));
       }
       if constexpr (FP8) {
-        const float sk = ks, sv = vs;
+        float sk = ks, sv = vs;
+        if constexpr (DYN) {
+          // the token's own scales, as the dynamic cache write takes them:
+          // integer max of the bf16 magnitude bits (NaN > Inf > finite) over
+          // this head's row, or over every head's row of the token
+          uint32_t km = 0u, vm = 0u;
+#pragma unroll
+          for (int e = 0; e < VPL; ++e) {
+            km = max(km, (uint32_t)kb[e] & 0x7FFFu);
+            vm = max(vm, (uint32_t)vb[e] & 0x7FFFu);
+          }
+          if (p.dyn_all_heads) {
+            // the token's whole K and V rows (all heads) in 16-byte chunks,
+            // two per lane in flight at a time
+            const int nch = p.num_kv_heads * (D / 8);
+            const uint4* kr = reinterpret_cast<const uint4*>(p.k_new + (int64_t)b * p.num_kv_heads * D);
+            const uint4* vr = reinterpret_cast<const uint4*>(p.v_new + (int64_t)b * p.num_kv_heads * D);
+            for (int base = 0; base < nch; base += 2 * kWave) {
+              uint4 kc[2], vc[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int j = base + u * kWave + lane;
+                kc[u] = j < nch ? kr[j] : make_uint4(0u, 0u, 0u, 0u);
+                vc[u] = j < nch ? vr[j] : make_uint4(0u, 0u, 0u, 0u);
+              }
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const uint32_t kw4[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+                const uint32_t vw4[4] = {vc[u].x, vc[u].y, vc[u].z, vc[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  km = max(km, max(kw4[i] & 0x7FFFu, (kw4[i] >> 16) & 0x7FFFu));
+                  vm = max(vm, max(vw4[i] & 0x7FFFu, (vw4[i] >> 16) & 0x7FFFu));
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int off = kWave / 2; off > 0; off /= 2) {
+            km = max(km, (uint32_t)__shfl_xor((int)km, off));
+            vm = max(vm, (uint32_t)__shfl_xor((int)vm, off));
+          }
+          constexpr float fmax = FMT == kFmtE5M2 ? 57344.0f : 448.0f;
+          const float ak = bf16_bits_to_f32(km), av = bf16_bits_to_f32(vm);
+          sk = ak == 0.0f ? 1.0f : ak / fmax;
+          sv = av == 0.0f ? 1.0f : av / fmax;
+          sk_new = sk;
+          sv_new = sv;
+          if (lane == 0) {
+            const int64_t so = ((int64_t)pid * p.num_kv_heads + h) * kPage + r_new;
+            const_cast<float*>(p.k_scale)[so] = sk;
+            const_cast<float*>(p.v_scale)[so] = sv;
+          }
+        }
         uint8_t kq[VPL], vq[VPL];
 #pragma unroll
         for (int e = 0; e < VPL; ++e) {
@@ -446,7 +529,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   struct Tile {
     uint4 k[TP][NI];
     uint4 v[TP][NI];
+    f32x4 sk[DYN ? TP : 1];     // dynamic scales of rows 4qd..4qd+3 of each page
+    f32x4 sv[DYN ? TP : 1];
   };
+  const int64_t scale_row0 = (int64_t)h * kPage + 4 * qd;   // in a pool page: [head][row]
 
   auto load_tile = [&](int t, Tile& tl) {
 #pragma unroll
@@ -459,6 +545,11 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       for (int i = 0; i < NI; ++i) {
         tl.k[pg][i] = load_stream(kp + i * kWave + lane);
         tl.v[pg][i] = load_stream(vp + i * kWave + lane);
+      }
+      if constexpr (DYN) {
+        const int64_t so = (int64_t)pid * p.num_kv_heads * kPage + scale_row0;
+        tl.sk[pg] = *reinterpret_cast<const f32x4*>(p.k_scale + so);
+        tl.sv[pg] = *reinterpret_cast<const f32x4*>(p.v_scale + so);
       }
     }
   };
@@ -502,6 +593,17 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
           tl.v[pg][i] = w;
         }
       }
+      if constexpr (DYN) {
+        if (qd == r_new / 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (e == r_new % 4) {
+              tl.sk[pg][e] = sk_new;
+              tl.sv[pg][e] = sv_new;
+            }
+          }
+        }
+      }
     }
   };
 
@@ -535,6 +637,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[pg][e] = sacc[e] * c_log2;
+      if constexpr (DYN) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[pg][e] *= tl.sk[pg][e];
+      }
     }
     // ---- masking: positions outside [lo, L), past the run, invalid pages --
     // (wave-uniform decision; only boundary tiles take it)
@@ -661,10 +767,14 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       for (int e = 0; e < 4; ++e) {
         const float pe = __builtin_amdgcn_exp2f(x[pg][e] - m_use);
         pv[e] = pe;
-        // P = hi + lo: hi is pe truncated to bf16 (query columns), lo the
+        // dynamic scales: the row's V scale joins P (masked rows stay 0
+        // whatever their pool entry holds)
+        float pw = pe;
+        if constexpr (DYN) pw = pe == 0.0f ? 0.0f : pe * tl.sv[pg][e];
+        // P = hi + lo: hi is pw truncated to bf16 (query columns), lo the
         // exact residue, rounded to bf16 (duplicate columns)
-        const float hi = __uint_as_float(__float_as_uint(pe) & 0xFFFF0000u);
-        u[e] = lo_col ? pe - hi : hi;
+        const float hi = __uint_as_float(__float_as_uint(pw) & 0xFFFF0000u);
+        u[e] = lo_col ? pw - hi : hi;
       }
       psum_pg[pg] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
 #pragma unroll
@@ -714,6 +824,21 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     // chunk q of a slot: page q / (2 NI), K (then V) chunk q % NI
     auto stage_tile = [&](int t, int slot) {
       uint8_t* dst = my_region + slot * TILE_BYTES;
+      if constexpr (DYN) {
+        // lane l < 8 TP: page l / 8, K (l % 8 < 4) or V scales, rows 4(l % 4)..+3;
+        // issued first, so the tile's K/V wait covers it
+        if (lane < 8 * TP) {
+          static_assert(TP == 2, "the scale loads cover two pages");
+          const int pid0 = __builtin_amdgcn_readlane(page_or0, (TP * t) & (kWave - 1));
+          const int pid1 = __builtin_amdgcn_readlane(page_or0, (TP * t + 1) & (kWave - 1));
+          const int pid = lane < 8 ? pid0 : pid1;
+          const float* pool = (lane % 8) < 4 ? p.k_scale : p.v_scale;
+          const float* src = pool + (int64_t)pid * p.num_kv_heads * kPage + (int64_t)h * kPage +
+                             4 * (lane % 4);
+          __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(dst + KV_BYTES), 16, 0,
+                                           0);
+        }
+      }
 #pragma unroll
       for (int pg = 0; pg < TP; ++pg) {
         const int idx = TP * t + pg;
@@ -737,9 +862,9 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       for (int j = 0; j < LPT / 4; ++j) {
         const uint32_t a = base + 4096u * j;
         if (later >= 2 && SLOTS >= 3)
-          lds_read4<2 * LPT>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
+          lds_read4<2 * VPT>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
         else if (later >= 1 && SLOTS >= 2)
-          lds_read4<LPT>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
+          lds_read4<VPT>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
         else
           lds_read4<0>(a, ch[4 * j], ch[4 * j + 1], ch[4 * j + 2], ch[4 * j + 3]);
       }
@@ -750,6 +875,12 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
           tl.k[pg][i] = ch[2 * NI * pg + i];
           tl.v[pg][i] = ch[2 * NI * pg + NI + i];
         }
+      if constexpr (DYN) {
+        static_assert(TP == 2, "the scale reads cover two pages");
+        const uint32_t sb = (uint32_t)(uintptr_t)(lds_void_t*)(my_region + slot * TILE_BYTES +
+                                                               KV_BYTES) + 16u * qd;
+        lds_read4_s64(sb, tl.sk[0], tl.sv[0], tl.sk[1], tl.sv[1]);
+      }
     };
     Tile t0;
     fused_prefetch();
@@ -958,23 +1089,30 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodePara
   else reinterpret_cast<float*>(p.out)[row * D + d] = r;
 }
 
-template <int D, int FMT, int TP, int RING, int SLOTS, bool FUSED, bool ATT8>
+// Arithmetic modes of the split kernel.
+constexpr int kModeBf16 = 0;   // codes expanded to bf16, static scales
+constexpr int kModeFp8 = 1;    // all-FP8 attention
+constexpr int kModeDyn = 2;    // codes expanded to bf16, dynamic per-token scales
+
+template <int D, int FMT, int TP, int RING, int SLOTS, bool FUSED, int MODE>
 static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_t stream,
                                  hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NW = kSplitWaves;
+  constexpr bool ATT8 = MODE == kModeFp8, DYN = MODE == kModeDyn;
   const dim3 grid((unsigned)p.num_parts, (unsigned)p.num_kv_heads, (unsigned)num_seqs);
   if (ev_before && ev_after) {
     // the events take the kernel's own start and end timestamps
-    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8>),
+    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8, DYN>),
                           grid, dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8>),
+    hipLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8, DYN>),
                        grid, dim3(NW * kWave), 0, stream, p);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.direct) return err;
   DecodeParams pr = p;
-  if (FMT == kFmtBf16) pr.v_scale = nullptr;
+  // the reduce kernel applies a static V scale only (dynamic ones are in P)
+  if (FMT == kFmtBf16 || DYN) pr.v_scale = nullptr;
   hipLaunchKernelGGL((paged_decode_reduce_kernel<D>),
                      dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(D), 0,
                      stream, pr);
@@ -987,35 +1125,48 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
 // 2x1s1 (the same with the next tile staged in LDS).
 // KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 4x1, 2x1s1, 2x1s2,
 // 4x1s1) overrides it for tuning sweeps; a shape whose LDS ring would pass
-// 64 KiB is rejected. The all-FP8 mode (att8) is built for the two planned
-// shapes only.
+// 64 KiB is rejected. The all-FP8 and dynamic-scale modes are built for the
+// two planned shapes only.
 template <int D, int FMT, int TP, int RING, int SLOTS>
-static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused, bool att8,
+static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused, int mode,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int E = FMT == kFmtBf16 ? 2 : 1;
-  if constexpr (kSplitWaves * SLOTS * TP * 2 * kPage * D * E > kMaxLdsRing) {
+  constexpr int kv_ring = kSplitWaves * SLOTS * TP * 2 * kPage * D * E;
+  constexpr bool planned = FMT != kFmtBf16 && TP == 2 && RING == 1 && SLOTS <= 1;
+  if constexpr (kv_ring > kMaxLdsRing) {
     return hipErrorInvalidValue;
   } else {
-    if (att8) {
-      if constexpr (FMT != kFmtBf16 && TP == 2 && RING == 1 && SLOTS <= 1) {
-        return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, true>(
+    if (mode == kModeFp8) {
+      if constexpr (planned) {
+        return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, kModeFp8>(
                            p, num_seqs, stream, ev_before, ev_after)
-                     : launch_variant<D, FMT, TP, RING, SLOTS, false, true>(
+                     : launch_variant<D, FMT, TP, RING, SLOTS, false, kModeFp8>(
                            p, num_seqs, stream, ev_before, ev_after);
       } else {
         return hipErrorInvalidValue;
       }
     }
-    return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, false>(p, num_seqs, stream,
-                                                                         ev_before, ev_after)
-                 : launch_variant<D, FMT, TP, RING, SLOTS, false, false>(p, num_seqs, stream,
-                                                                          ev_before, ev_after);
+    if (mode == kModeDyn) {
+      if constexpr (planned &&
+                    kv_ring + kSplitWaves * SLOTS * TP * kTileScaleBytesPerPage <= kMaxLdsRing) {
+        return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, kModeDyn>(
+                           p, num_seqs, stream, ev_before, ev_after)
+                     : launch_variant<D, FMT, TP, RING, SLOTS, false, kModeDyn>(
+                           p, num_seqs, stream, ev_before, ev_after);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
+    return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, kModeBf16>(
+                       p, num_seqs, stream, ev_before, ev_after)
+                 : launch_variant<D, FMT, TP, RING, SLOTS, false, kModeBf16>(
+                       p, num_seqs, stream, ev_before, ev_after);
   }
 }
 
 template <int D, int FMT>
 static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, int plan_slots,
-                               bool att8, hipStream_t stream, hipEvent_t ev_before,
+                               int mode, hipStream_t stream, hipEvent_t ev_before,
                                hipEvent_t ev_after) {
   int tp = 2, ring = 1, slots = plan_slots;
   if (const char* env = getenv("KVFP8_SPLIT_VARIANT")) {
@@ -1025,7 +1176,7 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, 
   }
 #define KVFP8_SHAPE(TP_, RING_, SLOTS_)                                                 \
   if (tp == TP_ && ring == RING_ && slots == SLOTS_)                                    \
-    return launch_shape<D, FMT, TP_, RING_, SLOTS_>(p, num_seqs, fused, att8, stream,   \
+    return launch_shape<D, FMT, TP_, RING_, SLOTS_>(p, num_seqs, fused, mode, stream,   \
                                                     ev_before, ev_after);
   KVFP8_SHAPE(2, 1, 0)
   KVFP8_SHAPE(2, 2, 0)
@@ -1039,17 +1190,17 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, 
 
 template <int D>
 static hipError_t launch_dim(const DecodeParams& p, int fmt, int num_seqs, bool fused, int slots,
-                             bool att8, hipStream_t stream, hipEvent_t ev_before,
+                             int mode, hipStream_t stream, hipEvent_t ev_before,
                              hipEvent_t ev_after) {
   switch (fmt) {
     case kFmtBf16:
-      return launch_typed<D, kFmtBf16>(p, num_seqs, fused, slots, att8, stream, ev_before,
+      return launch_typed<D, kFmtBf16>(p, num_seqs, fused, slots, mode, stream, ev_before,
                                        ev_after);
     case kFmtE4M3:
-      return launch_typed<D, kFmtE4M3>(p, num_seqs, fused, slots, att8, stream, ev_before,
+      return launch_typed<D, kFmtE4M3>(p, num_seqs, fused, slots, mode, stream, ev_before,
                                        ev_after);
     case kFmtE5M2:
-      return launch_typed<D, kFmtE5M2>(p, num_seqs, fused, slots, att8, stream, ev_before,
+      return launch_typed<D, kFmtE5M2>(p, num_seqs, fused, slots, mode, stream, ev_before,
                                        ev_after);
     default:
       return hipErrorInvalidValue;
@@ -1057,15 +1208,17 @@ static hipError_t launch_dim(const DecodeParams& p, int fmt, int num_seqs, bool 
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
-                               bool fused, int slots, bool att8, hipStream_t stream,
+                               bool fused, int slots, bool att8, bool dyn, hipStream_t stream,
                                hipEvent_t ev_before, hipEvent_t ev_after) {
+  if (att8 && dyn) return hipErrorInvalidValue;
+  const int mode = att8 ? kModeFp8 : dyn ? kModeDyn : kModeBf16;
   switch (head_dim) {
     case 64:
-      return launch_dim<64>(p, fmt, num_seqs, fused, slots, att8, stream, ev_before, ev_after);
+      return launch_dim<64>(p, fmt, num_seqs, fused, slots, mode, stream, ev_before, ev_after);
     case 128:
-      return launch_dim<128>(p, fmt, num_seqs, fused, slots, att8, stream, ev_before, ev_after);
+      return launch_dim<128>(p, fmt, num_seqs, fused, slots, mode, stream, ev_before, ev_after);
     case 256:
-      return launch_dim<256>(p, fmt, num_seqs, fused, slots, att8, stream, ev_before, ev_after);
+      return launch_dim<256>(p, fmt, num_seqs, fused, slots, mode, stream, ev_before, ev_after);
     default:
       return hipErrorInvalidValue;
   }

@@ -91,7 +91,8 @@ enum kvq_status {
                                      inconsistent shapes */
   KVQ_ERR_UNSUPPORTED = -2,       /* head_dim not in {64,128,256}, page size
                                      not 16, Hq % Hkv != 0, group > 8 (> 16
-                                     with KVQ_ATTN_FP8) */
+                                     with KVQ_ATTN_FP8), dynamic scales with
+                                     KVQ_ATTN_FP8 or Hkv > 256 */
   KVQ_ERR_WORKSPACE_TOO_SMALL = -3,
   KVQ_ERR_HIP = -4                /* a HIP runtime call or launch failed */
 };
@@ -99,10 +100,31 @@ enum kvq_status {
 /* Cache element type of a layer. `auto` in the engine flags maps to bf16. */
 enum kvq_dtype { KVQ_BF16 = 0, KVQ_FP8_E4M3 = 1, KVQ_FP8_E5M2 = 2 };
 
-/* Scale granularity: one FP32 scale for the whole layer tensor, or one per KV
- * head ("cooking-agi", section "how to enable it in the engine": per tensor
- * or per attention head). K and V always have separate scale arrays. */
-enum kvq_scale_mode { KVQ_SCALE_PER_TENSOR = 0, KVQ_SCALE_PER_KV_HEAD = 1 };
+/* Scale granularity. K and V always have separate scales.
+ *   KVQ_SCALE_PER_TENSOR, KVQ_SCALE_PER_KV_HEAD: static scales, one FP32 value
+ *     for the layer tensor or one per KV head ("cooking-agi", section "how to
+ *     enable it in the engine": per tensor or per attention head), set once
+ *     (kvq_kv_scale_from_amax) and passed as fp32 [1] or [Hkv].
+ *   KVQ_SCALE_PER_TOKEN, KVQ_SCALE_PER_TOKEN_HEAD: dynamic scales, one per
+ *     written token ("FP8量化与长上下文推理" section 2.2: every new token gets
+ *     its own scale; "cooking-agi", section "dynamic vs static scale": each
+ *     token's largest value lands on the format maximum). The write computes
+ *     s = amax / 448 (57344 for e5m2; 1 when amax is 0, NaN when a value is
+ *     NaN) over all of the token's K (or V) values, PER_TOKEN, or over those of
+ *     one KV head, PER_TOKEN_HEAD, and stores it beside the page: the scales
+ *     of a layer are two fp32 pools [num_pages][Hkv][16] (K and V), entry
+ *     [page][h][row] the scale of slot page * 16 + row for KV head h (with
+ *     PER_TOKEN every head holds the same value). Attention reads each
+ *     attended position's own scales. Written by kvq_kv_cache_write_dynamic
+ *     and kvq_decode_step_dynamic; read by kvq_paged_decode_attention (its
+ *     k_scale / v_scale arguments are then the pools, 16-byte aligned). Only
+ *     with KVQ_ATTN_BF16 arithmetic, and Hkv <= 256. Ignored for bf16 layers. */
+enum kvq_scale_mode {
+  KVQ_SCALE_PER_TENSOR = 0,
+  KVQ_SCALE_PER_KV_HEAD = 1,
+  KVQ_SCALE_PER_TOKEN = 2,
+  KVQ_SCALE_PER_TOKEN_HEAD = 3
+};
 
 /* Output element type of the attention. */
 enum kvq_out_dtype { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 };
@@ -153,12 +175,31 @@ typedef struct kvq_layer_desc {
  *                 are copied unchanged.
  * Only the bytes of the written (slot, head) rows change.
  * For fp8 layers each element becomes E4M3_sat_RNE(fp32(x) / s_h), or
- * E5M2_sat_RNE(fp32(x) / s_h) for an e5m2 layer (above).
+ * E5M2_sat_RNE(fp32(x) / s_h) for an e5m2 layer (above). A layer with dynamic
+ * scales (KVQ_SCALE_PER_TOKEN*) gives KVQ_ERR_INVALID_ARG: use
+ * kvq_kv_cache_write_dynamic.
  */
 int kvq_kv_cache_write(const kvq_layer_desc* desc, const void* k, const void* v,
                        const int64_t* slot_mapping, int64_t num_tokens,
                        void* k_cache, void* v_cache, int64_t num_pages,
                        const float* k_scale, const float* v_scale, void* stream);
+
+/*
+ * kvq_kv_cache_write_dynamic - the cache write of a layer with dynamic
+ * per-token scales (scale_mode KVQ_SCALE_PER_TOKEN or _PER_TOKEN_HEAD, see
+ * kvq_scale_mode): each written token's scales are computed from its own
+ * values, stored into the pools at its slot, and its codes are
+ * E4M3_sat_RNE(fp32(x) / s) (E5M2 for an e5m2 layer) with those scales.
+ *   k_scales, v_scales  device fp32 pools [num_pages][Hkv][16], 16-byte
+ *                 aligned; only the entries of written slots change
+ *   other arguments as for kvq_kv_cache_write
+ * A static scale mode on an fp8 layer gives KVQ_ERR_INVALID_ARG; a bf16 layer
+ * copies as kvq_kv_cache_write does (the pools are not used).
+ */
+int kvq_kv_cache_write_dynamic(const kvq_layer_desc* desc, const void* k, const void* v,
+                               const int64_t* slot_mapping, int64_t num_tokens,
+                               void* k_cache, void* v_cache, int64_t num_pages,
+                               float* k_scales, float* v_scales, void* stream);
 
 /*
  * kvq_decode_workspace_bytes - size of the FP32 split workspace that
@@ -179,7 +220,8 @@ int kvq_decode_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
  *     z_t = sm_scale * sum_d q[d] * kh[t][d],  p = softmax(z),
  *     out[d] = sum_t p_t * vh[t][d]
  * where kh = decode(code) * k_scale[h] and vh = decode(code) * v_scale[h] for
- * fp8 layers, and the bf16 values for bf16 layers. L == 0 gives zeros.
+ * fp8 layers (with dynamic scales: the pools' entries of position t's slot),
+ * and the bf16 values for bf16 layers. L == 0 gives zeros.
  *   out           device [B][Hq][D], fp32 or bf16 per out_dtype
  *   q             device bf16 [B][Hq][D]
  *   k_cache, v_cache  as written by kvq_kv_cache_write; num_pages pages
@@ -195,7 +237,8 @@ int kvq_decode_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
  *   max_context_len  host int, an upper bound of every context_lens[b]; it
  *                 sizes the partition plan and must match the value given to
  *                 kvq_decode_workspace_bytes
- *   k_scale, v_scale  as for kvq_kv_cache_write
+ *   k_scale, v_scale  as for kvq_kv_cache_write, or the scale pools of a
+ *                 layer with dynamic scales
  *   workspace     device scratch of at least the bytes reported by
  *                 kvq_decode_workspace_bytes (may be NULL when that is 0);
  *                 clobbered. Calls that share a workspace must be ordered on
@@ -226,6 +269,8 @@ int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out,
  *   k_new, v_new  device bf16 [B][Hkv][D]
  *   k_cache, v_cache  writable caches (layout above)
  *   all other arguments as for kvq_paged_decode_attention
+ * A layer with dynamic scales gives KVQ_ERR_INVALID_ARG: use
+ * kvq_decode_step_dynamic.
  */
 int kvq_decode_step(const kvq_layer_desc* desc, const void* k_new,
                     const void* v_new, void* k_cache, void* v_cache,
@@ -237,6 +282,26 @@ int kvq_decode_step(const kvq_layer_desc* desc, const void* k_new,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvq_decode_step_dynamic - kvq_decode_step for a layer with dynamic
+ * per-token scales: the new token's scales are computed as
+ * kvq_kv_cache_write_dynamic computes them and stored into the pools, then
+ * the attention reads every position's scales from the pools. Same results,
+ * bit for bit, as kvq_kv_cache_write_dynamic followed by
+ * kvq_paged_decode_attention.
+ *   k_scales, v_scales  device fp32 pools [num_pages][Hkv][16], 16-byte
+ *                 aligned, writable
+ *   other arguments as for kvq_decode_step
+ */
+int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new,
+                            const void* v_new, void* k_cache, void* v_cache,
+                            int64_t num_pages, void* out, int32_t out_dtype,
+                            const void* q, const int32_t* block_tables,
+                            int32_t max_pages_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len,
+                            float* k_scales, float* v_scales, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * kvq_kv_scale_from_amax - static scale calibration of one layer tensor:
  * s = fp32(amax) / 448 over x, per KV head or over the whole tensor per
  * desc->scale_mode ("FP8量化与长上下文推理" section 1.1: scale = max_abs/448;
@@ -246,6 +311,7 @@ int kvq_decode_step(const kvq_layer_desc* desc, const void* k_new,
  * quantise anything); a NaN anywhere in the reduced values gives NaN.
  *   x          device bf16 [T][Hkv][D]
  *   scale_out  device fp32 [1] or [Hkv]
+ * A dynamic scale mode gives KVQ_ERR_INVALID_ARG (the write sets those).
  */
 int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x,
                            int64_t num_tokens, float* scale_out, void* stream);

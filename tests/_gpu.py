@@ -48,16 +48,19 @@ def host(t):
 
 class GpuLayer:
     """One layer on the GPU: poisoned caches, scales calibrated by the
-    library, every position of the case written by the library."""
+    library, every position of the case written by the library. dyn:
+    "per_token" / "per_token_head" for dynamic scales (pools start as NaN,
+    so a read of an unwritten slot's scale would show)."""
 
     def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
-                 scales=None, fmt=None, attn="bf16"):
+                 scales=None, fmt=None, attn="bf16", dyn=None):
         self.case = case
         fmt = cache_fmt(fp8, fmt)
         self.fp8 = fp8 = fmt != "bf16"
+        mode = dyn if dyn else ("per_kv_head" if per_head else "per_tensor")
         self.desc = kv.layer_desc(case.num_q_heads, case.num_kv_heads, case.head_dim, fmt,
-                                  "per_kv_head" if per_head else "per_tensor",
-                                  window, sm_scale, attn)
+                                  mode, window, sm_scale, attn)
+        self.dyn = bool(dyn) and fp8
         self.k_new = bf16_dev(case.k_new)
         self.v_new = bf16_dev(case.v_new)
         self.slots = i64_dev(case.slots)
@@ -65,7 +68,11 @@ class GpuLayer:
         self.k_cache = u8_dev(pc)
         self.v_cache = u8_dev(pc)
         n = case.num_kv_heads if per_head else 1
-        if fp8:
+        if self.dyn:
+            shape = kv.scale_pool_shape(self.desc, case.num_pages)
+            self.k_scale = torch.full(shape, float("nan"), dtype=torch.float32, device=dev())
+            self.v_scale = torch.full(shape, float("nan"), dtype=torch.float32, device=dev())
+        elif fp8:
             if scales is None:
                 self.k_scale = torch.empty(n, dtype=torch.float32, device=dev())
                 self.v_scale = torch.empty(n, dtype=torch.float32, device=dev())
@@ -76,8 +83,12 @@ class GpuLayer:
                 self.v_scale = torch.tensor(scales[1], dtype=torch.float32, device=dev())
         else:
             self.k_scale = self.v_scale = None
-        kv.kv_cache_write(self.desc, self.k_new, self.v_new, self.slots, self.k_cache,
-                          self.v_cache, self.k_scale, self.v_scale)
+        if self.dyn:
+            kv.kv_cache_write_dynamic(self.desc, self.k_new, self.v_new, self.slots,
+                                      self.k_cache, self.v_cache, self.k_scale, self.v_scale)
+        else:
+            kv.kv_cache_write(self.desc, self.k_new, self.v_new, self.slots, self.k_cache,
+                              self.v_cache, self.k_scale, self.v_scale)
         self.q = bf16_dev(case.q)
         self.block_tables = i32_dev(case.block_tables)
         self.context_lens = i32_dev(case.lens)
@@ -105,16 +116,27 @@ class OracleLayer:
     """The same layer through the oracle (its own scales, its own caches)."""
 
     def __init__(self, case, fp8=True, per_head=True, window=0, sm_scale=0.0,
-                 scales=None, fmt=None, attn="bf16"):
+                 scales=None, fmt=None, attn="bf16", dyn=None):
         fmt = cache_fmt(fp8, fmt)
         self.fmt = _ORACLE_FMT[fmt]
         self.attn = attn
         fp8 = fmt != "bf16"
+        self.dyn = bool(dyn) and fp8
+        if self.dyn:
+            per_head = {"per_token": oracle.PER_TOKEN,
+                        "per_token_head": oracle.PER_TOKEN_HEAD}[dyn]
         self.case, self.fp8, self.per_head = case, fp8, per_head
         self.window, self.sm_scale = window, sm_scale
         self.k_cache = synth.poisoned_cache(case.num_pages, case.num_kv_heads,
                                             case.head_dim, fp8)
         self.v_cache = self.k_cache.copy()
+        if self.dyn:
+            self.ks, self.vs = oracle.scale_pools(case.num_pages, case.num_kv_heads)
+            self.ks[:] = np.nan
+            self.vs[:] = np.nan
+            oracle.kv_cache_write_dyn(self.k_cache, self.v_cache, case.k_new, case.v_new,
+                                      case.slots, self.fmt, per_head, self.ks, self.vs)
+            return
         if fp8:
             if scales is None:
                 self.ks = oracle.scale_from_amax(case.k_new, per_head, fmt=self.fmt)

@@ -162,3 +162,52 @@ def test_fp8_attention_mode_checks():
     bad.attn_dtype = 7
     with pytest.raises(kv.Kvfp8Error):
         kv.decode_workspace_bytes(bad, 1, 1024)
+
+
+def write_dyn(L, desc, k=FAKE, v=FAKE, slots=FAKE, T=4, kc=FAKE, vc=FAKE, P=8, ks=FAKE,
+              vs=FAKE):
+    return L.kvq_kv_cache_write_dynamic(ctypes.byref(desc), k, v, slots, T, kc, vc, P, ks, vs,
+                                        None)
+
+
+def step_dyn(L, desc, ks=FAKE, vs=FAKE, out=FAKE):
+    return L.kvq_decode_step_dynamic(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, 8, out, 0,
+                                     FAKE, FAKE, 8, FAKE, 1, 100, ks, vs, FAKE, 1 << 30, None)
+
+
+def test_dynamic_scale_mode_checks(L):
+    dyn = kv.layer_desc(32, 8, 128, scale_mode="per_token")
+    dynh = kv.layer_desc(32, 8, 128, "fp8_e5m2", scale_mode="per_token_head")
+    static = kv.layer_desc(32, 8, 128)
+    assert dyn.dynamic and dynh.dynamic and not static.dynamic
+    # each write / decode-step entry point takes its own kind of scales
+    assert write(L, dyn) == INVALID
+    assert write_dyn(L, static) == INVALID
+    assert step_dyn(L, static) == INVALID
+    assert L.kvq_decode_step(ctypes.byref(dyn), FAKE, FAKE, FAKE, FAKE, 8, FAKE, 0, FAKE, FAKE,
+                             8, FAKE, 1, 100, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+    # pools: present and 16-byte aligned
+    assert write_dyn(L, dyn, ks=None) == INVALID
+    assert write_dyn(L, dynh, vs=FAKE_ODD) == INVALID
+    assert attend(L, dyn, ks=FAKE_ODD) == INVALID
+    assert step_dyn(L, dyn, vs=None) == INVALID
+    assert write_dyn(L, dyn, T=-1) == INVALID
+    assert write_dyn(L, dyn, T=0) == OK
+    # static calibration does not apply; FP8 arithmetic does not combine with it
+    assert L.kvq_kv_scale_from_amax(ctypes.byref(dyn), FAKE, 4, FAKE, None) == INVALID
+    assert attend(L, kv.layer_desc(32, 8, 128, scale_mode="per_token", attn="fp8")) == UNSUPPORTED
+    assert write_dyn(L, kv.layer_desc(512, 512, 64, scale_mode="per_token")) == UNSUPPORTED
+    # a bf16 layer ignores the scale mode and copies
+    assert write_dyn(L, kv.layer_desc(32, 8, 128, "bf16", scale_mode="per_token"), ks=None,
+                     vs=None, T=0) == OK
+    bad = kv.layer_desc(32, 8, 128)
+    bad.scale_mode = 4
+    assert write(L, bad) == INVALID
+
+
+def test_dynamic_plan_leaves_the_lds_ring_for_d256():
+    # a staged fp8 D=256 tile with its scales would pass 64 KiB of ring: the
+    # plan takes the register shape, so the same workspace size follows
+    s = kv.decode_workspace_bytes(kv.layer_desc(8, 2, 256), 1, 65536)
+    d = kv.decode_workspace_bytes(kv.layer_desc(8, 2, 256, scale_mode="per_token_head"), 1, 65536)
+    assert s >= 0 and d >= 0
