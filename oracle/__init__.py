@@ -98,6 +98,11 @@ def lib():
                                                 ctypes.c_int, _u16p, _u16p, _i64p,
                                                 ctypes.c_int64, _u8p, _u8p, ctypes.c_int64,
                                                 _f32p, _f32p, ctypes.c_int]
+        L.orc_prefill_attention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_double, _u16p, _u8p, _u8p,
+                                            _i32p, ctypes.c_int, _i32p, _i32p, _f32p, _f32p,
+                                            _i32p, ctypes.c_int64, _f64p, ctypes.c_int]
         L.orc_softmax_weighted_sum.argtypes = [_f64p, _f64p, ctypes.c_int64,
                                                ctypes.c_int, _f64p]
         att = [ctypes.c_int] * 7 + [ctypes.c_double, _u16p, _u8p, _u8p, _i32p,
@@ -331,4 +336,34 @@ def attention_fp8attn(q, k_cache, v_cache, block_tables, context_lens, num_kv_he
                                    context_lens, num_kv_heads, dtype, per_head,
                                    window, sm_scale, k_scale, v_scale)
     lib().orc_attention_fp8attn(*args, _threads(nthreads))
+    return out
+
+
+def prefill_attention(q, k_cache, v_cache, block_tables, query_start, context_lens,
+                      num_kv_heads, dtype, per_head=True, window=0, sm_scale=0.0, k_scale=None,
+                      v_scale=None, rows=None, nthreads=None) -> np.ndarray:
+    """Chunked-prefill attention: q bf16 [T][Hq][D] holds every sequence's
+    new rows (sequence b's rows are query_start[b] .. query_start[b+1]-1, its
+    last positions); each row attends causally to its prefix (window-limited).
+    rows: optional indices of the rows to compute. float64 [n_rows][Hq][D]."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    T, Hq, D = q.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B = lens.shape[0]
+    assert qs.shape == (B + 1,) and qs[0] == 0 and qs[-1] == T
+    ks = np.ascontiguousarray(k_scale if k_scale is not None else [1.0], dtype=np.float32)
+    vs = np.ascontiguousarray(v_scale if v_scale is not None else [1.0], dtype=np.float32)
+    kc = np.ascontiguousarray(k_cache, dtype=np.uint8)
+    vc = np.ascontiguousarray(v_cache, dtype=np.uint8)
+    rw = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n_rows = T if rw is None else rw.shape[0]
+    out = np.zeros((n_rows, Hq, D), dtype=np.float64)
+    lib().orc_prefill_attention(B, Hq, num_kv_heads, D, dtype, int(per_head), int(window),
+                                float(sm_scale or 0.0), _ptr(q, _u16p), _ptr(kc, _u8p),
+                                _ptr(vc, _u8p), _ptr(bt, _i32p), bt.shape[1], _ptr(qs, _i32p),
+                                _ptr(lens, _i32p), _ptr(ks, _f32p), _ptr(vs, _f32p),
+                                None if rw is None else _ptr(rw, _i32p), n_rows,
+                                _ptr(out, _f64p), _threads(nthreads))
     return out

@@ -675,16 +675,15 @@ void orc_softmax_weighted_sum(const double* z, const double* v, int64_t n,
 
 /* Gather the attended window of one (sequence, query head): logits z and
  * dequantised values v (float64). Returns the window length n. */
-static int64_t gather(const att_args* a, int b, int i, double* z, double* v) {
+static int64_t gather_at(const att_args* a, int b, int i, int64_t L, const uint16_t* qi,
+                         double* z, double* v) {
   int G = a->Hq / a->Hkv;
   int h = i / G;
-  int64_t L = a->lens[b];
   if (L <= 0) return 0;
   int64_t lo = (a->window > 0 && L > a->window) ? L - a->window : 0;
   /* per_head: 0 per tensor, 1 per KV head, 2 / 3 dynamic (per-slot pools) */
   double ks = a->dtype != 0 && a->per_head < 2 ? (double)a->ks[a->per_head ? h : 0] : 1.0;
   double vs = a->dtype != 0 && a->per_head < 2 ? (double)a->vs[a->per_head ? h : 0] : 1.0;
-  const uint16_t* qi = a->q + ((int64_t)b * a->Hq + i) * a->D;
   /* the query as the attention reads it: its bf16 values, or (all-FP8
    * variant) their e4m3 codes times the row's scale */
   double qv[512];
@@ -715,6 +714,10 @@ static int64_t gather(const att_args* a, int b, int i, double* z, double* v) {
     z[t - lo] = a->sm_scale * dot;
   }
   return L - lo;
+}
+
+static int64_t gather(const att_args* a, int b, int i, double* z, double* v) {
+  return gather_at(a, b, i, a->lens[b], a->q + ((int64_t)b * a->Hq + i) * a->D, z, v);
 }
 
 typedef struct {
@@ -953,6 +956,75 @@ void orc_attention_lowprec(int B, int Hq, int Hkv, int D, int dtype,
   a.acc_bits = acc_bits;
   a.acc_tile = acc_tile;
   run_attention(&a, 2, nthreads);
+}
+
+/* Prefill (chunked prefill) attention: the causal self-attention of a chunk
+ * of new tokens over the paged cache ("State of FP8 KV cache and attention
+ * quantization in vLLM", section "Single-request benchmark": prefill is the
+ * compute-bound phase, self-attention over the input, quadratic in its
+ * length). Sequence b's n_b = qs[b+1] - qs[b] query rows are its last n_b
+ * written positions: row j sits at position pos = lens[b] - n_b + j and
+ * attends to [lo, pos] (lo = max(0, pos + 1 - W) with a window W), i.e. it
+ * is the decode attention of a context of pos + 1 positions. Rows are taken
+ * one (row, head) at a time; `rows` (n_rows entries, or NULL for all T) picks
+ * which rows to compute, and out is [n_rows][Hq][D]. A row whose position
+ * falls before 0 gives zeros. */
+typedef struct {
+  const att_args* a;
+  const int32_t* qs;
+  const int32_t* rows;
+  int64_t lo, hi;        /* range of (row index, head) pairs */
+} pf_job;
+
+static void* prefill_worker(void* p) {
+  pf_job* j = (pf_job*)p;
+  const att_args* a = j->a;
+  int64_t maxn = 0;
+  for (int b = 0; b < a->B; ++b)
+    if (a->lens[b] > maxn) maxn = a->lens[b];
+  double* z = (double*)malloc(sizeof(double) * (size_t)(maxn > 0 ? maxn : 1));
+  double* v = (double*)malloc(sizeof(double) * (size_t)(maxn > 0 ? maxn : 1) * a->D);
+  for (int64_t idx = j->lo; idx < j->hi; ++idx) {
+    int64_t ri = idx / a->Hq;
+    int i = (int)(idx % a->Hq);
+    int64_t row = j->rows ? j->rows[ri] : ri;
+    int b = 0;
+    while (b + 1 < a->B && j->qs[b + 1] <= row) ++b;
+    int64_t n = j->qs[b + 1] - j->qs[b];
+    int64_t pos = a->lens[b] - n + (row - j->qs[b]);
+    double* out = a->out + idx * a->D;
+    int64_t cnt = gather_at(a, b, i, pos + 1, a->q + (row * a->Hq + i) * a->D, z, v);
+    orc_softmax_weighted_sum(z, v, cnt, a->D, out);
+  }
+  free(z);
+  free(v);
+  return NULL;
+}
+
+void orc_prefill_attention(int B, int Hq, int Hkv, int D, int dtype, int per_head, int window,
+                           double sm_scale, const uint16_t* q, const uint8_t* kc,
+                           const uint8_t* vc, const int32_t* bt, int max_pages,
+                           const int32_t* query_start, const int32_t* lens, const float* ks,
+                           const float* vs, const int32_t* rows, int64_t n_rows, double* out,
+                           int nthreads) {
+  att_args a;
+  fill_args(&a, B, Hq, Hkv, D, dtype, per_head, window, sm_scale, q, kc, vc, bt, max_pages,
+            lens, ks, vs, out);
+  int64_t total = n_rows * Hq;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > total) nthreads = total > 0 ? (int)total : 1;
+  pthread_t th[256];
+  pf_job jobs[256];
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t].a = &a;
+    jobs[t].qs = query_start;
+    jobs[t].rows = rows;
+    jobs[t].lo = total * t / nthreads;
+    jobs[t].hi = total * (t + 1) / nthreads;
+    pthread_create(&th[t], NULL, prefill_worker, &jobs[t]);
+  }
+  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
 }
 
 /* All-FP8 attention: q quantised to e4m3 per (sequence, query head) with

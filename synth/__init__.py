@@ -186,3 +186,37 @@ WORKLOADS = {
 def batched_lens(workload: int = BATCHED, num_seqs: int = 8, lo: int = 18000,
                  hi: int = 22000) -> np.ndarray:
     return rng(workload, "lens").integers(lo, hi + 1, size=num_seqs).astype(np.int32)
+
+
+@dataclass
+class PrefillCase(DecodeCase):
+    """A chunked-prefill input: every position of every sequence is in
+    k_new / v_new (written to the caches before the attention), and sequence
+    b's last n_b positions are queries: q is [sum n_b][Hq][D], sequence b's
+    rows are query_start[b] .. query_start[b+1]-1."""
+    query_start: np.ndarray = field(default=None)   # int32 [B+1]
+
+    @property
+    def num_query_rows(self):
+        return int(self.query_start[-1])
+
+    @property
+    def max_query_len(self):
+        return int(np.diff(self.query_start).max()) if self.num_seqs else 0
+
+
+def prefill_case(workload: int, num_q_heads: int, num_kv_heads: int, head_dim: int, lens,
+                 chunk_lens, shuffle: bool = False, spare_frac: float = 0.0,
+                 values: str = "normal") -> PrefillCase:
+    """Sequences of lens[b] positions whose last chunk_lens[b] are the new
+    (query) rows; K/V and block tables as decode_case draws them."""
+    base = decode_case(workload, num_q_heads, num_kv_heads, head_dim, lens, shuffle,
+                       spare_frac, values)
+    n = np.asarray(chunk_lens, dtype=np.int32)
+    assert n.shape == base.lens.shape and np.all(n <= base.lens) and np.all(n >= 0)
+    qs = np.zeros(n.size + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(n)
+    q = normal(workload, "extra", (int(qs[-1]), num_q_heads, head_dim))
+    return PrefillCase(base.num_q_heads, base.num_kv_heads, base.head_dim, base.lens,
+                       bf16_bits(q), base.k_new, base.v_new, base.slots, base.block_tables,
+                       base.num_pages, base.seq_of_row, base.pos_of_row, qs)
