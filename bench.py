@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 GIB = 1 << 30
 
 WORKLOADS = {
@@ -325,6 +326,91 @@ def sweep(torch, kv, w, contexts, steps, warmup):
     return out
 
 
+PREFILL_LENGTHS = [1024, 2048, 4096, 8192, 16384, 32768]
+
+
+def prefill_bench(torch, kv, w, lengths, steps, warmup):
+    """Single-request prefill per layer (the TTFT share of one layer): the
+    cache write of a whole prompt of L tokens, then chunked-prefill attention
+    of all L rows over it, for fp8 and bf16 caches; fits TTFT_layer = a L^2 +
+    b L + c (the post's single-request TTFT model) and reports the prefill
+    kernel's MFMA roofline at the longest prompt."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, D = 1, w["Hq"], w["Hkv"], w["D"]
+    rows = []
+    for dt in ("fp8_e4m3", "bf16"):
+        d = kv.layer_desc(Hq, Hkv, D, dt, "per_kv_head")
+        for L in lengths:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(L)
+            pages = (L + 15) // 16
+            kc = torch.empty(kv.cache_shape(d, pages), dtype=torch.uint8, device=dev)
+            vc = torch.empty_like(kc)
+            k = torch.randn((L, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+            v = torch.randn((L, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+            q = torch.randn((L, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+            out = torch.empty((L, Hq, D), dtype=torch.bfloat16, device=dev)
+            slots = torch.arange(L, dtype=torch.int64, device=dev)
+            bt = torch.arange(pages, dtype=torch.int32, device=dev).view(1, pages)
+            qs = torch.tensor([0, L], dtype=torch.int32, device=dev)
+            lens = torch.tensor([L], dtype=torch.int32, device=dev)
+            ks = vs = None
+            if d.fp8:       # static calibration, untimed
+                ks = torch.empty(Hkv, dtype=torch.float32, device=dev)
+                vs = torch.empty(Hkv, dtype=torch.float32, device=dev)
+                kv.kv_scale_from_amax(d, k, ks)
+                kv.kv_scale_from_amax(d, v, vs)
+
+            def write():
+                kv.kv_cache_write(d, k, v, slots, kc, vc, ks, vs)
+
+            def attend():
+                kv.paged_prefill_attention(d, out, q, kc, vc, bt, qs, lens, L, ks, vs)
+
+            def timed(fn):
+                for _ in range(warmup):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(steps):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / steps
+
+            wms = timed(write)
+            ams = timed(attend)
+            flops = 4.0 * D * Hq * L * (L + 1) / 2          # q k^T and P v over the causal pairs
+            tfs = flops / (ams * 1e-3) / 1e12
+            rows.append(dict(cache=dt, prompt=L, write_us=round(wms * 1e3, 2),
+                             attention_us=round(ams * 1e3, 2),
+                             layer_us=round((wms + ams) * 1e3, 2), attention_tflops=round(tfs, 1),
+                             frac_mfma_bf16=round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)))
+            log(f"prefill {dt:8s} L={L:6d} write {wms * 1e3:9.1f} us attention {ams * 1e3:10.1f} us "
+                f"({tfs:6.1f} TFLOP/s)")
+            del kc, vc, k, v, q, out
+            torch.cuda.empty_cache()
+    fits = {}
+    for dt in ("fp8_e4m3", "bf16"):
+        pts = [r for r in rows if r["cache"] == dt]
+        x = np.array([r["prompt"] for r in pts], np.float64)
+        y = np.array([r["layer_us"] for r in pts], np.float64)
+        a, b_, c_ = np.polyfit(x, y, 2)
+        fits[dt] = dict(a_us_per_token2=a, b_us_per_token=b_, c_us=c_)
+    top = [r for r in rows if r["prompt"] == max(lengths)]
+    fp8_top = [r for r in top if r["cache"] == "fp8_e4m3"][0]
+    return dict(points=rows, fits=fits,
+                quadratic_ratio_fp8_over_bf16=fits["fp8_e4m3"]["a_us_per_token2"] /
+                fits["bf16"]["a_us_per_token2"],
+                roofline={"bound": "mfma", "kernel": "paged_prefill_kernel (fp8 cache)",
+                          "achieved": fp8_top["attention_tflops"],
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": fp8_top["frac_mfma_bf16"], "prompt": max(lengths),
+                          "algorithmic_flops": 4 * D * Hq * max(lengths) * (max(lengths) + 1) // 2})
+
+
 def cpu_baseline(w, ctx, min_seconds=10.0):
     """The float64 oracle on the headline layer (all heads, full context),
     repeated until at least min_seconds of wall time."""
@@ -374,6 +460,10 @@ def main():
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="fused: kvq_decode_step per layer; separate: write + attention calls")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the single-request prefill (TTFT) sweep")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="print the prefill sweep only (no decode headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -407,6 +497,10 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.prefill_only:
+        res = prefill_bench(torch, kv, WORKLOADS["llama8b"], PREFILL_LENGTHS, 5, 2)
+        print(json.dumps(res))
+        return
     ctx = args.context or w["ctx"]
     NL = args.layers or w["layers"]
     torch.manual_seed(0)
@@ -510,6 +604,8 @@ def main():
     if not args.no_sweep and args.workload == "llama8b":
         contexts = [1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
         result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
+    if not args.no_prefill and args.workload == "llama8b":
+        result["prefill"] = prefill_bench(torch, kv, w, PREFILL_LENGTHS, 5, 2)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)...")
         result["cpu_baseline"] = cpu_baseline(WORKLOADS["llama8b"], 131072)

@@ -98,6 +98,8 @@ def lib():
         L.kvq_kv_cache_write_dynamic.argtypes = [dp, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp]
         L.kvq_decode_step_dynamic.argtypes = [dp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, vp,
                                               i32, i32, vp, vp, vp, sz, vp]
+        L.kvq_paged_prefill_attention.argtypes = [dp, vp, i32, vp, vp, vp, i64, vp, i32, vp,
+                                                  vp, i32, i32, vp, vp, vp]
         L.kvq_kv_scale_from_amax.argtypes = [dp, vp, i64, vp, vp]
         L.kvq_e4m3_quantize.argtypes = [vp, i64, vp, vp, vp]
         L.kvq_e5m2_quantize.argtypes = [vp, i64, vp, vp, vp]
@@ -109,7 +111,7 @@ def lib():
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
                   "kvq_e4m3_quantize", "kvq_e5m2_quantize", "kvq_profile_begin",
                   "kvq_profile_end", "kvq_kv_cache_write_dynamic",
-                  "kvq_decode_step_dynamic"):
+                  "kvq_decode_step_dynamic", "kvq_paged_prefill_attention"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -318,6 +320,45 @@ def decode_step_dynamic(desc, k_new, v_new, k_cache, v_cache, out, q, block_tabl
         _ptr(out), out_dtype, _ptr(q), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, int(max_context_len), _ptr(k_scales), _ptr(v_scales),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_prefill_attention(desc, out, q, k_cache, v_cache, block_tables, query_start,
+                            context_lens, max_query_len, k_scale=None, v_scale=None,
+                            stream=None):
+    """Chunked-prefill attention: q, out [T, Hq, D] (bf16 / float32 or bf16)
+    hold every sequence's new rows (sequence b's rows query_start[b] ..
+    query_start[b+1]-1, int32 [B+1], are its last positions; context_lens
+    int32 [B] counts the written positions, the chunk included); each row
+    attends causally to its prefix. max_query_len: host bound of the rows per
+    sequence."""
+    import torch
+    _need(out, "out")
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache")
+    _need(block_tables, "block_tables", torch.int32)
+    _need(query_start, "query_start", torch.int32)
+    _need(context_lens, "context_lens", torch.int32)
+    _need(k_scale, "k_scale", torch.float32)
+    _need(v_scale, "v_scale", torch.float32)
+    if out.dtype == torch.float32:
+        out_dtype = OUT_F32
+    elif out.dtype == torch.bfloat16:
+        out_dtype = OUT_BF16
+    else:
+        raise ValueError("out must be float32 or bfloat16")
+    T = q.shape[0]
+    if tuple(q.shape) != (T, desc.num_q_heads, desc.head_dim) or out.shape != q.shape:
+        raise ValueError("q, out must be [T, Hq, D]")
+    B = context_lens.numel()
+    if query_start.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("query_start must be [B+1], block_tables [B, max_pages]")
+    num_pages = k_cache.numel() * k_cache.element_size() // (desc.num_kv_heads * desc.page_bytes)
+    _check("kvq_paged_prefill_attention", lib().kvq_paged_prefill_attention(
+        ctypes.byref(desc), _ptr(out), out_dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        num_pages, _ptr(block_tables), block_tables.shape[1], _ptr(query_start),
+        _ptr(context_lens), B, int(max_query_len), _ptr(k_scale), _ptr(v_scale),
+        _stream(stream)))
 
 
 def kv_scale_from_amax(desc, x, scale_out, stream=None):

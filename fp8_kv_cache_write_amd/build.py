@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvfp8.so")
-SOURCES = ["api.cpp", "kv_cache_write.hip", "paged_decode.hip"]
+SOURCES = ["api.cpp", "kv_cache_write.hip", "paged_decode.hip", "paged_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("KVFP8_ARCH", "gfx950")

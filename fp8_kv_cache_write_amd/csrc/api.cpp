@@ -372,6 +372,57 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new, const
                        v_scales, workspace, workspace_bytes, k_new, v_new, true, stream);
 }
 
+int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t out_dtype,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                int64_t num_pages, const int32_t* block_tables,
+                                int32_t max_pages_per_seq, const int32_t* query_start,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_query_len, const float* k_scale,
+                                const float* v_scale, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (desc->attn_dtype != KVQ_ATTN_BF16 || dynamic_scales(desc)) return KVQ_ERR_UNSUPPORTED;
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16) return KVQ_ERR_INVALID_ARG;
+  if (num_seqs < 0 || max_query_len < 0 || num_pages < 0 || max_pages_per_seq < 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_query_len == 0) return KVQ_OK;
+  if (num_pages == 0 || max_pages_per_seq == 0) return KVQ_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
+    return KVQ_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(query_start, 4) || !aligned(context_lens, 4))
+    return KVQ_ERR_INVALID_ARG;
+  const bool fp8 = desc->cache_dtype != KVQ_BF16;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return KVQ_ERR_INVALID_ARG;
+  PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint8_t*>(k_cache);
+  p.v_cache = static_cast<const uint8_t*>(v_cache);
+  p.block_tables = block_tables;
+  p.query_start = query_start;
+  p.context_lens = context_lens;
+  p.num_pages = num_pages;
+  p.k_scale = fp8 ? k_scale : nullptr;
+  p.v_scale = fp8 ? v_scale : nullptr;
+  p.out = out;
+  p.num_seqs = num_seqs;
+  p.num_q_heads = desc->num_q_heads;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.group = desc->num_q_heads / desc->num_kv_heads;
+  p.max_pages_per_seq = max_pages_per_seq;
+  p.max_query_len = max_query_len;
+  p.window = desc->sliding_window;
+  p.scale_per_head = desc->scale_mode == KVQ_SCALE_PER_KV_HEAD ? 1 : 0;
+  p.out_bf16 = out_dtype == KVQ_OUT_BF16 ? 1 : 0;
+  const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
+                                         : 1.0f / sqrtf((float)desc->head_dim);
+  p.sm_scale_log2 = sm * 1.4426950408889634f;
+  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype,
+                                      static_cast<hipStream_t>(stream), nullptr, nullptr);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
 int kvq_kv_scale_from_amax(const kvq_layer_desc* desc, const void* x, int64_t num_tokens,
                            float* scale_out, void* stream) {
   int st = check_desc(desc);

@@ -75,4 +75,36 @@ hipError_t launch_kv_cache_write_dyn(int fmt, const uint16_t* k, const uint16_t*
                                      int64_t num_pages, float* k_pool, float* v_pool,
                                      int all_heads, hipStream_t stream);
 
+// Chunked-prefill attention: sequence b's query rows query_start[b] ..
+// query_start[b+1]-1 are its last positions; each attends causally.
+struct PrefillParams {
+  const uint16_t* q;             // bf16 [T][Hq][D]
+  const uint8_t* k_cache;        // [P][Hkv][PB]
+  const uint8_t* v_cache;
+  const int32_t* block_tables;   // [B][max_pages_per_seq]
+  const int32_t* query_start;    // [B+1]
+  const int32_t* context_lens;   // [B], the chunk included
+  int64_t num_pages;
+  const float* k_scale;          // [1] or [Hkv]; unused for bf16
+  const float* v_scale;
+  void* out;                     // [T][Hq][D] f32 or bf16
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                     // G <= 16
+  int max_pages_per_seq;
+  int max_query_len;
+  int window;                    // 0 = full
+  int scale_per_head;
+  int out_bf16;
+  int qblocks;                   // set by the launcher
+  int pos_per_block;             // set by the launcher
+  float sm_scale_log2;
+};
+
+constexpr int kPrefillWaves = 4;
+
+hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt,
+                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after);
+
 }  // namespace kvfp8

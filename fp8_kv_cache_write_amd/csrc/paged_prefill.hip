@@ -1,0 +1,390 @@
+// paged_prefill.hip - chunked-prefill attention over the paged FP8 (e4m3,
+// e5m2) or bf16 KV cache on gfx950: every new query row attends causally to
+// its prefix (window-limited), softmax(q k^T) v with online-softmax
+// rescaling and FP32 accumulation.
+//
+// Prefill is the compute-bound phase of the pages' single-request benchmark
+// ("State of FP8 KV cache and attention quantization in vLLM", section
+// "Single-request benchmark": the quadratic TTFT term is self-attention over
+// the input); the same post (section "Large head-dim limits") traces the FA3
+// FP8 prefill slowdown to the register cost of two-level accumulation. On
+// CDNA4 the MFMA reads and writes its accumulator in FP32 on every
+// instruction, so each 32-position product (level 1, inside the MFMA) is
+// promoted into the FP32 accumulator (level 2) at once, with no second copy
+// of the output tile.
+//
+// Design (MI355X):
+//  * the MFMA layout of the decode kernel: A = 16 key rows straight from the
+//    cache layout (fp8 codes expanded exactly to bf16), B = 16 query columns;
+//    here a column is one (query position, head of the GQA group) pair, so a
+//    16-column group holds 16/G positions of all G heads;
+//  * a work-group of 4 waves covers NCG column groups per wave and shares
+//    every 2-page K/V tile: the tile is staged once into LDS (direct
+//    global->LDS loads, double-buffered) and each wave reads it into its
+//    operand registers;
+//  * work-groups are mapped XCD-aware: the query blocks of one (sequence, KV
+//    head) run on one XCD and share its L2, heaviest (latest) blocks first.
+#include <hip/hip_ext.h>
+#include <math.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace kvfp8 {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr float kLazyLog2 = 8.0f;   // running max raised only past +8 (P <= 256)
+constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, work-groups dealt round-robin
+
+// Max over the four lanes c, c+16, c+32, c+48 that hold one MFMA column.
+__device__ __forceinline__ float col_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float col_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace
+
+template <int D, int FMT, int NCG>
+__global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
+    const PrefillParams p) {
+  constexpr int NW = kPrefillWaves;
+  constexpr bool FP8 = FMT != kFmtBf16;
+  constexpr int E = FP8 ? 1 : 2;
+  constexpr int PB = kPage * D * E;     // bytes of one (page, head) block
+  constexpr int NI = PB / 1024;         // 1 KiB loads per page per tensor
+  constexpr int NK = D / 32;            // q k^T MFMAs per page
+  constexpr int NBLK = D / 16;          // P*V output blocks of 16 dims
+  constexpr int TILE = 2 * 2 * PB;      // K and V of 2 pages
+  constexpr int LPT = 2 * 2 * NI;       // 1 KiB loads per tile
+  static_assert(LPT % NW == 0, "every wave stages the same number of chunks");
+  static_assert(2 * TILE <= 64 * 1024, "direct-to-LDS loads address the first 64 KiB");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int qd = lane >> 4;             // row quad of the MFMA layout
+  const int c = lane & 15;              // MFMA column
+
+  // ---- which (sequence, KV head, query block): XCD-aware ------------------
+  const int per_xcd = (int)gridDim.x / kNumXcd;
+  const int logical = (int)(blockIdx.x % kNumXcd) * per_xcd + (int)(blockIdx.x / kNumXcd);
+  const int total = p.num_seqs * p.num_kv_heads * p.qblocks;
+  if (logical >= total) return;
+  const int bh = logical / p.qblocks;
+  const int qb = p.qblocks - 1 - logical % p.qblocks;     // latest (heaviest) block first
+  const int b = bh / p.num_kv_heads;
+  const int h = bh % p.num_kv_heads;
+  const int G = p.group;
+  const int ppc = 16 / G;               // positions per column group
+
+  const int q0 = p.query_start[b];
+  const int n = p.query_start[b + 1] - q0;
+  int L = p.context_lens[b];
+  if (L > p.max_pages_per_seq * kPage) L = p.max_pages_per_seq * kPage;
+  const int r0 = qb * p.pos_per_block;
+  if (r0 >= n) return;
+  const int r_last = min(r0 + p.pos_per_block, n) - 1;
+  const int off = L - n;                // position of query row r is off + r
+
+  // ---- this lane's query columns ------------------------------------------
+  int qpos[NCG], qrow[NCG];
+  bool col_ok[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int slot = c / G;
+    const int r = r0 + (wave * NCG + cg) * ppc + slot;
+    col_ok[cg] = slot < ppc && r < n && off + r >= 0;
+    qpos[cg] = col_ok[cg] ? off + r : -1;
+    qrow[cg] = col_ok[cg] ? q0 + r : -1;
+  }
+  const int g = c % G;
+  bf16x8 qop[NCG][NK];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const uint16_t* qr = p.q + ((int64_t)max(qrow[cg], 0) * p.num_q_heads + h * G + g) * D;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const int d0 = FP8 ? 16 * (4 * (s / 2) + qd) + 8 * (s % 2) : 8 * (4 * s + qd);
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (col_ok[cg]) w = *reinterpret_cast<const uint4*>(qr + d0);
+      qop[cg][s] = bits_to_bf16x8(w);
+    }
+  }
+  const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
+  const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
+  const float c_log2 = ks * p.sm_scale_log2;
+
+  // ---- key range of the work-group: [key_lo, key_hi] ----------------------
+  const int pos_first = off + r0, pos_last = off + r_last;
+  const int key_lo = p.window > 0 ? max(0, pos_first + 1 - p.window) : 0;
+  const int key_hi = pos_last;
+  const int first_page = (key_lo / kPage) & ~1;             // tiles on 2-page pairs
+  const int end_page = key_hi >= 0 ? key_hi / kPage + 1 : 0;
+  const int ntiles = end_page > first_page ? (end_page - first_page + 1) / 2 : 0;
+  // keys every column of the work-group may see without a mask
+  const int free_lo = p.window > 0 ? pos_last + 1 - p.window : 0;
+  const int free_hi = pos_first;   // a key <= this is at or before every column's position
+
+  const int32_t* bt_row = p.block_tables + (int64_t)b * p.max_pages_per_seq;
+  auto page_id = [&](int idx) -> int {      // uniform; -1: missing or invalid
+    if (idx >= end_page) return -1;
+    const int pid = bt_row[idx];
+    return (pid < 0 || (int64_t)pid >= p.num_pages) ? -1 : pid;
+  };
+
+  __shared__ __align__(16) uint8_t smem[2 * TILE];
+  const int64_t page_stride = (int64_t)p.num_kv_heads * PB;
+  const uint8_t* kbase = p.k_cache + (int64_t)h * PB;
+  const uint8_t* vbase = p.v_cache + (int64_t)h * PB;
+
+  // chunk j of a tile slot: page j / (2 NI), K (j % 2NI < NI) or V, 1 KiB i
+  auto stage = [&](int t) {
+    uint8_t* dst = smem + (t & 1) * TILE;
+#pragma unroll
+    for (int u = 0; u < LPT / NW; ++u) {
+      const int j = wave * (LPT / NW) + u;
+      const int pg = j / (2 * NI), kv = (j % (2 * NI)) / NI, i = j % NI;
+      const int pid = max(page_id(first_page + 2 * t + pg), 0);   // missing: page 0, masked
+      const uint8_t* src = (kv ? vbase : kbase) + (int64_t)pid * page_stride + 1024 * i;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + 16 * lane),
+                                       (lds_void_t*)(dst + 1024 * j), 16, 0, 0);
+    }
+  };
+
+  float m_run[NCG], l_run[NCG];
+  f32x4 acc[NCG][NBLK];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    m_run[cg] = -INFINITY;
+    l_run[cg] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) acc[cg][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  if (ntiles > 0) stage(0);
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's loads of tile t are done; after the barrier everyone's are,
+    // and every wave has finished reading the slot tile t + 1 goes to
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint8_t* slot = smem + (t & 1) * TILE;
+    uint4 tk[2][NI], tv[2][NI];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        tk[pg][i] = *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + i) + 16 * lane);
+        tv[pg][i] =
+            *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + NI + i) + 16 * lane);
+      }
+    if (t + 1 < ntiles) stage(t + 1);
+
+    // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
+    f32x4 sacc[NCG][2];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) sacc[cg][pg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        bf16x8 kop;
+        if constexpr (FP8) {
+          const uint4 w = tk[pg][s / 2];
+          kop = (s % 2 == 0) ? fp8x8_to_bf16x8<FMT>(w.x, w.y) : fp8x8_to_bf16x8<FMT>(w.z, w.w);
+        } else {
+          kop = bits_to_bf16x8(tk[pg][s]);
+        }
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[cg][s], sacc[cg][pg],
+                                                                 0, 0, 0);
+      }
+    }
+
+    // ---- masks: causal, window, missing pages (boundary tiles only) --------
+    const int k0 = (first_page + 2 * t) * kPage;            // first key of the tile
+    const int pid0 = page_id(first_page + 2 * t), pid1 = page_id(first_page + 2 * t + 1);
+    const bool need_mask = k0 < free_lo || k0 + 2 * kPage - 1 > free_hi || pid0 < 0 || pid1 < 0;
+
+    uint32_t vkeep[4] = {~0u, ~0u, ~0u, ~0u};
+    if (need_mask) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kp = k0 + pg * kPage + 4 * qd + e;
+          const bool ok = (pg == 0 ? pid0 : pid1) >= 0 && kp <= key_hi;
+          if (!ok) vkeep[2 * pg + e / 2] &= (e % 2) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+    }
+    bf16x8 pop[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float x[2][4];
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[pg][e] = sacc[cg][pg][e] * c_log2;
+      if (need_mask) {
+        const int lo_c = p.window > 0 ? qpos[cg] + 1 - p.window : 0;
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          const bool page_ok = (pg == 0 ? pid0 : pid1) >= 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kp = k0 + pg * kPage + 4 * qd + e;
+            if (!(page_ok && kp <= qpos[cg] && kp >= lo_c)) x[pg][e] = -INFINITY;
+          }
+        }
+      }
+      // online softmax (log2 domain), lazy rescale
+      float tmax = x[0][0];
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[pg][e]);
+      tmax = col_max(tmax);
+      const bool grow = tmax > m_run[cg] + kLazyLog2;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+        const float m_new = grow ? tmax : m_run[cg];
+        const float alpha = m_new == m_run[cg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[cg] - m_new);
+#pragma unroll
+        for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[cg][i][e] *= alpha;
+        l_run[cg] *= alpha;
+        m_run[cg] = m_new;
+      }
+      const float m_use = m_run[cg] == -INFINITY ? 0.0f : m_run[cg];
+      float ps = 0.0f;
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pe[e] = __builtin_amdgcn_exp2f(x[pg][e] - m_use);
+          ps += pe[e];
+        }
+        // P^T operand: k index 8qd + 4pg + e is key row 4qd+e of page pg
+        const bf16x4 p4 = __builtin_convertvector((f32x4){pe[0], pe[1], pe[2], pe[3]}, bf16x4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pop[cg][4 * pg + e] = p4[e];
+      }
+      l_run[cg] += ps;
+    }
+
+    // ---- P*V: one k=32 MFMA per 16-dim block and column group --------------
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      uint4 vb;
+      if constexpr (FP8) {
+        const int i = blk / 4, ep = blk % 4;
+        const uint4 wa = tv[0][i], wb = tv[1][i];
+        const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
+        const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
+        vb = __builtin_bit_cast(uint4, cat(fp8x4_to_bf16x4<FMT>(da), fp8x4_to_bf16x4<FMT>(db)));
+      } else {
+        const int i = blk / 2, ep = blk % 2;
+        const uint4 wa = tv[0][i], wb = tv[1][i];
+        vb = ep == 0 ? make_uint4(wa.x, wa.y, wb.x, wb.y) : make_uint4(wa.z, wa.w, wb.z, wb.w);
+      }
+      if (need_mask) {
+        // masked keys have p = 0, but rows past the last query position
+        // (unwritten: poison) and rows of missing pages may hold NaN codes,
+        // and 0 * NaN is NaN: zero them (bf16 pairs x, y = page 0 rows
+        // 4qd..4qd+3, z, w = page 1)
+        vb.x &= vkeep[0]; vb.y &= vkeep[1]; vb.z &= vkeep[2]; vb.w &= vkeep[3];
+      }
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+        acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vb), pop[cg],
+                                                               acc[cg][blk], 0, 0, 0);
+    }
+  }
+
+  // ---- output rows: o / l * s_v --------------------------------------------
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const float l = col_sum(l_run[cg]);
+    if (!col_ok[cg]) continue;
+    const bool has = l > 0.0f || l != l;                 // NaN stays NaN
+    const float scale = has ? vs / l : 0.0f;
+    const int64_t orow = ((int64_t)qrow[cg] * p.num_q_heads + h * G + g) * D;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int d;
+        if constexpr (FP8) d = 64 * (blk / 4) + 16 * qd + 4 * e + (blk % 4);
+        else d = 32 * (blk / 2) + 8 * qd + 2 * e + (blk % 2);
+        const float r = has ? acc[cg][blk][e] * scale : 0.0f;
+        if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[orow + d] = (__bf16)r;
+        else reinterpret_cast<float*>(p.out)[orow + d] = r;
+      }
+    }
+  }
+}
+
+namespace {
+
+template <int D, int FMT>
+hipError_t launch_prefill_typed(PrefillParams p, hipStream_t stream, hipEvent_t ev_before,
+                                hipEvent_t ev_after) {
+  constexpr int NCG = D >= 256 ? 1 : 2;
+  const int ppc = 16 / p.group;
+  p.pos_per_block = kPrefillWaves * NCG * ppc;
+  p.qblocks = (p.max_query_len + p.pos_per_block - 1) / p.pos_per_block;
+  const int64_t total = (int64_t)p.num_seqs * p.num_kv_heads * p.qblocks;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (ev_before && ev_after) {
+    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
+                          dim3(kPrefillWaves * kWave), 0, stream, ev_before, ev_after, 0, p);
+  } else {
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
+                       dim3(kPrefillWaves * kWave), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, hipStream_t stream,
+                              hipEvent_t ev_before, hipEvent_t ev_after) {
+  switch (fmt) {
+    case kFmtBf16: return launch_prefill_typed<D, kFmtBf16>(p, stream, ev_before, ev_after);
+    case kFmtE4M3: return launch_prefill_typed<D, kFmtE4M3>(p, stream, ev_before, ev_after);
+    case kFmtE5M2: return launch_prefill_typed<D, kFmtE5M2>(p, stream, ev_before, ev_after);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt,
+                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+  if (p.group < 1 || p.group > 16) return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: return launch_prefill_dim<64>(p, fmt, stream, ev_before, ev_after);
+    case 128: return launch_prefill_dim<128>(p, fmt, stream, ev_before, ev_after);
+    case 256: return launch_prefill_dim<256>(p, fmt, stream, ev_before, ev_after);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvfp8

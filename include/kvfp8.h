@@ -302,6 +302,44 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * kvq_paged_prefill_attention - the prefill (or chunked-prefill) attention of
+ * a chunk of new tokens over the paged cache ("State of FP8 KV cache and
+ * attention quantization in vLLM", section "Single-request benchmark":
+ * prefill is self-attention over the input, its cost quadratic in the input
+ * length). Sequence b contributes n_b = query_start[b+1] - query_start[b]
+ * query rows (rows query_start[b] .. query_start[b+1]-1 of q and out); they
+ * are its last n_b positions, already written into the caches
+ * (kvq_kv_cache_write), so row j sits at position pos = context_lens[b] -
+ * n_b + j and attends causally to [lo, pos], lo = max(0, pos + 1 - W) with a
+ * sliding window W:
+ *     out[row][i][d] = sum_t softmax_t(z) vh[t][d],
+ *     z_t = sm_scale * sum_d q[row][i][d] kh[t][d],  t in [lo, pos],
+ * with kh, vh as for kvq_paged_decode_attention. Probabilities enter the P*V
+ * product rounded to bf16; accumulation is FP32. A row whose position is
+ * below 0 (n_b > context_lens[b]) gives zeros.
+ *   out           device [T][Hq][D], fp32 or bf16 per out_dtype; T =
+ *                 query_start[num_seqs]
+ *   q             device bf16 [T][Hq][D]
+ *   query_start   device int32 [num_seqs + 1], query_start[0] = 0,
+ *                 non-decreasing
+ *   context_lens  device int32 [num_seqs], positions written, the chunk
+ *                 included; cut to max_pages_per_seq * 16 on the device
+ *   max_query_len host int >= every n_b (sizes the grid; rows past it are
+ *                 not computed)
+ *   other arguments as for kvq_paged_decode_attention (static scales only:
+ *   dynamic scales and KVQ_ATTN_FP8 give KVQ_ERR_UNSUPPORTED). No workspace.
+ */
+int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out,
+                                int32_t out_dtype, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                int64_t num_pages, const int32_t* block_tables,
+                                int32_t max_pages_per_seq,
+                                const int32_t* query_start,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_query_len, const float* k_scale,
+                                const float* v_scale, void* stream);
+
+/*
  * kvq_kv_scale_from_amax - static scale calibration of one layer tensor:
  * s = fp32(amax) / 448 over x, per KV head or over the whole tensor per
  * desc->scale_mode ("FP8量化与长上下文推理" section 1.1: scale = max_abs/448;

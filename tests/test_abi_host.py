@@ -211,3 +211,20 @@ def test_dynamic_plan_leaves_the_lds_ring_for_d256():
     s = kv.decode_workspace_bytes(kv.layer_desc(8, 2, 256), 1, 65536)
     d = kv.decode_workspace_bytes(kv.layer_desc(8, 2, 256, scale_mode="per_token_head"), 1, 65536)
     assert s >= 0 and d >= 0
+
+
+def test_prefill_argument_checks(L):
+    def pf(desc, out=FAKE, q=FAKE, qs=FAKE, lens=FAKE, B=1, mq=16, ks=FAKE, vs=FAKE, P=8):
+        return L.kvq_paged_prefill_attention(ctypes.byref(desc), out, 0, q, FAKE, FAKE, P, FAKE,
+                                             8, qs, lens, B, mq, ks, vs, None)
+    d = kv.layer_desc(32, 8, 128)
+    assert pf(d, out=None) == INVALID
+    assert pf(d, qs=None) == INVALID
+    assert pf(d, out=FAKE_ODD) == INVALID
+    assert pf(d, ks=None) == INVALID               # fp8 layers need scales
+    assert pf(d, B=-1) == INVALID
+    assert pf(d, B=0) == OK and pf(d, mq=0) == OK   # nothing to do
+    assert pf(d, P=0) == INVALID
+    assert pf(kv.layer_desc(32, 8, 128, attn="fp8")) == UNSUPPORTED
+    assert pf(kv.layer_desc(32, 8, 128, scale_mode="per_token")) == UNSUPPORTED
+    assert pf(kv.layer_desc(32, 8, 96)) == UNSUPPORTED

@@ -1,0 +1,163 @@
+"""GPU parity of chunked-prefill attention (kvq_paged_prefill_attention)
+against the oracle: every new row of a chunk attends causally to its
+(window-limited) prefix ("State of FP8 KV cache and attention quantization in
+vLLM", section "Single-request benchmark": prefill is self-attention over the
+input).
+
+Tolerance: the kernel rounds each probability to bf16 for the P*V product
+(relative error <= 2^-8: bf16 keeps 8 significand bits) while the normaliser
+sums the FP32 values, so an output moves by at most 2^-8 of the largest
+attended |v| (the weights sum to one), plus FP32 rounding; the tests assert
+that bound and the attention gate (scaled by the output's magnitude on
+outlier data)."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_write_amd as kv
+import oracle
+import synth
+from _gpu import GpuLayer, OracleLayer, dev, host, i32_dev
+from test_gpu_parity import GATE_MAX_ABS, GATE_MEAN_ABS, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(kv.LIB_PATH):
+        from fp8_kv_cache_write_amd import build
+        build.build()
+    yield
+
+
+def gpu_prefill(g, case, out_dtype=torch.float32):
+    out = torch.empty((case.num_query_rows, case.num_q_heads, case.head_dim), dtype=out_dtype,
+                      device=dev())
+    kv.paged_prefill_attention(g.desc, out, g.q, g.k_cache, g.v_cache, g.block_tables,
+                               i32_dev(case.query_start), g.context_lens, case.max_query_len,
+                               g.k_scale, g.v_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_prefill(o, case, rows=None):
+    return oracle.prefill_attention(case.q, o.k_cache, o.v_cache, case.block_tables,
+                                    case.query_start, case.lens, case.num_kv_heads, o.fmt,
+                                    o.per_head, o.window, o.sm_scale, o.ks, o.vs, rows)
+
+
+def vmax(o, case):
+    """Largest |decoded v| of the written positions (bounds the P rounding)."""
+    x = np.abs(synth.bits_to_f32(case.v_new)).max()
+    return float(x) * 1.07     # the cache rounding moves a value by <= 1/16
+
+
+def check(out, ref, o, case, label):
+    g = host(out.float()).astype(np.float64)
+    d = np.abs(g - ref)
+    mx, mean = float(d.max()), float(d.mean())
+    scale = max(1.0, float(np.abs(ref).max()))
+    bound = 2.0 ** -8 * vmax(o, case) + 1e-5 * scale
+    say(f"[{label}] max_abs={mx:.3e} mean_abs={mean:.3e} bound={bound:.3e} "
+        f"(output scale {scale:.2f})")
+    assert np.all(np.isfinite(g)), label
+    assert mx <= GATE_MAX_ABS * scale and mean <= GATE_MEAN_ABS * scale, (label, mx, mean)
+    assert mx <= bound, (label, mx, bound)
+
+
+CASES = [
+    # (label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values)
+    ("tiny-whole", synth.TINY, 4, 2, 64, [256], [256], "fp8_e4m3", 0, "tiny"),
+    ("d128-g4-ragged", 140, 32, 8, 128, [300, 77, 16, 5], [300, 40, 16, 0], "fp8_e4m3", 0,
+     "normal"),
+    ("d128-chunk-at-end", 141, 32, 8, 128, [2000, 1500], [256, 513], "fp8_e4m3", 0, "normal"),
+    ("d128-g8", 142, 64, 8, 128, [700], [700], "fp8_e4m3", 0, "drift"),
+    ("d128-g1", 143, 8, 8, 128, [400, 33], [130, 33], "fp8_e4m3", 0, "normal"),
+    ("d128-g3", 144, 6, 2, 128, [500], [250], "fp8_e4m3", 0, "normal"),
+    ("d64-window128", synth.GPTOSS, 64, 8, 64, [1000, 129], [500, 129], "fp8_e4m3", 128,
+     "normal"),
+    ("d128-window113", 145, 16, 2, 128, [900, 300], [450, 7], "fp8_e4m3", 113, "normal"),
+    ("d256", synth.HD256, 8, 2, 256, [600, 90], [600, 31], "fp8_e4m3", 0, "normal"),
+    ("d128-e5m2", 146, 32, 8, 128, [800], [300], "fp8_e5m2", 0, "normal"),
+    ("d128-bf16", 147, 32, 8, 128, [500, 64], [250, 64], "bf16", 0, "normal"),
+    ("d64-bf16-sw", 148, 16, 2, 64, [700], [700], "bf16", 128, "normal"),
+    ("d256-bf16", 149, 8, 2, 256, [300], [300], "bf16", 21, "normal"),
+]
+
+
+@pytest.mark.parametrize("label,wl,Hq,Hkv,D,lens,chunks,fmt,window,values", CASES,
+                         ids=[c[0] for c in CASES])
+def test_prefill(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values):
+    case = synth.prefill_case(wl, Hq, Hkv, D, lens, chunks, shuffle=True, spare_frac=0.25,
+                              values=values)
+    g = GpuLayer(case, window=window, fmt=fmt)
+    o = OracleLayer(case, window=window, fmt=fmt)
+    assert np.array_equal(host(g.k_cache), o.k_cache)
+    check(gpu_prefill(g, case), oracle_prefill(o, case), o, case, f"prefill-{label}")
+
+
+def test_prefill_bf16_output_is_the_rounded_f32_output():
+    case = synth.prefill_case(150, 32, 8, 128, [600, 200], [300, 200], shuffle=True)
+    g = GpuLayer(case)
+    f = gpu_prefill(g, case)
+    b = gpu_prefill(g, case, torch.bfloat16)
+    assert torch.equal(f.to(torch.bfloat16), b)
+
+
+def test_prefill_last_row_tracks_decode():
+    # the last row of each chunk is the decode attention of its sequence;
+    # the two kernels differ only in P's rounding (bf16 here)
+    case = synth.prefill_case(151, 32, 8, 128, [3000, 1000], [64, 1000], shuffle=True)
+    g = GpuLayer(case)
+    pf = host(gpu_prefill(g, case))
+    last = case.query_start[1:] - 1
+    q_last = torch.from_numpy(np.ascontiguousarray(case.q[last]).view(np.int16)).to(dev()) \
+        .view(torch.bfloat16)
+    out = torch.empty((2, 32, 128), dtype=torch.float32, device=dev())
+    ws = kv.alloc_workspace(g.desc, 2, int(case.lens.max()))
+    kv.paged_decode_attention(g.desc, out, q_last, g.k_cache, g.v_cache, g.block_tables,
+                              g.context_lens, int(case.lens.max()), g.k_scale, g.v_scale, ws)
+    torch.cuda.synchronize()
+    d = np.abs(pf[last] - host(out)).max()
+    assert d <= 2.0 ** -8 * vmax(None, case) + 1e-5, d
+
+
+def test_prefill_llama8b_8k_whole_prompt_sampled():
+    case = synth.prefill_case(synth.LLAMA8B, 32, 8, 128, [8192], [8192])
+    g = GpuLayer(case)
+    out = host(gpu_prefill(g, case))
+    o = OracleLayer(case)
+    rows = np.array([0, 1, 15, 16, 31, 32, 1000, 4095, 4096, 8000, 8191], np.int32)
+    ref = oracle_prefill(o, case, rows)
+    check(torch.from_numpy(out[rows]), ref, o, case, "prefill-8B-8k-sampled")
+
+
+def test_prefill_llama8b_32k_chunk_sampled():
+    # a 2048-row chunk at the end of a 32768-position context
+    case = synth.prefill_case(synth.LLAMA8B, 32, 8, 128, [32768], [2048])
+    g = GpuLayer(case)
+    out = host(gpu_prefill(g, case))
+    o = OracleLayer(case)
+    rows = np.array([0, 1, 511, 512, 1024, 2047], np.int32)
+    ref = oracle_prefill(o, case, rows)
+    check(torch.from_numpy(out[rows]), ref, o, case, "prefill-8B-32k-chunk-sampled")
+
+
+def test_prefill_empty_and_argument_checks():
+    case = synth.prefill_case(152, 8, 2, 64, [40], [0])
+    g = GpuLayer(case)
+    out = torch.zeros((0, 8, 64), dtype=torch.float32, device=dev())
+    kv.paged_prefill_attention(g.desc, out, g.q, g.k_cache, g.v_cache, g.block_tables,
+                               i32_dev(case.query_start), g.context_lens, 0, g.k_scale,
+                               g.v_scale)
+    bad = kv.layer_desc(8, 2, 64, attn="fp8")
+    with pytest.raises(kv.Kvfp8Error):
+        kv.paged_prefill_attention(bad, out, g.q, g.k_cache, g.v_cache, g.block_tables,
+                                   i32_dev(case.query_start), g.context_lens, 1, g.k_scale,
+                                   g.v_scale)
