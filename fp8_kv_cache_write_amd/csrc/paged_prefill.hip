@@ -125,7 +125,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   }
   const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
   const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
-  const float c_log2 = ks * p.sm_scale_log2;
+  float c_log2 = ks * p.sm_scale_log2;
+  if (c_log2 < 0.0f) {              // keep the scale non-negative: q -> -q is exact
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        uint4 w = __builtin_bit_cast(uint4, qop[cg][s]);
+        w.x ^= 0x80008000u; w.y ^= 0x80008000u; w.z ^= 0x80008000u; w.w ^= 0x80008000u;
+        qop[cg][s] = bits_to_bf16x8(w);
+      }
+    c_log2 = -c_log2;
+  }
 
   // ---- key range of the work-group: [key_lo, key_hi] ----------------------
   const int pos_first = off + r0, pos_last = off + r_last;
@@ -138,10 +149,25 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   const int free_lo = p.window > 0 ? pos_last + 1 - p.window : 0;
   const int free_hi = pos_first;   // a key <= this is at or before every column's position
 
+  // Page ids of the key range, 64 per register chunk (lane l: page base + l),
+  // the next chunk loaded ahead, so a tile's loads never wait for its
+  // block-table entries.
   const int32_t* bt_row = p.block_tables + (int64_t)b * p.max_pages_per_seq;
-  auto page_id = [&](int idx) -> int {      // uniform; -1: missing or invalid
+  auto load_chunk = [&](int base) -> int {
+    const int idx = base + lane;
+    return idx < end_page ? bt_row[idx] : -1;
+  };
+  int chunk_base = first_page;
+  int chunk = load_chunk(first_page);
+  int chunk_next = load_chunk(first_page + kWave);
+  auto page_id = [&](int idx) -> int {      // uniform, idx non-decreasing; -1: missing or invalid
     if (idx >= end_page) return -1;
-    const int pid = bt_row[idx];
+    if (idx - chunk_base >= kWave) {
+      chunk = chunk_next;
+      chunk_base += kWave;
+      chunk_next = load_chunk(chunk_base + kWave);
+    }
+    const int pid = __builtin_amdgcn_readlane(chunk, idx - chunk_base);
     return (pid < 0 || (int64_t)pid >= p.num_pages) ? -1 : pid;
   };
 
@@ -150,14 +176,17 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   const uint8_t* kbase = p.k_cache + (int64_t)h * PB;
   const uint8_t* vbase = p.v_cache + (int64_t)h * PB;
 
-  // chunk j of a tile slot: page j / (2 NI), K (j % 2NI < NI) or V, 1 KiB i
-  auto stage = [&](int t) {
+  // chunk j of a tile slot: page j / (2 NI), K (j % 2NI < NI) or V, 1 KiB i;
+  // pid_a / pid_b receive the tile's two page ids (-1: missing, masked)
+  auto stage = [&](int t, int& pid_a, int& pid_b) {
     uint8_t* dst = smem + (t & 1) * TILE;
+    pid_a = page_id(first_page + 2 * t);
+    pid_b = page_id(first_page + 2 * t + 1);
 #pragma unroll
     for (int u = 0; u < LPT / NW; ++u) {
       const int j = wave * (LPT / NW) + u;
       const int pg = j / (2 * NI), kv = (j % (2 * NI)) / NI, i = j % NI;
-      const int pid = max(page_id(first_page + 2 * t + pg), 0);   // missing: page 0, masked
+      const int pid = max(pg == 0 ? pid_a : pid_b, 0);          // missing: page 0, masked
       const uint8_t* src = (kv ? vbase : kbase) + (int64_t)pid * page_stride + 1024 * i;
       __builtin_amdgcn_global_load_lds((glb_void_t*)(src + 16 * lane),
                                        (lds_void_t*)(dst + 1024 * j), 16, 0, 0);
@@ -174,8 +203,11 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     for (int i = 0; i < NBLK; ++i) acc[cg][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  if (ntiles > 0) stage(0);
+  int pid0 = -1, pid1 = -1, pid_next0 = -1, pid_next1 = -1;
+  if (ntiles > 0) stage(0, pid_next0, pid_next1);
   for (int t = 0; t < ntiles; ++t) {
+    pid0 = pid_next0;
+    pid1 = pid_next1;
     // this wave's loads of tile t are done; after the barrier everyone's are,
     // and every wave has finished reading the slot tile t + 1 goes to
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -190,7 +222,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         tv[pg][i] =
             *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + NI + i) + 16 * lane);
       }
-    if (t + 1 < ntiles) stage(t + 1);
+    if (t + 1 < ntiles) stage(t + 1, pid_next0, pid_next1);
 
     // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
     f32x4 sacc[NCG][2];
@@ -216,30 +248,47 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       }
     }
 
-    // ---- masks: causal, window, missing pages (boundary tiles only) --------
+    // ---- masks (boundary tiles only) ----------------------------------------
     const int k0 = (first_page + 2 * t) * kPage;            // first key of the tile
-    const int pid0 = page_id(first_page + 2 * t), pid1 = page_id(first_page + 2 * t + 1);
+    // causal / window / missing pages: those logits become -inf
     const bool need_mask = k0 < free_lo || k0 + 2 * kPage - 1 > free_hi || pid0 < 0 || pid1 < 0;
-
-    uint32_t vkeep[4] = {~0u, ~0u, ~0u, ~0u};
-    if (need_mask) {
+    // masked keys get p = 0, but unwritten rows (positions >= L) and rows of
+    // missing pages may hold NaN codes, and 0 * NaN is NaN: zero those rows'
+    // V codes in the tile registers (rows 4qd..4qd+3 of each page per lane)
+    if (k0 + 2 * kPage > L || pid0 < 0 || pid1 < 0) {
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg)
+      for (int pg = 0; pg < 2; ++pg) {
+        const bool page_ok = (pg == 0 ? pid0 : pid1) >= 0;
+        uint32_t keep_lo = 0u, keep_hi = 0u;              // rows 4qd+{0,1} / {2,3} (bf16)
+        uint32_t keep8 = 0u;                              // rows 4qd+0..3, one byte each (fp8)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int kp = k0 + pg * kPage + 4 * qd + e;
-          const bool ok = (pg == 0 ? pid0 : pid1) >= 0 && kp <= key_hi;
-          if (!ok) vkeep[2 * pg + e / 2] &= (e % 2) ? 0x0000FFFFu : 0xFFFF0000u;
+          const bool ok = page_ok && k0 + pg * kPage + 4 * qd + e < L;
+          keep8 |= ok ? 0xFFu << (8 * e) : 0u;
+          const uint32_t half = ok ? (e % 2 ? 0xFFFF0000u : 0x0000FFFFu) : 0u;
+          if (e < 2) keep_lo |= half; else keep_hi |= half;
         }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if constexpr (FP8) {
+            tv[pg][i].x &= keep8; tv[pg][i].y &= keep8; tv[pg][i].z &= keep8; tv[pg][i].w &= keep8;
+          } else {
+            tv[pg][i].x &= keep_lo; tv[pg][i].y &= keep_hi;
+            tv[pg][i].z &= keep_lo; tv[pg][i].w &= keep_hi;
+          }
+        }
+      }
     }
+
     bf16x8 pop[NCG];
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
+      // raw logits; the scale c_log2 >= 0 is applied inside the exponent
       float x[2][4];
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[pg][e] = sacc[cg][pg][e] * c_log2;
+        for (int e = 0; e < 4; ++e) x[pg][e] = sacc[cg][pg][e];
       if (need_mask) {
         const int lo_c = p.window > 0 ? qpos[cg] + 1 - p.window : 0;
 #pragma unroll
@@ -258,7 +307,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
         for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[pg][e]);
-      tmax = col_max(tmax);
+      tmax = col_max(tmax) * c_log2;
       const bool grow = tmax > m_run[cg] + kLazyLog2;
       if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
         const float m_new = grow ? tmax : m_run[cg];
@@ -277,7 +326,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         float pe[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pe[e] = __builtin_amdgcn_exp2f(x[pg][e] - m_use);
+          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[pg][e], c_log2, -m_use));
           ps += pe[e];
         }
         // P^T operand: k index 8qd + 4pg + e is key row 4qd+e of page pg
@@ -302,13 +351,6 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         const int i = blk / 2, ep = blk % 2;
         const uint4 wa = tv[0][i], wb = tv[1][i];
         vb = ep == 0 ? make_uint4(wa.x, wa.y, wb.x, wb.y) : make_uint4(wa.z, wa.w, wb.z, wb.w);
-      }
-      if (need_mask) {
-        // masked keys have p = 0, but rows past the last query position
-        // (unwritten: poison) and rows of missing pages may hold NaN codes,
-        // and 0 * NaN is NaN: zero them (bf16 pairs x, y = page 0 rows
-        // 4qd..4qd+3, z, w = page 1)
-        vb.x &= vkeep[0]; vb.y &= vkeep[1]; vb.z &= vkeep[2]; vb.w &= vkeep[3];
       }
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg)
