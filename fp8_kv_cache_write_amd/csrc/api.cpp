@@ -418,7 +418,7 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
   const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
                                          : 1.0f / sqrtf((float)desc->head_dim);
   p.sm_scale_log2 = sm * 1.4426950408889634f;
-  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype,
+  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype, cu_count(),
                                       static_cast<hipStream_t>(stream), nullptr, nullptr);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

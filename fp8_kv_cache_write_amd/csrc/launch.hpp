@@ -104,7 +104,8 @@ struct PrefillParams {
 
 constexpr int kPrefillWaves = 4;
 
-hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt,
+// cus: compute units of the device (sizes the query blocks).
+hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, int cus,
                                 hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after);
 
 }  // namespace kvfp8

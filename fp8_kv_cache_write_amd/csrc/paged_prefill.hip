@@ -26,6 +26,7 @@
 //    head) run on one XCD and share its L2, heaviest (latest) blocks first.
 #include <hip/hip_ext.h>
 #include <math.h>
+#include <stdlib.h>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -58,7 +59,7 @@ __device__ __forceinline__ float col_sum(float x) {
 
 }  // namespace
 
-template <int D, int FMT, int NCG>
+template <int D, int FMT, int NCG, int SLOTS>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     const PrefillParams p) {
   constexpr int NW = kPrefillWaves;
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   constexpr int TILE = 2 * 2 * PB;      // K and V of 2 pages
   constexpr int LPT = 2 * 2 * NI;       // 1 KiB loads per tile
   static_assert(LPT % NW == 0, "every wave stages the same number of chunks");
-  static_assert(2 * TILE <= 64 * 1024, "direct-to-LDS loads address the first 64 KiB");
+  static_assert(SLOTS * TILE <= 64 * 1024, "direct-to-LDS loads address the first 64 KiB");
+  static_assert(SLOTS == 2 || SLOTS == 3, "two or three staged tiles");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     return (pid < 0 || (int64_t)pid >= p.num_pages) ? -1 : pid;
   };
 
-  __shared__ __align__(16) uint8_t smem[2 * TILE];
+  __shared__ __align__(16) uint8_t smem[SLOTS * TILE];
   const int64_t page_stride = (int64_t)p.num_kv_heads * PB;
   const uint8_t* kbase = p.k_cache + (int64_t)h * PB;
   const uint8_t* vbase = p.v_cache + (int64_t)h * PB;
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   // chunk j of a tile slot: page j / (2 NI), K (j % 2NI < NI) or V, 1 KiB i;
   // pid_a / pid_b receive the tile's two page ids (-1: missing, masked)
   auto stage = [&](int t, int& pid_a, int& pid_b) {
-    uint8_t* dst = smem + (t & 1) * TILE;
+    uint8_t* dst = smem + (t % SLOTS) * TILE;
     pid_a = page_id(first_page + 2 * t);
     pid_b = page_id(first_page + 2 * t + 1);
 #pragma unroll
@@ -203,16 +205,22 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     for (int i = 0; i < NBLK; ++i) acc[cg][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  int pid0 = -1, pid1 = -1, pid_next0 = -1, pid_next1 = -1;
-  if (ntiles > 0) stage(0, pid_next0, pid_next1);
+  // page ids of the staged tiles t, t + 1, t + 2 (the last with three slots)
+  int pq0a = -1, pq0b = -1, pq1a = -1, pq1b = -1, pq2a = -1, pq2b = -1;
+  if (ntiles > 0) stage(0, pq0a, pq0b);
+  if (SLOTS == 3 && ntiles > 1) stage(1, pq1a, pq1b);
   for (int t = 0; t < ntiles; ++t) {
-    pid0 = pid_next0;
-    pid1 = pid_next1;
-    // this wave's loads of tile t are done; after the barrier everyone's are,
-    // and every wave has finished reading the slot tile t + 1 goes to
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int pid0 = pq0a, pid1 = pq0b;
+    // this wave's loads of tile t are done (with three slots those of tile
+    // t + 1 may still be in flight: loads complete in order); after the
+    // barrier everyone's are, and every wave has finished reading the slot
+    // the next staged tile goes to (that of tile t - 1)
+    if (SLOTS == 3 && t + 1 < ntiles)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT / NW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const uint8_t* slot = smem + (t & 1) * TILE;
+    const uint8_t* slot = smem + (t % SLOTS) * TILE;
     uint4 tk[2][NI], tv[2][NI];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
@@ -222,7 +230,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         tv[pg][i] =
             *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + NI + i) + 16 * lane);
       }
-    if (t + 1 < ntiles) stage(t + 1, pid_next0, pid_next1);
+    if (t + SLOTS - 1 < ntiles) {
+      if (SLOTS == 3) stage(t + 2, pq2a, pq2b);
+      else stage(t + 1, pq1a, pq1b);
+    }
+    pq0a = pq1a; pq0b = pq1b;
+    pq1a = pq2a; pq1b = pq2b;
 
     // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
     f32x4 sacc[NCG][2];
@@ -384,47 +397,72 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 
 namespace {
 
-template <int D, int FMT>
-hipError_t launch_prefill_typed(PrefillParams p, hipStream_t stream, hipEvent_t ev_before,
-                                hipEvent_t ev_after) {
-  constexpr int NCG = D >= 256 ? 1 : 2;
-  const int ppc = 16 / p.group;
-  p.pos_per_block = kPrefillWaves * NCG * ppc;
-  p.qblocks = (p.max_query_len + p.pos_per_block - 1) / p.pos_per_block;
-  const int64_t total = (int64_t)p.num_seqs * p.num_kv_heads * p.qblocks;
-  if (total == 0) return hipSuccess;
+template <int D, int FMT, int NCG>
+hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stream,
+                                hipEvent_t ev_before, hipEvent_t ev_after) {
+  constexpr int TILE = 2 * 2 * kPage * D * (FMT == kFmtBf16 ? 2 : 1);
+  constexpr int SLOTS = 3 * TILE <= 64 * 1024 ? 3 : 2;
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (ev_before && ev_after) {
-    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
+    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, SLOTS>), dim3((unsigned)grid),
                           dim3(kPrefillWaves * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, SLOTS>), dim3((unsigned)grid),
                        dim3(kPrefillWaves * kWave), 0, stream, p);
   }
   return hipGetLastError();
 }
 
+// Column groups per wave: the most the registers allow (each shares the
+// tile's fp8 -> bf16 expansion and LDS reads), fewer when the grid would
+// leave compute units idle (short prompts): at least two work-groups per CU.
+template <int D, int FMT>
+hipError_t launch_prefill_typed(PrefillParams p, int cus, hipStream_t stream,
+                                hipEvent_t ev_before, hipEvent_t ev_after) {
+  constexpr int NCG_MAX = D >= 256 ? 1 : (D == 128 && FMT == kFmtBf16 ? 2 : 3);
+  const int ppc = 16 / p.group;
+  // KVFP8_PREFILL_COLUMN_GROUPS=n (1..3) forces the count (tests, sweeps)
+  int forced = 0;
+  if (const char* env = getenv("KVFP8_PREFILL_COLUMN_GROUPS")) forced = atoi(env);
+  int ncg = forced >= 1 && forced <= NCG_MAX ? forced : NCG_MAX;
+  int64_t total = 0;
+  for (;; --ncg) {
+    p.pos_per_block = kPrefillWaves * ncg * ppc;
+    p.qblocks = (p.max_query_len + p.pos_per_block - 1) / p.pos_per_block;
+    total = (int64_t)p.num_seqs * p.num_kv_heads * p.qblocks;
+    if (ncg == 1 || forced || total >= 2LL * cus) break;
+  }
+  if (total == 0) return hipSuccess;
+  if constexpr (NCG_MAX >= 3) {
+    if (ncg == 3) return launch_prefill_shape<D, FMT, 3>(p, total, stream, ev_before, ev_after);
+  }
+  if constexpr (NCG_MAX >= 2) {
+    if (ncg == 2) return launch_prefill_shape<D, FMT, 2>(p, total, stream, ev_before, ev_after);
+  }
+  return launch_prefill_shape<D, FMT, 1>(p, total, stream, ev_before, ev_after);
+}
+
 template <int D>
-hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, hipStream_t stream,
+hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, int cus, hipStream_t stream,
                               hipEvent_t ev_before, hipEvent_t ev_after) {
   switch (fmt) {
-    case kFmtBf16: return launch_prefill_typed<D, kFmtBf16>(p, stream, ev_before, ev_after);
-    case kFmtE4M3: return launch_prefill_typed<D, kFmtE4M3>(p, stream, ev_before, ev_after);
-    case kFmtE5M2: return launch_prefill_typed<D, kFmtE5M2>(p, stream, ev_before, ev_after);
+    case kFmtBf16: return launch_prefill_typed<D, kFmtBf16>(p, cus, stream, ev_before, ev_after);
+    case kFmtE4M3: return launch_prefill_typed<D, kFmtE4M3>(p, cus, stream, ev_before, ev_after);
+    case kFmtE5M2: return launch_prefill_typed<D, kFmtE5M2>(p, cus, stream, ev_before, ev_after);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt,
+hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, int cus,
                                 hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
   if (p.group < 1 || p.group > 16) return hipErrorInvalidValue;
   switch (head_dim) {
-    case 64: return launch_prefill_dim<64>(p, fmt, stream, ev_before, ev_after);
-    case 128: return launch_prefill_dim<128>(p, fmt, stream, ev_before, ev_after);
-    case 256: return launch_prefill_dim<256>(p, fmt, stream, ev_before, ev_after);
+    case 64: return launch_prefill_dim<64>(p, fmt, cus, stream, ev_before, ev_after);
+    case 128: return launch_prefill_dim<128>(p, fmt, cus, stream, ev_before, ev_after);
+    case 256: return launch_prefill_dim<256>(p, fmt, cus, stream, ev_before, ev_after);
     default: return hipErrorInvalidValue;
   }
 }

@@ -102,6 +102,21 @@ def test_prefill(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values):
     check(gpu_prefill(g, case), oracle_prefill(o, case), o, case, f"prefill-{label}")
 
 
+@pytest.mark.parametrize("groups", ["1", "2", "3"])
+@pytest.mark.parametrize("fmt,D,G", [("fp8_e4m3", 128, 4), ("fp8_e4m3", 64, 8),
+                                     ("fp8_e5m2", 128, 2), ("bf16", 64, 4)])
+def test_prefill_column_groups(groups, fmt, D, G, monkeypatch):
+    # every column-group count of the kernel, all rows compared (counts above
+    # what a shape supports fall back to its largest)
+    monkeypatch.setenv("KVFP8_PREFILL_COLUMN_GROUPS", groups)
+    case = synth.prefill_case(153, 2 * G, 2, D, [700, 333], [700, 200], shuffle=True,
+                              spare_frac=0.2)
+    g = GpuLayer(case, fmt=fmt)
+    o = OracleLayer(case, fmt=fmt)
+    check(gpu_prefill(g, case), oracle_prefill(o, case), o, case,
+          f"prefill {fmt} D={D} G={G} groups={groups}")
+
+
 def test_prefill_bf16_output_is_the_rounded_f32_output():
     case = synth.prefill_case(150, 32, 8, 128, [600, 200], [300, 200], shuffle=True)
     g = GpuLayer(case)
