@@ -59,7 +59,7 @@ __device__ __forceinline__ float col_sum(float x) {
 
 }  // namespace
 
-template <int D, int FMT, int NCG, int SLOTS>
+template <int D, int FMT, int NCG>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     const PrefillParams p) {
   constexpr int NW = kPrefillWaves;
@@ -72,8 +72,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   constexpr int TILE = 2 * 2 * PB;      // K and V of 2 pages
   constexpr int LPT = 2 * 2 * NI;       // 1 KiB loads per tile
   static_assert(LPT % NW == 0, "every wave stages the same number of chunks");
-  static_assert(SLOTS * TILE <= 64 * 1024, "direct-to-LDS loads address the first 64 KiB");
-  static_assert(SLOTS == 2 || SLOTS == 3, "two or three staged tiles");
+  static_assert(2 * TILE <= 64 * 1024, "direct-to-LDS loads address the first 64 KiB");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -173,7 +172,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     return (pid < 0 || (int64_t)pid >= p.num_pages) ? -1 : pid;
   };
 
-  __shared__ __align__(16) uint8_t smem[SLOTS * TILE];
+  __shared__ __align__(16) uint8_t smem[2 * TILE];
   const int64_t page_stride = (int64_t)p.num_kv_heads * PB;
   const uint8_t* kbase = p.k_cache + (int64_t)h * PB;
   const uint8_t* vbase = p.v_cache + (int64_t)h * PB;
@@ -181,7 +180,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   // chunk j of a tile slot: page j / (2 NI), K (j % 2NI < NI) or V, 1 KiB i;
   // pid_a / pid_b receive the tile's two page ids (-1: missing, masked)
   auto stage = [&](int t, int& pid_a, int& pid_b) {
-    uint8_t* dst = smem + (t % SLOTS) * TILE;
+    uint8_t* dst = smem + (t & 1) * TILE;
     pid_a = page_id(first_page + 2 * t);
     pid_b = page_id(first_page + 2 * t + 1);
 #pragma unroll
@@ -205,22 +204,19 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     for (int i = 0; i < NBLK; ++i) acc[cg][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // page ids of the staged tiles t, t + 1, t + 2 (the last with three slots)
-  int pq0a = -1, pq0b = -1, pq1a = -1, pq1b = -1, pq2a = -1, pq2b = -1;
-  if (ntiles > 0) stage(0, pq0a, pq0b);
-  if (SLOTS == 3 && ntiles > 1) stage(1, pq1a, pq1b);
+  // Two LDS slots: tile t + 1 is staged while tile t is computed. (A third
+  // slot gains nothing: the work-group barrier's release fence waits for
+  // every outstanding load; a bare barrier with hand-placed waits measured
+  // slower, the compiler then no longer overlapping the slot reads.)
+  int pid_next0 = -1, pid_next1 = -1;
+  if (ntiles > 0) stage(0, pid_next0, pid_next1);
   for (int t = 0; t < ntiles; ++t) {
-    const int pid0 = pq0a, pid1 = pq0b;
-    // this wave's loads of tile t are done (with three slots those of tile
-    // t + 1 may still be in flight: loads complete in order); after the
-    // barrier everyone's are, and every wave has finished reading the slot
-    // the next staged tile goes to (that of tile t - 1)
-    if (SLOTS == 3 && t + 1 < ntiles)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT / NW) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int pid0 = pid_next0, pid1 = pid_next1;
+    // this wave's loads of tile t are done; after the barrier everyone's are,
+    // and every wave has finished reading the slot tile t + 1 goes to
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const uint8_t* slot = smem + (t % SLOTS) * TILE;
+    const uint8_t* slot = smem + (t & 1) * TILE;
     uint4 tk[2][NI], tv[2][NI];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
@@ -230,12 +226,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         tv[pg][i] =
             *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + NI + i) + 16 * lane);
       }
-    if (t + SLOTS - 1 < ntiles) {
-      if (SLOTS == 3) stage(t + 2, pq2a, pq2b);
-      else stage(t + 1, pq1a, pq1b);
-    }
-    pq0a = pq1a; pq0b = pq1b;
-    pq1a = pq2a; pq1b = pq2b;
+    if (t + 1 < ntiles) stage(t + 1, pid_next0, pid_next1);
 
     // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
     f32x4 sacc[NCG][2];
@@ -400,15 +391,13 @@ namespace {
 template <int D, int FMT, int NCG>
 hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
-  constexpr int TILE = 2 * 2 * kPage * D * (FMT == kFmtBf16 ? 2 : 1);
-  constexpr int SLOTS = 3 * TILE <= 64 * 1024 ? 3 : 2;
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (ev_before && ev_after) {
-    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, SLOTS>), dim3((unsigned)grid),
+    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
                           dim3(kPrefillWaves * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, SLOTS>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
                        dim3(kPrefillWaves * kWave), 0, stream, p);
   }
   return hipGetLastError();
