@@ -329,7 +329,7 @@ def sweep(torch, kv, w, contexts, steps, warmup):
 PREFILL_LENGTHS = [1024, 2048, 4096, 8192, 16384, 32768]
 
 
-def prefill_bench(torch, kv, w, lengths, steps, warmup):
+def prefill_bench(torch, kv, w, lengths, steps, warmup, scales="per_kv_head"):
     """Single-request prefill per layer (the TTFT share of one layer): the
     cache write of a whole prompt of L tokens, then chunked-prefill attention
     of all L rows over it, for fp8 and bf16 caches; fits TTFT_layer = a L^2 +
@@ -340,7 +340,7 @@ def prefill_bench(torch, kv, w, lengths, steps, warmup):
     B, Hq, Hkv, D = 1, w["Hq"], w["Hkv"], w["D"]
     rows = []
     for dt in ("fp8_e4m3", "bf16"):
-        d = kv.layer_desc(Hq, Hkv, D, dt, "per_kv_head")
+        d = kv.layer_desc(Hq, Hkv, D, dt, scales if dt != "bf16" else "per_kv_head")
         for L in lengths:
             gen = torch.Generator(device=dev)
             gen.manual_seed(L)
@@ -356,14 +356,20 @@ def prefill_bench(torch, kv, w, lengths, steps, warmup):
             qs = torch.tensor([0, L], dtype=torch.int32, device=dev)
             lens = torch.tensor([L], dtype=torch.int32, device=dev)
             ks = vs = None
-            if d.fp8:       # static calibration, untimed
+            if d.dynamic:   # per-token scales: pools, set by the (timed) write
+                ks = torch.zeros(kv.scale_pool_shape(d, pages), dtype=torch.float32, device=dev)
+                vs = torch.zeros_like(ks)
+            elif d.fp8:     # static calibration, untimed
                 ks = torch.empty(Hkv, dtype=torch.float32, device=dev)
                 vs = torch.empty(Hkv, dtype=torch.float32, device=dev)
                 kv.kv_scale_from_amax(d, k, ks)
                 kv.kv_scale_from_amax(d, v, vs)
 
             def write():
-                kv.kv_cache_write(d, k, v, slots, kc, vc, ks, vs)
+                if d.dynamic:
+                    kv.kv_cache_write_dynamic(d, k, v, slots, kc, vc, ks, vs)
+                else:
+                    kv.kv_cache_write(d, k, v, slots, kc, vc, ks, vs)
 
             def attend():
                 kv.paged_prefill_attention(d, out, q, kc, vc, bt, qs, lens, L, ks, vs)
@@ -401,7 +407,7 @@ def prefill_bench(torch, kv, w, lengths, steps, warmup):
         fits[dt] = dict(a_us_per_token2=a, b_us_per_token=b_, c_us=c_)
     top = [r for r in rows if r["prompt"] == max(lengths)]
     fp8_top = [r for r in top if r["cache"] == "fp8_e4m3"][0]
-    return dict(points=rows, fits=fits,
+    return dict(points=rows, fits=fits, scales=scales,
                 quadratic_ratio_fp8_over_bf16=fits["fp8_e4m3"]["a_us_per_token2"] /
                 fits["bf16"]["a_us_per_token2"],
                 roofline={"bound": "mfma", "kernel": "paged_prefill_kernel (fp8 cache)",
@@ -498,7 +504,8 @@ def main():
 
     w = WORKLOADS[args.workload]
     if args.prefill_only:
-        res = prefill_bench(torch, kv, WORKLOADS["llama8b"], PREFILL_LENGTHS, 5, 2)
+        res = prefill_bench(torch, kv, WORKLOADS["llama8b"], PREFILL_LENGTHS, 5, 2,
+                            scales=args.scales)
         print(json.dumps(res))
         return
     ctx = args.context or w["ctx"]

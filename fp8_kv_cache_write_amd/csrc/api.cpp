@@ -381,7 +381,8 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
                                 const float* v_scale, void* stream) {
   int st = check_desc(desc);
   if (st) return st;
-  if (desc->attn_dtype != KVQ_ATTN_BF16 || dynamic_scales(desc)) return KVQ_ERR_UNSUPPORTED;
+  if (desc->attn_dtype != KVQ_ATTN_BF16) return KVQ_ERR_UNSUPPORTED;
+  const bool dyn = dynamic_scales(desc);
   if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16) return KVQ_ERR_INVALID_ARG;
   if (num_seqs < 0 || max_query_len < 0 || num_pages < 0 || max_pages_per_seq < 0)
     return KVQ_ERR_INVALID_ARG;
@@ -393,7 +394,8 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
       !aligned(block_tables, 4) || !aligned(query_start, 4) || !aligned(context_lens, 4))
     return KVQ_ERR_INVALID_ARG;
   const bool fp8 = desc->cache_dtype != KVQ_BF16;
-  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, dyn ? 16 : 4) ||
+              !aligned(v_scale, dyn ? 16 : 4)))
     return KVQ_ERR_INVALID_ARG;
   PrefillParams p{};
   p.q = static_cast<const uint16_t*>(q);
@@ -418,8 +420,9 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
   const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
                                          : 1.0f / sqrtf((float)desc->head_dim);
   p.sm_scale_log2 = sm * 1.4426950408889634f;
-  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype, cu_count(),
-                                      static_cast<hipStream_t>(stream), nullptr, nullptr);
+  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype, dyn,
+                                      cu_count(), static_cast<hipStream_t>(stream), nullptr,
+                                      nullptr);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

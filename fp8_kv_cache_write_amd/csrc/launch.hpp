@@ -85,7 +85,7 @@ struct PrefillParams {
   const int32_t* query_start;    // [B+1]
   const int32_t* context_lens;   // [B], the chunk included
   int64_t num_pages;
-  const float* k_scale;          // [1] or [Hkv]; unused for bf16
+  const float* k_scale;          // [1] or [Hkv], or the pools [P][Hkv][16]; unused for bf16
   const float* v_scale;
   void* out;                     // [T][Hq][D] f32 or bf16
   int num_seqs;
@@ -104,8 +104,10 @@ struct PrefillParams {
 
 constexpr int kPrefillWaves = 4;
 
-// cus: compute units of the device (sizes the query blocks).
-hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, int cus,
-                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after);
+// cus: compute units of the device (sizes the query blocks). dyn: dynamic
+// per-token scales (p.k_scale / p.v_scale are the pools [P][Hkv][16]).
+hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, bool dyn,
+                                int cus, hipStream_t stream, hipEvent_t ev_before,
+                                hipEvent_t ev_after);
 
 }  // namespace kvfp8

@@ -59,7 +59,7 @@ __device__ __forceinline__ float col_sum(float x) {
 
 }  // namespace
 
-template <int D, int FMT, int NCG>
+template <int D, int FMT, int NCG, bool DYN>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     const PrefillParams p) {
   constexpr int NW = kPrefillWaves;
@@ -69,8 +69,11 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   constexpr int NI = PB / 1024;         // 1 KiB loads per page per tensor
   constexpr int NK = D / 32;            // q k^T MFMAs per page
   constexpr int NBLK = D / 16;          // P*V output blocks of 16 dims
-  constexpr int TILE = 2 * 2 * PB;      // K and V of 2 pages
+  constexpr int KV_BYTES = 2 * 2 * PB;  // K and V of 2 pages
+  // dynamic scales: the tile's 2 pages x (16 K + 16 V) fp32 follow them
+  constexpr int TILE = KV_BYTES + (DYN ? 2 * 2 * kPage * 4 : 0);
   constexpr int LPT = 2 * 2 * NI;       // 1 KiB loads per tile
+  static_assert(!DYN || FP8, "dynamic scales belong to fp8 caches");
   static_assert(LPT % NW == 0, "every wave stages the same number of chunks");
   static_assert(2 * TILE <= 64 * 1024, "direct-to-LDS loads address the first 64 KiB");
 
@@ -124,8 +127,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       qop[cg][s] = bits_to_bf16x8(w);
     }
   }
-  const float ks = FP8 ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
-  const float vs = FP8 ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
+  // static scales; dynamic ones (pools [page][head][row]) are per position
+  const float ks = FP8 && !DYN ? p.k_scale[p.scale_per_head ? h : 0] : 1.0f;
+  const float vs = FP8 && !DYN ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
   float c_log2 = ks * p.sm_scale_log2;
   if (c_log2 < 0.0f) {              // keep the scale non-negative: q -> -q is exact
 #pragma unroll
@@ -192,6 +196,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       __builtin_amdgcn_global_load_lds((glb_void_t*)(src + 16 * lane),
                                        (lds_void_t*)(dst + 1024 * j), 16, 0, 0);
     }
+    if constexpr (DYN) {
+      // lane l < 16: page l / 8, K (l % 8 < 4) or V scales of rows
+      // 4 (l % 4) .. +3; every wave loads the same 256 bytes, so each wave's
+      // wait covers them
+      if (lane < 16) {
+        const int pid = max(lane < 8 ? pid_a : pid_b, 0);
+        const float* pool = (lane % 8) < 4 ? p.k_scale : p.v_scale;
+        const float* src = pool + ((int64_t)pid * p.num_kv_heads + h) * kPage + 4 * (lane % 4);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(dst + KV_BYTES), 16, 0,
+                                         0);
+      }
+    }
   };
 
   float m_run[NCG], l_run[NCG];
@@ -226,6 +242,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         tv[pg][i] =
             *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + NI + i) + 16 * lane);
       }
+    // dynamic scales of this lane's rows 4qd..4qd+3 of each page
+    f32x4 sk[2], sv[2];
+    if constexpr (DYN) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        sk[pg] = *reinterpret_cast<const f32x4*>(slot + KV_BYTES + 16 * (8 * pg + qd));
+        sv[pg] = *reinterpret_cast<const f32x4*>(slot + KV_BYTES + 16 * (8 * pg + 4 + qd));
+      }
+    }
     if (t + 1 < ntiles) stage(t + 1, pid_next0, pid_next1);
 
     // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
@@ -272,6 +297,11 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
           const uint32_t half = ok ? (e % 2 ? 0xFFFF0000u : 0x0000FFFFu) : 0u;
           if (e < 2) keep_lo |= half; else keep_hi |= half;
         }
+        if constexpr (DYN) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!(page_ok && k0 + pg * kPage + 4 * qd + e < L)) sk[pg][e] = sv[pg][e] = 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
           if constexpr (FP8) {
@@ -284,15 +314,25 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       }
     }
 
+    // static scales: raw logits, c_log2 >= 0 applied inside the exponent;
+    // dynamic: each row's logits times c_log2 s_k (row), exponent scale 1
+    float csk[2][4];
+    if constexpr (DYN) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) csk[pg][e] = c_log2 * sk[pg][e];
+    }
+    const float cexp = DYN ? 1.0f : c_log2;
     bf16x8 pop[NCG];
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
-      // raw logits; the scale c_log2 >= 0 is applied inside the exponent
       float x[2][4];
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[pg][e] = sacc[cg][pg][e];
+        for (int e = 0; e < 4; ++e)
+          x[pg][e] = DYN ? sacc[cg][pg][e] * csk[pg][e] : sacc[cg][pg][e];
       if (need_mask) {
         const int lo_c = p.window > 0 ? qpos[cg] + 1 - p.window : 0;
 #pragma unroll
@@ -311,7 +351,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
         for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[pg][e]);
-      tmax = col_max(tmax) * c_log2;
+      tmax = col_max(tmax) * cexp;
       const bool grow = tmax > m_run[cg] + kLazyLog2;
       if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
         const float m_new = grow ? tmax : m_run[cg];
@@ -330,8 +370,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         float pe[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[pg][e], c_log2, -m_use));
+          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[pg][e], cexp, -m_use));
           ps += pe[e];
+        }
+        // dynamic scales: the row's V scale joins P (the normaliser took p)
+        if constexpr (DYN) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pe[e] *= sv[pg][e];
         }
         // P^T operand: k index 8qd + 4pg + e is key row 4qd+e of page pg
         const bf16x4 p4 = __builtin_convertvector((f32x4){pe[0], pe[1], pe[2], pe[3]}, bf16x4);
@@ -388,16 +433,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 
 namespace {
 
-template <int D, int FMT, int NCG>
+template <int D, int FMT, int NCG, bool DYN>
 hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (ev_before && ev_after) {
-    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
+    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, DYN>), dim3((unsigned)grid),
                           dim3(kPrefillWaves * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, DYN>), dim3((unsigned)grid),
                        dim3(kPrefillWaves * kWave), 0, stream, p);
   }
   return hipGetLastError();
@@ -406,7 +451,7 @@ hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stre
 // Column groups per wave: the most the registers allow (each shares the
 // tile's fp8 -> bf16 expansion and LDS reads), fewer when the grid would
 // leave compute units idle (short prompts): at least two work-groups per CU.
-template <int D, int FMT>
+template <int D, int FMT, bool DYN>
 hipError_t launch_prefill_typed(PrefillParams p, int cus, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NCG_MAX = D >= 256 ? 1 : (D == 128 && FMT == kFmtBf16 ? 2 : 3);
@@ -424,34 +469,49 @@ hipError_t launch_prefill_typed(PrefillParams p, int cus, hipStream_t stream,
   }
   if (total == 0) return hipSuccess;
   if constexpr (NCG_MAX >= 3) {
-    if (ncg == 3) return launch_prefill_shape<D, FMT, 3>(p, total, stream, ev_before, ev_after);
+    if (ncg == 3)
+      return launch_prefill_shape<D, FMT, 3, DYN>(p, total, stream, ev_before, ev_after);
   }
   if constexpr (NCG_MAX >= 2) {
-    if (ncg == 2) return launch_prefill_shape<D, FMT, 2>(p, total, stream, ev_before, ev_after);
+    if (ncg == 2)
+      return launch_prefill_shape<D, FMT, 2, DYN>(p, total, stream, ev_before, ev_after);
   }
-  return launch_prefill_shape<D, FMT, 1>(p, total, stream, ev_before, ev_after);
+  return launch_prefill_shape<D, FMT, 1, DYN>(p, total, stream, ev_before, ev_after);
 }
 
 template <int D>
-hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, int cus, hipStream_t stream,
-                              hipEvent_t ev_before, hipEvent_t ev_after) {
+hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, bool dyn, int cus,
+                              hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+  if (dyn) {
+    switch (fmt) {
+      case kFmtE4M3:
+        return launch_prefill_typed<D, kFmtE4M3, true>(p, cus, stream, ev_before, ev_after);
+      case kFmtE5M2:
+        return launch_prefill_typed<D, kFmtE5M2, true>(p, cus, stream, ev_before, ev_after);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (fmt) {
-    case kFmtBf16: return launch_prefill_typed<D, kFmtBf16>(p, cus, stream, ev_before, ev_after);
-    case kFmtE4M3: return launch_prefill_typed<D, kFmtE4M3>(p, cus, stream, ev_before, ev_after);
-    case kFmtE5M2: return launch_prefill_typed<D, kFmtE5M2>(p, cus, stream, ev_before, ev_after);
+    case kFmtBf16:
+      return launch_prefill_typed<D, kFmtBf16, false>(p, cus, stream, ev_before, ev_after);
+    case kFmtE4M3:
+      return launch_prefill_typed<D, kFmtE4M3, false>(p, cus, stream, ev_before, ev_after);
+    case kFmtE5M2:
+      return launch_prefill_typed<D, kFmtE5M2, false>(p, cus, stream, ev_before, ev_after);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, int cus,
-                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, bool dyn,
+                                int cus, hipStream_t stream, hipEvent_t ev_before,
+                                hipEvent_t ev_after) {
   if (p.group < 1 || p.group > 16) return hipErrorInvalidValue;
   switch (head_dim) {
-    case 64: return launch_prefill_dim<64>(p, fmt, cus, stream, ev_before, ev_after);
-    case 128: return launch_prefill_dim<128>(p, fmt, cus, stream, ev_before, ev_after);
-    case 256: return launch_prefill_dim<256>(p, fmt, cus, stream, ev_before, ev_after);
+    case 64: return launch_prefill_dim<64>(p, fmt, dyn, cus, stream, ev_before, ev_after);
+    case 128: return launch_prefill_dim<128>(p, fmt, dyn, cus, stream, ev_before, ev_after);
+    case 256: return launch_prefill_dim<256>(p, fmt, dyn, cus, stream, ev_before, ev_after);
     default: return hipErrorInvalidValue;
   }
 }

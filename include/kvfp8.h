@@ -326,8 +326,9 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new,
  *                 included; cut to max_pages_per_seq * 16 on the device
  *   max_query_len host int >= every n_b (sizes the grid; rows past it are
  *                 not computed)
- *   other arguments as for kvq_paged_decode_attention (static scales only:
- *   dynamic scales and KVQ_ATTN_FP8 give KVQ_ERR_UNSUPPORTED). No workspace.
+ *   other arguments as for kvq_paged_decode_attention (static scales or the
+ *   pools of dynamic per-token scales; KVQ_ATTN_FP8 gives
+ *   KVQ_ERR_UNSUPPORTED). No workspace.
  */
 int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out,
                                 int32_t out_dtype, const void* q,

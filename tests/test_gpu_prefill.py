@@ -176,3 +176,36 @@ def test_prefill_empty_and_argument_checks():
         kv.paged_prefill_attention(bad, out, g.q, g.k_cache, g.v_cache, g.block_tables,
                                    i32_dev(case.query_start), g.context_lens, 1, g.k_scale,
                                    g.v_scale)
+
+
+DYN_CASES = [
+    # (label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values)
+    ("d128-spread", 160, 32, 8, 128, [900, 77, 5], [900, 40, 0], "fp8_e4m3", 0, "spread"),
+    ("d128-chunk-at-end", 161, 32, 8, 128, [2000], [513], "fp8_e4m3", 0, "spread"),
+    ("d64-window", synth.GPTOSS, 64, 8, 64, [1000, 129], [500, 129], "fp8_e4m3", 128, "spread"),
+    ("d256-e5m2", synth.HD256, 8, 2, 256, [600, 90], [600, 31], "fp8_e5m2", 0, "spread"),
+    ("d128-g1-normal", 162, 8, 8, 128, [400], [130], "fp8_e4m3", 0, "normal"),
+]
+
+
+@pytest.mark.parametrize("dyn", ["per_token", "per_token_head"])
+@pytest.mark.parametrize("label,wl,Hq,Hkv,D,lens,chunks,fmt,window,values", DYN_CASES,
+                         ids=[c[0] for c in DYN_CASES])
+def test_prefill_dynamic_scales(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values, dyn):
+    # every position attended with its own (dynamic, per-token) K and V scales
+    case = synth.prefill_case(wl, Hq, Hkv, D, lens, chunks, shuffle=True, spare_frac=0.25,
+                              values=values)
+    g = GpuLayer(case, window=window, fmt=fmt, dyn=dyn)
+    o = OracleLayer(case, window=window, fmt=fmt, dyn=dyn)
+    assert np.array_equal(host(g.k_cache), o.k_cache)
+    check(gpu_prefill(g, case), oracle_prefill(o, case), o, case, f"prefill-dyn-{dyn}-{label}")
+
+
+@pytest.mark.parametrize("groups", ["1", "2", "3"])
+def test_prefill_dynamic_column_groups(groups, monkeypatch):
+    monkeypatch.setenv("KVFP8_PREFILL_COLUMN_GROUPS", groups)
+    case = synth.prefill_case(163, 16, 4, 128, [700, 333], [700, 200], shuffle=True,
+                              spare_frac=0.2, values="spread")
+    g = GpuLayer(case, dyn="per_token_head")
+    o = OracleLayer(case, dyn="per_token_head")
+    check(gpu_prefill(g, case), oracle_prefill(o, case), o, case, f"prefill-dyn groups={groups}")
