@@ -102,7 +102,8 @@ def lib():
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_double, _u16p, _u8p, _u8p,
                                             _i32p, ctypes.c_int, _i32p, _i32p, _f32p, _f32p,
-                                            _i32p, ctypes.c_int64, _f64p, ctypes.c_int]
+                                            _i32p, ctypes.c_int64, _f64p, ctypes.c_int,
+                                            ctypes.c_int]
         L.orc_softmax_weighted_sum.argtypes = [_f64p, _f64p, ctypes.c_int64,
                                                ctypes.c_int, _f64p]
         att = [ctypes.c_int] * 7 + [ctypes.c_double, _u16p, _u8p, _u8p, _i32p,
@@ -341,11 +342,12 @@ def attention_fp8attn(q, k_cache, v_cache, block_tables, context_lens, num_kv_he
 
 def prefill_attention(q, k_cache, v_cache, block_tables, query_start, context_lens,
                       num_kv_heads, dtype, per_head=True, window=0, sm_scale=0.0, k_scale=None,
-                      v_scale=None, rows=None, nthreads=None) -> np.ndarray:
+                      v_scale=None, rows=None, nthreads=None, fp8attn=False) -> np.ndarray:
     """Chunked-prefill attention: q bf16 [T][Hq][D] holds every sequence's
     new rows (sequence b's rows are query_start[b] .. query_start[b+1]-1, its
     last positions); each row attends causally to its prefix (window-limited).
-    rows: optional indices of the rows to compute. float64 [n_rows][Hq][D]."""
+    rows: optional indices of the rows to compute. fp8attn: the all-FP8
+    arithmetic of attention_fp8attn, row by row. float64 [n_rows][Hq][D]."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     T, Hq, D = q.shape
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -365,5 +367,5 @@ def prefill_attention(q, k_cache, v_cache, block_tables, query_start, context_le
                                 _ptr(vc, _u8p), _ptr(bt, _i32p), bt.shape[1], _ptr(qs, _i32p),
                                 _ptr(lens, _i32p), _ptr(ks, _f32p), _ptr(vs, _f32p),
                                 None if rw is None else _ptr(rw, _i32p), n_rows,
-                                _ptr(out, _f64p), _threads(nthreads))
+                                _ptr(out, _f64p), int(bool(fp8attn)), _threads(nthreads))
     return out

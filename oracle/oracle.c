@@ -974,7 +974,11 @@ typedef struct {
   const int32_t* qs;
   const int32_t* rows;
   int64_t lo, hi;        /* range of (row index, head) pairs */
+  int fp8attn;           /* the all-FP8 arithmetic (fp8attn_sum, q quantised) */
 } pf_job;
+
+static void fp8attn_sum(const double* z, const double* v, int64_t n, int64_t lo, int D,
+                        double* out);
 
 static void* prefill_worker(void* p) {
   pf_job* j = (pf_job*)p;
@@ -994,7 +998,12 @@ static void* prefill_worker(void* p) {
     int64_t pos = a->lens[b] - n + (row - j->qs[b]);
     double* out = a->out + idx * a->D;
     int64_t cnt = gather_at(a, b, i, pos + 1, a->q + (row * a->Hq + i) * a->D, z, v);
-    orc_softmax_weighted_sum(z, v, cnt, a->D, out);
+    if (j->fp8attn) {
+      int64_t lo = (a->window > 0 && pos + 1 > a->window) ? pos + 1 - a->window : 0;
+      fp8attn_sum(z, v, cnt, lo, a->D, out);
+    } else {
+      orc_softmax_weighted_sum(z, v, cnt, a->D, out);
+    }
   }
   free(z);
   free(v);
@@ -1006,10 +1015,11 @@ void orc_prefill_attention(int B, int Hq, int Hkv, int D, int dtype, int per_hea
                            const uint8_t* vc, const int32_t* bt, int max_pages,
                            const int32_t* query_start, const int32_t* lens, const float* ks,
                            const float* vs, const int32_t* rows, int64_t n_rows, double* out,
-                           int nthreads) {
+                           int fp8attn, int nthreads) {
   att_args a;
   fill_args(&a, B, Hq, Hkv, D, dtype, per_head, window, sm_scale, q, kc, vc, bt, max_pages,
             lens, ks, vs, out);
+  a.q8 = fp8attn ? 1 : 0;
   int64_t total = n_rows * Hq;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
@@ -1022,6 +1032,7 @@ void orc_prefill_attention(int B, int Hq, int Hkv, int D, int dtype, int per_hea
     jobs[t].rows = rows;
     jobs[t].lo = total * t / nthreads;
     jobs[t].hi = total * (t + 1) / nthreads;
+    jobs[t].fp8attn = fp8attn;
     pthread_create(&th[t], NULL, prefill_worker, &jobs[t]);
   }
   for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);

@@ -105,3 +105,29 @@ def test_row_subset_matches_the_full_computation():
     full = prefill(case, kc, vc, ks, vs, 33)
     rows = np.array([0, 5, 119, 120, 209], np.int32)
     assert np.array_equal(prefill(case, kc, vc, ks, vs, 33, rows=rows), full[rows])
+
+
+def test_fp8attn_last_row_is_the_decode_fp8attn():
+    # the all-FP8 arithmetic row by row: each sequence's last row is the
+    # (pinned) all-FP8 decode attention
+    case = synth.prefill_case(135, 16, 4, 128, [300, 77, 5], [64, 77, 2], shuffle=True)
+    kc, vc, ks, vs = fill(case)
+    for window in (0, 50):
+        out = oracle.prefill_attention(case.q, kc, vc, case.block_tables, case.query_start,
+                                       case.lens, 4, FP8, True, window, 0.0, ks, vs,
+                                       fp8attn=True)
+        last = case.query_start[1:] - 1
+        dec = oracle.attention_fp8attn(case.q[last], kc, vc, case.block_tables, case.lens, 4,
+                                       FP8, True, window, 0.0, ks, vs)
+        assert np.array_equal(out[last], dec), window
+
+
+def test_fp8attn_zero_query_gives_the_window_mean():
+    # q = 0: s_q = 1, every logit 0, every block's p = e4m3(1) = 1
+    case = synth.prefill_case(136, 8, 2, 64, [100, 37], [30, 37], shuffle=True)
+    kc, vc, ks, vs = fill(case)
+    zero = np.zeros_like(case.q)
+    out = oracle.prefill_attention(zero, kc, vc, case.block_tables, case.query_start, case.lens,
+                                   2, FP8, True, 7, 0.0, ks, vs, fp8attn=True)
+    ref = prefill(case, kc, vc, ks, vs, 7, q=zero)
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
