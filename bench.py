@@ -329,7 +329,7 @@ def sweep(torch, kv, w, contexts, steps, warmup):
 PREFILL_LENGTHS = [1024, 2048, 4096, 8192, 16384, 32768]
 
 
-def prefill_bench(torch, kv, w, lengths, steps, warmup, scales="per_kv_head"):
+def prefill_bench(torch, kv, w, lengths, steps, warmup, scales="per_kv_head", attn="bf16"):
     """Single-request prefill per layer (the TTFT share of one layer): the
     cache write of a whole prompt of L tokens, then chunked-prefill attention
     of all L rows over it, for fp8 and bf16 caches; fits TTFT_layer = a L^2 +
@@ -340,7 +340,8 @@ def prefill_bench(torch, kv, w, lengths, steps, warmup, scales="per_kv_head"):
     B, Hq, Hkv, D = 1, w["Hq"], w["Hkv"], w["D"]
     rows = []
     for dt in ("fp8_e4m3", "bf16"):
-        d = kv.layer_desc(Hq, Hkv, D, dt, scales if dt != "bf16" else "per_kv_head")
+        d = kv.layer_desc(Hq, Hkv, D, dt, scales if dt != "bf16" else "per_kv_head",
+                          attn=attn if dt != "bf16" else "bf16")
         for L in lengths:
             gen = torch.Generator(device=dev)
             gen.manual_seed(L)
@@ -407,7 +408,7 @@ def prefill_bench(torch, kv, w, lengths, steps, warmup, scales="per_kv_head"):
         fits[dt] = dict(a_us_per_token2=a, b_us_per_token=b_, c_us=c_)
     top = [r for r in rows if r["prompt"] == max(lengths)]
     fp8_top = [r for r in top if r["cache"] == "fp8_e4m3"][0]
-    return dict(points=rows, fits=fits, scales=scales,
+    return dict(points=rows, fits=fits, scales=scales, attention=attn,
                 quadratic_ratio_fp8_over_bf16=fits["fp8_e4m3"]["a_us_per_token2"] /
                 fits["bf16"]["a_us_per_token2"],
                 roofline={"bound": "mfma", "kernel": "paged_prefill_kernel (fp8 cache)",
@@ -505,7 +506,7 @@ def main():
     w = WORKLOADS[args.workload]
     if args.prefill_only:
         res = prefill_bench(torch, kv, WORKLOADS["llama8b"], PREFILL_LENGTHS, 5, 2,
-                            scales=args.scales)
+                            scales=args.scales, attn=args.attn)
         print(json.dumps(res))
         return
     ctx = args.context or w["ctx"]

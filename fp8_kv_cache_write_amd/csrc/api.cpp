@@ -381,8 +381,8 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
                                 const float* v_scale, void* stream) {
   int st = check_desc(desc);
   if (st) return st;
-  if (desc->attn_dtype != KVQ_ATTN_BF16) return KVQ_ERR_UNSUPPORTED;
   const bool dyn = dynamic_scales(desc);
+  const bool att8 = desc->attn_dtype == KVQ_ATTN_FP8;   // fp8 caches only (check_desc)
   if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16) return KVQ_ERR_INVALID_ARG;
   if (num_seqs < 0 || max_query_len < 0 || num_pages < 0 || max_pages_per_seq < 0)
     return KVQ_ERR_INVALID_ARG;
@@ -420,7 +420,7 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
   const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
                                          : 1.0f / sqrtf((float)desc->head_dim);
   p.sm_scale_log2 = sm * 1.4426950408889634f;
-  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype, dyn,
+  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype, dyn, att8,
                                       cu_count(), static_cast<hipStream_t>(stream), nullptr,
                                       nullptr);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

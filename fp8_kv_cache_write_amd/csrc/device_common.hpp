@@ -166,6 +166,80 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ---------------------------------------------------------------------------
+// Max over the four lanes c, c+16, c+32, c+48 that hold one column of a
+// 16x16 MFMA tile, with the gfx950 row swaps (VALU, no LDS round trip).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float mfma_col_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// ---------------------------------------------------------------------------
+// All-FP8 attention: one query row as e4m3 codes with s_q = amax / 448 (the
+// 4 lanes of an MFMA column hold the row, NK pieces of 8 values each; the
+// codes go out as 8-byte fp8 MFMA operands in the same order). Returns s_q.
+//   The codes are those of the IEEE quotient x / s_q. With r = 1 / s_q
+// (correctly rounded), q0 = x r, e = fma(-q0, s_q, x), fma(e, r, q0) is that
+// quotient by Markstein's theorem when nothing underflows; checked
+// exhaustively over every bf16 amax and every bf16 x with |x| <= amax, the
+// e4m3 codes of the two agree for all s_q >= 2^-100 (and the quotients
+// themselves wherever they reach 2^-12). A row with a smaller or non-finite
+// scale, or a NaN element, takes the division (the wave as a whole). The
+// hardware conversion (round to nearest even) gives the saturating encoder's
+// codes on [-448, 448] and just beyond, where the quotients lie (checked for
+// every fp32 value there); only the NaN codes differ, hence NaN rows divide.
+// ---------------------------------------------------------------------------
+template <int NK>
+__device__ __forceinline__ float quantize_q_e4m3(const bf16x8 (&q)[NK], uint64_t (&q8)[NK]) {
+  float am = 0.0f;
+  uint32_t mag = 0u;                               // largest |x| bits: NaN > Inf > finite
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf((float)q[s][j]));
+    const uint4 w = __builtin_bit_cast(uint4, q[s]);
+    const uint32_t m4 = max(max(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
+                            max(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
+    mag = max(mag, max(m4 & 0xFFFFu, m4 >> 16));
+  }
+  am = mfma_col_max(am);
+  const float q_scale = am == 0.0f ? 1.0f : am / 448.0f;
+  const bool fast = q_scale >= 0x1p-100f && q_scale <= 0x1p+120f && mag <= 0x7F80u;
+  if (__builtin_amdgcn_ballot_w64(!fast) == 0ull) {
+    const float r = 1.0f / q_scale;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      float qq[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (float)q[s][j];
+        const float q0 = x * r;
+        qq[j] = __builtin_fmaf(__builtin_fmaf(-q0, q_scale, x), r, q0);
+      }
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(qq[0], qq[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(qq[2], qq[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(qq[4], qq[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(qq[6], qq[7], hi, true);
+      q8[s] = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      uint64_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        w |= (uint64_t)e4m3_encode_sat((float)q[s][j] / q_scale) << (8 * j);
+      q8[s] = w;
+    }
+  }
+  return q_scale;
+}
+
 __device__ __forceinline__ bf16x8 bits_to_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }

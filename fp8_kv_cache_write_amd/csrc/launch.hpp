@@ -106,8 +106,9 @@ constexpr int kPrefillWaves = 4;
 
 // cus: compute units of the device (sizes the query blocks). dyn: dynamic
 // per-token scales (p.k_scale / p.v_scale are the pools [P][Hkv][16]).
+// att8: all-FP8 attention (e4m3 q and P, fp8 MFMA); fp8 caches, static scales.
 hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, bool dyn,
-                                int cus, hipStream_t stream, hipEvent_t ev_before,
+                                bool att8, int cus, hipStream_t stream, hipEvent_t ev_before,
                                 hipEvent_t ev_after);
 
 }  // namespace kvfp8

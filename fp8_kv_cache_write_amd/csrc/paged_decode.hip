@@ -213,66 +213,12 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       qop[s] = bits_to_bf16x8(w);
     }
   }
-  // All-FP8 mode: the query row as e4m3 codes with s_q = amax / 448 (the
-  // 4 lanes of a column hold the whole row), packed as 8-byte MFMA operands
-  // in the same order. Run once the first tile's loads are in flight, so it
-  // overlaps their latency.
-  //   The codes are those of the IEEE quotient x / s_q. With r = 1 / s_q
-  // (correctly rounded), q0 = x r, e = fma(-q0, s_q, x), fma(e, r, q0) is
-  // that quotient by Markstein's theorem when nothing underflows; checked
-  // exhaustively over every bf16 amax and every bf16 x with |x| <= amax, the
-  // e4m3 codes of the two agree for all s_q >= 2^-100 (and the quotients
-  // themselves wherever they reach 2^-12). A row with a smaller or non-finite
-  // scale takes the division. The hardware conversion (round to nearest
-  // even) gives the saturating encoder's codes on [-448, 448] and just
-  // beyond, where the quotients lie (checked for every fp32 value there).
+  // All-FP8 mode: the query row as e4m3 codes (quantize_q_e4m3), run once
+  // the first tile's loads are in flight, so it overlaps their latency.
   uint64_t qop8[ATT8 ? NK : 1];
   float q_scale = 1.0f;
   auto quantize_q = [&]() {
-    if constexpr (ATT8) {
-      float am = 0.0f;
-      uint32_t mag = 0u;                               // largest |x| bits: NaN > Inf > finite
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf((float)qop[s][j]));
-        const uint4 w = __builtin_bit_cast(uint4, qop[s]);
-        const uint32_t m4 = max(max(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
-                                max(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
-        mag = max(mag, max(m4 & 0xFFFFu, m4 >> 16));
-      }
-      am = col_max(am);
-      q_scale = am == 0.0f ? 1.0f : am / 448.0f;
-      // a NaN element takes the division path too (the encoders' NaN codes differ)
-      const bool fast = q_scale >= 0x1p-100f && q_scale <= 0x1p+120f && mag <= 0x7F80u;
-      if (__builtin_amdgcn_ballot_w64(!fast) == 0ull) {
-        const float r = 1.0f / q_scale;
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-          float qq[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float x = (float)qop[s][j];
-            const float q0 = x * r;
-            qq[j] = __builtin_fmaf(__builtin_fmaf(-q0, q_scale, x), r, q0);
-          }
-          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(qq[0], qq[1], 0, false);
-          lo = __builtin_amdgcn_cvt_pk_fp8_f32(qq[2], qq[3], lo, true);
-          int hi = __builtin_amdgcn_cvt_pk_fp8_f32(qq[4], qq[5], 0, false);
-          hi = __builtin_amdgcn_cvt_pk_fp8_f32(qq[6], qq[7], hi, true);
-          qop8[s] = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-          uint64_t w = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            w |= (uint64_t)e4m3_encode_sat((float)qop[s][j] / q_scale) << (8 * j);
-          qop8[s] = w;
-        }
-      }
-    }
+    if constexpr (ATT8) q_scale = quantize_q_e4m3<NK>(qop, qop8);
   };
   // static scales: one per head or tensor; dynamic ones are per position
   // (the pools p.k_scale / p.v_scale [page][head][row]), applied per row

@@ -59,7 +59,7 @@ __device__ __forceinline__ float col_sum(float x) {
 
 }  // namespace
 
-template <int D, int FMT, int NCG, bool DYN>
+template <int D, int FMT, int NCG, bool DYN, bool ATT8>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     const PrefillParams p) {
   constexpr int NW = kPrefillWaves;
@@ -74,6 +74,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   constexpr int TILE = KV_BYTES + (DYN ? 2 * 2 * kPage * 4 : 0);
   constexpr int LPT = 2 * 2 * NI;       // 1 KiB loads per tile
   static_assert(!DYN || FP8, "dynamic scales belong to fp8 caches");
+  static_assert(!ATT8 || (FP8 && !DYN), "all-FP8 attention: fp8 caches, static scales");
   static_assert(LPT % NW == 0, "every wave stages the same number of chunks");
   static_assert(2 * TILE <= 64 * 1024, "direct-to-LDS loads address the first 64 KiB");
 
@@ -141,6 +142,14 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         qop[cg][s] = bits_to_bf16x8(w);
       }
     c_log2 = -c_log2;
+  }
+  // All-FP8 mode: every column's query row as e4m3 codes, s_q per column
+  uint64_t qop8[ATT8 ? NCG : 1][ATT8 ? NK : 1];
+  float cq[NCG];                    // logit scale of each column group's column
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    cq[cg] = c_log2;
+    if constexpr (ATT8) cq[cg] = quantize_q_e4m3<NK>(qop[cg], qop8[cg]) * c_log2;
   }
 
   // ---- key range of the work-group: [key_lo, key_hi] ----------------------
@@ -263,6 +272,22 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     for (int s = 0; s < NK; ++s) {
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
+        if constexpr (ATT8) {
+          // the K codes themselves are the operand (fp8 x fp8 MFMA)
+          const uint4 w = tk[pg][s / 2];
+          const long kop8 = (long)((s % 2 == 0) ? (((uint64_t)w.y << 32) | w.x)
+                                                : (((uint64_t)w.w << 32) | w.z));
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            if constexpr (FMT == kFmtE5M2)
+              sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(
+                  kop8, (long)qop8[cg][s], sacc[cg][pg], 0, 0, 0);
+            else
+              sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                  kop8, (long)qop8[cg][s], sacc[cg][pg], 0, 0, 0);
+          }
+          continue;
+        }
         bf16x8 kop;
         if constexpr (FP8) {
           const uint4 w = tk[pg][s / 2];
@@ -323,16 +348,21 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) csk[pg][e] = c_log2 * sk[pg][e];
     }
-    const float cexp = DYN ? 1.0f : c_log2;
     bf16x8 pop[NCG];
+    uint64_t pop8[ATT8 ? NCG : 1];
+    float fb[ATT8 ? NCG : 1];          // all-FP8: weight 2^(tile max - running max)
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
+      // static scales: raw logits, the scale applied inside the exponent;
+      // all-FP8: logits scaled here (s_q differs per column)
+      const float cexp = (DYN || ATT8) ? 1.0f : c_log2;
       float x[2][4];
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          x[pg][e] = DYN ? sacc[cg][pg][e] * csk[pg][e] : sacc[cg][pg][e];
+          x[pg][e] = DYN ? sacc[cg][pg][e] * csk[pg][e]
+                         : (ATT8 ? sacc[cg][pg][e] * cq[cg] : sacc[cg][pg][e]);
       if (need_mask) {
         const int lo_c = p.window > 0 ? qpos[cg] + 1 - p.window : 0;
 #pragma unroll
@@ -364,6 +394,30 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         m_run[cg] = m_new;
       }
       const float m_use = m_run[cg] == -INFINITY ? 0.0f : m_run[cg];
+      if constexpr (ATT8) {
+        // P of this 32-position block as e4m3 relative to the block's own max
+        // (tmax); the normaliser takes the FP32 values
+        const bool live = tmax != -INFINITY;
+        const float mb = live ? tmax : 0.0f;
+        fb[cg] = live ? __builtin_amdgcn_exp2f(tmax - m_use) : 0.0f;
+        float ps = 0.0f;
+        uint32_t pw[2];
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          float pe[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pe[e] = __builtin_amdgcn_exp2f(x[pg][e] - mb);
+            ps += pe[e];
+          }
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(pe[0], pe[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(pe[2], pe[3], w, true);
+          pw[pg] = (uint32_t)w;
+        }
+        pop8[cg] = ((uint64_t)pw[1] << 32) | pw[0];
+        l_run[cg] += fb[cg] * ps;
+        continue;
+      }
       float ps = 0.0f;
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
@@ -387,6 +441,33 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     }
 
     // ---- P*V: one k=32 MFMA per 16-dim block and column group --------------
+    if constexpr (ATT8) {
+      // fp8 x fp8 products of the block, each added into the FP32 sum with
+      // its weight fb (level 1: the MFMA over 32 positions; level 2: FP32)
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const int i = blk / 4, ep = blk % 4;
+        const uint4 wa = tv[0][i], wb = tv[1][i];
+        const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
+        const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
+        const long vop = (long)(((uint64_t)db << 32) | da);
+        f32x4 tpv[NCG];
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          if constexpr (FMT == kFmtE5M2)
+            tpv[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(
+                vop, (long)pop8[cg], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          else
+            tpv[cg] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                vop, (long)pop8[cg], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[cg][blk][e] += fb[cg] * tpv[cg][e];
+      }
+      continue;
+    }
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
       uint4 vb;
@@ -433,16 +514,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 
 namespace {
 
-template <int D, int FMT, int NCG, bool DYN>
+template <int D, int FMT, int NCG, bool DYN, bool ATT8>
 hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   if (ev_before && ev_after) {
-    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, DYN>), dim3((unsigned)grid),
+    hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, DYN, ATT8>), dim3((unsigned)grid),
                           dim3(kPrefillWaves * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, DYN>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, DYN, ATT8>), dim3((unsigned)grid),
                        dim3(kPrefillWaves * kWave), 0, stream, p);
   }
   return hipGetLastError();
@@ -451,7 +532,7 @@ hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stre
 // Column groups per wave: the most the registers allow (each shares the
 // tile's fp8 -> bf16 expansion and LDS reads), fewer when the grid would
 // leave compute units idle (short prompts): at least two work-groups per CU.
-template <int D, int FMT, bool DYN>
+template <int D, int FMT, bool DYN, bool ATT8>
 hipError_t launch_prefill_typed(PrefillParams p, int cus, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NCG_MAX = D >= 256 ? 1 : (D == 128 && FMT == kFmtBf16 ? 2 : 3);
@@ -470,34 +551,44 @@ hipError_t launch_prefill_typed(PrefillParams p, int cus, hipStream_t stream,
   if (total == 0) return hipSuccess;
   if constexpr (NCG_MAX >= 3) {
     if (ncg == 3)
-      return launch_prefill_shape<D, FMT, 3, DYN>(p, total, stream, ev_before, ev_after);
+      return launch_prefill_shape<D, FMT, 3, DYN, ATT8>(p, total, stream, ev_before, ev_after);
   }
   if constexpr (NCG_MAX >= 2) {
     if (ncg == 2)
-      return launch_prefill_shape<D, FMT, 2, DYN>(p, total, stream, ev_before, ev_after);
+      return launch_prefill_shape<D, FMT, 2, DYN, ATT8>(p, total, stream, ev_before, ev_after);
   }
-  return launch_prefill_shape<D, FMT, 1, DYN>(p, total, stream, ev_before, ev_after);
+  return launch_prefill_shape<D, FMT, 1, DYN, ATT8>(p, total, stream, ev_before, ev_after);
 }
 
 template <int D>
-hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, bool dyn, int cus,
+hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, bool dyn, bool att8, int cus,
                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
-  if (dyn) {
+  if (dyn && att8) return hipErrorInvalidValue;
+  if (dyn || att8) {
     switch (fmt) {
       case kFmtE4M3:
-        return launch_prefill_typed<D, kFmtE4M3, true>(p, cus, stream, ev_before, ev_after);
+        return dyn ? launch_prefill_typed<D, kFmtE4M3, true, false>(p, cus, stream, ev_before,
+                                                                     ev_after)
+                   : launch_prefill_typed<D, kFmtE4M3, false, true>(p, cus, stream, ev_before,
+                                                                     ev_after);
       case kFmtE5M2:
-        return launch_prefill_typed<D, kFmtE5M2, true>(p, cus, stream, ev_before, ev_after);
+        return dyn ? launch_prefill_typed<D, kFmtE5M2, true, false>(p, cus, stream, ev_before,
+                                                                     ev_after)
+                   : launch_prefill_typed<D, kFmtE5M2, false, true>(p, cus, stream, ev_before,
+                                                                     ev_after);
       default: return hipErrorInvalidValue;
     }
   }
   switch (fmt) {
     case kFmtBf16:
-      return launch_prefill_typed<D, kFmtBf16, false>(p, cus, stream, ev_before, ev_after);
+      return launch_prefill_typed<D, kFmtBf16, false, false>(p, cus, stream, ev_before,
+                                                             ev_after);
     case kFmtE4M3:
-      return launch_prefill_typed<D, kFmtE4M3, false>(p, cus, stream, ev_before, ev_after);
+      return launch_prefill_typed<D, kFmtE4M3, false, false>(p, cus, stream, ev_before,
+                                                             ev_after);
     case kFmtE5M2:
-      return launch_prefill_typed<D, kFmtE5M2, false>(p, cus, stream, ev_before, ev_after);
+      return launch_prefill_typed<D, kFmtE5M2, false, false>(p, cus, stream, ev_before,
+                                                             ev_after);
     default: return hipErrorInvalidValue;
   }
 }
@@ -505,13 +596,15 @@ hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, bool dyn, int cus
 }  // namespace
 
 hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, bool dyn,
-                                int cus, hipStream_t stream, hipEvent_t ev_before,
+                                bool att8, int cus, hipStream_t stream, hipEvent_t ev_before,
                                 hipEvent_t ev_after) {
   if (p.group < 1 || p.group > 16) return hipErrorInvalidValue;
   switch (head_dim) {
-    case 64: return launch_prefill_dim<64>(p, fmt, dyn, cus, stream, ev_before, ev_after);
-    case 128: return launch_prefill_dim<128>(p, fmt, dyn, cus, stream, ev_before, ev_after);
-    case 256: return launch_prefill_dim<256>(p, fmt, dyn, cus, stream, ev_before, ev_after);
+    case 64: return launch_prefill_dim<64>(p, fmt, dyn, att8, cus, stream, ev_before, ev_after);
+    case 128:
+      return launch_prefill_dim<128>(p, fmt, dyn, att8, cus, stream, ev_before, ev_after);
+    case 256:
+      return launch_prefill_dim<256>(p, fmt, dyn, att8, cus, stream, ev_before, ev_after);
     default: return hipErrorInvalidValue;
   }
 }

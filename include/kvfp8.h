@@ -315,8 +315,11 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new,
  *     out[row][i][d] = sum_t softmax_t(z) vh[t][d],
  *     z_t = sm_scale * sum_d q[row][i][d] kh[t][d],  t in [lo, pos],
  * with kh, vh as for kvq_paged_decode_attention. Probabilities enter the P*V
- * product rounded to bf16; accumulation is FP32. A row whose position is
- * below 0 (n_b > context_lens[b]) gives zeros.
+ * product rounded to bf16; accumulation is FP32. With KVQ_ATTN_FP8 the
+ * arithmetic is that of the all-FP8 decode mode, row by row (e4m3 query per
+ * row, P per aligned 32-position block relative to the block's largest
+ * logit). A row whose position is below 0 (n_b > context_lens[b]) gives
+ * zeros.
  *   out           device [T][Hq][D], fp32 or bf16 per out_dtype; T =
  *                 query_start[num_seqs]
  *   q             device bf16 [T][Hq][D]
@@ -327,8 +330,8 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new,
  *   max_query_len host int >= every n_b (sizes the grid; rows past it are
  *                 not computed)
  *   other arguments as for kvq_paged_decode_attention (static scales or the
- *   pools of dynamic per-token scales; KVQ_ATTN_FP8 gives
- *   KVQ_ERR_UNSUPPORTED). No workspace.
+ *   pools of dynamic per-token scales; KVQ_ATTN_FP8 with static scales). No
+ *   workspace.
  */
 int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out,
                                 int32_t out_dtype, const void* q,

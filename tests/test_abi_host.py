@@ -225,6 +225,6 @@ def test_prefill_argument_checks(L):
     assert pf(d, B=-1) == INVALID
     assert pf(d, B=0) == OK and pf(d, mq=0) == OK   # nothing to do
     assert pf(d, P=0) == INVALID
-    assert pf(kv.layer_desc(32, 8, 128, attn="fp8")) == UNSUPPORTED
+    assert pf(kv.layer_desc(32, 8, 128, "bf16", attn="fp8")) == UNSUPPORTED
     assert pf(kv.layer_desc(32, 8, 128, scale_mode="per_token"), ks=FAKE_ODD) == INVALID
     assert pf(kv.layer_desc(32, 8, 96)) == UNSUPPORTED

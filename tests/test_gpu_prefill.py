@@ -49,7 +49,8 @@ def gpu_prefill(g, case, out_dtype=torch.float32):
 def oracle_prefill(o, case, rows=None):
     return oracle.prefill_attention(case.q, o.k_cache, o.v_cache, case.block_tables,
                                     case.query_start, case.lens, case.num_kv_heads, o.fmt,
-                                    o.per_head, o.window, o.sm_scale, o.ks, o.vs, rows)
+                                    o.per_head, o.window, o.sm_scale, o.ks, o.vs, rows,
+                                    fp8attn=o.attn == "fp8")
 
 
 def vmax(o, case):
@@ -171,7 +172,7 @@ def test_prefill_empty_and_argument_checks():
     kv.paged_prefill_attention(g.desc, out, g.q, g.k_cache, g.v_cache, g.block_tables,
                                i32_dev(case.query_start), g.context_lens, 0, g.k_scale,
                                g.v_scale)
-    bad = kv.layer_desc(8, 2, 64, attn="fp8")
+    bad = kv.layer_desc(8, 2, 64, "bf16", attn="fp8")      # FP8 attention needs an fp8 cache
     with pytest.raises(kv.Kvfp8Error):
         kv.paged_prefill_attention(bad, out, g.q, g.k_cache, g.v_cache, g.block_tables,
                                    i32_dev(case.query_start), g.context_lens, 1, g.k_scale,
@@ -209,3 +210,96 @@ def test_prefill_dynamic_column_groups(groups, monkeypatch):
     g = GpuLayer(case, dyn="per_token_head")
     o = OracleLayer(case, dyn="per_token_head")
     check(gpu_prefill(g, case), oracle_prefill(o, case), o, case, f"prefill-dyn groups={groups}")
+
+
+def keys_per_row(case, window):
+    """Number of attended positions of every query row."""
+    n = []
+    for b, L in enumerate(case.lens):
+        m = case.query_start[b + 1] - case.query_start[b]
+        for j in range(m):
+            pos = L - m + j
+            n.append(min(pos + 1, window) if window else pos + 1)
+    return np.array(n)
+
+
+def check_fp8attn(out, ref, case, window, label, outliers=False):
+    """All-FP8 arithmetic: the oracle quantises q and P by the same rules, so
+    the two differ where FP32 logit rounding (the oracle works in float64)
+    moves a probability across an e4m3 rounding boundary: one code step, at
+    most 1/8 of that p (p <= 1, and the normaliser is >= 1), so a row moves
+    by at most 1/8 of twice its largest |v| per flip. Over a long window of
+    unit-scale values a flip is diluted below the gate; a row that attends
+    fewer than one 32-position block, or a sharp softmax over outlier values,
+    is not. So: the mean gate (scaled by the output's magnitude) everywhere,
+    the max gate on rows of at least 32 positions of unit-scale workloads,
+    and the flip bound (two flips: 1/4 of the largest attended |v|) on every
+    row."""
+    g = host(out.float()).astype(np.float64)
+    d = np.abs(g - ref)
+    mean = float(d.mean())
+    scale = max(1.0, float(np.abs(ref).max()))
+    nk = keys_per_row(case, window)
+    long_rows = nk >= 32
+    mx_long = float(d[long_rows].max()) if long_rows.any() else 0.0
+    mx_short = float(d[~long_rows].max()) if (~long_rows).any() else 0.0
+    say(f"[{label}] max_abs={mx_long:.3e} (rows >= 32 positions) {mx_short:.3e} (shorter) "
+        f"mean_abs={mean:.3e} (output scale {scale:.2f})")
+    assert np.all(np.isfinite(g)), label
+    assert mean <= GATE_MEAN_ABS * scale, (label, mean)
+    if not outliers:
+        assert mx_long <= GATE_MAX_ABS * scale, (label, mx_long)
+    assert max(mx_long, mx_short) <= 0.25 * vmax(None, case), (label, mx_long, mx_short)
+
+
+FP8ATTN_CASES = [
+    # (label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values)
+    ("tiny", synth.TINY, 4, 2, 64, [256], [256], "fp8_e4m3", 0, "tiny"),
+    ("d128-ragged", 170, 32, 8, 128, [900, 77, 5], [900, 40, 0], "fp8_e4m3", 0, "normal"),
+    ("d128-chunk-at-end", 171, 32, 8, 128, [2000], [513], "fp8_e4m3", 0, "normal"),
+    ("g16", 172, 64, 4, 128, [600], [600], "fp8_e4m3", 0, "normal"),
+    ("d64-window", synth.GPTOSS, 64, 8, 64, [1000, 129], [500, 129], "fp8_e4m3", 128, "normal"),
+    ("d256-e5m2", synth.HD256, 8, 2, 256, [600, 90], [600, 31], "fp8_e5m2", 0, "normal"),
+    ("g8-drift", 173, 64, 8, 128, [700], [700], "fp8_e4m3", 0, "drift"),
+]
+
+
+@pytest.mark.parametrize("label,wl,Hq,Hkv,D,lens,chunks,fmt,window,values", FP8ATTN_CASES,
+                         ids=[c[0] for c in FP8ATTN_CASES])
+def test_prefill_fp8_attention(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values):
+    case = synth.prefill_case(wl, Hq, Hkv, D, lens, chunks, shuffle=True, spare_frac=0.25,
+                              values=values)
+    g = GpuLayer(case, window=window, fmt=fmt, attn="fp8")
+    o = OracleLayer(case, window=window, fmt=fmt, attn="fp8")
+    check_fp8attn(gpu_prefill(g, case), oracle_prefill(o, case), case, window,
+                  f"prefill-fp8attn-{label}", outliers=values == "tiny")
+
+
+@pytest.mark.parametrize("groups", ["1", "2", "3"])
+def test_prefill_fp8_attention_column_groups(groups, monkeypatch):
+    monkeypatch.setenv("KVFP8_PREFILL_COLUMN_GROUPS", groups)
+    case = synth.prefill_case(174, 16, 4, 128, [700, 333], [700, 200], shuffle=True,
+                              spare_frac=0.2)
+    g = GpuLayer(case, attn="fp8")
+    o = OracleLayer(case, attn="fp8")
+    check_fp8attn(gpu_prefill(g, case), oracle_prefill(o, case), case, 0,
+                  f"prefill-fp8attn groups={groups}")
+
+
+def test_prefill_fp8_attention_last_row_is_the_decode_kernels():
+    # same codes, same blocks, same logit arithmetic: the last row of each
+    # chunk and the all-FP8 decode kernel differ only in FP32 summation order
+    case = synth.prefill_case(175, 32, 8, 128, [3000, 1000], [64, 1000], shuffle=True)
+    g = GpuLayer(case, attn="fp8")
+    pf = host(gpu_prefill(g, case))
+    last = case.query_start[1:] - 1
+    q_last = torch.from_numpy(np.ascontiguousarray(case.q[last]).view(np.int16)).to(dev()) \
+        .view(torch.bfloat16)
+    out = torch.empty((2, 32, 128), dtype=torch.float32, device=dev())
+    ws = kv.alloc_workspace(g.desc, 2, int(case.lens.max()))
+    kv.paged_decode_attention(g.desc, out, q_last, g.k_cache, g.v_cache, g.block_tables,
+                              g.context_lens, int(case.lens.max()), g.k_scale, g.v_scale, ws)
+    torch.cuda.synchronize()
+    d = np.abs(pf[last] - host(out)).max()
+    say(f"[prefill vs decode, all-FP8] max_abs={d:.3e}")
+    assert d <= 1e-5 * max(1.0, float(np.abs(host(out)).max())), d
