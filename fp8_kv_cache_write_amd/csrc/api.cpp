@@ -156,10 +156,15 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
     p.off_l = p.off_o = p.bytes = 0;
     return p;
   }
+  // Slots: (m, l, o[D]) per (sequence, query head, partition). The reduce
+  // kernel reads whole chunks of up to kReduceChunk partitions and weights
+  // the slots past a row's partitions with 0, so the o region ends with a
+  // chunk of slack that keeps those reads inside the workspace (the m and l
+  // regions are followed by the next region).
   const size_t rows = (size_t)num_seqs * d->num_q_heads * p.num_parts;
   p.off_l = round_up(rows * sizeof(float), 256);
   p.off_o = p.off_l + round_up(rows * sizeof(float), 256);
-  p.bytes = p.off_o + round_up(rows * d->head_dim * sizeof(float), 256);
+  p.bytes = p.off_o + round_up((rows + kReduceChunk) * d->head_dim * sizeof(float), 256);
   return p;
 }
 

@@ -56,6 +56,9 @@ struct DecodeParams {
 // Waves per work-group of the split kernel.
 constexpr int kSplitWaves = 4;
 
+// Partitions the reduce kernel reads per chunk, at most (one per lane).
+constexpr int kReduceChunk = 64;
+
 // fused = true: the split kernel also writes k_new / v_new into the caches at
 // position L-1 of every sequence (p.k_cache / p.v_cache must be writable).
 // slots: split-kernel tile shape, 1 = LDS-staged tiles, 0 = register tiles.

@@ -952,87 +952,104 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 // over every planned partition: the split kernel leaves an empty partial
 // (m = -inf, l = 0) in the slots of partitions a sequence does not reach, so
 // the merge needs neither the context length nor a second round trip. Each
-// wave owns 64 dims of one (sequence, query head) and needs no barrier: lane
-// j reads m_j and l_j, lane d the partial outputs o_j[d] of the first 64
-// partitions, all issued before the first wait; the weight of partition j
-// comes from lane j through readlane, and a partition of weight 0 is skipped
-// (its o was never written). Partitions past 64 are read in further chunks.
-__device__ __forceinline__ float wave_max_all(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off /= 2) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+// wave owns 64 dims of one (sequence, query head) and needs no barrier. The
+// partitions are taken NPC at a time (one chunk for up to 64 partitions):
+// lane j reads m_j and l_j, then lane d the partial outputs o_j[d] of the
+// chunk, all issued before the first wait. The wave max and sum run on DPP row
+// rotations and the gfx950 row swaps (no LDS round trip); the weights w_j
+// reach every lane as broadcast LDS reads, four at a time. A partition of
+// weight 0 adds nothing (its o may never have been written), and a later
+// chunk with a larger max rescales what the earlier ones summed.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum_all(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off /= 2) x += __shfl_xor(x, off);
-  return x;
+template <bool MAX>
+__device__ __forceinline__ float wave_all(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  x = op(x, dpp_mov<0x128>(x));           // row_ror:8
+  x = op(x, dpp_mov<0x124>(x));           // row_ror:4
+  x = op(x, dpp_mov<0x122>(x));           // row_ror:2
+  x = op(x, dpp_mov<0x121>(x));           // row_ror:1 -> every lane holds its row's result
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = op(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
-__device__ __forceinline__ float lane_value(float x, int j) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
-}
-
-template <int D>
+template <int D, int NPC>
 __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodeParams p) {
+  static_assert(NPC % 4 == 0 && NPC <= kWave, "a chunk is at most one wave of partitions");
+  __shared__ __align__(16) float sw[D / kWave][NPC];
   const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
   const int d = threadIdx.x;              // D threads: wave w owns dims 64w..64w+63
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int h = hq / p.group;
   const int np = p.num_parts;
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
-  const float* ms = p.ws_m + row * np;
-  const float* ls = p.ws_l + row * np;
-  const float* os = p.ws_o + row * np * D + d;
+  const float* mrow = p.ws_m + row * np;
+  const float* lrow = p.ws_l + row * np;
+  const float* orow = p.ws_o + row * np * D;
   const float vs = p.v_scale ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
 
-  // ---- every load of the first chunk up front (indexes clamped in range) ----
-  float ov[kWave];
-#pragma unroll
-  for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(u, np - 1) * D];
-  const float m0 = lane < np ? ms[lane] : -INFINITY;
-  const float l0 = lane < np ? ls[lane] : 0.0f;
-
-  // ---- M and the normaliser ---------------------------------------------------
-  float m = m0;
-  bool nan_m = m0 != m0;                  // a NaN partial makes the row NaN
-  for (int j = kWave + lane; j < np; j += kWave) {
-    const float mj = ms[j];
-    nan_m |= mj != mj;
-    m = fmaxf(m, mj);
-  }
-  const bool any_nan = __builtin_amdgcn_ballot_w64(nan_m) != 0ull;
-  const float M = wave_max_all(m);
-  const bool empty = (M == -INFINITY);
-  const float w0 = empty ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);   // 0 for m0 = -inf
-  float lsum = w0 * l0;
-  for (int j = kWave + lane; j < np; j += kWave)
-    lsum += (empty ? 0.0f : __builtin_amdgcn_exp2f(ms[j] - M)) * ls[j];
-  const float L = wave_sum_all(lsum);
-
-  // ---- weighted sum of the partial outputs (4 independent chains) -------------
+  float M = -INFINITY, L = 0.0f;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  bool any_nan = false;                   // a NaN partial makes the row NaN
+  for (int base = 0; base < np; base += NPC) {
+    // Every load of the chunk, unconditionally: the workspace ends with a
+    // chunk's worth of slack, and slots past this row's partitions (other
+    // rows' partials, slack) get weight 0 below.
+    const float mv = mrow[base + lane];
+    const float lv = lrow[base + lane];
+    float ov[NPC];
 #pragma unroll
-  for (int u = 0; u < kWave; ++u) {
-    const float wu = lane_value(w0, u);
-    acc[u % 4] += wu != 0.0f ? wu * ov[u] : 0.0f;
-  }
-  for (int base = kWave; base < np; base += kWave) {
-    const int j = base + lane;
-    const float wl = (j < np && !empty) ? __builtin_amdgcn_exp2f(ms[j] - M) : 0.0f;
+    for (int u = 0; u < NPC; ++u) ov[u] = orow[(int64_t)(base + u) * D + d];
+    const bool in = lane < NPC && base + lane < np;
+    const float mj = in ? mv : -INFINITY;
+    const float lj = in ? lv : 0.0f;
+    any_nan |= __builtin_amdgcn_ballot_w64(mj != mj) != 0ull;
+    const float Mn = fmaxf(M, wave_all<true>(mj));
+    // weights relative to Mn (to 0 while nothing is attended: all weights 0);
+    // what earlier chunks summed is rescaled to it
+    const float Mr = Mn == -INFINITY ? 0.0f : Mn;
+    const float r = __builtin_amdgcn_exp2f(M - Mr);     // 0 while M = -inf
 #pragma unroll
-    for (int u = 0; u < kWave; ++u) ov[u] = os[(int64_t)min(base + u, np - 1) * D];
+    for (int e = 0; e < 4; ++e) acc[e] *= r;
+    L *= r;
+    M = Mn;
+    const float wj = in ? __builtin_amdgcn_exp2f(mj - Mr) : 0.0f;   // 0 for m_j = -inf
+    L += wave_all<false>(wj * lj);
+    if (lane < NPC) sw[wave][lane] = wj;
 #pragma unroll
-    for (int u = 0; u < kWave; ++u) {
-      const float wu = lane_value(wl, u);
-      acc[u % 4] += wu != 0.0f ? wu * ov[u] : 0.0f;
+    for (int u = 0; u < NPC; u += 4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&sw[wave][u]);
+      const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w[e], w[e] != 0.0f ? ov[u + e] : 0.0f, acc[e]);
     }
   }
   const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   const float r = any_nan ? __builtin_nanf("") : (L > 0.0f ? o / L * vs : 0.0f);
   if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
   else reinterpret_cast<float*>(p.out)[row * D + d] = r;
+}
+
+template <int D>
+static void launch_reduce(const DecodeParams& pr, int num_seqs, hipStream_t stream) {
+  const dim3 grid((unsigned)pr.num_q_heads, (unsigned)num_seqs);
+  static_assert(kReduceChunk == 64, "the largest chunk below is the workspace's slack");
+  if (pr.num_parts <= 16)
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 16>), grid, dim3(D), 0, stream, pr);
+  else if (pr.num_parts <= 32)
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 32>), grid, dim3(D), 0, stream, pr);
+  else
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 64>), grid, dim3(D), 0, stream, pr);
 }
 
 // Arithmetic modes of the split kernel.
@@ -1059,9 +1076,7 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
   DecodeParams pr = p;
   // the reduce kernel applies a static V scale only (dynamic ones are in P)
   if (FMT == kFmtBf16 || DYN) pr.v_scale = nullptr;
-  hipLaunchKernelGGL((paged_decode_reduce_kernel<D>),
-                     dim3((unsigned)p.num_q_heads, (unsigned)num_seqs), dim3(D), 0,
-                     stream, pr);
+  launch_reduce<D>(pr, num_seqs, stream);
   return hipGetLastError();
 }
 

@@ -260,6 +260,42 @@ def test_attention_forced_split_partitions(ppw, monkeypatch):
         check_attention(g, o, label)
 
 
+REDUCE_CASES = [
+    # (longest context, other lengths): with 1 page per wave a partition is 4
+    # pages, so these give 16, 17, 32, 33, 64, 65 and 130 partitions: every
+    # chunk size of the reduce kernel, its edges, and two and three chunks
+    (1024, [3, 0]), (1040, [700]), (2048, [1]), (2064, [1000]), (4096, [64]),
+    (4112, [17]), (8320, [4111]),
+]
+
+
+@pytest.mark.parametrize("longest,others", REDUCE_CASES, ids=[str(c[0]) for c in REDUCE_CASES])
+def test_reduce_chunks(longest, others, monkeypatch):
+    # The largest logit of sequence 0 sits near its end (a key equal to the
+    # first query of each group), so a later chunk raises the running max and
+    # rescales what the earlier ones summed; sequence 1 has it at position 10,
+    # so the later chunks add with small weights. Shorter sequences leave
+    # partitions that hold only an empty partial.
+    monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", "1")
+    lens = [longest] + others
+    case = synth.decode_case(75, 16, 4, 128, lens, shuffle=True, spare_frac=0.1)
+    k = synth.bits_to_f32(case.k_new).copy()
+    q = synth.bits_to_f32(case.q)
+    for b, pos in ((0, longest - 30), (1, 10)):
+        if b < len(lens) and pos < lens[b]:
+            r = int(np.flatnonzero((case.seq_of_row == b) & (case.pos_of_row == pos))[0])
+            for h in range(4):
+                k[r, h] = q[b, 4 * h]
+    case.k_new = synth.bf16_bits(k)
+    for fp8 in (True, False):
+        label = f"reduce chunks L={longest} fp8={fp8}"
+        say(label)
+        g = GpuLayer(case, fp8=fp8)
+        o = OracleLayer(case, fp8=fp8)
+        check_attention(g, o, label)
+        check_attention(g, o, label + "-bf16out", out_dtype=torch.bfloat16)
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("fp8", [True, False])
 def test_attention_boundary_lengths(D, fp8):
