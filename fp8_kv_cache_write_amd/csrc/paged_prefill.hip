@@ -41,14 +41,19 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 constexpr float kLazyLog2 = 8.0f;   // running max raised only past +8 (P <= 256)
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, work-groups dealt round-robin
 
+// IEEE maximum (a NaN operand gives NaN): one v_maximum3_f32, with none of
+// the input quieting that fmaxf needs on operands of unknown origin. A NaN
+// logit makes its row NaN either way (its p is NaN).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over the four lanes c, c+16, c+32, c+48 that hold one MFMA column.
 __device__ __forceinline__ float col_max(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float col_sum(float x) {
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[pg][e]);
+        for (int e = 0; e < 4; ++e) tmax = vmax(tmax, x[pg][e]);
       tmax = col_max(tmax) * cexp;
       const bool grow = tmax > m_run[cg] + kLazyLog2;
       if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         const bool live = tmax != -INFINITY;
         const float mb = live ? tmax : 0.0f;
         fb[cg] = live ? __builtin_amdgcn_exp2f(tmax - m_use) : 0.0f;
-        float ps = 0.0f;
+        float ps = -0.0f;
         uint32_t pw[2];
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         l_run[cg] += fb[cg] * ps;
         continue;
       }
-      float ps = 0.0f;
+      float ps = -0.0f;                    // -0 + p is p: no add for the first term
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
         float pe[4];

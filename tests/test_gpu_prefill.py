@@ -165,6 +165,40 @@ def test_prefill_llama8b_32k_chunk_sampled():
     check(torch.from_numpy(out[rows]), ref, o, case, "prefill-8B-32k-chunk-sampled")
 
 
+@pytest.mark.parametrize("fmt,attn", [("fp8_e4m3", "bf16"), ("bf16", "bf16"),
+                                      ("fp8_e4m3", "fp8")])
+def test_prefill_nan_rows(fmt, attn):
+    # A NaN query element makes its (row, head) NaN; a NaN key element (code
+    # 0x7F in an fp8 cache, scales fixed so the NaN does not reach them)
+    # makes NaN exactly the rows that attend its position, for the query
+    # heads of its KV head; every other row matches the oracle.
+    case = synth.prefill_case(154, 16, 4, 128, [300, 200], [300, 100], shuffle=True)
+    q = synth.bits_to_f32(case.q).copy()
+    q[5, 3, 7] = np.nan                                   # sequence 0, row 5, head 3
+    case.q = synth.bf16_bits(q)
+    k = synth.bits_to_f32(case.k_new).copy()
+    r = int(np.flatnonzero((case.seq_of_row == 1) & (case.pos_of_row == 150))[0])
+    k[r, 2, 11] = np.nan                                  # sequence 1, position 150, KV head 2
+    case.k_new = synth.bf16_bits(k)
+    scales = ([0.05] * 4, [0.05] * 4)
+    g = GpuLayer(case, fmt=fmt, attn=attn, scales=scales)
+    o = OracleLayer(case, fmt=fmt, attn=attn, scales=scales)
+    out = host(gpu_prefill(g, case)).astype(np.float64)
+    ref = oracle_prefill(o, case)
+    want = {(5, 3)} | {(300 + j, h) for j in range(100) for h in range(8, 12) if 100 + j >= 150}
+    nan_g = np.isnan(out).all(-1)
+    assert not np.any(np.isnan(out) & ~nan_g[..., None]), "partly NaN rows"
+    assert set(map(tuple, np.argwhere(nan_g).tolist())) == want
+    assert np.array_equal(nan_g, np.isnan(ref).all(-1))
+    fin = ~nan_g
+    d = np.abs(out[fin] - ref[fin])
+    bound = 2.0 ** -8 * vmax(None, case) + 1e-5 * max(1.0, float(np.abs(ref[fin]).max()))
+    if attn == "fp8":
+        assert float(d.mean()) <= GATE_MEAN_ABS, (fmt, attn)
+    else:
+        assert float(d.max()) <= bound, (fmt, attn, float(d.max()))
+
+
 def test_prefill_empty_and_argument_checks():
     case = synth.prefill_case(152, 8, 2, 64, [40], [0])
     g = GpuLayer(case)
