@@ -42,32 +42,36 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
 }
 
+// IEEE maximum (a NaN operand gives NaN): one v_maximum3_f32, with none of
+// the input quieting that fmaxf needs on operands of unknown origin. A NaN
+// logit makes its column's result NaN either way (its p is NaN).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over the four lanes c, c+16, c+32, c+48 that hold one MFMA column,
 // with the gfx950 row swaps (VALU, no LDS round trip).
 __device__ __forceinline__ float col_max(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 constexpr float kLazyLog2 = 8.0f;   // running max raised only past +8 (P <= 256)
 constexpr int kFoldTiles = 4;       // level-1 P*V accumulation length in tiles
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float wave_max_col(float x) {
-  // lanes c, c+16, c+32, c+48 hold the same MFMA column
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
+// Sum over the four lanes c, c+16, c+32, c+48 that hold one MFMA column (the
+// row swaps give both lanes of a pair the same operands, so every lane of the
+// column ends with the same value).
 __device__ __forceinline__ float wave_sum_col(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ---- LDS staging of K/V tiles -------------------------------------------------
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 #pragma unroll
     for (int pg = 0; pg < TP; ++pg)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[pg][e]);
+      for (int e = 0; e < 4; ++e) tmax = vmax(tmax, x[pg][e]);
     tmax = col_max(tmax);
     const bool grow = tmax > m_run + kLazyLog2;          // -inf > -inf is false
     if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
@@ -659,7 +663,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       const bool live = tmax != -INFINITY;
       const float mb = live ? tmax : 0.0f;
       const float fb = live ? __builtin_amdgcn_exp2f(tmax - m_use) : 0.0f;
-      float ps = 0.0f;
+      float ps = -0.0f;                  // -0 + p is p: no add for the first term
       uint32_t pw[TP];
 #pragma unroll
       for (int pg = 0; pg < TP; ++pg) {
