@@ -329,6 +329,71 @@ def sweep(torch, kv, w, contexts, steps, warmup):
 PREFILL_LENGTHS = [1024, 2048, 4096, 8192, 16384, 32768]
 
 
+CHUNKED_PREFILL = [(512, 8192), (512, 32768), (512, 131072), (2048, 131072)]
+
+
+def chunked_prefill_bench(torch, kv, w, cases, steps, warmup, scales="per_kv_head", attn="bf16"):
+    """Chunked prefill per layer: the last `chunk` rows of a context of
+    `ctx` positions (already in the fp8 cache) attend causally to their
+    prefix, once with the key split (a workspace from
+    alloc_prefill_workspace) and once without. Flops: 4 D Hq per (row,
+    attended key) pair."""
+    dev = torch.device("cuda:0")
+    Hq, Hkv, D = w["Hq"], w["Hkv"], w["D"]
+    d = kv.layer_desc(Hq, Hkv, D, "fp8_e4m3", scales, attn=attn)
+    rows = []
+    for chunk, L in cases:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(chunk * 7 + L)
+        pages = (L + 15) // 16
+        kc = torch.empty(kv.cache_shape(d, pages), dtype=torch.uint8, device=dev)
+        vc = torch.empty_like(kc)
+        k = torch.randn((L, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((L, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        q = torch.randn((chunk, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+        out = torch.empty((chunk, Hq, D), dtype=torch.bfloat16, device=dev)
+        slots = torch.arange(L, dtype=torch.int64, device=dev)
+        bt = torch.arange(pages, dtype=torch.int32, device=dev).view(1, pages)
+        qs = torch.tensor([0, chunk], dtype=torch.int32, device=dev)
+        lens = torch.tensor([L], dtype=torch.int32, device=dev)
+        if d.dynamic:
+            ks = torch.zeros(kv.scale_pool_shape(d, pages), dtype=torch.float32, device=dev)
+            vs = torch.zeros_like(ks)
+            kv.kv_cache_write_dynamic(d, k, v, slots, kc, vc, ks, vs)
+        else:
+            ks = torch.empty(Hkv, dtype=torch.float32, device=dev)
+            vs = torch.empty(Hkv, dtype=torch.float32, device=dev)
+            kv.kv_scale_from_amax(d, k, ks)
+            kv.kv_scale_from_amax(d, v, vs)
+            kv.kv_cache_write(d, k, v, slots, kc, vc, ks, vs)
+        ws = kv.alloc_prefill_workspace(d, 1, chunk, pages)
+        flops = 4.0 * D * Hq * (chunk * L - chunk * (chunk - 1) / 2)
+        res = dict(chunk=chunk, context=L, workspace_bytes=0 if ws is None else ws.numel())
+        for tag, wsp in (("split", ws), ("no_split", None)):
+            def attend():
+                kv.paged_prefill_attention(d, out, q, kc, vc, bt, qs, lens, chunk, ks, vs,
+                                           workspace=wsp)
+            for _ in range(warmup):
+                attend()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                attend()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            res[tag + "_us"] = round(us, 2)
+            res[tag + "_tflops"] = round(flops / (us * 1e-6) / 1e12, 1)
+        rows.append(res)
+        log(f"chunked prefill chunk={chunk:5d} ctx={L:6d}: split {res['split_us']:9.1f} us "
+            f"({res['split_tflops']:6.1f} TFLOP/s), no split {res['no_split_us']:9.1f} us "
+            f"({res['no_split_tflops']:6.1f} TFLOP/s)")
+        del kc, vc, k, v, q, out, ws
+        torch.cuda.empty_cache()
+    return dict(points=rows, cache="fp8_e4m3", scales=scales, attention=attn)
+
+
 def prefill_bench(torch, kv, w, lengths, steps, warmup, scales="per_kv_head", attn="bf16"):
     """Single-request prefill per layer (the TTFT share of one layer): the
     cache write of a whole prompt of L tokens, then chunked-prefill attention
@@ -507,6 +572,8 @@ def main():
     if args.prefill_only:
         res = prefill_bench(torch, kv, WORKLOADS["llama8b"], PREFILL_LENGTHS, 5, 2,
                             scales=args.scales, attn=args.attn)
+        res["chunked"] = chunked_prefill_bench(torch, kv, WORKLOADS["llama8b"], CHUNKED_PREFILL,
+                                               5, 2, scales=args.scales, attn=args.attn)
         print(json.dumps(res))
         return
     ctx = args.context or w["ctx"]
@@ -614,6 +681,7 @@ def main():
         result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
     if not args.no_prefill and args.workload == "llama8b":
         result["prefill"] = prefill_bench(torch, kv, w, PREFILL_LENGTHS, 5, 2)
+        result["chunked_prefill"] = chunked_prefill_bench(torch, kv, w, CHUNKED_PREFILL, 5, 2)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)...")
         result["cpu_baseline"] = cpu_baseline(WORKLOADS["llama8b"], 131072)

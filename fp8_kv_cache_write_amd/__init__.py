@@ -99,7 +99,8 @@ def lib():
         L.kvq_decode_step_dynamic.argtypes = [dp, vp, vp, vp, vp, i64, vp, i32, vp, vp, i32, vp,
                                               i32, i32, vp, vp, vp, sz, vp]
         L.kvq_paged_prefill_attention.argtypes = [dp, vp, i32, vp, vp, vp, i64, vp, i32, vp,
-                                                  vp, i32, i32, vp, vp, vp]
+                                                  vp, i32, i32, vp, vp, vp, sz, vp]
+        L.kvq_prefill_workspace_bytes.argtypes = [dp, i32, i32, i32, ctypes.POINTER(sz)]
         L.kvq_kv_scale_from_amax.argtypes = [dp, vp, i64, vp, vp]
         L.kvq_e4m3_quantize.argtypes = [vp, i64, vp, vp, vp]
         L.kvq_e5m2_quantize.argtypes = [vp, i64, vp, vp, vp]
@@ -111,7 +112,8 @@ def lib():
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
                   "kvq_e4m3_quantize", "kvq_e5m2_quantize", "kvq_profile_begin",
                   "kvq_profile_end", "kvq_kv_cache_write_dynamic",
-                  "kvq_decode_step_dynamic", "kvq_paged_prefill_attention"):
+                  "kvq_decode_step_dynamic", "kvq_paged_prefill_attention",
+                  "kvq_prefill_workspace_bytes"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -236,6 +238,22 @@ def alloc_workspace(desc, num_seqs, max_context_len, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
+def prefill_workspace_bytes(desc, num_seqs, max_query_len, max_pages_per_seq):
+    n = ctypes.c_size_t(0)
+    _check("kvq_prefill_workspace_bytes", lib().kvq_prefill_workspace_bytes(
+        ctypes.byref(desc), int(num_seqs), int(max_query_len), int(max_pages_per_seq),
+        ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_prefill_workspace(desc, num_seqs, max_query_len, max_pages_per_seq, device="cuda"):
+    """A uint8 device tensor for the key split of one prefill call (None when
+    the plan has no split)."""
+    import torch
+    n = prefill_workspace_bytes(desc, num_seqs, max_query_len, max_pages_per_seq)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def _decode_checks(desc, out, q, k_cache, v_cache, block_tables, context_lens, k_scale,
                    v_scale, workspace):
     import torch
@@ -324,13 +342,14 @@ def decode_step_dynamic(desc, k_new, v_new, k_cache, v_cache, out, q, block_tabl
 
 def paged_prefill_attention(desc, out, q, k_cache, v_cache, block_tables, query_start,
                             context_lens, max_query_len, k_scale=None, v_scale=None,
-                            stream=None):
+                            workspace=None, stream=None):
     """Chunked-prefill attention: q, out [T, Hq, D] (bf16 / float32 or bf16)
     hold every sequence's new rows (sequence b's rows query_start[b] ..
     query_start[b+1]-1, int32 [B+1], are its last positions; context_lens
     int32 [B] counts the written positions, the chunk included); each row
     attends causally to its prefix. max_query_len: host bound of the rows per
-    sequence."""
+    sequence. workspace: from alloc_prefill_workspace (lets a short chunk over
+    a long context split its keys), or None (no split)."""
     import torch
     _need(out, "out")
     _need(q, "q", torch.bfloat16)
@@ -341,6 +360,7 @@ def paged_prefill_attention(desc, out, q, k_cache, v_cache, block_tables, query_
     _need(context_lens, "context_lens", torch.int32)
     _need(k_scale, "k_scale", torch.float32)
     _need(v_scale, "v_scale", torch.float32)
+    _need(workspace, "workspace")
     if out.dtype == torch.float32:
         out_dtype = OUT_F32
     elif out.dtype == torch.bfloat16:
@@ -358,6 +378,7 @@ def paged_prefill_attention(desc, out, q, k_cache, v_cache, block_tables, query_
         ctypes.byref(desc), _ptr(out), out_dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache),
         num_pages, _ptr(block_tables), block_tables.shape[1], _ptr(query_start),
         _ptr(context_lens), B, int(max_query_len), _ptr(k_scale), _ptr(v_scale),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream)))
 
 

@@ -377,13 +377,35 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new, const
                        v_scales, workspace, workspace_bytes, k_new, v_new, true, stream);
 }
 
+static PrefillPlan prefill_plan(const kvq_layer_desc* d, int32_t num_seqs,
+                                int32_t max_query_len, int32_t max_pages_per_seq,
+                                bool allow_split) {
+  return plan_paged_prefill(d->head_dim, (int)d->cache_dtype, d->num_q_heads, d->num_kv_heads,
+                            num_seqs, max_query_len, max_pages_per_seq, cu_count(),
+                            allow_split);
+}
+
+int kvq_prefill_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
+                                int32_t max_query_len, int32_t max_pages_per_seq,
+                                size_t* bytes) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!bytes || num_seqs < 0 || max_query_len < 0 || max_pages_per_seq < 0)
+    return KVQ_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (num_seqs == 0 || max_query_len == 0 || max_pages_per_seq == 0) return KVQ_OK;
+  *bytes = prefill_plan(desc, num_seqs, max_query_len, max_pages_per_seq, true).bytes;
+  return KVQ_OK;
+}
+
 int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t out_dtype,
                                 const void* q, const void* k_cache, const void* v_cache,
                                 int64_t num_pages, const int32_t* block_tables,
                                 int32_t max_pages_per_seq, const int32_t* query_start,
                                 const int32_t* context_lens, int32_t num_seqs,
                                 int32_t max_query_len, const float* k_scale,
-                                const float* v_scale, void* stream) {
+                                const float* v_scale, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   int st = check_desc(desc);
   if (st) return st;
   const bool dyn = dynamic_scales(desc);
@@ -391,8 +413,14 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
   if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16) return KVQ_ERR_INVALID_ARG;
   if (num_seqs < 0 || max_query_len < 0 || num_pages < 0 || max_pages_per_seq < 0)
     return KVQ_ERR_INVALID_ARG;
+  if (!workspace && workspace_bytes != 0) return KVQ_ERR_INVALID_ARG;
+  if (workspace && !aligned(workspace, 256)) return KVQ_ERR_INVALID_ARG;
   if (num_seqs == 0 || max_query_len == 0) return KVQ_OK;
   if (num_pages == 0 || max_pages_per_seq == 0) return KVQ_ERR_INVALID_ARG;
+  // no workspace: no key split; a workspace must hold the split's partials
+  const PrefillPlan plan =
+      prefill_plan(desc, num_seqs, max_query_len, max_pages_per_seq, workspace != nullptr);
+  if (workspace_bytes < plan.bytes) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
     return KVQ_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -425,9 +453,14 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out, int32_t o
   const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
                                          : 1.0f / sqrtf((float)desc->head_dim);
   p.sm_scale_log2 = sm * 1.4426950408889634f;
-  hipError_t e = launch_paged_prefill(p, desc->head_dim, (int)desc->cache_dtype, dyn, att8,
-                                      cu_count(), static_cast<hipStream_t>(stream), nullptr,
-                                      nullptr);
+  if (plan.bytes) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    p.ws_m = reinterpret_cast<float*>(ws);
+    p.ws_l = reinterpret_cast<float*>(ws + plan.off_l);
+    p.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
+  }
+  hipError_t e = launch_paged_prefill(p, plan, desc->head_dim, (int)desc->cache_dtype, dyn,
+                                      att8, static_cast<hipStream_t>(stream), nullptr, nullptr);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -51,6 +51,7 @@ struct DecodeParams {
   int out_bf16;
   int direct;                    // num_parts == 1: the split kernel finishes
   float sm_scale_log2;           // sm_scale * log2(e)
+  const int32_t* row_limit;      // merge only: rows at or past *row_limit are skipped
 };
 
 // Waves per work-group of the split kernel.
@@ -100,18 +101,46 @@ struct PrefillParams {
   int window;                    // 0 = full
   int scale_per_head;
   int out_bf16;
-  int qblocks;                   // set by the launcher
-  int pos_per_block;             // set by the launcher
+  int qblocks;                   // set from the plan
+  int pos_per_block;             // set from the plan
+  int num_parts;                 // key partitions (1: no split; set from the plan)
+  int part_tiles;                // 32-position tiles per key partition
+  float* ws_m;                   // split only: [rows][Hq][num_parts] (log2 domain)
+  float* ws_l;                   //   [rows][Hq][num_parts]
+  float* ws_o;                   //   [rows][Hq][num_parts][D], unnormalised
   float sm_scale_log2;
 };
 
 constexpr int kPrefillWaves = 4;
 
-// cus: compute units of the device (sizes the query blocks). dyn: dynamic
-// per-token scales (p.k_scale / p.v_scale are the pools [P][Hkv][16]).
-// att8: all-FP8 attention (e4m3 q and P, fp8 MFMA); fp8 caches, static scales.
-hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, bool dyn,
-                                bool att8, int cus, hipStream_t stream, hipEvent_t ev_before,
-                                hipEvent_t ev_after);
+// The prefill launch geometry, a pure function of its arguments (and the
+// KVFP8_PREFILL_COLUMN_GROUPS / KVFP8_PREFILL_KEY_PARTS overrides): column
+// groups per wave, query blocks, and the key split with its workspace. The
+// key range [0, max_pages_per_seq * 16) is cut into num_parts partitions when
+// the query blocks alone would leave compute units idle (a short chunk over a
+// long context) and a workspace may be used; the partitions' partial results
+// are merged by the decode path's FP32 reduce kernel.
+struct PrefillPlan {
+  int ncg, pos_per_block, qblocks, num_parts, part_tiles;
+  size_t off_l, off_o, bytes;    // workspace layout; bytes = 0 without a split
+};
+PrefillPlan plan_paged_prefill(int head_dim, int fmt, int num_q_heads, int num_kv_heads,
+                               int num_seqs, int max_query_len, int max_pages_per_seq, int cus,
+                               bool allow_split);
+
+// dyn: dynamic per-token scales (p.k_scale / p.v_scale are the pools
+// [P][Hkv][16]). att8: all-FP8 attention (e4m3 q and P, fp8 MFMA); fp8
+// caches, static scales. plan: from plan_paged_prefill with the same
+// arguments; with a split, p.ws_* point into a workspace of plan.bytes.
+hipError_t launch_paged_prefill(const PrefillParams& p, const PrefillPlan& plan, int head_dim,
+                                int fmt, bool dyn, bool att8, hipStream_t stream,
+                                hipEvent_t ev_before, hipEvent_t ev_after);
+
+// The decode path's FP32 partition merge over `rows` rows of p.num_q_heads
+// heads (grid rows x heads): p.ws_*, p.num_parts, p.out, p.out_bf16, the
+// static V scale (or null), p.group, p.scale_per_head. Rows at or past
+// *row_limit (a device int, when given) are skipped.
+hipError_t launch_partition_merge(const DecodeParams& p, int head_dim, int rows,
+                                  hipStream_t stream);
 
 }  // namespace kvfp8

@@ -994,6 +994,7 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodePara
   const int d = threadIdx.x;              // D threads: wave w owns dims 64w..64w+63
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
+  if (p.row_limit && b >= *p.row_limit) return;   // past the last row (prefill merge)
   const int h = hq / p.group;
   const int np = p.num_parts;
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
@@ -1170,6 +1171,18 @@ static hipError_t launch_dim(const DecodeParams& p, int fmt, int num_seqs, bool 
     default:
       return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_partition_merge(const DecodeParams& p, int head_dim, int rows,
+                                  hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  switch (head_dim) {
+    case 64: launch_reduce<64>(p, rows, stream); break;
+    case 128: launch_reduce<128>(p, rows, stream); break;
+    case 256: launch_reduce<256>(p, rows, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,

@@ -28,6 +28,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -88,12 +90,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   const int qd = lane >> 4;             // row quad of the MFMA layout
   const int c = lane & 15;              // MFMA column
 
-  // ---- which (sequence, KV head, query block): XCD-aware ------------------
+  // ---- which (sequence, KV head, key partition, query block): XCD-aware ---
+  // Consecutive logical blocks share a (sequence, KV head, key partition),
+  // so the query blocks reading the same keys run on one XCD (one L2).
   const int per_xcd = (int)gridDim.x / kNumXcd;
   const int logical = (int)(blockIdx.x % kNumXcd) * per_xcd + (int)(blockIdx.x / kNumXcd);
-  const int total = p.num_seqs * p.num_kv_heads * p.qblocks;
+  const int per_bh = p.qblocks * p.num_parts;
+  const int total = p.num_seqs * p.num_kv_heads * per_bh;
   if (logical >= total) return;
-  const int bh = logical / p.qblocks;
+  const int bh = logical / per_bh;
+  const int part = (logical % per_bh) / p.qblocks;
   const int qb = p.qblocks - 1 - logical % p.qblocks;     // latest (heaviest) block first
   const int b = bh / p.num_kv_heads;
   const int h = bh % p.num_kv_heads;
@@ -110,15 +116,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   const int off = L - n;                // position of query row r is off + r
 
   // ---- this lane's query columns ------------------------------------------
+  // col_row: the column is a row of this sequence (its output is written);
+  // col_ok: that row's position is not below 0 (it attends something)
   int qpos[NCG], qrow[NCG];
-  bool col_ok[NCG];
+  bool col_ok[NCG], col_row[NCG];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const int slot = c / G;
     const int r = r0 + (wave * NCG + cg) * ppc + slot;
-    col_ok[cg] = slot < ppc && r < n && off + r >= 0;
+    col_row[cg] = slot < ppc && r < n;
+    col_ok[cg] = col_row[cg] && off + r >= 0;
     qpos[cg] = col_ok[cg] ? off + r : -1;
-    qrow[cg] = col_ok[cg] ? q0 + r : -1;
+    qrow[cg] = col_row[cg] ? q0 + r : -1;
   }
   const int g = c % G;
   bf16x8 qop[NCG][NK];
@@ -161,9 +170,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   const int pos_first = off + r0, pos_last = off + r_last;
   const int key_lo = p.window > 0 ? max(0, pos_first + 1 - p.window) : 0;
   const int key_hi = pos_last;
-  const int first_page = (key_lo / kPage) & ~1;             // tiles on 2-page pairs
+  int first_page = (key_lo / kPage) & ~1;                   // tiles on 2-page pairs
   const int end_page = key_hi >= 0 ? key_hi / kPage + 1 : 0;
-  const int ntiles = end_page > first_page ? (end_page - first_page + 1) / 2 : 0;
+  int ntiles = end_page > first_page ? (end_page - first_page + 1) / 2 : 0;
+  if (p.num_parts > 1) {
+    // this partition's tiles (absolute tile index = page / 2) of that range
+    const int t_lo = max(first_page / 2, part * p.part_tiles);
+    const int t_hi = min(first_page / 2 + ntiles, (part + 1) * p.part_tiles);
+    first_page = 2 * t_lo;
+    ntiles = max(t_hi - t_lo, 0);
+  }
   // keys every column of the work-group may see without a mask
   const int free_lo = p.window > 0 ? pos_last + 1 - p.window : 0;
   const int free_hi = pos_first;   // a key <= this is at or before every column's position
@@ -494,11 +510,42 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     }
   }
 
-  // ---- output rows: o / l * s_v --------------------------------------------
+  // ---- key split: this partition's unnormalised partial (m, l, o) -------------
+  // (an empty partition leaves m = -inf, l = 0, o = 0; a NaN l carries a NaN
+  // m so the merge keeps it; the merge applies the static V scale)
+  if (p.num_parts > 1) {
+    // the workspace holds num_seqs * max_query_len rows (every row, when each
+    // sequence has at most max_query_len of them)
+    const int64_t ws_rows = (int64_t)p.num_seqs * p.max_query_len;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float l = col_sum(l_run[cg]);
+      if (!col_row[cg] || qrow[cg] >= ws_rows) continue;
+      const int64_t slot =
+          ((int64_t)qrow[cg] * p.num_q_heads + h * G + g) * p.num_parts + part;
+      if (qd == 0) {
+        p.ws_m[slot] = l != l ? __builtin_nanf("") : m_run[cg];
+        p.ws_l[slot] = l;
+      }
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int d;
+          if constexpr (FP8) d = 64 * (blk / 4) + 16 * qd + 4 * e + (blk % 4);
+          else d = 32 * (blk / 2) + 8 * qd + 2 * e + (blk % 2);
+          p.ws_o[slot * D + d] = acc[cg][blk][e];
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- output rows: o / l * s_v (rows at negative positions: zeros) ---------
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const float l = col_sum(l_run[cg]);
-    if (!col_ok[cg]) continue;
+    if (!col_row[cg]) continue;
     const bool has = l > 0.0f || l != l;                 // NaN stays NaN
     const float scale = has ? vs / l : 0.0f;
     const int64_t orow = ((int64_t)qrow[cg] * p.num_q_heads + h * G + g) * D;
@@ -520,7 +567,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 namespace {
 
 template <int D, int FMT, int NCG, bool DYN, bool ATT8>
-hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stream,
+hipError_t launch_prefill_shape(const PrefillParams& p, int64_t total, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
@@ -534,65 +581,63 @@ hipError_t launch_prefill_shape(PrefillParams p, int64_t total, hipStream_t stre
   return hipGetLastError();
 }
 
-// Column groups per wave: the most the registers allow (each shares the
-// tile's fp8 -> bf16 expansion and LDS reads), fewer when the grid would
-// leave compute units idle (short prompts): at least two work-groups per CU.
+// Column groups per wave the registers allow (each shares the tile's
+// fp8 -> bf16 expansion and LDS reads).
+int prefill_ncg_max(int head_dim, int fmt) {
+  return head_dim >= 256 ? 1 : (head_dim == 128 && fmt == kFmtBf16 ? 2 : 3);
+}
+
 template <int D, int FMT, bool DYN, bool ATT8>
-hipError_t launch_prefill_typed(PrefillParams p, int cus, hipStream_t stream,
+hipError_t launch_prefill_typed(PrefillParams p, const PrefillPlan& pl, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NCG_MAX = D >= 256 ? 1 : (D == 128 && FMT == kFmtBf16 ? 2 : 3);
-  const int ppc = 16 / p.group;
-  // KVFP8_PREFILL_COLUMN_GROUPS=n (1..3) forces the count (tests, sweeps)
-  int forced = 0;
-  if (const char* env = getenv("KVFP8_PREFILL_COLUMN_GROUPS")) forced = atoi(env);
-  int ncg = forced >= 1 && forced <= NCG_MAX ? forced : NCG_MAX;
-  int64_t total = 0;
-  for (;; --ncg) {
-    p.pos_per_block = kPrefillWaves * ncg * ppc;
-    p.qblocks = (p.max_query_len + p.pos_per_block - 1) / p.pos_per_block;
-    total = (int64_t)p.num_seqs * p.num_kv_heads * p.qblocks;
-    if (ncg == 1 || forced || total >= 2LL * cus) break;
-  }
+  p.pos_per_block = pl.pos_per_block;
+  p.qblocks = pl.qblocks;
+  p.num_parts = pl.num_parts;
+  p.part_tiles = pl.part_tiles;
+  const int64_t total = (int64_t)p.num_seqs * p.num_kv_heads * p.qblocks * p.num_parts;
   if (total == 0) return hipSuccess;
+  if (pl.ncg > NCG_MAX) return hipErrorInvalidValue;
   if constexpr (NCG_MAX >= 3) {
-    if (ncg == 3)
+    if (pl.ncg == 3)
       return launch_prefill_shape<D, FMT, 3, DYN, ATT8>(p, total, stream, ev_before, ev_after);
   }
   if constexpr (NCG_MAX >= 2) {
-    if (ncg == 2)
+    if (pl.ncg == 2)
       return launch_prefill_shape<D, FMT, 2, DYN, ATT8>(p, total, stream, ev_before, ev_after);
   }
   return launch_prefill_shape<D, FMT, 1, DYN, ATT8>(p, total, stream, ev_before, ev_after);
 }
 
 template <int D>
-hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, bool dyn, bool att8, int cus,
-                              hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+hipError_t launch_prefill_dim(const PrefillParams& p, const PrefillPlan& pl, int fmt, bool dyn,
+                              bool att8, hipStream_t stream, hipEvent_t ev_before,
+                              hipEvent_t ev_after) {
   if (dyn && att8) return hipErrorInvalidValue;
   if (dyn || att8) {
     switch (fmt) {
       case kFmtE4M3:
-        return dyn ? launch_prefill_typed<D, kFmtE4M3, true, false>(p, cus, stream, ev_before,
+        return dyn ? launch_prefill_typed<D, kFmtE4M3, true, false>(p, pl, stream, ev_before,
                                                                      ev_after)
-                   : launch_prefill_typed<D, kFmtE4M3, false, true>(p, cus, stream, ev_before,
+                   : launch_prefill_typed<D, kFmtE4M3, false, true>(p, pl, stream, ev_before,
                                                                      ev_after);
       case kFmtE5M2:
-        return dyn ? launch_prefill_typed<D, kFmtE5M2, true, false>(p, cus, stream, ev_before,
+        return dyn ? launch_prefill_typed<D, kFmtE5M2, true, false>(p, pl, stream, ev_before,
                                                                      ev_after)
-                   : launch_prefill_typed<D, kFmtE5M2, false, true>(p, cus, stream, ev_before,
+                   : launch_prefill_typed<D, kFmtE5M2, false, true>(p, pl, stream, ev_before,
                                                                      ev_after);
       default: return hipErrorInvalidValue;
     }
   }
   switch (fmt) {
     case kFmtBf16:
-      return launch_prefill_typed<D, kFmtBf16, false, false>(p, cus, stream, ev_before,
+      return launch_prefill_typed<D, kFmtBf16, false, false>(p, pl, stream, ev_before,
                                                              ev_after);
     case kFmtE4M3:
-      return launch_prefill_typed<D, kFmtE4M3, false, false>(p, cus, stream, ev_before,
+      return launch_prefill_typed<D, kFmtE4M3, false, false>(p, pl, stream, ev_before,
                                                              ev_after);
     case kFmtE5M2:
-      return launch_prefill_typed<D, kFmtE5M2, false, false>(p, cus, stream, ev_before,
+      return launch_prefill_typed<D, kFmtE5M2, false, false>(p, pl, stream, ev_before,
                                                              ev_after);
     default: return hipErrorInvalidValue;
   }
@@ -600,18 +645,114 @@ hipError_t launch_prefill_dim(const PrefillParams& p, int fmt, bool dyn, bool at
 
 }  // namespace
 
-hipError_t launch_paged_prefill(const PrefillParams& p, int head_dim, int fmt, bool dyn,
-                                bool att8, int cus, hipStream_t stream, hipEvent_t ev_before,
-                                hipEvent_t ev_after) {
+// Smallest key partition of the split, in 32-position tiles.
+constexpr int kMinPartTiles = 16;
+
+PrefillPlan plan_paged_prefill(int head_dim, int fmt, int num_q_heads, int num_kv_heads,
+                               int num_seqs, int max_query_len, int max_pages_per_seq, int cus,
+                               bool allow_split) {
+  PrefillPlan pl{};
+  const int G = num_q_heads / num_kv_heads;
+  const int ppc = 16 / G;                                  // positions per column group
+  const int ncg_max = prefill_ncg_max(head_dim, fmt);
+  // overrides for tests and sweeps: KVFP8_PREFILL_COLUMN_GROUPS=n (1..3),
+  // KVFP8_PREFILL_KEY_PARTS=n (n key partitions; 1 = no split)
+  int forced = 0, forced_parts = 0;
+  if (const char* env = getenv("KVFP8_PREFILL_COLUMN_GROUPS")) forced = atoi(env);
+  if (const char* env = getenv("KVFP8_PREFILL_KEY_PARTS")) forced_parts = atoi(env);
+  if (forced < 1 || forced > ncg_max) forced = 0;
+  auto blocks = [&](int ncg) -> int64_t {
+    const int ppb = kPrefillWaves * ncg * ppc;
+    return ((int64_t)max_query_len + ppb - 1) / ppb;
+  };
+  auto groups = [&](int ncg) -> int64_t { return (int64_t)num_seqs * num_kv_heads * blocks(ncg); };
+  int ncg = forced ? forced : ncg_max;
+  const int64_t rows = (int64_t)num_seqs * max_query_len;
+  const int max_tiles = (max_pages_per_seq + 1) / 2;
+  // Split the keys when the query blocks leave compute units idle and the
+  // key range is at least twice the chunk (a chunk at the end of a long
+  // context; whole prompts keep the column-group reduction below). The merge
+  // grid has a row per query row, so the rows must fit its y dimension.
+  // The partition count is chosen by the waves of work-groups it makes (two
+  // resident per CU): time ~ waves / parts, plus 2 % per extra wave for the
+  // fixed cost of each work-group; unsplit, ~ the waves of the query blocks.
+  int parts = 1;
+  if (allow_split && rows <= 65535) {
+    const int64_t slots = 2LL * cus, base = groups(ncg);
+    if (forced_parts >= 1) {
+      parts = std::min(forced_parts, std::max(max_tiles, 1));
+    } else if (base < 4 * slots && max_tiles >= 2 * kMinPartTiles &&
+               (int64_t)max_pages_per_seq * kPage >= 2LL * max_query_len) {
+      double best = (double)((base + slots - 1) / slots);
+      for (int k = 1; k <= 4; ++k) {
+        const int64_t np = std::min<int64_t>(k * slots / base, max_tiles / kMinPartTiles);
+        if (np < 2) continue;
+        const int64_t waves = (base * np + slots - 1) / slots;
+        const double cost = (double)waves / (double)np * (1.0 + 0.02 * (double)(waves - 1));
+        if (cost < best) {
+          best = cost;
+          parts = (int)np;
+        }
+      }
+    }
+  }
+  if (parts > 1) {
+    pl.part_tiles = (max_tiles + parts - 1) / parts;
+    parts = (max_tiles + pl.part_tiles - 1) / pl.part_tiles;
+  }
+  if (parts <= 1) {
+    parts = 1;
+    pl.part_tiles = max_tiles;
+    // fewer column groups when the grid would leave compute units idle
+    // (short prompts): at least two work-groups per CU
+    if (!forced)
+      while (ncg > 1 && groups(ncg) < 2LL * cus) --ncg;
+  }
+  pl.ncg = ncg;
+  pl.pos_per_block = kPrefillWaves * ncg * ppc;
+  pl.qblocks = (int)blocks(ncg);
+  pl.num_parts = parts;
+  if (parts > 1) {
+    // (m, l, o[D]) per (query row, query head, partition), as the decode
+    // split's workspace, with the merge's chunk of slack after o
+    auto round_up = [](size_t x, size_t a) { return (x + a - 1) / a * a; };
+    const size_t slots = (size_t)rows * num_q_heads * parts;
+    pl.off_l = round_up(slots * sizeof(float), 256);
+    pl.off_o = pl.off_l + round_up(slots * sizeof(float), 256);
+    pl.bytes = pl.off_o + round_up((slots + kReduceChunk) * head_dim * sizeof(float), 256);
+  }
+  return pl;
+}
+
+hipError_t launch_paged_prefill(const PrefillParams& p, const PrefillPlan& pl, int head_dim,
+                                int fmt, bool dyn, bool att8, hipStream_t stream,
+                                hipEvent_t ev_before, hipEvent_t ev_after) {
   if (p.group < 1 || p.group > 16) return hipErrorInvalidValue;
+  if (pl.num_parts > 1 && (!p.ws_m || !p.ws_l || !p.ws_o)) return hipErrorInvalidValue;
+  hipError_t e;
   switch (head_dim) {
-    case 64: return launch_prefill_dim<64>(p, fmt, dyn, att8, cus, stream, ev_before, ev_after);
-    case 128:
-      return launch_prefill_dim<128>(p, fmt, dyn, att8, cus, stream, ev_before, ev_after);
-    case 256:
-      return launch_prefill_dim<256>(p, fmt, dyn, att8, cus, stream, ev_before, ev_after);
+    case 64: e = launch_prefill_dim<64>(p, pl, fmt, dyn, att8, stream, ev_before, ev_after); break;
+    case 128: e = launch_prefill_dim<128>(p, pl, fmt, dyn, att8, stream, ev_before, ev_after); break;
+    case 256: e = launch_prefill_dim<256>(p, pl, fmt, dyn, att8, stream, ev_before, ev_after); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess || pl.num_parts <= 1) return e;
+  // merge the partitions: FP32, the static V scale applied here (dynamic
+  // scales are already in P; bf16 caches have none)
+  DecodeParams dp{};
+  dp.ws_m = p.ws_m;
+  dp.ws_l = p.ws_l;
+  dp.ws_o = p.ws_o;
+  dp.out = p.out;
+  dp.num_q_heads = p.num_q_heads;
+  dp.num_kv_heads = p.num_kv_heads;
+  dp.group = p.group;
+  dp.num_parts = pl.num_parts;
+  dp.scale_per_head = p.scale_per_head;
+  dp.out_bf16 = p.out_bf16;
+  dp.v_scale = (fmt != kFmtBf16 && !dyn) ? p.v_scale : nullptr;
+  dp.row_limit = p.query_start + p.num_seqs;
+  return launch_partition_merge(dp, head_dim, p.num_seqs * p.max_query_len, stream);
 }
 
 }  // namespace kvfp8

@@ -329,9 +329,18 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new,
  *                 included; cut to max_pages_per_seq * 16 on the device
  *   max_query_len host int >= every n_b (sizes the grid; rows past it are
  *                 not computed)
+ *   workspace     NULL (workspace_bytes 0): every query block attends its
+ *                 whole key range in one work-group. Otherwise device
+ *                 scratch, 256-byte aligned, of at least the bytes
+ *                 kvq_prefill_workspace_bytes reports for the same
+ *                 (desc, num_seqs, max_query_len, max_pages_per_seq): a
+ *                 short chunk over a long context then splits its keys into
+ *                 partitions whose FP32 partial results the decode path's
+ *                 reduce kernel merges (same formula as the decode split).
+ *                 Clobbered; calls that share one must be ordered on a
+ *                 stream. Too small: KVQ_ERR_WORKSPACE_TOO_SMALL.
  *   other arguments as for kvq_paged_decode_attention (static scales or the
- *   pools of dynamic per-token scales; KVQ_ATTN_FP8 with static scales). No
- *   workspace.
+ *   pools of dynamic per-token scales; KVQ_ATTN_FP8 with static scales).
  */
 int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out,
                                 int32_t out_dtype, const void* q,
@@ -341,7 +350,22 @@ int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out,
                                 const int32_t* query_start,
                                 const int32_t* context_lens, int32_t num_seqs,
                                 int32_t max_query_len, const float* k_scale,
-                                const float* v_scale, void* stream);
+                                const float* v_scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_prefill_workspace_bytes - size of the workspace that lets
+ * kvq_paged_prefill_attention split the keys of a short chunk over a long
+ * context (host only, no device work). Writes the size to *bytes; 0 when the
+ * plan for these arguments has no split (then the call needs no workspace).
+ * The plan depends only on these arguments and the current device's
+ * compute-unit count: it splits when the query blocks alone would leave
+ * compute units idle and max_pages_per_seq * 16 is at least twice
+ * max_query_len.
+ */
+int kvq_prefill_workspace_bytes(const kvq_layer_desc* desc, int32_t num_seqs,
+                                int32_t max_query_len, int32_t max_pages_per_seq,
+                                size_t* bytes);
 
 /*
  * kvq_kv_scale_from_amax - static scale calibration of one layer tensor:

@@ -214,10 +214,17 @@ def test_dynamic_plan_leaves_the_lds_ring_for_d256():
 
 
 def test_prefill_argument_checks(L):
-    def pf(desc, out=FAKE, q=FAKE, qs=FAKE, lens=FAKE, B=1, mq=16, ks=FAKE, vs=FAKE, P=8):
+    def pf(desc, out=FAKE, q=FAKE, qs=FAKE, lens=FAKE, B=1, mq=16, ks=FAKE, vs=FAKE, P=8,
+           mp=8, ws=None, wsb=0):
         return L.kvq_paged_prefill_attention(ctypes.byref(desc), out, 0, q, FAKE, FAKE, P, FAKE,
-                                             8, qs, lens, B, mq, ks, vs, None)
+                                             mp, qs, lens, B, mq, ks, vs, ws, wsb, None)
     d = kv.layer_desc(32, 8, 128)
+    assert pf(d, ws=None, wsb=256) == INVALID       # a size without a workspace
+    assert pf(d, ws=FAKE_ODD, wsb=1 << 20) == INVALID   # not 256-byte aligned
+    # a 16-row chunk over 131072 positions splits its keys: a workspace must hold them
+    need = kv.prefill_workspace_bytes(d, 1, 16, 8192)
+    assert need > 0
+    assert pf(d, mp=8192, ws=FAKE, wsb=need - 256) == WS_SMALL
     assert pf(d, out=None) == INVALID
     assert pf(d, qs=None) == INVALID
     assert pf(d, out=FAKE_ODD) == INVALID
@@ -228,3 +235,26 @@ def test_prefill_argument_checks(L):
     assert pf(kv.layer_desc(32, 8, 128, "bf16", attn="fp8")) == UNSUPPORTED
     assert pf(kv.layer_desc(32, 8, 128, scale_mode="per_token"), ks=FAKE_ODD) == INVALID
     assert pf(kv.layer_desc(32, 8, 96)) == UNSUPPORTED
+
+
+def test_prefill_workspace_plan(monkeypatch):
+    d = kv.layer_desc(32, 8, 128)
+    monkeypatch.delenv("KVFP8_PREFILL_KEY_PARTS", raising=False)
+    # a short chunk over a long context splits; the partials are
+    # (m, l, o[D]) per (row, query head, partition), plus the merge's slack
+    n = kv.prefill_workspace_bytes(d, 1, 512, 2048)
+    assert n >= 512 * 32 * 2 * (128 + 2) * 4
+    assert kv.prefill_workspace_bytes(d, 1, 512, 8192) >= n
+    # whole prompts (keys shorter than twice the chunk) and short key ranges
+    # keep one partition; so do batches with more rows than the merge grid holds
+    assert kv.prefill_workspace_bytes(d, 1, 32768, 2048) == 0
+    assert kv.prefill_workspace_bytes(d, 1, 512, 32) == 0
+    assert kv.prefill_workspace_bytes(d, 8, 16384, 65536) == 0
+    assert kv.prefill_workspace_bytes(d, 0, 512, 2048) == 0
+    # enough query blocks to fill the device: no split
+    assert kv.prefill_workspace_bytes(d, 64, 512, 2048) == 0
+    # the override forces a split even where the plan would not
+    monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", "3")
+    assert kv.prefill_workspace_bytes(d, 1, 64, 40) > 0
+    monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", "1")
+    assert kv.prefill_workspace_bytes(d, 1, 512, 8192) == 0

@@ -36,21 +36,28 @@ def _gpu():
     yield
 
 
-def gpu_prefill(g, case, out_dtype=torch.float32):
-    out = torch.empty((case.num_query_rows, case.num_q_heads, case.head_dim), dtype=out_dtype,
-                      device=dev())
+def gpu_prefill(g, case, out_dtype=torch.float32, split=False, context_lens=None):
+    # split: pass the workspace that lets the plan split the keys; the output
+    # starts as NaN, so a row the kernels never write shows
+    out = torch.full((case.num_query_rows, case.num_q_heads, case.head_dim), float("nan"),
+                     dtype=out_dtype, device=dev())
+    ws = None
+    if split:
+        ws = kv.alloc_prefill_workspace(g.desc, case.num_seqs, case.max_query_len,
+                                        case.block_tables.shape[1])
+    lens = g.context_lens if context_lens is None else i32_dev(context_lens)
     kv.paged_prefill_attention(g.desc, out, g.q, g.k_cache, g.v_cache, g.block_tables,
-                               i32_dev(case.query_start), g.context_lens, case.max_query_len,
-                               g.k_scale, g.v_scale)
+                               i32_dev(case.query_start), lens, case.max_query_len,
+                               g.k_scale, g.v_scale, workspace=ws)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_prefill(o, case, rows=None):
+def oracle_prefill(o, case, rows=None, lens=None):
     return oracle.prefill_attention(case.q, o.k_cache, o.v_cache, case.block_tables,
-                                    case.query_start, case.lens, case.num_kv_heads, o.fmt,
-                                    o.per_head, o.window, o.sm_scale, o.ks, o.vs, rows,
-                                    fp8attn=o.attn == "fp8")
+                                    case.query_start, case.lens if lens is None else lens,
+                                    case.num_kv_heads, o.fmt, o.per_head, o.window, o.sm_scale,
+                                    o.ks, o.vs, rows, fp8attn=o.attn == "fp8")
 
 
 def vmax(o, case):
@@ -337,3 +344,80 @@ def test_prefill_fp8_attention_last_row_is_the_decode_kernels():
     d = np.abs(pf[last] - host(out)).max()
     say(f"[prefill vs decode, all-FP8] max_abs={d:.3e}")
     assert d <= 1e-5 * max(1.0, float(np.abs(host(out)).max())), d
+
+
+SPLIT_CASES = [
+    # (label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values, attn, dyn)
+    ("d128-chunk64", 180, 32, 8, 128, [6000], [64], "fp8_e4m3", 0, "normal", "bf16", None),
+    ("d128-ragged", 181, 32, 8, 128, [5000, 3000, 100], [200, 1, 100], "fp8_e4m3", 0, "normal",
+     "bf16", None),
+    ("d128-window", 182, 32, 8, 128, [4000, 2100], [300, 33], "fp8_e4m3", 128, "normal", "bf16",
+     None),
+    ("d64-g8", synth.GPTOSS, 64, 8, 64, [3000], [96], "fp8_e4m3", 0, "normal", "bf16", None),
+    ("d256", synth.HD256, 8, 2, 256, [4000], [40], "fp8_e4m3", 0, "normal", "bf16", None),
+    ("bf16-cache", 183, 32, 8, 128, [3000], [100], "bf16", 0, "normal", "bf16", None),
+    ("e5m2", 184, 32, 8, 128, [3000], [100], "fp8_e5m2", 0, "normal", "bf16", None),
+    ("dyn", 185, 32, 8, 128, [4000, 1000], [64, 20], "fp8_e4m3", 0, "spread", "bf16",
+     "per_token_head"),
+    ("att8", 186, 32, 8, 128, [4000], [70], "fp8_e4m3", 0, "normal", "fp8", None),
+    ("att8-g16", 187, 64, 4, 128, [2500], [50], "fp8_e4m3", 0, "normal", "fp8", None),
+]
+
+
+@pytest.mark.parametrize("label,wl,Hq,Hkv,D,lens,chunks,fmt,window,values,attn,dyn", SPLIT_CASES,
+                         ids=[c[0] for c in SPLIT_CASES])
+def test_prefill_key_split(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values, attn, dyn,
+                           monkeypatch):
+    # a short chunk over a long context: the plan splits the keys (the
+    # workspace size says so), the merge gives the oracle's rows, and the
+    # unsplit kernel agrees to the same bound
+    monkeypatch.delenv("KVFP8_PREFILL_KEY_PARTS", raising=False)
+    case = synth.prefill_case(wl, Hq, Hkv, D, lens, chunks, shuffle=True, spare_frac=0.2,
+                              values=values)
+    g = GpuLayer(case, window=window, fmt=fmt, attn=attn, dyn=dyn)
+    o = OracleLayer(case, window=window, fmt=fmt, attn=attn, dyn=dyn)
+    assert kv.prefill_workspace_bytes(g.desc, case.num_seqs, case.max_query_len,
+                                      case.block_tables.shape[1]) > 0
+    ref = oracle_prefill(o, case)
+    for split in (True, False):
+        out = gpu_prefill(g, case, split=split)
+        tag = f"prefill split={split} {label}"
+        if attn == "fp8":
+            check_fp8attn(out, ref, case, window, tag)
+        else:
+            check(out, ref, o, case, tag)
+    b16 = gpu_prefill(g, case, torch.bfloat16, split=True)
+    assert torch.equal(gpu_prefill(g, case, split=True).to(torch.bfloat16), b16)
+
+
+@pytest.mark.parametrize("parts", ["2", "7", "200"])
+def test_prefill_forced_key_partitions(parts, monkeypatch):
+    # any partition count, whole prompts included (partitions past a row's
+    # position stay empty); 200 asks for more partitions than tiles, so every
+    # partition is one tile and the merge takes two chunks
+    monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", parts)
+    case = synth.prefill_case(188, 16, 4, 128, [3000, 700, 40], [40, 700, 40], shuffle=True,
+                              spare_frac=0.2)
+    for window in (0, 100):
+        g = GpuLayer(case, window=window)
+        o = OracleLayer(case, window=window)
+        check(gpu_prefill(g, case, split=True), oracle_prefill(o, case), o, case,
+              f"prefill parts={parts} window={window}")
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_rows_before_position_zero_are_zero(split, monkeypatch):
+    # a chunk longer than the context: its first rows sit at negative
+    # positions and give zeros; the others attend [0, pos]
+    if split:
+        monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", "2")
+    case = synth.prefill_case(189, 16, 4, 128, [64, 100], [64, 30], shuffle=True)
+    g = GpuLayer(case)
+    o = OracleLayer(case)
+    lens = np.array([40, 100], np.int32)
+    out = host(gpu_prefill(g, case, split=split, context_lens=lens)).astype(np.float64)
+    ref = oracle_prefill(o, case, lens=lens)
+    assert np.all(out[:24] == 0.0) and np.all(ref[:24] == 0.0)
+    assert np.all(np.isfinite(out))
+    d = float(np.abs(out - ref).max())
+    assert d <= 2.0 ** -8 * vmax(None, case) + 1e-5, d
