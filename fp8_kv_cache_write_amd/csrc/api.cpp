@@ -16,7 +16,7 @@ using namespace kvfp8;
 
 namespace {
 
-constexpr int kMaxGroup = 8;        // bf16-MFMA attention (P carried as hi + lo)
+constexpr int kMaxGroup = 16;       // bf16-MFMA attention (P carried as hi + lo)
 constexpr int kMaxGroupFp8 = 16;    // all-FP8 attention
 constexpr int kMaxPagesPerWave = 64;
 constexpr int kMaxDynHeads = 256;   // dynamic scales: LDS per-head maxima of the write

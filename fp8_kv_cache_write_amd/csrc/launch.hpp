@@ -41,7 +41,7 @@ struct DecodeParams {
   const uint16_t* v_new;         //   token at position L-1 of every sequence
   int num_q_heads;
   int num_kv_heads;
-  int group;                     // G = Hq / Hkv, <= 8 (<= 16 in the all-FP8 mode)
+  int group;                     // G = Hq / Hkv, <= 16
   int max_pages_per_seq;
   int window;                    // 0 = full
   int pages_per_wave;            // <= 64

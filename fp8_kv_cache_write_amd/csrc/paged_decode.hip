@@ -19,7 +19,8 @@
 //  * the GQA group shares each K/V tile through the MFMA B operand: columns
 //    0..G-1 carry the group's queries, columns G..2G-1 carry the same queries
 //    again and receive the low half of P (P = hi + lo, both bf16), so P*V is
-//    accurate to ~2^-17 at no extra MFMA cost;
+//    accurate to ~2^-17 at no extra MFMA cost (for G > 8 the 16 columns hold
+//    queries and a second P*V MFMA takes the low halves);
 //  * per 2-page tile the P*V MFMA result (level 1, FP32) is added to the FP32
 //    running accumulator after the online-softmax rescale (level 2);
 //  * the waves of a work-group merge their (m, l, o) through LDS; the reduce
@@ -170,7 +171,8 @@ __device__ __forceinline__ PartitionRange partition_range(const DecodeParams& p,
   return r;
 }
 
-template <int D, int FMT, int NW, int TP, int RING, int SLOTS, bool FUSED, bool ATT8, bool DYN>
+template <int D, int FMT, int NW, int TP, int RING, int SLOTS, bool FUSED, bool ATT8, bool DYN,
+          bool WIDE>
 __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
     const DecodeParams p) {
   constexpr bool FP8 = FMT != kFmtBf16;
@@ -179,9 +181,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   constexpr int NI = PB / 1024;         // 1 KiB wave loads per page per tensor
   constexpr int NK = D / 32;            // q k^T MFMAs per page
   constexpr int NBLK = D / 16;          // P*V output blocks of 16 dims
-  constexpr int GMAX = ATT8 ? 16 : 8;   // query columns: G (+ G low halves of P)
+  constexpr int GMAX = 16;              // query columns: G (+ G low halves of P)
   static_assert(!ATT8 || FP8, "the all-FP8 mode reads fp8 caches");
   static_assert(!DYN || (FP8 && !ATT8), "dynamic scales: fp8 caches, bf16 arithmetic");
+  static_assert(!WIDE || !ATT8, "the all-FP8 mode has no low halves of P");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -194,10 +197,13 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const int part_pages = NW * p.pages_per_wave;
 
   // Column c < G: query c (high half of P); G <= c < 2G: query c - G (low
-  // half of P); other columns idle. The all-FP8 mode has no low halves
-  // (P is e4m3 on purpose) and takes up to 16 queries.
-  const int g = c < G ? c : ((!ATT8 && c < 2 * G) ? c - G : -1);
-  const bool lo_col = !ATT8 && (c >= G) && (c < 2 * G);
+  // half of P); other columns idle. With G > 8 (wide) the 16 columns hold
+  // queries only, and P*V runs twice into the same accumulator: once with
+  // the high halves, once with the low ones. The all-FP8 mode has no low
+  // halves (P is e4m3 on purpose).
+  constexpr bool wide = WIDE;           // G > 8 (the launcher picks the instance)
+  const int g = c < G ? c : ((!ATT8 && !wide && c < 2 * G) ? c - G : -1);
+  const bool lo_col = !ATT8 && !wide && (c >= G) && (c < 2 * G);
 
   // Loads that do not depend on the context length go out before it is
   // known, so a work-group waits for one memory round trip, not two, before
@@ -709,10 +715,10 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       return;
     }
     float psum_pg[TP];
-    bf16x8 pop[TP / 2];
+    bf16x8 pop[TP / 2], pop_lo[TP / 2];    // pop_lo: wide mode only
 #pragma unroll
     for (int pg = 0; pg < TP; ++pg) {
-      float u[4], pv[4];
+      float u[4], ulo[4], pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float pe = __builtin_amdgcn_exp2f(x[pg][e] - m_use);
@@ -725,6 +731,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         // exact residue, rounded to bf16 (duplicate columns)
         const float hi = __uint_as_float(__float_as_uint(pw) & 0xFFFF0000u);
         u[e] = lo_col ? pw - hi : hi;
+        ulo[e] = pw - hi;
       }
       psum_pg[pg] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
 #pragma unroll
@@ -732,6 +739,14 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         const bf16x2 v2 = __builtin_convertvector((float2_t){u[e], u[e + 1]}, bf16x2);
         pop[pg / 2][4 * (pg % 2) + e] = v2[0];
         pop[pg / 2][4 * (pg % 2) + e + 1] = v2[1];
+      }
+      if constexpr (wide) {
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const bf16x2 v2 = __builtin_convertvector((float2_t){ulo[e], ulo[e + 1]}, bf16x2);
+          pop_lo[pg / 2][4 * (pg % 2) + e] = v2[0];
+          pop_lo[pg / 2][4 * (pg % 2) + e + 1] = v2[1];
+        }
       }
     }
     float psum = psum_pg[0];
@@ -762,6 +777,9 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
         }
         lvl1[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vb), pop[pp], lvl1[blk],
                                                             0, 0, 0);
+        if constexpr (wide)
+          lvl1[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vb), pop_lo[pp],
+                                                              lvl1[blk], 0, 0, 0);
       }
     }
     // ---- level 2: every kFoldTiles tiles ----------------------------------
@@ -887,7 +905,7 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   // A NaN logit (a NaN query element or cache code) leaves l NaN but may
   // never raise the running max; carry it in m so the merges keep it.
   if (l_run != l_run) m_run = __builtin_nanf("");
-  if constexpr (!ATT8) {
+  if constexpr (!ATT8 && !wide) {
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
@@ -1062,7 +1080,7 @@ constexpr int kModeBf16 = 0;   // codes expanded to bf16, static scales
 constexpr int kModeFp8 = 1;    // all-FP8 attention
 constexpr int kModeDyn = 2;    // codes expanded to bf16, dynamic per-token scales
 
-template <int D, int FMT, int TP, int RING, int SLOTS, bool FUSED, int MODE>
+template <int D, int FMT, int TP, int RING, int SLOTS, bool FUSED, int MODE, bool WIDE = false>
 static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_t stream,
                                  hipEvent_t ev_before, hipEvent_t ev_after) {
   constexpr int NW = kSplitWaves;
@@ -1070,10 +1088,10 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
   const dim3 grid((unsigned)p.num_parts, (unsigned)p.num_kv_heads, (unsigned)num_seqs);
   if (ev_before && ev_after) {
     // the events take the kernel's own start and end timestamps
-    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8, DYN>),
+    hipExtLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8, DYN, WIDE>),
                           grid, dim3(NW * kWave), 0, stream, ev_before, ev_after, 0, p);
   } else {
-    hipLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8, DYN>),
+    hipLaunchKernelGGL((paged_decode_split_kernel<D, FMT, NW, TP, RING, SLOTS, FUSED, ATT8, DYN, WIDE>),
                        grid, dim3(NW * kWave), 0, stream, p);
   }
   hipError_t err = hipGetLastError();
@@ -1091,8 +1109,8 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
 // 2x1s1 (the same with the next tile staged in LDS).
 // KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 4x1, 2x1s1, 2x1s2,
 // 4x1s1) overrides it for tuning sweeps; a shape whose LDS ring would pass
-// 64 KiB is rejected. The all-FP8 and dynamic-scale modes are built for the
-// two planned shapes only.
+// 64 KiB is rejected. The all-FP8 and dynamic-scale modes, and groups above
+// 8, are built for the two planned shapes only.
 template <int D, int FMT, int TP, int RING, int SLOTS>
 static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused, int mode,
                                hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
@@ -1112,12 +1130,31 @@ static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused, 
         return hipErrorInvalidValue;
       }
     }
+    // G > 8 outside the all-FP8 mode: the WIDE instance (P*V once per half of
+    // P), built for the plan's two shapes
+    constexpr bool planned_any = TP == 2 && RING == 1 && SLOTS <= 1;
+    const bool wide = p.group > 8;
     if (mode == kModeDyn) {
       if constexpr (planned &&
                     kv_ring + kSplitWaves * SLOTS * TP * kTileScaleBytesPerPage <= kMaxLdsRing) {
+        if (wide)
+          return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, kModeDyn, true>(
+                             p, num_seqs, stream, ev_before, ev_after)
+                       : launch_variant<D, FMT, TP, RING, SLOTS, false, kModeDyn, true>(
+                             p, num_seqs, stream, ev_before, ev_after);
         return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, kModeDyn>(
                            p, num_seqs, stream, ev_before, ev_after)
                      : launch_variant<D, FMT, TP, RING, SLOTS, false, kModeDyn>(
+                           p, num_seqs, stream, ev_before, ev_after);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
+    if (wide) {
+      if constexpr (planned_any) {
+        return fused ? launch_variant<D, FMT, TP, RING, SLOTS, true, kModeBf16, true>(
+                           p, num_seqs, stream, ev_before, ev_after)
+                     : launch_variant<D, FMT, TP, RING, SLOTS, false, kModeBf16, true>(
                            p, num_seqs, stream, ev_before, ev_after);
       } else {
         return hipErrorInvalidValue;

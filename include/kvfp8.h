@@ -133,7 +133,8 @@ enum kvq_out_dtype { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 };
  * Arithmetic of the attention over an fp8 cache.
  *   KVQ_ATTN_BF16  the cache codes expand exactly to bf16 and q stays bf16;
  *                  q k^T has exact products, P is carried to about 2^-16
- *                  (bf16 high part + bf16 residue). Group size G <= 8.
+ *                  (bf16 high part + bf16 residue). Group size G <= 16
+ *                  (above 8 the decode kernel runs P*V twice, once per part).
  *   KVQ_ATTN_FP8   the whole attention in FP8 e4m3 ("State of FP8 KV cache
  *                  and attention quantization in vLLM", introduction: QK and
  *                  ScoreV products in FP8): each query row is quantised to
@@ -151,7 +152,7 @@ enum kvq_attn_dtype { KVQ_ATTN_BF16 = 0, KVQ_ATTN_FP8 = 1 };
 /* Per-layer descriptor. */
 typedef struct kvq_layer_desc {
   int32_t num_q_heads;     /* Hq */
-  int32_t num_kv_heads;    /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 8 */
+  int32_t num_kv_heads;    /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 16 */
   int32_t head_dim;        /* D in {64, 128, 256} */
   int32_t page_size;       /* must be 16 */
   int32_t cache_dtype;     /* enum kvq_dtype */

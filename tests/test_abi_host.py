@@ -70,7 +70,7 @@ def attend(L, desc, out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, P=8, bt=FAKE, mp=8,
     (dict(head_dim=96), UNSUPPORTED),
     (dict(head_dim=512), UNSUPPORTED),
     (dict(num_q_heads=30, num_kv_heads=8), UNSUPPORTED),
-    (dict(num_q_heads=64, num_kv_heads=4), UNSUPPORTED),   # group 16 > 8
+    (dict(num_q_heads=68, num_kv_heads=4), UNSUPPORTED),   # group 17 > 16
     (dict(num_q_heads=0), INVALID),
     (dict(sliding_window=-1), INVALID),
     (dict(sm_scale=-1.0), INVALID),
@@ -147,15 +147,15 @@ def test_no_oracle_in_the_product():
 
 
 def test_fp8_attention_mode_checks():
-    # the all-FP8 mode reads fp8 caches only and takes groups up to 16;
-    # the bf16-arithmetic mode stops at 8
+    # the all-FP8 mode reads fp8 caches only; both modes take groups up to 16
     with pytest.raises(kv.Kvfp8Error):
         kv.decode_workspace_bytes(kv.layer_desc(32, 8, 128, "bf16", attn="fp8"), 1, 1024)
     assert kv.decode_workspace_bytes(kv.layer_desc(64, 4, 128, attn="fp8"), 1, 4096) >= 0
     assert kv.decode_workspace_bytes(kv.layer_desc(64, 4, 128, "fp8_e5m2", attn="fp8"), 1,
                                      4096) >= 0
+    assert kv.decode_workspace_bytes(kv.layer_desc(64, 4, 128, attn="bf16"), 1, 4096) >= 0
     with pytest.raises(kv.Kvfp8Error):
-        kv.decode_workspace_bytes(kv.layer_desc(64, 4, 128, attn="bf16"), 1, 1024)
+        kv.decode_workspace_bytes(kv.layer_desc(68, 4, 128, attn="bf16"), 1, 1024)
     with pytest.raises(kv.Kvfp8Error):
         kv.decode_workspace_bytes(kv.layer_desc(128, 4, 128, attn="fp8"), 1, 1024)
     bad = kv.layer_desc(32, 8, 128)

@@ -112,6 +112,7 @@ ATT_CASES = [
     ("g1-d64", 121, 4, 4, 64, [300], "fp8_e4m3", 0, "spread"),
     ("window-odd", synth.GPTOSS, 64, 8, 64, [3001, 129, 40], "fp8_e4m3", 128, "spread"),
     ("window-113", 122, 16, 2, 128, [1000, 500], "fp8_e4m3", 113, "normal"),
+    ("g16", 126, 64, 4, 128, [2000, 40], "fp8_e4m3", 0, "spread"),
 ]
 
 
@@ -173,6 +174,7 @@ def run_decode_step_dynamic(g, case, knew, vnew):
     ("d64-window", 16, 2, 64, [700, 129, 3], "fp8_e4m3", 100),
     ("d256-e5m2", 8, 2, 256, [777, 31], "fp8_e5m2", 0),
     ("g8", 64, 8, 128, [2050, 48], "fp8_e4m3", 0),
+    ("g16", 64, 4, 128, [1500, 20], "fp8_e4m3", 0),
 ])
 def test_dynamic_decode_step_equals_write_then_attend(label, Hq, Hkv, D, lens, fmt, window, dyn):
     say(f"dynamic decode step {label} {dyn}")
