@@ -544,8 +544,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(each sequence and KV head is independent; sharding is the caller's). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
