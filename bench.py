@@ -11,10 +11,12 @@ Default run (about a minute of GPU time):
   * headline: Llama-3.1-8B-shaped layer (32 q / 8 KV heads, head_dim 128),
     batch 1, context 131072, fp8 e4m3 cache with per-KV-head scales, 32
     layers per step -> value = KV GB/s of the whole step;
-  * sweep over contexts 1k..128k for the fp8 and the bf16 cache with a linear
-    fit us/layer = slope * context + intercept (the ITL fit of "State of FP8
-    KV cache and attention quantization in vLLM", section "Single-request
-    benchmark"), the fp8/bf16 slope ratio and the break-even context;
+  * sweep over contexts 16..128k for the fp8 and the bf16 cache with a linear
+    fit us/layer = slope * context + intercept over 8k..128k (the ITL fit of
+    "State of FP8 KV cache and attention quantization in vLLM", section
+    "Single-request benchmark"), the fp8/bf16 slope ratio and the break-even
+    context, beside the cost of one dependent launch in a captured graph (the
+    floor under the intercept);
   * roofline of the split kernel from HIP events around its launches;
   * the float64 CPU oracle timed on the host as a reported baseline.
 
@@ -289,6 +291,28 @@ def fit(xs, ys):
     return slope, my - slope * mx
 
 
+def graph_kernel_floor(torch, n=64, reps=20):
+    """Mean cost of one launch in a captured graph of n dependent 1-element
+    torch kernels: the per-kernel floor that every layer step's kernels pay."""
+    x = torch.zeros(1, device="cuda")
+    x.add_(1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            x.add_(1)
+    for _ in range(3):
+        g.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n)
+
+
 def sweep(torch, kv, w, contexts, steps, warmup):
     rows = []
     for dt in ("fp8_e4m3", "bf16"):
@@ -315,7 +339,8 @@ def sweep(torch, kv, w, contexts, steps, warmup):
         if len(pts) >= 2:
             s, b = fit([p[0] for p in pts], [p[1] for p in pts])
             fits[dt] = dict(slope_us_per_token=s, intercept_us=b)
-    out = dict(points=rows, fit_range="8192..%d" % max(contexts))
+    out = dict(points=rows, fit_range="8192..%d" % max(contexts),
+               graph_kernel_floor_us=round(graph_kernel_floor(torch), 3))
     if "fp8_e4m3" in fits and "bf16" in fits:
         f, bb = fits["fp8_e4m3"], fits["bf16"]
         out["fits"] = fits
@@ -678,7 +703,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_sweep and args.workload == "llama8b":
-        contexts = [1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
+        contexts = [16, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
         result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
     if not args.no_prefill and args.workload == "llama8b":
         result["prefill"] = prefill_bench(torch, kv, w, PREFILL_LENGTHS, 5, 2)

@@ -351,10 +351,10 @@ def test_full_llama8b_128k(llama8b_128k, variant):
     assert np.array_equal(host(g.k_cache), o.k_cache)
     assert np.array_equal(host(g.v_cache), o.v_cache)
     out, ref = check_attention(g, o, f"8B-128k-{variant}")
-    if variant == "fp8-per-head":
+    if fp8:
         unq = unquantised_reference(case)
         d = np.abs(host(out).astype(np.float64) - unq)
-        say(f"[8B-128k] error vs unquantised bf16 attention: max={d.max():.3e} "
+        say(f"[8B-128k-{variant}] error vs unquantised bf16 attention: max={d.max():.3e} "
             f"mean={d.mean():.3e} (reported, not gated)")
 
 
