@@ -78,6 +78,7 @@ struct Plan {
   int pages_per_wave;
   int num_parts;
   int slots;                   // split-kernel shape: LDS-staged tiles (1) or registers (0)
+  int rotate;                  // partition order rotated per (sequence, KV head)
   size_t off_l, off_o, bytes;  // workspace layout (bytes)
 };
 
@@ -98,6 +99,16 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // while it computes; more use the register shape. When one partition per
 // sequence is cheap enough (short contexts, sliding windows) the split kernel
 // writes the output itself and the reduce kernel is skipped.
+//
+// Partition order: work-groups reach the 8 XCDs round-robin in launch order,
+// so partition x of every (sequence, KV head) runs on XCD x mod 8 unless the
+// kernel rotates the partition index by the unit index. In a batch of
+// unequal lengths the short or empty last partitions then pile onto one XCD;
+// rotated, they spread (8 sequences of 18k-22k positions: 2-3 % faster).
+// With one sequence, A/B runs on MI355X found the rotation 2-3 % faster for
+// 64-page runs (the 8B layer at 131072 positions), neutral for the 70B
+// layer, and 4-5 % slower for short runs (8k-16k positions, head_dim 256
+// at 65536), so it is used for batches and for 64-page runs.
 constexpr double kCoResidentPenalty = 0.035;
 
 Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
@@ -150,6 +161,9 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
   Plan p;
   p.pages_per_wave = (int)ppw;
   p.slots = slots;
+  p.rotate = (num_seqs > 1 || ppw >= kMaxPagesPerWave) ? 1 : 0;
+  // KVFP8_PARTITION_ROTATE=0|1 overrides the partition order (tuning sweeps).
+  if (const char* env = getenv("KVFP8_PARTITION_ROTATE")) p.rotate = atoi(env) ? 1 : 0;
   p.num_parts = (int)((pages_max + kSplitWaves * ppw - 1) / (kSplitWaves * ppw));
   if (p.num_parts <= 1) {
     p.num_parts = 1;
@@ -322,6 +336,7 @@ int decode_common(const kvq_layer_desc* desc, void* out, int32_t out_dtype, cons
   p.dyn_all_heads = desc->scale_mode == KVQ_SCALE_PER_TOKEN ? 1 : 0;
   p.out_bf16 = out_dtype == KVQ_OUT_BF16 ? 1 : 0;
   p.direct = plan.num_parts == 1 ? 1 : 0;
+  p.rotate = plan.rotate;
   const float sm = desc->sm_scale > 0.0f ? desc->sm_scale
                                          : 1.0f / sqrtf((float)desc->head_dim);
   p.sm_scale_log2 = sm * 1.4426950408889634f;

@@ -50,6 +50,8 @@ struct DecodeParams {
   int dyn_all_heads;             // dynamic, one scale per token over all heads (fused step)
   int out_bf16;
   int direct;                    // num_parts == 1: the split kernel finishes
+  int rotate;                    // split kernel: work-group x of unit u runs partition
+                                 //   (x + u) mod num_parts, u = head + Hkv * sequence
   float sm_scale_log2;           // sm_scale * log2(e)
   const int32_t* row_limit;      // merge only: rows at or past *row_limit are skipped
 };

@@ -188,9 +188,15 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int part = blockIdx.x;
+  // Work-groups reach the XCDs round-robin in launch order (blockIdx.x
+  // fastest), so partition x of every (sequence, KV head) runs on XCD x mod 8.
+  // With p.rotate the partition index is rotated by the unit index, which
+  // spreads the short or empty last partitions of a batch over the XCDs
+  // (the plan decides; it is an ordering only, every partition still runs).
   const int h = blockIdx.y;
   const int b = blockIdx.z;
+  const int rot = p.rotate ? (int)(blockIdx.y + gridDim.y * blockIdx.z) : 0;
+  const int part = (int)((blockIdx.x + rot) % gridDim.x);
   const int G = p.group;
   const int qd = lane >> 4;             // row quad of the MFMA layout
   const int c = lane & 15;              // MFMA column

@@ -555,6 +555,48 @@ def test_decode_step_every_tile_variant(variant, monkeypatch):
             assert np.array_equal(host(out), host(ref_gpu.attend())), label
 
 
+PARTITION_ORDER_CASES = [
+    # (pages per wave, lengths): a ragged batch with empty and partial last
+    # partitions, one sequence with 64-page runs, and the plan's own choice
+    ("2", [1000, 4099, 1, 0, 17]), ("64", [9000]), ("auto", [6000, 4500, 7]),
+]
+
+
+@pytest.mark.parametrize("ppw,lens", PARTITION_ORDER_CASES,
+                         ids=[c[0] for c in PARTITION_ORDER_CASES])
+def test_partition_order_bit_identical(ppw, lens, monkeypatch):
+    # The rotated and the plain partition order run the same partitions on
+    # other work-groups: the outputs, caches and fused-step results agree
+    # bit for bit, and both pass the oracle gate.
+    if ppw == "auto":
+        monkeypatch.delenv("KVFP8_PAGES_PER_WAVE", raising=False)
+    else:
+        monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
+    case = synth.decode_case(92, 32, 8, 128, lens, shuffle=True, spare_frac=0.2)
+    pre = split_newest(case)
+    knew, vnew = newest_rows(case)
+    o = OracleLayer(case)
+    ref = o.attend()
+    got = {}
+    for rot in ("0", "1"):
+        monkeypatch.setenv("KVFP8_PARTITION_ROTATE", rot)
+        label = f"partition order rotate={rot} ppw={ppw} lens={lens}"
+        say(label)
+        full = GpuLayer(case)
+        att = full.attend()
+        g = GpuLayer(pre, scales=full.scales_host())
+        g.q = bf16_dev(case.q)
+        step = run_decode_step(g, case, knew, vnew)
+        assert np.array_equal(host(g.k_cache), o.k_cache), label
+        assert np.array_equal(host(g.v_cache), o.v_cache), label
+        assert np.array_equal(host(step), host(att)), label
+        mx, mean = errors(att, ref)
+        say(f"[{label}] max_abs={mx:.3e} mean_abs={mean:.3e}")
+        assert mx <= GATE_MAX_ABS and mean <= GATE_MEAN_ABS and mx <= tight_bound(ref), label
+        got[rot] = host(att)
+    assert np.array_equal(got["0"], got["1"])
+
+
 WIDE_CASES = [
     # (label, wl, Hq, Hkv, D, lens, fp8, window, values): G = 9..16, where
     # the 16 MFMA columns hold queries and P*V runs once per half of P
