@@ -222,8 +222,9 @@ def time_steps(torch, kv, stack, steps, warmup, profile=True):
     return ms, (split_ms / n if n else None), n
 
 
-def time_steps_graph(torch, stack, steps, warmup):
-    """The step captured once as a HIP graph, replayed: mean ms per step.
+def time_steps_graph(torch, stack, steps, warmup, per_step=False):
+    """The step captured once as a HIP graph, replayed: mean ms per step
+    (and, with per_step, the sorted ms of every replay of a second pass).
     The replayed outputs are checked against the eager step's."""
     stack.step()
     torch.cuda.synchronize()
@@ -244,8 +245,63 @@ def time_steps_graph(torch, stack, steps, warmup):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    if per_step:
+        # a second pass with an event pair around every replay, for the spread
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        del g
+        return ms, sorted(a.elapsed_time(b) for a, b in evs)
     del g
-    return e0.elapsed_time(e1) / steps
+    return ms
+
+
+def percentile(sorted_xs, q):
+    """Linear-interpolated percentile of an ascending list."""
+    if len(sorted_xs) == 1:
+        return sorted_xs[0]
+    pos = (len(sorted_xs) - 1) * q
+    lo = int(math.floor(pos))
+    hi = min(lo + 1, len(sorted_xs) - 1)
+    return sorted_xs[lo] + (sorted_xs[hi] - sorted_xs[lo]) * (pos - lo)
+
+
+def read_ceiling_gbs(torch, kv, reps=5):
+    """Measured device ceilings on a 4 GiB buffer: the library's plain
+    streaming read (kvq_stream_read: every byte once, 16-byte non-temporal
+    loads, best over work-group counts) and torch's device copy (read +
+    write bytes). GB/s each."""
+    x = torch.ones(GIB, dtype=torch.float32, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        kv.stream_read(x, sink)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            kv.stream_read(x, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 4 * GIB * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2 * 4 * GIB * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return best, copy
 
 
 KERNEL_SOURCES = ["fp8_kv_cache_write_amd/csrc/paged_decode.hip",
@@ -532,7 +588,14 @@ def cpu_baseline(w, ctx, min_seconds=10.0):
             break
     kv_bytes = ctx * w["Hkv"] * w["D"] * 2
     gbs = kv_bytes * reps / el / 1e9
+    host = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            host = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
+                host_cpu=f"{host}, {os.cpu_count()} logical CPUs visible",
                 sample=f"{w['desc']}, context {ctx}, fp8 per-KV-head, all {w['Hq']} query "
                        f"heads, attention only, {reps} repetitions in {el:.1f} s "
                        f"({el / reps * 1e3:.0f} ms per layer step)")
@@ -628,7 +691,7 @@ def main():
     log(f"headline: {w['desc']}, {ctx_desc}, {NL} layers, cache {args.cache}, attention "
         f"{args.attn}, scales {args.scales}")
     # the timed region: K steps, each one replay of the captured decode step
-    ms = time_steps_graph(torch, stack, args.steps, args.warmup)
+    ms, per_step = time_steps_graph(torch, stack, args.steps, args.warmup, per_step=True)
     # eager steps with the split kernel's launches timed by the library
     ms_eager, split_ms, nsplit = time_steps(torch, kv, stack, args.steps, args.warmup)
     # the other path, for comparison (graph-replayed too)
@@ -680,6 +743,8 @@ def main():
         "ms_per_step_eager": round(ms_eager, 5),
         f"ms_per_step_{other}_path": round(ms_other, 5),
         "us_per_layer_step": round(ms * 1e3 / NL, 3),
+        "us_per_layer_step_p10_p50_p90": [round(percentile(per_step, q) * 1e3 / NL, 3)
+                                          for q in (0.1, 0.5, 0.9)],
         "kv_gbs": round(kv_gbs, 2),
         "kv_frac_of_hbm_peak": round(kv_gbs / HBM_PEAK_GBS, 4),
         "roofline": {
@@ -701,6 +766,15 @@ def main():
     }
     del stack
     torch.cuda.empty_cache()
+    ceiling, copy_gbs = read_ceiling_gbs(torch, kv)
+    result["measured_ceilings"] = {
+        "read_gbs": round(ceiling, 1),
+        "read_how": "kvq_stream_read over 4 GiB: every byte once, 16-byte non-temporal loads, "
+                    "best of 1024-8192 work-groups",
+        "copy_gbs": round(copy_gbs, 1), "copy_how": "torch copy_ of 4 GiB, read + write bytes",
+        "split_kernel_frac_of_read": round(achieved / ceiling, 4) if achieved else None,
+        "step_frac_of_read": round(value / ceiling, 4),
+        "step_frac_of_copy": round(value / copy_gbs, 4)}
 
     if not args.no_sweep and args.workload == "llama8b":
         contexts = [16, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]

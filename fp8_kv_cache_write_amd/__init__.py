@@ -108,12 +108,13 @@ def lib():
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_profile_begin.argtypes = [i32]
         L.kvq_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+        L.kvq_stream_read.argtypes = [vp, i64, vp, i32, vp]
         for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes", "kvq_decode_step",
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
                   "kvq_e4m3_quantize", "kvq_e5m2_quantize", "kvq_profile_begin",
                   "kvq_profile_end", "kvq_kv_cache_write_dynamic",
                   "kvq_decode_step_dynamic", "kvq_paged_prefill_attention",
-                  "kvq_prefill_workspace_bytes"):
+                  "kvq_prefill_workspace_bytes", "kvq_stream_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -420,6 +421,20 @@ def e5m2_quantize(x, scale, out, stream=None):
 
 def profile_begin(max_launches):
     _check("kvq_profile_begin", lib().kvq_profile_begin(int(max_launches)))
+
+
+def stream_read(src, sink, stream=None):
+    """Timing aid: read every byte of the contiguous device tensor src once
+    (16-byte non-temporal loads); sink (int32, one word per work-group,
+    sink.numel() work-groups) receives per-work-group XOR checksums."""
+    import torch
+    if not src.is_contiguous() or src.numel() * src.element_size() % 16:
+        raise ValueError("src must be contiguous with a size that is a multiple of 16 bytes")
+    if sink.dtype != torch.int32 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous int32 tensor")
+    _check("kvq_stream_read",
+           lib().kvq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                 sink.numel(), _stream(stream)))
 
 
 def profile_end():

@@ -7,7 +7,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvfp8.so")
-SOURCES = ["api.cpp", "kv_cache_write.hip", "paged_decode.hip", "paged_prefill.hip"]
+SOURCES = ["api.cpp", "kv_cache_write.hip", "paged_decode.hip", "paged_prefill.hip",
+           "stream_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("KVFP8_ARCH", "gfx950")

@@ -516,6 +516,17 @@ int kvq_e5m2_quantize(const float* x, int64_t n, const float* scale, uint8_t* ou
   return quantize_common(KVQ_FP8_E5M2, x, n, scale, out, stream);
 }
 
+int kvq_stream_read(const void* src, int64_t n_bytes, uint32_t* sink, int32_t num_blocks,
+                    void* stream) {
+  if (n_bytes < 0 || n_bytes % 16 != 0 || num_blocks <= 0) return KVQ_ERR_INVALID_ARG;
+  if (n_bytes == 0) return KVQ_OK;
+  if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4)) return KVQ_ERR_INVALID_ARG;
+  return launch_stream_read(src, n_bytes, sink, num_blocks, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? KVQ_OK
+             : KVQ_ERR_HIP;
+}
+
 int kvq_profile_begin(int32_t max_launches) {
   if (max_launches <= 0) return KVQ_ERR_INVALID_ARG;
   if ((int)g_prof.ev.size() < 2 * max_launches) {

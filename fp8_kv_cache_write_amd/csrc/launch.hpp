@@ -23,6 +23,11 @@ hipError_t launch_scale_from_amax(const uint16_t* x, int64_t num_tokens,
 hipError_t launch_quantize(int fmt, const float* x, int64_t n, const float* scale,
                            uint8_t* out, hipStream_t stream);
 
+// A plain streaming read of n_bytes (a multiple of 16) with one XOR checksum
+// word per work-group written to sink[0..num_blocks) (stream_read.hip).
+hipError_t launch_stream_read(const void* src, int64_t n_bytes, uint32_t* sink,
+                              int num_blocks, hipStream_t stream);
+
 // Everything the split-decode and reduce kernels read; passed by value.
 struct DecodeParams {
   const uint16_t* q;             // bf16 [B][Hq][D]

@@ -412,6 +412,21 @@ const char* kvq_status_string(int32_t status);
 int kvq_profile_begin(int32_t max_launches);
 int kvq_profile_end(double* total_ms, int64_t* launches);
 
+/*
+ * Timing aid: a plain streaming read, the reference point for the split
+ * kernel's bandwidth. Reads every byte of src[0, n_bytes) once with 16-byte
+ * non-temporal loads (num_blocks work-groups of 256 threads, each a
+ * contiguous share) and writes the XOR of each work-group's 32-bit words
+ * into sink[0, num_blocks). So the XOR of all of sink equals the XOR of
+ * every 32-bit word of src.
+ *   src:  device, 16-byte aligned; n_bytes a multiple of 16 (0: no launch)
+ *   sink: device uint32 [num_blocks], written
+ * Returns KVQ_ERR_INVALID_ARG for a bad size, count or pointer, KVQ_ERR_HIP
+ * if the launch fails. Asynchronous on stream; allocates nothing.
+ */
+int kvq_stream_read(const void* src, int64_t n_bytes, uint32_t* sink, int32_t num_blocks,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -103,6 +103,18 @@ def test_write_argument_checks(L):
     assert write(L, b, T=0, ks=None, vs=None) == OK
 
 
+def test_stream_read_argument_checks(L):
+    # every rejection happens on the host, before any launch
+    sr = L.kvq_stream_read
+    assert sr(FAKE, 17, FAKE, 4, None) == INVALID        # not a multiple of 16 bytes
+    assert sr(FAKE, -16, FAKE, 4, None) == INVALID
+    assert sr(FAKE, 1024, FAKE, 0, None) == INVALID      # no work-groups
+    assert sr(None, 1024, FAKE, 4, None) == INVALID
+    assert sr(FAKE_ODD, 1024, FAKE, 4, None) == INVALID  # src not 16-byte aligned
+    assert sr(FAKE, 1024, None, 4, None) == INVALID
+    assert sr(None, 0, None, 4, None) == OK              # nothing to read, no launch
+
+
 def test_attention_argument_checks(L):
     d = kv.layer_desc(32, 8, 128)
     assert attend(L, d, q=None) == INVALID
