@@ -369,6 +369,56 @@ def graph_kernel_floor(torch, n=64, reps=20):
     return e0.elapsed_time(e1) * 1e3 / (reps * n)
 
 
+def gptoss_sweep(torch, kv, w, contexts, steps, warmup, window=128, per_type=12):
+    """The gpt-oss-like hybrid by layer type: graph-timed per-layer cost of a
+    full-attention layer and of a sliding-window layer, each with an fp8 and
+    a bf16 cache, over contexts. From them, the per-step cost of three model
+    configurations of per_type full + per_type windowed layers (all bf16,
+    all fp8, and fp8 with the windowed layers kept bf16: the skip path) and
+    a linear fit of each against context (the vLLM post's gpt-oss
+    comparison, "Single-request benchmark")."""
+    rows = []
+    for ctx in contexts:
+        t = {}
+        for kind, win in (("full", 0), ("window", window)):
+            for dt in ("fp8_e4m3", "bf16"):
+                e = 1 if dt.startswith("fp8") else 2
+                if win == 0:
+                    NL = layers_for(ctx * w["Hkv"] * w["D"] * 2 * e, hi=64)
+                else:
+                    NL = 32   # a window reads 128 positions: launch-bound at any size
+                st = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, dt,
+                                window=win, seed=ctx + 7)
+                t[(kind, dt)] = time_steps_graph(torch, st, steps, warmup) * 1e3 / NL
+                del st
+                torch.cuda.empty_cache()
+        row = dict(context=ctx, full_fp8_us=round(t[("full", "fp8_e4m3")], 3),
+                   full_bf16_us=round(t[("full", "bf16")], 3),
+                   window_fp8_us=round(t[("window", "fp8_e4m3")], 3),
+                   window_bf16_us=round(t[("window", "bf16")], 3))
+        row["step_us"] = {
+            "all_bf16": round(per_type * (t[("full", "bf16")] + t[("window", "bf16")]), 2),
+            "all_fp8": round(per_type * (t[("full", "fp8_e4m3")] + t[("window", "fp8_e4m3")]),
+                             2),
+            "fp8_skip_window": round(per_type * (t[("full", "fp8_e4m3")]
+                                                 + t[("window", "bf16")]), 2)}
+        log(f"gptoss ctx={ctx:6d} full fp8/bf16 {row['full_fp8_us']:.2f}/{row['full_bf16_us']:.2f}"
+            f" us, window fp8/bf16 {row['window_fp8_us']:.2f}/{row['window_bf16_us']:.2f} us")
+        rows.append(row)
+    out = dict(points=rows, layers=f"{per_type} full + {per_type} window-{window}",
+               window_note="windowed layers read 128 positions, so their caches stay in the "
+                           "Infinity Cache across replays; they are launch-bound either way")
+    fits = {}
+    for cfg in ("all_bf16", "all_fp8", "fp8_skip_window"):
+        s_, b_ = fit([r["context"] for r in rows], [r["step_us"][cfg] for r in rows])
+        fits[cfg] = dict(slope_us_per_token=s_, intercept_us=b_)
+    out["fits"] = fits
+    bb = fits["all_bf16"]["slope_us_per_token"]
+    out["slope_ratio_all_fp8_over_bf16"] = fits["all_fp8"]["slope_us_per_token"] / bb
+    out["slope_ratio_skip_over_bf16"] = fits["fp8_skip_window"]["slope_us_per_token"] / bb
+    return out
+
+
 def sweep(torch, kv, w, contexts, steps, warmup):
     rows = []
     for dt in ("fp8_e4m3", "bf16"):
@@ -779,6 +829,9 @@ def main():
     if not args.no_sweep and args.workload == "llama8b":
         contexts = [16, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
         result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
+    if not args.no_sweep and args.workload == "gptoss":
+        result["gptoss_sweep"] = gptoss_sweep(torch, kv, w, [8192, 32768, 65536, 131072],
+                                              args.sweep_steps, 2)
     if not args.no_prefill and args.workload == "llama8b":
         result["prefill"] = prefill_bench(torch, kv, w, PREFILL_LENGTHS, 5, 2)
         result["chunked_prefill"] = chunked_prefill_bench(torch, kv, w, CHUNKED_PREFILL, 5, 2)

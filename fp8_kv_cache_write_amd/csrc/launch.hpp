@@ -70,13 +70,15 @@ constexpr int kReduceChunk = 64;
 // fused = true: the split kernel also writes k_new / v_new into the caches at
 // position L-1 of every sequence (p.k_cache / p.v_cache must be writable).
 // slots: split-kernel tile shape, 1 = LDS-staged tiles, 0 = register tiles.
+// tile_pages: pages per tile, 2 (every mode) or 4 (bf16 arithmetic, static
+// scales).
 // fmt: cache element format, kFmtBf16 / kFmtE4M3 / kFmtE5M2 (device_common.hpp).
 // att8: all-FP8 attention (e4m3 Q and P, fp8 MFMA); fp8 caches only.
 // dyn: dynamic per-token scales (p.k_scale / p.v_scale are the pools); fp8
 // caches, bf16 arithmetic.
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
-                               bool fused, int slots, bool att8, bool dyn, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after);
+                               bool fused, int slots, int tile_pages, bool att8, bool dyn,
+                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after);
 
 // Cache write with dynamic per-token scales: per token (all_heads = 1) or per
 // token and KV head, stored for each slot into the pools [P][Hkv][16].

@@ -1112,7 +1112,9 @@ static hipError_t launch_variant(const DecodeParams& p, int num_seqs, hipStream_
 // Tile shape of the split kernel: TP pages per tile, RING register buffers,
 // SLOTS LDS buffers (SLOTS > 0: LDS-staged loads, one register tile).
 // The plan picks 2x1 (2-page tiles, loaded and computed one at a time) or
-// 2x1s1 (the same with the next tile staged in LDS).
+// 2x1s1 (the same with the next tile staged in LDS), and 4x1s1 (4-page
+// staged tiles) for fp8 caches at head_dim 64 in the bf16-arithmetic mode
+// with static scales.
 // KVFP8_SPLIT_VARIANT=TPxRING or TPxRINGsSLOTS (2x1, 2x2, 4x1, 2x1s1, 2x1s2,
 // 4x1s1) overrides it for tuning sweeps; a shape whose LDS ring would pass
 // 64 KiB is rejected. The all-FP8 and dynamic-scale modes, and groups above
@@ -1175,9 +1177,9 @@ static hipError_t launch_shape(const DecodeParams& p, int num_seqs, bool fused, 
 
 template <int D, int FMT>
 static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, int plan_slots,
-                               int mode, hipStream_t stream, hipEvent_t ev_before,
-                               hipEvent_t ev_after) {
-  int tp = 2, ring = 1, slots = plan_slots;
+                               int plan_tile_pages, int mode, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after) {
+  int tp = plan_tile_pages, ring = 1, slots = plan_slots;
   if (const char* env = getenv("KVFP8_SPLIT_VARIANT")) {
     int a = 0, c = 0, sl = 0;
     const int n = sscanf(env, "%dx%ds%d", &a, &c, &sl);
@@ -1199,18 +1201,18 @@ static hipError_t launch_typed(const DecodeParams& p, int num_seqs, bool fused, 
 
 template <int D>
 static hipError_t launch_dim(const DecodeParams& p, int fmt, int num_seqs, bool fused, int slots,
-                             int mode, hipStream_t stream, hipEvent_t ev_before,
+                             int tile_pages, int mode, hipStream_t stream, hipEvent_t ev_before,
                              hipEvent_t ev_after) {
   switch (fmt) {
     case kFmtBf16:
-      return launch_typed<D, kFmtBf16>(p, num_seqs, fused, slots, mode, stream, ev_before,
-                                       ev_after);
+      return launch_typed<D, kFmtBf16>(p, num_seqs, fused, slots, tile_pages, mode, stream,
+                                       ev_before, ev_after);
     case kFmtE4M3:
-      return launch_typed<D, kFmtE4M3>(p, num_seqs, fused, slots, mode, stream, ev_before,
-                                       ev_after);
+      return launch_typed<D, kFmtE4M3>(p, num_seqs, fused, slots, tile_pages, mode, stream,
+                                       ev_before, ev_after);
     case kFmtE5M2:
-      return launch_typed<D, kFmtE5M2>(p, num_seqs, fused, slots, mode, stream, ev_before,
-                                       ev_after);
+      return launch_typed<D, kFmtE5M2>(p, num_seqs, fused, slots, tile_pages, mode, stream,
+                                       ev_before, ev_after);
     default:
       return hipErrorInvalidValue;
   }
@@ -1229,17 +1231,20 @@ hipError_t launch_partition_merge(const DecodeParams& p, int head_dim, int rows,
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_dim, int fmt, int num_seqs,
-                               bool fused, int slots, bool att8, bool dyn, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after) {
+                               bool fused, int slots, int tile_pages, bool att8, bool dyn,
+                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
   if (att8 && dyn) return hipErrorInvalidValue;
   const int mode = att8 ? kModeFp8 : dyn ? kModeDyn : kModeBf16;
   switch (head_dim) {
     case 64:
-      return launch_dim<64>(p, fmt, num_seqs, fused, slots, mode, stream, ev_before, ev_after);
+      return launch_dim<64>(p, fmt, num_seqs, fused, slots, tile_pages, mode, stream, ev_before,
+                            ev_after);
     case 128:
-      return launch_dim<128>(p, fmt, num_seqs, fused, slots, mode, stream, ev_before, ev_after);
+      return launch_dim<128>(p, fmt, num_seqs, fused, slots, tile_pages, mode, stream, ev_before,
+                             ev_after);
     case 256:
-      return launch_dim<256>(p, fmt, num_seqs, fused, slots, mode, stream, ev_before, ev_after);
+      return launch_dim<256>(p, fmt, num_seqs, fused, slots, tile_pages, mode, stream, ev_before,
+                             ev_after);
     default:
       return hipErrorInvalidValue;
   }

@@ -497,6 +497,9 @@ DECODE_STEP_CASES = [
     ("d256-bf16", 8, 2, 256, [300, 15], False, 21),
     ("g8-fp8", 64, 8, 128, [2050, 48], True, 0),
     ("g16-fp8", 64, 4, 128, [1500, 33], True, 0),
+    # head_dim 64 fp8 with LDS-staged runs of 4 and 8 pages: 4-page tiles
+    ("d64-fp8-g8-4page", 64, 8, 64, [8192], True, 0),
+    ("d64-fp8-g8-4page-ragged", 64, 8, 64, [8192, 3000], True, 0),
     ("g12-bf16-window", 48, 4, 64, [900, 200], False, 77),
 ]
 
