@@ -1010,13 +1010,17 @@ __device__ __forceinline__ float wave_all(float x) {
 }
 
 template <int D, int NPC>
-__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const DecodeParams p) {
   static_assert(NPC % 4 == 0 && NPC <= kWave, "a chunk is at most one wave of partitions");
-  __shared__ __align__(16) float sw[D / kWave][NPC];
-  const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int d = threadIdx.x;              // D threads: wave w owns dims 64w..64w+63
-  const int hq = blockIdx.x;
+  // One wave per work-group: work-group x merges dims 64*(x mod D/64) .. +63
+  // of query head x / (D/64), so the partials of a row are read by D/64
+  // compute units at once rather than one.
+  constexpr int kSlices = D / kWave;
+  __shared__ __align__(16) float sw[1][NPC];
+  const int lane = threadIdx.x;
+  const int wave = 0;
+  const int d = (int)(blockIdx.x % kSlices) * kWave + lane;
+  const int hq = (int)(blockIdx.x / kSlices);
   const int b = blockIdx.y;
   if (p.row_limit && b >= *p.row_limit) return;   // past the last row (prefill merge)
   const int h = hq / p.group;
@@ -1071,14 +1075,14 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const DecodePara
 
 template <int D>
 static void launch_reduce(const DecodeParams& pr, int num_seqs, hipStream_t stream) {
-  const dim3 grid((unsigned)pr.num_q_heads, (unsigned)num_seqs);
+  const dim3 grid((unsigned)(pr.num_q_heads * (D / kWave)), (unsigned)num_seqs);
   static_assert(kReduceChunk == 64, "the largest chunk below is the workspace's slack");
   if (pr.num_parts <= 16)
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 16>), grid, dim3(D), 0, stream, pr);
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 16>), grid, dim3(kWave), 0, stream, pr);
   else if (pr.num_parts <= 32)
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 32>), grid, dim3(D), 0, stream, pr);
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 32>), grid, dim3(kWave), 0, stream, pr);
   else
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 64>), grid, dim3(D), 0, stream, pr);
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 64>), grid, dim3(kWave), 0, stream, pr);
 }
 
 // Arithmetic modes of the split kernel.
