@@ -222,6 +222,42 @@ def time_steps(torch, kv, stack, steps, warmup, profile=True):
     return ms, (split_ms / n if n else None), n
 
 
+def same_size_read_us(torch, kv, nbytes, min_total=2 * GIB, reps=10):
+    """Graph-timed plain streaming read (kvq_stream_read) of nbytes per
+    launch, over enough distinct buffers that the Infinity Cache cannot
+    serve them: the mean launch time, best of 1024 and 4096 work-groups.
+    What a read-only kernel with no attention work takes for one layer's
+    bytes."""
+    nbytes = nbytes // 16 * 16
+    n = max(8, min(64, math.ceil(min_total / nbytes)))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(n)]
+    best = None
+    for blocks in (1024, 4096):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        kv.stream_read(bufs[0], sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for b in bufs:
+                kv.stream_read(b, sink)
+        for _ in range(3):
+            g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        best = us if best is None else min(best, us)
+        del g
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
 def time_steps_graph(torch, stack, steps, warmup, per_step=False):
     """The step captured once as a HIP graph, replayed: mean ms per step
     (and, with per_step, the sorted ms of every replay of a second pass).
@@ -835,6 +871,13 @@ def main():
         "split_kernel_frac_of_read": round(achieved / ceiling, 4) if achieved else None,
         "step_frac_of_read": round(value / ceiling, 4),
         "step_frac_of_copy": round(value / copy_gbs, 4)}
+    # the same read, one launch per layer's split bytes, graph-replayed: the
+    # time a kernel with no attention work needs for this layer's bytes
+    rd_us = same_size_read_us(torch, kv, split_bytes)
+    result["measured_ceilings"]["same_size_read_us"] = round(rd_us, 3)
+    result["measured_ceilings"]["split_kernel_over_same_size_read"] = (
+        round(split_ms * 1e3 / rd_us, 4) if split_ms else None)
+    result["measured_ceilings"]["step_over_same_size_read"] = round(ms * 1e3 / NL / rd_us, 4)
 
     if not args.no_sweep and args.workload == "llama8b":
         contexts = [16, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
