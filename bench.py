@@ -229,7 +229,7 @@ def same_size_read_us(torch, kv, nbytes, min_total=2 * GIB, reps=10):
     What a read-only kernel with no attention work takes for one layer's
     bytes."""
     nbytes = nbytes // 16 * 16
-    n = max(8, min(64, math.ceil(min_total / nbytes)))
+    n = max(8, min(256, math.ceil(min_total / nbytes)))
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(n)]
     best = None
     for blocks in (1024, 4096):
@@ -467,13 +467,20 @@ def sweep(torch, kv, w, contexts, steps, warmup):
             _, split_ms, _ = time_steps(torch, kv, st, 2, 1)
             us_layer = ms * 1e3 / NL
             gbs = st.total_kv_bytes() / (ms * 1e-3) / 1e9
-            rows.append(dict(cache=dt, context=ctx, layers=NL, us_per_layer=round(us_layer, 3),
-                             kv_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
-                             split_us=round(split_ms * 1e3, 3) if split_ms else None))
-            log(f"sweep {dt:8s} ctx={ctx:6d} layers={NL:3d} {us_layer:8.2f} us/layer "
-                f"{gbs:7.1f} GB/s split={rows[-1]['split_us']} us")
+            d0 = st.layers[0]["desc"]
+            split_bytes = st.split_bytes(d0) + st.write_bytes(d0)
             del st
             torch.cuda.empty_cache()
+            # (from 4096 positions: smaller reads would run from the Infinity Cache)
+            read_us = same_size_read_us(torch, kv, split_bytes) if ctx >= 4096 else None
+            rows.append(dict(cache=dt, context=ctx, layers=NL, us_per_layer=round(us_layer, 3),
+                             kv_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+                             split_us=round(split_ms * 1e3, 3) if split_ms else None,
+                             same_size_read_us=round(read_us, 3) if read_us else None,
+                             step_over_same_size_read=round(us_layer / read_us, 3)
+                             if read_us else None))
+            log(f"sweep {dt:8s} ctx={ctx:6d} layers={NL:3d} {us_layer:8.2f} us/layer "
+                f"{gbs:7.1f} GB/s split={rows[-1]['split_us']} us read={read_us} us")
     fits = {}
     for dt in ("fp8_e4m3", "bf16"):
         pts = [(r["context"], r["us_per_layer"]) for r in rows
