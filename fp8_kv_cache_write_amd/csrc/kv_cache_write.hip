@@ -16,6 +16,23 @@
 
 namespace kvfp8 {
 
+// Quantise 16 bf16 values (two 16-byte words) to 16 codes: 4 words, byte b of
+// word j the code of element 4j + b.
+template <int FMT>
+__device__ __forceinline__ void quantize16(const uint32_t* w, float s, uint32_t (&q)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int e = j * 4 + b;
+      const uint32_t bits = (w[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
+      o |= fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / s) << (8 * b);
+    }
+    q[j] = o;
+  }
+}
+
 // Quantise 16 dims (d0 .. d0+15) of row r of K and of V and store them into
 // the (page, head) blocks kb, vb: K as one 16-byte store (one layout chunk),
 // V as 16 byte stores (the V layout interleaves 4 rows per dim).
@@ -23,71 +40,119 @@ template <int FMT>
 __device__ __forceinline__ void store_chunk_fp8(uint8_t* kb, uint8_t* vb, int r, int d0,
                                                 const uint32_t* kw, const uint32_t* vw,
                                                 float sk, float sv) {
-  uint32_t kq[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int e = j * 4 + b;
-      const uint32_t bits = (kw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-      w |= fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sk) << (8 * b);
-    }
-    kq[j] = w;
-  }
+  uint32_t kq[4], vq[4];
+  quantize16<FMT>(kw, sk, kq);
+  quantize16<FMT>(vw, sv, vq);
   *reinterpret_cast<uint4*>(kb + k_byte<1>(r, d0)) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t bits = (vw[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-    vb[v_byte<1>(r, d0 + e)] = (uint8_t)fp8_encode_sat<FMT>(bf16_bits_to_f32(bits) / sv);
-  }
+  for (int e = 0; e < 16; ++e) vb[v_byte<1>(r, d0 + e)] = (uint8_t)(vq[e / 4] >> (8 * (e % 4)));
 }
 
-// One thread per (token, kv head, 16-dim chunk). It reads 16 bf16 of K and of
-// V (two 16-byte loads each) and writes
-//   fp8 : K as one 16-byte store (one layout chunk), V as 16 byte stores
-//         (the V layout interleaves 4 rows per dim, so a row's dims are 4 bytes
-//         apart);
+// Lanes of one wave exchange words through LDS: the fences and the wave
+// barrier keep the compiler from moving the LDS accesses across it; the LDS
+// itself serves one wave's accesses in order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kWriteThreads = 256;
+
+// Four lanes per (quad of tokens, kv head, 16-dim chunk): lane j of a quad
+// handles token 4*tq + j. Each lane reads 16 bf16 of K and of V (two 16-byte
+// loads each) and writes
+//   fp8 : K as one 16-byte store (one layout chunk). V: when the quad's four
+//         tokens go to four consecutive slots starting at a multiple of 4 (a
+//         row quad of one page, as a prefill writes them), the lanes swap
+//         their codes through LDS and lane j stores the 16 bytes of dims
+//         4j .. 4j+3 of the chunk for all four rows; otherwise 16 byte stores
+//         (the V layout interleaves 4 rows per dim, so a row's dims are 4
+//         bytes apart);
 //   bf16: K as two 16-byte stores, V as 16 two-byte stores.
 template <int FMT>
-__global__ __launch_bounds__(256) void kv_cache_write_kernel(
+__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int64_t* __restrict__ slots, int64_t num_tokens, int num_kv_heads,
     int head_dim, uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
     int64_t num_pages, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, int scale_per_head) {
-  const int chunks = head_dim / 16;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = num_tokens * num_kv_heads * chunks;
-  if (gid >= total) return;
-  const int c = (int)(gid % chunks);
-  const int64_t th = gid / chunks;
-  const int h = (int)(th % num_kv_heads);
-  const int64_t t = th / num_kv_heads;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_pages * kPage) return;   // skipped / outside the pool
-  const int64_t page = slot / kPage;
-  const int r = (int)(slot % kPage);
-
-  const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)c * 16;
-  const uint4* ks = reinterpret_cast<const uint4*>(k + src);
-  const uint4* vs = reinterpret_cast<const uint4*>(v + src);
-  uint4 kx[2] = {ks[0], ks[1]};
-  uint4 vx[2] = {vs[0], vs[1]};
-  const uint32_t* kw = reinterpret_cast<const uint32_t*>(kx);
-  const uint32_t* vw = reinterpret_cast<const uint32_t*>(vx);
-
   constexpr bool FP8 = FMT != kFmtBf16;
   constexpr int E = FP8 ? 1 : 2;
+  const int chunks = head_dim / 16;
+  const int64_t quads = (num_tokens + 3) / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = quads * 4 * num_kv_heads * chunks;
+  const int j = (int)(gid & 3);
+  const int64_t rest = gid >> 2;
+  const int c = (int)(rest % chunks);
+  const int64_t th = rest / chunks;
+  const int h = (int)(th % num_kv_heads);
+  const int64_t t = (th / num_kv_heads) * 4 + j;
+  // no lane returns before the quad's ballot: every lane of a wave takes part
+  const bool live = gid < total && t < num_tokens;
+  const int64_t slot = live ? slots[t] : -1;
+  const bool ok = slot >= 0 && slot < num_pages * kPage;   // else skipped / outside the pool
+  const int64_t page = ok ? slot / kPage : 0;
+  const int r = (int)(slot & (kPage - 1));
   const int64_t pb = (int64_t)kPage * head_dim * E;
   uint8_t* kb = k_cache + (page * num_kv_heads + h) * pb;
   uint8_t* vb = v_cache + (page * num_kv_heads + h) * pb;
   const int d0 = c * 16;
 
+  uint4 kx[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  uint4 vx[2] = {kx[0], kx[1]};
+  if (ok) {
+    const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)c * 16;
+    const uint4* ks = reinterpret_cast<const uint4*>(k + src);
+    const uint4* vs = reinterpret_cast<const uint4*>(v + src);
+    kx[0] = ks[0];
+    kx[1] = ks[1];
+    vx[0] = vs[0];
+    vx[1] = vs[1];
+  }
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(kx);
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(vx);
+
   if constexpr (FP8) {
-    store_chunk_fp8<FMT>(kb, vb, r, d0, kw, vw, k_scale[scale_per_head ? h : 0],
-                         v_scale[scale_per_head ? h : 0]);
+    const float sk = k_scale[scale_per_head ? h : 0];
+    const float sv = v_scale[scale_per_head ? h : 0];
+    // lane j's slot must be the quad's first slot + j, that slot a multiple of 4
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t slot0 = __shfl(slot, lane & ~3);
+    const bool run = ok && slot == slot0 + j && (slot0 & 3) == 0;
+    const uint64_t bal = __ballot(run);
+    const bool quad = ((bal >> (lane & ~3)) & 0xFull) == 0xFull;
+    uint32_t kq[4], vq[4];
+    quantize16<FMT>(kw, sk, kq);
+    quantize16<FMT>(vw, sv, vq);
+    if (ok)
+      *reinterpret_cast<uint4*>(kb + k_byte<1>(r, d0)) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+    // [lane / 4][row j][word]: the quad's codes, four words per row
+    __shared__ uint32_t xchg[kWriteThreads / 4][4][4];
+    const int qi = threadIdx.x >> 2;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) xchg[qi][j][w] = vq[w];
+    wave_lds_sync();
+    if (quad) {
+      // lane j: dims 4j .. 4j+3 of the chunk, rows r-j .. r-j+3 (one 16-byte span)
+      uint32_t W[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) W[i] = xchg[qi][i][j];
+      uint32_t o[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        o[b] = ((W[0] >> (8 * b)) & 0xFFu) | (((W[1] >> (8 * b)) & 0xFFu) << 8) |
+               (((W[2] >> (8 * b)) & 0xFFu) << 16) | (((W[3] >> (8 * b)) & 0xFFu) << 24);
+      *reinterpret_cast<uint4*>(vb + v_byte<1>(r - j, d0 + 4 * j)) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    } else if (ok) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        vb[v_byte<1>(r, d0 + e)] = (uint8_t)(vq[e / 4] >> (8 * (e % 4)));
+    }
   } else {
+    if (!ok) return;
     // bf16 layers keep the bits: the skip-layer path.
     *reinterpret_cast<uint4*>(kb + k_byte<2>(r, d0)) = kx[0];
     *reinterpret_cast<uint4*>(kb + k_byte<2>(r, d0 + 8)) = kx[1];
@@ -251,19 +316,20 @@ hipError_t launch_kv_cache_write(int fmt, const uint16_t* k, const uint16_t* v,
                                  uint8_t* v_cache, int64_t num_pages,
                                  const float* k_scale, const float* v_scale,
                                  int scale_per_head, hipStream_t stream) {
-  const int64_t total = num_tokens * num_kv_heads * (head_dim / 16);
+  // four lanes per quad of tokens (the last quad may be partial)
+  const int64_t total = (num_tokens + 3) / 4 * 4 * num_kv_heads * (head_dim / 16);
   if (total == 0) return hipSuccess;
-  const int64_t blocks = (total + 255) / 256;
+  const int64_t blocks = (total + kWriteThreads - 1) / kWriteThreads;
   if (fmt == kFmtE4M3)
-    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtE4M3>, dim3((unsigned)blocks), dim3(256),
+    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtE4M3>, dim3((unsigned)blocks), dim3(kWriteThreads),
                        0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
                        k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
   else if (fmt == kFmtE5M2)
-    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtE5M2>, dim3((unsigned)blocks), dim3(256),
+    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtE5M2>, dim3((unsigned)blocks), dim3(kWriteThreads),
                        0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
                        k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
   else if (fmt == kFmtBf16)
-    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtBf16>, dim3((unsigned)blocks), dim3(256),
+    hipLaunchKernelGGL(kv_cache_write_kernel<kFmtBf16>, dim3((unsigned)blocks), dim3(kWriteThreads),
                        0, stream, k, v, slots, num_tokens, num_kv_heads, head_dim,
                        k_cache, v_cache, num_pages, k_scale, v_scale, scale_per_head);
   else

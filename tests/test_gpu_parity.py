@@ -166,6 +166,45 @@ def test_kv_cache_write_skips_negative_slots():
     assert np.array_equal(host(g.v_cache), o.v_cache)
 
 
+@pytest.mark.parametrize("fp8", [True, False])
+def test_kv_cache_write_mixed_slot_runs(fp8):
+    # The write stores a V row quad in 16-byte pieces only when four
+    # consecutive tokens go to four consecutive slots starting at a multiple
+    # of 4; every other pattern takes the byte stores. A mix of both, with
+    # skipped slots, runs broken inside a quad, runs starting off a quad, a
+    # quad split across tokens of different pages and a ragged tail (T % 4 =
+    # 3), against the oracle's whole caches (poison included).
+    Hkv, D, npg = 3, 128, 12
+    slots = ([0, 1, 2, 3] + [20, 21, 22, 23] +          # aligned runs
+             [5, 6, 7, 8] +                            # a run starting off a quad
+             [36, 37, -1, 39] +                        # a skipped slot inside a quad
+             [44, 45, 47, 46] +                        # a quad in the wrong order
+             [60, 61, 62, 63] + [64, 65, 66, 67] +     # the last quad of one page, the first of the next
+             [12, 13, 14, 15 + 16 * 11] +              # a run leaving the page in its last token
+             [100, 101, 102, 103] + [181, 182, 183])   # aligned, then a ragged tail
+    T = len(slots)
+    r = np.random.default_rng(11)
+    k = synth.bf16_bits(r.standard_normal((T, Hkv, D)).astype(np.float32) * 3)
+    v = synth.bf16_bits(r.standard_normal((T, Hkv, D)).astype(np.float32) * 3)
+    desc = kv.layer_desc(Hkv, Hkv, D, "fp8_e4m3" if fp8 else "bf16")
+    pc = synth.poisoned_cache(npg, Hkv, D, fp8)
+    kc, vc = torch.from_numpy(pc).to(dev()), torch.from_numpy(pc).to(dev())
+    sl = np.array(slots, np.int64)
+    ks = vs = None
+    oks = ovs = None
+    if fp8:
+        oks = oracle.scale_from_amax(k, True)
+        ovs = oracle.scale_from_amax(v, True)
+        ks = torch.from_numpy(oks).to(dev())
+        vs = torch.from_numpy(ovs).to(dev())
+    kv.kv_cache_write(desc, bf16_dev(k), bf16_dev(v), i64_dev(sl), kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    okc, ovc = pc.copy(), pc.copy()
+    oracle.kv_cache_write(okc, ovc, k, v, sl, oracle.FP8 if fp8 else oracle.BF16, True, oks, ovs)
+    assert np.array_equal(host(kc), okc)
+    assert np.array_equal(host(vc), ovc)
+
+
 @pytest.mark.parametrize("scale", [1.0, 0.0071428573, 0.2678571343, 7.0])
 def test_kv_cache_write_every_bf16_value(scale):
     # all 65536 bf16 patterns (NaN, Inf, subnormals included) as K and V
