@@ -33,21 +33,6 @@ __device__ __forceinline__ void quantize16(const uint32_t* w, float s, uint32_t 
   }
 }
 
-// Quantise 16 dims (d0 .. d0+15) of row r of K and of V and store them into
-// the (page, head) blocks kb, vb: K as one 16-byte store (one layout chunk),
-// V as 16 byte stores (the V layout interleaves 4 rows per dim).
-template <int FMT>
-__device__ __forceinline__ void store_chunk_fp8(uint8_t* kb, uint8_t* vb, int r, int d0,
-                                                const uint32_t* kw, const uint32_t* vw,
-                                                float sk, float sv) {
-  uint32_t kq[4], vq[4];
-  quantize16<FMT>(kw, sk, kq);
-  quantize16<FMT>(vw, sv, vq);
-  *reinterpret_cast<uint4*>(kb + k_byte<1>(r, d0)) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) vb[v_byte<1>(r, d0 + e)] = (uint8_t)(vq[e / 4] >> (8 * (e % 4)));
-}
-
 // Lanes of one wave exchange words through LDS: the fences and the wave
 // barrier keep the compiler from moving the LDS accesses across it; the LDS
 // itself serves one wave's accesses in order.
@@ -183,51 +168,106 @@ __device__ __forceinline__ uint32_t max_mag_bits(const uint32_t* w) {
 // (pool[page][head][row]) and writes the codes as the static write does.
 constexpr int kMaxDynHeads = 256;
 template <int FMT, bool ALL_HEADS>
-__global__ __launch_bounds__(256) void kv_cache_write_dyn_kernel(
+__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_dyn_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int64_t* __restrict__ slots, int num_kv_heads, int head_dim,
+    const int64_t* __restrict__ slots, int64_t num_tokens, int num_kv_heads, int head_dim,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, int64_t num_pages,
     float* __restrict__ k_pool, float* __restrict__ v_pool) {
+  // One work-group per quad of tokens; item it = 4 * (head, chunk) + j is
+  // token 4 * blockIdx.x + j, so the four tokens of a quad sit in adjacent
+  // lanes as in the static write.
   constexpr float fmax = FMT == kFmtE5M2 ? 57344.0f : 448.0f;
-  const int64_t t = blockIdx.x;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_pages * kPage) return;   // the whole work-group skips
-  const int64_t page = slot / kPage;
-  const int r = (int)(slot % kPage);
+  const int64_t t0 = (int64_t)blockIdx.x * 4;
   const int chunks = head_dim / 16;
-  const int items = num_kv_heads * chunks;
-  __shared__ uint32_t km[kMaxDynHeads], vm[kMaxDynHeads];
-  for (int i = threadIdx.x; i < num_kv_heads; i += blockDim.x) km[i] = vm[i] = 0u;
+  const int items4 = 4 * num_kv_heads * chunks;
+  __shared__ uint32_t km[4][kMaxDynHeads], vm[4][kMaxDynHeads];
+  __shared__ uint32_t xchg[kWriteThreads / 4][4][4];
+  for (int i = threadIdx.x; i < 4 * num_kv_heads; i += blockDim.x)
+    km[i / num_kv_heads][i % num_kv_heads] = vm[i / num_kv_heads][i % num_kv_heads] = 0u;
   __syncthreads();
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int h = it / chunks;
-    const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)(it % chunks) * 16;
+  // pass 1: the largest magnitude of each token's K and V (per head, or over
+  // all heads), as integer maxima of bf16 magnitude bits
+  for (int it = threadIdx.x; it < items4; it += blockDim.x) {
+    const int j = it & 3, item = it >> 2;
+    const int64_t t = t0 + j;
+    if (t >= num_tokens) continue;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_pages * kPage) continue;   // the token is skipped
+    const int h = item / chunks;
+    const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)(item % chunks) * 16;
     const uint4* ks = reinterpret_cast<const uint4*>(k + src);
     const uint4* vs = reinterpret_cast<const uint4*>(v + src);
     const uint4 kx[2] = {ks[0], ks[1]}, vx[2] = {vs[0], vs[1]};
-    atomicMax(&km[ALL_HEADS ? 0 : h], max_mag_bits(reinterpret_cast<const uint32_t*>(kx)));
-    atomicMax(&vm[ALL_HEADS ? 0 : h], max_mag_bits(reinterpret_cast<const uint32_t*>(vx)));
+    atomicMax(&km[j][ALL_HEADS ? 0 : h], max_mag_bits(reinterpret_cast<const uint32_t*>(kx)));
+    atomicMax(&vm[j][ALL_HEADS ? 0 : h], max_mag_bits(reinterpret_cast<const uint32_t*>(vx)));
   }
   __syncthreads();
+  // pass 2: s = amax / fmax (1 for zero, NaN for NaN), the pools, the codes
   const int64_t pb = (int64_t)kPage * head_dim;
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int h = it / chunks, c = it % chunks;
-    const float ak = bf16_bits_to_f32(km[ALL_HEADS ? 0 : h]);
-    const float av = bf16_bits_to_f32(vm[ALL_HEADS ? 0 : h]);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int qi = threadIdx.x >> 2;
+  for (int it = threadIdx.x; it < items4; it += blockDim.x) {
+    const int j = it & 3, item = it >> 2;
+    const int h = item / chunks, c = item % chunks;
+    const int64_t t = t0 + j;
+    const int64_t slot = t < num_tokens ? slots[t] : -1;
+    const bool ok = slot >= 0 && slot < num_pages * kPage;
+    const int64_t page = ok ? slot / kPage : 0;
+    const int r = (int)(slot & (kPage - 1));
+    const float ak = bf16_bits_to_f32(km[j][ALL_HEADS ? 0 : h]);
+    const float av = bf16_bits_to_f32(vm[j][ALL_HEADS ? 0 : h]);
     const float sk = ak == 0.0f ? 1.0f : ak / fmax;
     const float sv = av == 0.0f ? 1.0f : av / fmax;
-    const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)c * 16;
-    const uint4* ks = reinterpret_cast<const uint4*>(k + src);
-    const uint4* vs = reinterpret_cast<const uint4*>(v + src);
-    const uint4 kx[2] = {ks[0], ks[1]}, vx[2] = {vs[0], vs[1]};
-    store_chunk_fp8<FMT>(k_cache + (page * num_kv_heads + h) * pb,
-                         v_cache + (page * num_kv_heads + h) * pb, r, c * 16,
-                         reinterpret_cast<const uint32_t*>(kx),
-                         reinterpret_cast<const uint32_t*>(vx), sk, sv);
-    if (c == 0) {
-      k_pool[(page * num_kv_heads + h) * kPage + r] = sk;
-      v_pool[(page * num_kv_heads + h) * kPage + r] = sv;
+    uint4 kx[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+    uint4 vx[2] = {kx[0], kx[1]};
+    if (ok) {
+      const int64_t src = (t * num_kv_heads + h) * head_dim + (int64_t)c * 16;
+      const uint4* ks = reinterpret_cast<const uint4*>(k + src);
+      const uint4* vs = reinterpret_cast<const uint4*>(v + src);
+      kx[0] = ks[0];
+      kx[1] = ks[1];
+      vx[0] = vs[0];
+      vx[1] = vs[1];
     }
+    uint32_t kq[4], vq[4];
+    quantize16<FMT>(reinterpret_cast<const uint32_t*>(kx), sk, kq);
+    quantize16<FMT>(reinterpret_cast<const uint32_t*>(vx), sv, vq);
+    uint8_t* kb = k_cache + (page * num_kv_heads + h) * pb;
+    uint8_t* vb = v_cache + (page * num_kv_heads + h) * pb;
+    const int d0 = c * 16;
+    if (ok) {
+      *reinterpret_cast<uint4*>(kb + k_byte<1>(r, d0)) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+      if (c == 0) {
+        k_pool[(page * num_kv_heads + h) * kPage + r] = sk;
+        v_pool[(page * num_kv_heads + h) * kPage + r] = sv;
+      }
+    }
+    // V: 16-byte spans when the quad's tokens fill one row quad (see the
+    // static write), else byte stores
+    const int64_t slot0 = __shfl(slot, lane & ~3);
+    const bool run = ok && slot == slot0 + j && (slot0 & 3) == 0;
+    const uint64_t bal = __ballot(run);
+    const bool quad = ((bal >> (lane & ~3)) & 0xFull) == 0xFull;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) xchg[qi][j][w] = vq[w];
+    wave_lds_sync();
+    if (quad) {
+      uint32_t W[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) W[i] = xchg[qi][i][j];
+      uint32_t o[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        o[b] = ((W[0] >> (8 * b)) & 0xFFu) | (((W[1] >> (8 * b)) & 0xFFu) << 8) |
+               (((W[2] >> (8 * b)) & 0xFFu) << 16) | (((W[3] >> (8 * b)) & 0xFFu) << 24);
+      *reinterpret_cast<uint4*>(vb + v_byte<1>(r - j, d0 + 4 * j)) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    } else if (ok) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        vb[v_byte<1>(r, d0 + e)] = (uint8_t)(vq[e / 4] >> (8 * (e % 4)));
+    }
+    wave_lds_sync();   // this round's reads before the next round's writes
   }
 }
 
@@ -368,12 +408,14 @@ hipError_t launch_kv_cache_write_dyn(int fmt, const uint16_t* k, const uint16_t*
                                      int all_heads, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   if (num_kv_heads > kMaxDynHeads || num_tokens > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  const int items = num_kv_heads * (head_dim / 16);
-  const int threads = std::min(256, (items + kWave - 1) / kWave * kWave);
-  const dim3 grid((unsigned)num_tokens), block((unsigned)threads);
+  // one work-group per quad of tokens, four lanes per (head, 16-dim chunk)
+  const int items4 = 4 * num_kv_heads * (head_dim / 16);
+  const int threads = std::min(kWriteThreads, (items4 + kWave - 1) / kWave * kWave);
+  const dim3 grid((unsigned)((num_tokens + 3) / 4)), block((unsigned)threads);
 #define KVFP8_DYN(F, A)                                                                      \
   hipLaunchKernelGGL((kv_cache_write_dyn_kernel<F, A>), grid, block, 0, stream, k, v, slots, \
-                     num_kv_heads, head_dim, k_cache, v_cache, num_pages, k_pool, v_pool)
+                     num_tokens, num_kv_heads, head_dim, k_cache, v_cache, num_pages,         \
+                     k_pool, v_pool)
   if (fmt == kFmtE4M3) {
     if (all_heads) KVFP8_DYN(kFmtE4M3, true); else KVFP8_DYN(kFmtE4M3, false);
   } else if (fmt == kFmtE5M2) {

@@ -76,6 +76,39 @@ def test_dynamic_write_is_bit_exact(label, Hq, Hkv, D, lens, fmt, dyn):
     assert same_bits(host(g.v_scale), o.vs), label
 
 
+@pytest.mark.parametrize("dyn", ["per_token", "per_token_head"])
+def test_dynamic_write_mixed_slot_runs(dyn):
+    # 16-byte V stores for aligned runs of 4 slots, byte stores otherwise
+    # (skipped slots, broken and misaligned runs, a run leaving its page, a
+    # ragged tail), codes and scale pools against the oracle, poison included
+    Hkv, D, npg = 3, 128, 12
+    slots = ([0, 1, 2, 3] + [20, 21, 22, 23] + [5, 6, 7, 8] + [36, 37, -1, 39] +
+             [44, 45, 47, 46] + [60, 61, 62, 63] + [64, 65, 66, 67] +
+             [12, 13, 14, 15 + 16 * 11] + [100, 101, 102, 103] + [181, 182, 183])
+    T = len(slots)
+    r = np.random.default_rng(12)
+    x = r.standard_normal((2, T, Hkv, D)).astype(np.float32)
+    x *= np.exp2(r.integers(-6, 7, size=(2, T, Hkv, 1))).astype(np.float32)
+    k, v = synth.bf16_bits(x[0]), synth.bf16_bits(x[1])
+    desc = kv.layer_desc(Hkv, Hkv, D, "fp8_e4m3", dyn)
+    pc = synth.poisoned_cache(npg, Hkv, D, True)
+    kc, vc = torch.from_numpy(pc).to(dev()), torch.from_numpy(pc).to(dev())
+    kpool = torch.full((npg, Hkv, 16), float("nan"), dtype=torch.float32, device=dev())
+    vpool = kpool.clone()
+    sl = np.array(slots, np.int64)
+    kv.kv_cache_write_dynamic(desc, bf16_dev(k), bf16_dev(v), torch.from_numpy(sl).to(dev()),
+                              kc, vc, kpool, vpool)
+    torch.cuda.synchronize()
+    okc, ovc = pc.copy(), pc.copy()
+    okp = np.full((npg, Hkv, 16), np.nan, np.float32)
+    ovp = okp.copy()
+    mode = oracle.PER_TOKEN if dyn == "per_token" else oracle.PER_TOKEN_HEAD
+    oracle.kv_cache_write_dyn(okc, ovc, k, v, sl, oracle.FP8, mode, okp, ovp)
+    assert np.array_equal(host(kc), okc)
+    assert np.array_equal(host(vc), ovc)
+    assert same_bits(host(kpool), okp) and same_bits(host(vpool), ovp)
+
+
 def test_dynamic_write_special_tokens():
     # all-zero token: scale 1; NaN element: NaN scale and NaN codes; a token
     # whose largest value is in another head (per token) or in its own head
