@@ -194,6 +194,17 @@ __device__ __forceinline__ float mfma_col_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Largest magnitude of 8 bf16 values (one 16-byte word) as bf16 bits: each
+// half-word is masked and compared on its own, so as integers NaN > Inf >
+// every finite value.
+__device__ __forceinline__ uint32_t max_mag_bits8(uint4 w) {
+  const uint32_t a = max(max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu),
+                         max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu));
+  const uint32_t b = max(max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu),
+                         max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu));
+  return max(a, b);
+}
+
 // ---------------------------------------------------------------------------
 // All-FP8 attention: one query row as e4m3 codes with s_q = amax / 448 (the
 // 4 lanes of an MFMA column hold the row, NK pieces of 8 values each; the
@@ -217,10 +228,7 @@ __device__ __forceinline__ float quantize_q_e4m3(const bf16x8 (&q)[NK], uint64_t
   for (int s = 0; s < NK; ++s) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf((float)q[s][j]));
-    const uint4 w = __builtin_bit_cast(uint4, q[s]);
-    const uint32_t m4 = max(max(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
-                            max(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
-    mag = max(mag, max(m4 & 0xFFFFu, m4 >> 16));
+    mag = max(mag, max_mag_bits8(__builtin_bit_cast(uint4, q[s])));
   }
   am = mfma_col_max(am);
   const float q_scale = am == 0.0f ? 1.0f : am / 448.0f;

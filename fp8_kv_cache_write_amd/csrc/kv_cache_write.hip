@@ -271,61 +271,63 @@ __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_dyn_kernel(
   }
 }
 
-// Static scale calibration: s = fp32(amax) / fmax over one KV head (or over
-// every head); fmax = 448 (e4m3) or 57344 (e5m2). One work-group per output
-// scale; threads stride over the tensor in 16-byte loads. NaN anywhere gives
-// NaN, amax == 0 gives 1.
-__global__ __launch_bounds__(1024) void scale_from_amax_kernel(
-    const uint16_t* __restrict__ x, int64_t num_tokens, int num_kv_heads,
-    int head_dim, int per_head, float fmax, float* __restrict__ scale_out) {
-  const int h_out = blockIdx.x;
-  const int chunks = head_dim / 8;                 // 8 bf16 per 16 bytes
-  const int heads_here = per_head ? 1 : num_kv_heads;
-  const int64_t per_token = (int64_t)heads_here * chunks;
-  const int64_t total = num_tokens * per_token;
-  float amax = 0.0f;
-  bool nan = false;
-  for (int64_t i = threadIdx.x; i < total; i += blockDim.x) {
-    const int64_t t = i / per_token;
-    const int64_t rem = i % per_token;
-    const int h = per_head ? h_out : (int)(rem / chunks);
-    const int c = (int)(rem % chunks);
-    const uint4 w = *reinterpret_cast<const uint4*>(
-        x + (t * num_kv_heads + h) * head_dim + c * 8);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float f = fabsf(bf16_bits_to_f32((ws[j / 2] >> (16 * (j % 2))) & 0xFFFFu));
-      nan |= !(f == f);
-      amax = f > amax ? f : amax;
+// Static scale calibration: s[o] = fp32(amax) / fmax over the bf16 tensor
+// x [T][Hkv][D], per KV head (o = head) or per tensor (one o over every
+// head); fmax = 448 (e4m3) or 57344 (e5m2). NaN anywhere gives NaN, amax ==
+// 0 gives 1. Three launches, no workspace: the output words are cleared,
+// then many work-groups per output fold the largest bf16 magnitude bits of
+// their share into them with an integer atomicMax (as integers those bits
+// order NaN above Inf above every finite value), then the bits become the
+// scale.
+constexpr int kAmaxThreads = 256;
+
+__global__ void amax_clear_kernel(uint32_t* __restrict__ bits, int n_out) {
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o < n_out) bits[o] = 0u;
+}
+
+// Work-group (s, o) folds tokens [s * tps, (s + 1) * tps) of output o.
+__global__ __launch_bounds__(kAmaxThreads) void amax_bits_kernel(
+    const uint16_t* __restrict__ x, int64_t num_tokens, int num_kv_heads, int head_dim,
+    int per_head, int64_t tps, uint32_t* __restrict__ bits) {
+  const int o = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * tps;
+  const int64_t t1 = t0 + tps < num_tokens ? t0 + tps : num_tokens;
+  // 16-byte chunks of one token that belong to output o, and where they start
+  const int chunks = (per_head ? 1 : num_kv_heads) * (head_dim / 8);
+  const int64_t row = (int64_t)num_kv_heads * head_dim;            // bf16 per token
+  const int64_t first = per_head ? (int64_t)o * head_dim : 0;
+  uint32_t m = 0u;
+  if (t1 > t0) {
+    const int64_t n = (t1 - t0) * chunks;
+    for (int64_t i = threadIdx.x; i < n; i += kAmaxThreads) {
+      const int64_t t = t0 + i / chunks;
+      const int c = (int)(i % chunks);
+      const uint4 w = *reinterpret_cast<const uint4*>(x + t * row + first + (int64_t)c * 8);
+      m = max(m, max_mag_bits8(w));
     }
   }
-  __shared__ float red[1024 / kWave];
-  __shared__ int rnan[1024 / kWave];
-  for (int off = kWave / 2; off > 0; off /= 2) {
-    const float o = __shfl_xor(amax, off);
-    amax = o > amax ? o : amax;
-  }
-  const int any_nan = __any(nan) ? 1 : 0;
-  const int wid = threadIdx.x / kWave;
-  if (threadIdx.x % kWave == 0) {
-    red[wid] = amax;
-    rnan[wid] = any_nan;
-  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t red[kAmaxThreads / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float m = 0.0f;
-    int n = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
-      m = red[w] > m ? red[w] : m;
-      n |= rnan[w];
-    }
-    float s;
-    if (n) s = __builtin_nanf("");
-    else if (m == 0.0f) s = 1.0f;
-    else s = m / fmax;
-    scale_out[h_out] = s;
+#pragma unroll
+    for (int w = 1; w < kAmaxThreads / kWave; ++w) m = max(m, red[w]);
+    if (m != 0u) atomicMax(&bits[o], m);
   }
+}
+
+__global__ void amax_finish_kernel(uint32_t* __restrict__ bits, int n_out, float fmax) {
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= n_out) return;
+  const uint32_t b = bits[o];
+  float s;
+  if (b > 0x7F80u) s = __builtin_nanf("");        // a NaN was present
+  else if (b == 0u) s = 1.0f;                     // all zero
+  else s = bf16_bits_to_f32(b) / fmax;            // Inf gives Inf
+  reinterpret_cast<float*>(bits)[o] = s;
 }
 
 // Flat quantiser: out[i] = fp8(x[i] / s), 4 elements per thread.
@@ -380,9 +382,20 @@ hipError_t launch_kv_cache_write(int fmt, const uint16_t* k, const uint16_t* v,
 hipError_t launch_scale_from_amax(const uint16_t* x, int64_t num_tokens,
                                   int num_kv_heads, int head_dim, int per_head,
                                   float fmax, float* scale_out, hipStream_t stream) {
-  const int blocks = per_head ? num_kv_heads : 1;
-  hipLaunchKernelGGL(scale_from_amax_kernel, dim3(blocks), dim3(1024), 0, stream, x,
-                     num_tokens, num_kv_heads, head_dim, per_head, fmax, scale_out);
+  const int n_out = per_head ? num_kv_heads : 1;
+  const dim3 small((unsigned)((n_out + 255) / 256)), small_block(256);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(scale_out);   // holds magnitude bits meanwhile
+  hipLaunchKernelGGL(amax_clear_kernel, small, small_block, 0, stream, bits, n_out);
+  if (num_tokens > 0) {
+    // about 1024 work-groups in all, each a contiguous run of tokens
+    const int64_t slices = std::max<int64_t>(1, std::min<int64_t>(num_tokens, 1024 / n_out));
+    const int64_t tps = (num_tokens + slices - 1) / slices;
+    const int64_t used = (num_tokens + tps - 1) / tps;
+    hipLaunchKernelGGL(amax_bits_kernel, dim3((unsigned)used, (unsigned)n_out),
+                       dim3(kAmaxThreads), 0, stream, x, num_tokens, num_kv_heads, head_dim,
+                       per_head, tps, bits);
+  }
+  hipLaunchKernelGGL(amax_finish_kernel, small, small_block, 0, stream, bits, n_out, fmax);
   return hipGetLastError();
 }
 

@@ -115,6 +115,7 @@ def test_scale_from_amax_bit_exact(per_head):
     k = case.k_new.copy()
     k[5, 2, 7] = 0x7FC0                       # NaN in head 2
     k[:, 3, :] = 0                            # all-zero head 3
+    k[9, 1, 3] = 0xFF80                       # -Inf in head 1: its scale is +Inf
     desc = kv.layer_desc(8, 4, 128, scale_mode="per_kv_head" if per_head else "per_tensor")
     out = torch.empty(4 if per_head else 1, dtype=torch.float32, device=dev())
     kv.kv_scale_from_amax(desc, bf16_dev(k), out)
@@ -124,6 +125,10 @@ def test_scale_from_amax_bit_exact(per_head):
     k2 = case.k_new
     kv.kv_scale_from_amax(desc, bf16_dev(k2), out)
     assert np.array_equal(host(out), oracle.scale_from_amax(k2, per_head))
+    # many work-groups per scale: a long tensor
+    big = synth.decode_case(32, 8, 4, 128, [20000, 3001], values="normal").k_new
+    kv.kv_scale_from_amax(desc, bf16_dev(big), out)
+    assert np.array_equal(host(out), oracle.scale_from_amax(big, per_head))
 
 
 # ---------------------------------------------------------- cache write -----
