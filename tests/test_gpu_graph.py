@@ -1,10 +1,11 @@
 """The hot path under HIP graph capture: the decode step (write + split +
-reduce), the two-call decode, the dynamic-scale decode step and the split
-chunked prefill (prefill + merge) are captured once and replayed several
-times, with eager work of the program between the replays; every replay must
-give the eager result bit for bit. None of these launches records a memset
-(workspaces are written before they are read, and the counters of nothing
-need clearing)."""
+reduce), the two-call decode, the dynamic-scale decode step, the split
+chunked prefill (prefill + merge) and the static scale calibration with a
+prefill-sized cache write are captured once and replayed several times, with
+eager work of the program between the replays; every replay must give the
+eager result bit for bit. None of these launches records a memset
+(workspaces are written before they are read; the calibration clears its
+accumulator words with a kernel)."""
 
 import os
 
@@ -131,3 +132,27 @@ def test_split_prefill_graph(attn):
                                    workspace=ws)
 
     replay_and_compare(fn, [out], f"split prefill attn={attn}")
+
+
+@pytest.mark.parametrize("per_head", [True, False])
+def test_scale_calibration_and_prefill_write_graph(per_head):
+    # The static scale calibration (clear, many-work-group atomic maximum,
+    # finish: the caller's output words are the accumulator in between) and
+    # a prefill-sized cache write with it, captured together: every replay
+    # recomputes the scales from zero and rewrites the same bytes.
+    case = synth.decode_case(203, 32, 8, 128, [5000, 1000], shuffle=True, spare_frac=0.2)
+    desc = kv.layer_desc(32, 8, 128, scale_mode="per_kv_head" if per_head else "per_tensor")
+    k, v = bf16_dev(case.k_new), bf16_dev(case.v_new)
+    ks = torch.empty(8 if per_head else 1, dtype=torch.float32, device=dev())
+    vs = torch.empty_like(ks)
+    pc = synth.poisoned_cache(case.num_pages, 8, 128, True)
+    kc, vc = torch.from_numpy(pc).to(dev()), torch.from_numpy(pc).to(dev())
+    slots = torch.from_numpy(case.slots).to(dev())
+
+    def fn():
+        kv.kv_scale_from_amax(desc, k, ks)
+        kv.kv_scale_from_amax(desc, v, vs)
+        kv.kv_cache_write(desc, k, v, slots, kc, vc, ks, vs)
+
+    replay_and_compare(fn, [ks, vs], f"calibration + write per_head={per_head}",
+                       state=[kc, vc])
