@@ -125,9 +125,19 @@ __device__ __forceinline__ uint32_t e4m3_encode_sat_hw(float y) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
+// The same for e5m2 on v_cvt_pk_bf8_f32: NaN first, then a clamp to
+// [-57344, 57344] (finite and infinite overflow saturate; the write never
+// stores an infinity). Checked against e5m2_encode_sat on every fp32 value
+// by the flat e5m2 quantiser's test.
+__device__ __forceinline__ uint32_t e5m2_encode_sat_hw(float y) {
+  if (!(y == y)) return ((__float_as_uint(y) >> 24) & 0x80u) | 0x7Fu;
+  const float c = __builtin_fminf(__builtin_fmaxf(y, -57344.0f), 57344.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, c, 0, false) & 0xFFu;
+}
+
 template <int FMT>
 __device__ __forceinline__ uint32_t fp8_encode_sat(float y) {
-  if constexpr (FMT == kFmtE5M2) return e5m2_encode_sat(y);
+  if constexpr (FMT == kFmtE5M2) return e5m2_encode_sat_hw(y);
   else return e4m3_encode_sat_hw(y);
 }
 
