@@ -90,8 +90,8 @@ enum kvq_status {
   KVQ_ERR_INVALID_ARG = -1,       /* null / misaligned pointer, negative size,
                                      inconsistent shapes */
   KVQ_ERR_UNSUPPORTED = -2,       /* head_dim not in {64,128,256}, page size
-                                     not 16, Hq % Hkv != 0, group > 8 (> 16
-                                     with KVQ_ATTN_FP8), dynamic scales with
+                                     not 16, Hq % Hkv != 0, group > 16 (either
+                                     arithmetic mode), dynamic scales with
                                      KVQ_ATTN_FP8 or Hkv > 256 */
   KVQ_ERR_WORKSPACE_TOO_SMALL = -3,
   KVQ_ERR_HIP = -4                /* a HIP runtime call or launch failed */

@@ -321,3 +321,120 @@ def test_low_precision_single_level_accumulation_drifts():
     e2 = np.max(np.abs(two - ref))
     assert e1 > 1e-2, e1
     assert e2 < 1e-2, e2
+
+
+# ------------------------------------ second formulation: numpy brute force --
+def _decode_table(dtype):
+    """Values of all 256 codes from torch's float8 types (a library routine,
+    independent of the oracle's codec): e4m3fn for e4m3, e5m2 for e5m2."""
+    import torch
+    t = torch.float8_e5m2 if dtype == oracle.E5M2 else torch.float8_e4m3fn
+    return torch.arange(256, dtype=torch.uint8).view(t).to(torch.float64).numpy()
+
+
+def _layout_offsets(D, e):
+    """Byte offsets of (row, dim) inside one (page, head) block, written out
+    from the layout the library header documents (K: 16-byte chunks of 16/e
+    dims per row, chunk-major; V: 1 KiB groups of 64/e dims, row quads)."""
+    r = np.arange(16)[:, None]
+    d = np.arange(D)[None, :]
+    ce, db = 16 // e, 64 // e
+    k = ((d // ce) * 16 + r) * 16 + (d % ce) * e
+    v = (d // db) * 1024 + (r // 4) * 256 + (d % db) * 4 * e + (r % 4) * e
+    return k, v
+
+
+def _brute_force_attention(case, kc, vc, dtype, per_head, ks, vs, window):
+    """Decode attention written out in vectorised numpy float64: every
+    attended position's value is decode(code) * s[h] (s[0] per tensor),
+    gathered through the block table and the layout; logits
+    q . k / sqrt(D); softmax; weighted sum of the values."""
+    B, Hq, D = case.q.shape
+    Hkv = case.num_kv_heads
+    G = Hq // Hkv
+    e = 2 if dtype == BF16 else 1
+    koff, voff = _layout_offsets(D, e)
+    if dtype == BF16:
+        def values(cache, off):
+            lo = cache[:, :, off].astype(np.uint32)
+            hi = cache[:, :, off + 1].astype(np.uint32)
+            return ((hi << 24) | (lo << 16)).view(np.float32).astype(np.float64)
+        kx, vx = values(kc, koff), values(vc, voff)          # [P][H][16][D]
+    else:
+        tab = _decode_table(dtype)
+        kx, vx = tab[kc[:, :, koff]], tab[vc[:, :, voff]]
+        hs = np.arange(Hkv) if per_head else np.zeros(Hkv, int)
+        kx = kx * np.asarray(ks, np.float64)[hs][None, :, None, None]
+        vx = vx * np.asarray(vs, np.float64)[hs][None, :, None, None]
+    qf = synth.bits_to_f32(case.q).astype(np.float64)
+    out = np.zeros((B, Hq, D))
+    for b, L in enumerate(case.lens):
+        lo = max(0, L - window) if window else 0
+        t = np.arange(lo, L)
+        if t.size == 0:
+            continue
+        pages = case.block_tables[b, t // 16]
+        rows = t % 16
+        for h in range(Hkv):
+            kt = kx[pages, h, rows]                          # [n][D]
+            vt = vx[pages, h, rows]
+            z = qf[b, h * G:(h + 1) * G] @ kt.T / math.sqrt(D)   # [G][n]
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            out[b, h * G:(h + 1) * G] = (p @ vt) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def test_brute_force_tables_match_the_format():
+    # the brute force's two inputs checked against the header's worked
+    # example and the format's extremes
+    koff, voff = _layout_offsets(128, 1)
+    assert koff[5, 17] == 337 and voff[5, 17] == 325
+    t = _decode_table(FP8)
+    assert t[0x7E] == 448.0 and t[0x01] == 2.0 ** -9 and np.isnan(t[0x7F])
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa4_ragged_window", "per_tensor", "e5m2", "bf16"])
+def test_attention_matches_a_numpy_brute_force(name):
+    """The oracle's attention against a second, vectorised formulation on
+    the same codes, with distinct static scales per KV head (the per-head
+    scales of "State of FP8 KV cache and attention quantization in vLLM",
+    section "Kernel and vLLM improvements"; per tensor or per attention
+    head in "cooking-agi: FP8 and the KV cache", section "how to enable it
+    in the engine"). A head that read another head's K or V scale, or the
+    first head's for all, moves the output by far more than 1e-12."""
+    dtype, per_head, windows = FP8, True, (0,)
+    if name == "tiny":                       # the tiny workload itself
+        case = synth.decode_case(synth.TINY, **synth.WORKLOADS[synth.TINY])
+        ks = np.array([1.0 / 448, 5.0 / 448], np.float32)
+        vs = np.array([3.0 / 448, 0.5 / 448], np.float32)
+        ks = ks * oracle.scale_from_amax(case.k_new, True) * 448 / 10
+        vs = vs * oracle.scale_from_amax(case.v_new, True) * 448 / 10
+    elif name == "gqa4_ragged_window":      # G = 4, ragged batch, shuffled pool
+        case = synth.decode_case(31, 16, 4, 64, [300, 77, 513, 16, 1], shuffle=True,
+                                 spare_frac=0.3, values="tiny")
+        ks = oracle.scale_from_amax(case.k_new, True) * np.array([1, 2.5, 0.3, 7], np.float32)
+        vs = oracle.scale_from_amax(case.v_new, True) * np.array([4, 0.2, 1, 9], np.float32)
+        windows = (0, 100, 16, 1)
+    elif name == "per_tensor":
+        case = synth.decode_case(32, 8, 2, 128, [200, 45])
+        per_head = False
+        ks = np.array([0.037], np.float32)
+        vs = np.array([0.011], np.float32)
+    elif name == "e5m2":
+        case = synth.decode_case(33, 8, 2, 64, [150, 260], shuffle=True, values="tiny")
+        dtype = oracle.E5M2
+        ks = oracle.scale_from_amax(case.k_new, True, fmt=dtype) * np.array([1, 40], np.float32)
+        vs = oracle.scale_from_amax(case.v_new, True, fmt=dtype) * np.array([30, 1], np.float32)
+    else:
+        case = synth.decode_case(34, 8, 2, 128, [90, 33], shuffle=True)
+        dtype, ks, vs = BF16, None, None
+    assert per_head is False or ks is None or len(set(ks.tolist())) == len(ks)
+    kc = synth.poisoned_cache(case.num_pages, case.num_kv_heads, case.head_dim, dtype != BF16)
+    vc = kc.copy()
+    oracle.kv_cache_write(kc, vc, case.k_new, case.v_new, case.slots, dtype, per_head, ks, vs)
+    for w in windows:
+        got = oracle.attention(case.q, kc, vc, case.block_tables, case.lens, case.num_kv_heads,
+                               dtype, per_head, w, 0.0, ks, vs)
+        want = _brute_force_attention(case, kc, vc, dtype, per_head, ks, vs, w)
+        err = np.max(np.abs(got - want)) / max(1.0, np.max(np.abs(want)))
+        assert err <= 1e-12, (name, w, err)
