@@ -340,7 +340,9 @@ def read_ceiling_gbs(torch, kv, reps=5):
     return best, copy
 
 
-KERNEL_SOURCES = ["fp8_kv_cache_write_amd/csrc/paged_decode.hip",
+KERNEL_SOURCES = ["fp8_kv_cache_write_amd/csrc/paged_decode.hpp",
+                  "fp8_kv_cache_write_amd/csrc/paged_decode.hip",
+                  "fp8_kv_cache_write_amd/csrc/paged_decode_d128.hip",
                   "fp8_kv_cache_write_amd/csrc/device_common.hpp",
                   "fp8_kv_cache_write_amd/csrc/launch.hpp",
                   "fp8_kv_cache_write_amd/csrc/api.cpp"]

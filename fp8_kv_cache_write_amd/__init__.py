@@ -109,12 +109,13 @@ def lib():
         L.kvq_profile_begin.argtypes = [i32]
         L.kvq_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
         L.kvq_stream_read.argtypes = [vp, i64, vp, i32, vp]
+        L.kvq_set_tuning.argtypes = [i32, i32]
         for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes", "kvq_decode_step",
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
                   "kvq_e4m3_quantize", "kvq_e5m2_quantize", "kvq_profile_begin",
                   "kvq_profile_end", "kvq_kv_cache_write_dynamic",
                   "kvq_decode_step_dynamic", "kvq_paged_prefill_attention",
-                  "kvq_prefill_workspace_bytes", "kvq_stream_read"):
+                  "kvq_prefill_workspace_bytes", "kvq_stream_read", "kvq_set_tuning"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -417,6 +418,31 @@ def e4m3_quantize(x, scale, out, stream=None):
 def e5m2_quantize(x, scale, out, stream=None):
     """out[i] = e5m2_sat_rne(x[i] / scale[0]); x float32, out uint8."""
     _quantize("kvq_e5m2_quantize", x, scale, out, stream)
+
+
+# kvq_set_tuning knobs (include/kvfp8.h, enum kvq_tuning_knob)
+TUNING_KNOBS = {"pages_per_wave": 0, "partition_rotate": 1, "split_shape": 2,
+                "prefill_column_groups": 3, "prefill_key_parts": 4}
+
+
+def set_tuning(knob, value):
+    """Override one launch-plan choice for every later call (sweeps and
+    tests; see kvq_set_tuning). knob: a TUNING_KNOBS name; value None (or
+    -1) gives the choice back to the plan. split_shape takes "TPxRING" or
+    "TPxRINGsSLOTS" (e.g. "2x1s1") or the header's integer code."""
+    if value is None:
+        value = -1
+    elif knob == "split_shape" and isinstance(value, str):
+        tp, rest = value.split("x")
+        ring, _, slots = rest.partition("s")
+        value = 100 * int(tp) + 10 * int(ring) + int(slots or 0)
+    _check("kvq_set_tuning", lib().kvq_set_tuning(TUNING_KNOBS[knob], int(value)))
+
+
+def reset_tuning():
+    """Every knob back to the plan's choice."""
+    for k in TUNING_KNOBS:
+        set_tuning(k, None)
 
 
 def profile_begin(max_launches):

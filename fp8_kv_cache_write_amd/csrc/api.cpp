@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -13,6 +14,20 @@
 #include "launch.hpp"
 
 using namespace kvfp8;
+
+namespace {
+
+// kvq_set_tuning overrides, -1 = the plan decides.
+constexpr int kTuningKnobs = 5;
+std::atomic<int> g_tuning[kTuningKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}};
+
+}  // namespace
+
+namespace kvfp8 {
+int tuning_override(int knob) {
+  return knob >= 0 && knob < kTuningKnobs ? g_tuning[knob].load(std::memory_order_relaxed) : -1;
+}
+}  // namespace kvfp8
 
 namespace {
 
@@ -153,11 +168,8 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
     ppw = direct_ppw;
     slots = 0;
   }
-  // KVFP8_PAGES_PER_WAVE=n (1..64) overrides the run length (tuning sweeps).
-  if (const char* env = getenv("KVFP8_PAGES_PER_WAVE")) {
-    const long n = strtol(env, nullptr, 10);
-    if (n >= 1 && n <= kMaxPagesPerWave) ppw = n;
-  }
+  // an explicit override of the run length (kvq_set_tuning, sweeps and tests)
+  if (const int n = tuning_override(KVQ_TUNE_PAGES_PER_WAVE); n >= 1) ppw = n;
   if (att8) ppw = (ppw + 1) / 2 * 2;   // runs of whole 32-position blocks
   Plan p;
   p.pages_per_wave = (int)ppw;
@@ -175,8 +187,8 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
                      ? 4
                      : 2;
   p.rotate = (num_seqs > 1 || ppw >= kMaxPagesPerWave) ? 1 : 0;
-  // KVFP8_PARTITION_ROTATE=0|1 overrides the partition order (tuning sweeps).
-  if (const char* env = getenv("KVFP8_PARTITION_ROTATE")) p.rotate = atoi(env) ? 1 : 0;
+  // an explicit override of the partition order (kvq_set_tuning)
+  if (const int r = tuning_override(KVQ_TUNE_PARTITION_ROTATE); r >= 0) p.rotate = r;
   p.num_parts = (int)((pages_max + kSplitWaves * ppw - 1) / (kSplitWaves * ppw));
   if (p.num_parts <= 1) {
     p.num_parts = 1;
@@ -539,6 +551,24 @@ int kvq_stream_read(const void* src, int64_t n_bytes, uint32_t* sink, int32_t nu
                  hipSuccess
              ? KVQ_OK
              : KVQ_ERR_HIP;
+}
+
+int kvq_set_tuning(int32_t knob, int32_t value) {
+  if (knob < 0 || knob >= kTuningKnobs) return KVQ_ERR_INVALID_ARG;
+  bool ok = value == -1;
+  switch (knob) {
+    case KVQ_TUNE_PAGES_PER_WAVE: ok |= value >= 1 && value <= kMaxPagesPerWave; break;
+    case KVQ_TUNE_PARTITION_ROTATE: ok |= value == 0 || value == 1; break;
+    case KVQ_TUNE_SPLIT_SHAPE:
+      ok |= value == 210 || value == 220 || value == 410 || value == 211 || value == 212 ||
+            value == 411;
+      break;
+    case KVQ_TUNE_PREFILL_COLUMN_GROUPS: ok |= value >= 1 && value <= 3; break;
+    case KVQ_TUNE_PREFILL_KEY_PARTS: ok |= value >= 1; break;
+  }
+  if (!ok) return KVQ_ERR_INVALID_ARG;
+  g_tuning[knob].store(value, std::memory_order_relaxed);
+  return KVQ_OK;
 }
 
 int kvq_profile_begin(int32_t max_launches) {

@@ -61,6 +61,10 @@ struct DecodeParams {
   const int32_t* row_limit;      // merge only: rows at or past *row_limit are skipped
 };
 
+// The value of a kvq_set_tuning override (enum kvq_tuning_knob of kvfp8.h),
+// or -1 when the plan decides.
+int tuning_override(int knob);
+
 // Waves per work-group of the split kernel.
 constexpr int kSplitWaves = 4;
 
@@ -123,7 +127,7 @@ struct PrefillParams {
 constexpr int kPrefillWaves = 4;
 
 // The prefill launch geometry, a pure function of its arguments (and the
-// KVFP8_PREFILL_COLUMN_GROUPS / KVFP8_PREFILL_KEY_PARTS overrides): column
+// prefill overrides of kvq_set_tuning): column
 // groups per wave, query blocks, and the key split with its workspace. The
 // key range [0, max_pages_per_seq * 16) is cut into num_parts partitions when
 // the query blocks alone would leave compute units idle (a short chunk over a

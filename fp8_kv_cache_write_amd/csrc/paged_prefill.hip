@@ -30,6 +30,7 @@
 
 #include <algorithm>
 
+#include "../../include/kvfp8.h"
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -655,11 +656,10 @@ PrefillPlan plan_paged_prefill(int head_dim, int fmt, int num_q_heads, int num_k
   const int G = num_q_heads / num_kv_heads;
   const int ppc = 16 / G;                                  // positions per column group
   const int ncg_max = prefill_ncg_max(head_dim, fmt);
-  // overrides for tests and sweeps: KVFP8_PREFILL_COLUMN_GROUPS=n (1..3),
-  // KVFP8_PREFILL_KEY_PARTS=n (n key partitions; 1 = no split)
-  int forced = 0, forced_parts = 0;
-  if (const char* env = getenv("KVFP8_PREFILL_COLUMN_GROUPS")) forced = atoi(env);
-  if (const char* env = getenv("KVFP8_PREFILL_KEY_PARTS")) forced_parts = atoi(env);
+  // explicit overrides for tests and sweeps (kvq_set_tuning): column groups
+  // per wave (1..3) and key partitions (1 = no split)
+  int forced = std::max(tuning_override(KVQ_TUNE_PREFILL_COLUMN_GROUPS), 0);
+  int forced_parts = std::max(tuning_override(KVQ_TUNE_PREFILL_KEY_PARTS), 0);
   if (forced < 1 || forced > ncg_max) forced = 0;
   auto blocks = [&](int ncg) -> int64_t {
     const int ppb = kPrefillWaves * ncg * ppc;

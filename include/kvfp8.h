@@ -403,6 +403,34 @@ int kvq_e5m2_quantize(const float* x, int64_t n, const float* scale,
 const char* kvq_status_string(int32_t status);
 
 /*
+ * Tuning overrides for sweeps and tests (not for serving). The launch plan
+ * of the decode and prefill calls is a pure function of their arguments and
+ * the device's compute-unit count; kvq_set_tuning replaces one of its
+ * choices for every later call in the process, until it is set back to -1
+ * (the plan decides). Nothing else changes the plan: the environment is
+ * never read. The override is process-wide and not synchronised with calls
+ * in flight on other host threads.
+ *   KVQ_TUNE_PAGES_PER_WAVE      1..64: pages each split-kernel wave streams
+ *   KVQ_TUNE_PARTITION_ROTATE    0 plain, 1 rotated partition order
+ *   KVQ_TUNE_SPLIT_SHAPE         100*TP + 10*RING + SLOTS: tile pages,
+ *                                register tiles, LDS slots; one of 210, 220,
+ *                                410, 211, 212, 411 (a shape a mode is not
+ *                                built for fails the launch with KVQ_ERR_HIP)
+ *   KVQ_TUNE_PREFILL_COLUMN_GROUPS  1..3 query column groups per prefill wave
+ *   KVQ_TUNE_PREFILL_KEY_PARTS   >= 1 key partitions of a prefill with a
+ *                                workspace (1: no split)
+ * Returns KVQ_ERR_INVALID_ARG for an unknown knob or a value out of range.
+ */
+enum kvq_tuning_knob {
+  KVQ_TUNE_PAGES_PER_WAVE = 0,
+  KVQ_TUNE_PARTITION_ROTATE = 1,
+  KVQ_TUNE_SPLIT_SHAPE = 2,
+  KVQ_TUNE_PREFILL_COLUMN_GROUPS = 3,
+  KVQ_TUNE_PREFILL_KEY_PARTS = 4
+};
+int kvq_set_tuning(int32_t knob, int32_t value);
+
+/*
  * Profiling aid (not thread-safe): between kvq_profile_begin and
  * kvq_profile_end the library records a HIP event pair around every launch of
  * the split-decode kernel (up to max_launches of them) on the stream of that

@@ -249,9 +249,9 @@ def test_prefill_argument_checks(L):
     assert pf(kv.layer_desc(32, 8, 96)) == UNSUPPORTED
 
 
-def test_prefill_workspace_plan(monkeypatch):
+def test_prefill_workspace_plan(tune):
     d = kv.layer_desc(32, 8, 128)
-    monkeypatch.delenv("KVFP8_PREFILL_KEY_PARTS", raising=False)
+    tune("prefill_key_parts", None)
     # a short chunk over a long context splits; the partials are
     # (m, l, o[D]) per (row, query head, partition), plus the merge's slack
     n = kv.prefill_workspace_bytes(d, 1, 512, 2048)
@@ -266,7 +266,32 @@ def test_prefill_workspace_plan(monkeypatch):
     # enough query blocks to fill the device: no split
     assert kv.prefill_workspace_bytes(d, 64, 512, 2048) == 0
     # the override forces a split even where the plan would not
-    monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", "3")
+    tune("prefill_key_parts", 3)
     assert kv.prefill_workspace_bytes(d, 1, 64, 40) > 0
-    monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", "1")
+    tune("prefill_key_parts", 1)
     assert kv.prefill_workspace_bytes(d, 1, 512, 8192) == 0
+
+
+def test_tuning_overrides_are_explicit(tune, monkeypatch):
+    """The plan changes only through kvq_set_tuning: environment variables
+    named like the old sweep switches do nothing, out-of-range values are
+    rejected, and -1 gives a knob back to the plan."""
+    d = kv.layer_desc(32, 8, 128)
+    base = kv.decode_workspace_bytes(d, 1, 32768)
+    assert base > 0
+    for name in ("KVFP8_PAGES_PER_WAVE", "KVFP8_PARTITION_ROTATE", "KVFP8_SPLIT_VARIANT",
+                 "KVFP8_PREFILL_COLUMN_GROUPS", "KVFP8_PREFILL_KEY_PARTS"):
+        monkeypatch.setenv(name, "1")
+    assert kv.decode_workspace_bytes(d, 1, 32768) == base
+    # 2-page runs: 8x the partitions of the plan's 16-page runs
+    tune("pages_per_wave", 2)
+    assert kv.decode_workspace_bytes(d, 1, 32768) > 4 * base
+    tune("pages_per_wave", None)
+    assert kv.decode_workspace_bytes(d, 1, 32768) == base
+    L = kv.lib()
+    for knob, bad in ((0, 0), (0, 65), (1, 2), (2, 213), (2, 0), (3, 4), (4, 0), (5, 1),
+                      (-1, 1)):
+        assert L.kvq_set_tuning(knob, bad) == INVALID, (knob, bad)
+    for knob, good in ((0, 64), (1, 0), (2, 211), (3, 3), (4, 7)):
+        assert L.kvq_set_tuning(knob, good) == OK
+        assert L.kvq_set_tuning(knob, -1) == OK

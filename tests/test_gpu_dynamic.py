@@ -162,10 +162,10 @@ def test_dynamic_attention(label, wl, Hq, Hkv, D, lens, fmt, window, values, dyn
 
 @pytest.mark.parametrize("variant", ["2x1", "2x1s1"])
 @pytest.mark.parametrize("ppw", ["3", "4", "auto"])
-def test_dynamic_shapes_and_runs(variant, ppw, monkeypatch):
-    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+def test_dynamic_shapes_and_runs(variant, ppw, tune):
+    tune("split_shape", variant)
     if ppw != "auto":
-        monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
+        tune("pages_per_wave", int(ppw))
     case = synth.decode_case(123, 32, 4, 128, [1500, 37, 1], shuffle=True, spare_frac=0.2,
                              values="spread")
     check(GpuLayer(case, dyn="per_token_head"), OracleLayer(case, dyn="per_token_head"),

@@ -163,8 +163,8 @@ def test_e5m2_attention_small(label, wl, Hq, Hkv, D, lens, per_head, window, shu
     check_attention(g, o, f"e5m2-{label}")
 
 
-def test_e5m2_attention_forced_split(monkeypatch):
-    monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", "3")
+def test_e5m2_attention_forced_split(tune):
+    tune("pages_per_wave", 3)
     case = synth.decode_case(synth.LLAMA8B, 32, 8, 128, [2000, 37, 1], shuffle=True,
                              spare_frac=0.2)
     check_attention(GpuLayer(case, fmt=FMT), OracleLayer(case, fmt=FMT), "e5m2-forced-split")
@@ -207,8 +207,8 @@ def test_e5m2_decode_step_equals_write_then_attend(label, Hq, Hkv, D, lens, wind
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_e5m2_every_tile_variant(variant, monkeypatch):
-    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+def test_e5m2_every_tile_variant(variant, tune):
+    tune("split_shape", variant)
     for D, lens in ((128, [1000, 37, 1]), (64, [700, 129])):
         if not shape_fits(variant, D, True):
             continue

@@ -74,11 +74,11 @@ def test_fp8attn_small(label, wl, Hq, Hkv, D, lens, fmt, window, values):
 
 @pytest.mark.parametrize("variant", ["2x1", "2x1s1"])
 @pytest.mark.parametrize("ppw", ["3", "4", "auto"])
-def test_fp8attn_shapes_and_runs(variant, ppw, monkeypatch):
+def test_fp8attn_shapes_and_runs(variant, ppw, tune):
     # odd runs are rounded up to even ones (tiles stay on 32-position blocks)
-    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+    tune("split_shape", variant)
     if ppw != "auto":
-        monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
+        tune("pages_per_wave", int(ppw))
     case = synth.decode_case(59, 32, 4, 128, [1500, 37, 1], shuffle=True, spare_frac=0.2)
     check(GpuLayer(case, attn="fp8"), OracleLayer(case, attn="fp8"), f"fp8attn {variant} ppw={ppw}")
 

@@ -292,8 +292,8 @@ def test_attention_small(label, wl, Hq, Hkv, D, lens, fp8, per_head, window, shu
 
 
 @pytest.mark.parametrize("ppw", [1, 2, 3, 8])
-def test_attention_forced_split_partitions(ppw, monkeypatch):
-    monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", str(ppw))
+def test_attention_forced_split_partitions(ppw, tune):
+    tune("pages_per_wave", int(ppw))
     for fp8, window, lens in ((True, 0, [700, 1, 0, 33]), (True, 100, [700, 90]),
                               (False, 37, [513, 16, 17])):
         label = f"split ppw={ppw} fp8={fp8} window={window}"
@@ -314,13 +314,13 @@ REDUCE_CASES = [
 
 
 @pytest.mark.parametrize("longest,others", REDUCE_CASES, ids=[str(c[0]) for c in REDUCE_CASES])
-def test_reduce_chunks(longest, others, monkeypatch):
+def test_reduce_chunks(longest, others, tune):
     # The largest logit of sequence 0 sits near its end (a key equal to the
     # first query of each group), so a later chunk raises the running max and
     # rescales what the earlier ones summed; sequence 1 has it at position 10,
     # so the later chunks add with small weights. Shorter sequences leave
     # partitions that hold only an empty partial.
-    monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", "1")
+    tune("pages_per_wave", 1)
     lens = [longest] + others
     case = synth.decode_case(75, 16, 4, 128, lens, shuffle=True, spare_frac=0.1)
     k = synth.bits_to_f32(case.k_new).copy()
@@ -472,10 +472,10 @@ def shape_fits(variant, D, fp8):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_attention_every_tile_variant(variant, monkeypatch):
+def test_attention_every_tile_variant(variant, tune):
     # every compiled (pages per tile x register ring) shape of the split
     # kernel, on ragged lengths, a window and both cache dtypes
-    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+    tune("split_shape", variant)
     for D, fp8, window, lens in ((128, True, 0, [1000, 37, 1]), (64, True, 50, [700, 129]),
                                  (128, False, 0, [515, 64]), (256, True, 0, [333]),
                                  (256, False, 21, [300, 16])):
@@ -488,9 +488,9 @@ def test_attention_every_tile_variant(variant, monkeypatch):
         g = GpuLayer(case, fp8=fp8, window=window)
         o = OracleLayer(case, fp8=fp8, window=window)
         check_attention(g, o, label)
-        monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", "3")
+        tune("pages_per_wave", 3)
         check_attention(g, o, label + " ppw=3")
-        monkeypatch.delenv("KVFP8_PAGES_PER_WAVE")
+        tune("pages_per_wave", None)
 
 
 # ------------------------------------------------------ fused decode step ---
@@ -576,13 +576,13 @@ def test_decode_step_equals_write_then_attend(label, Hq, Hkv, D, lens, fp8, wind
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_decode_step_every_tile_variant(variant, monkeypatch):
-    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+def test_decode_step_every_tile_variant(variant, tune):
+    tune("split_shape", variant)
     for ppw in ("auto", "1", "3"):
         if ppw == "auto":
-            monkeypatch.delenv("KVFP8_PAGES_PER_WAVE", raising=False)
+            tune("pages_per_wave", None)
         else:
-            monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
+            tune("pages_per_wave", int(ppw))
         for D, fp8 in ((128, True), (64, False)):
             if not shape_fits(variant, D, fp8):
                 continue
@@ -611,14 +611,14 @@ PARTITION_ORDER_CASES = [
 
 @pytest.mark.parametrize("ppw,lens", PARTITION_ORDER_CASES,
                          ids=[c[0] for c in PARTITION_ORDER_CASES])
-def test_partition_order_bit_identical(ppw, lens, monkeypatch):
+def test_partition_order_bit_identical(ppw, lens, tune):
     # The rotated and the plain partition order run the same partitions on
     # other work-groups: the outputs, caches and fused-step results agree
     # bit for bit, and both pass the oracle gate.
     if ppw == "auto":
-        monkeypatch.delenv("KVFP8_PAGES_PER_WAVE", raising=False)
+        tune("pages_per_wave", None)
     else:
-        monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
+        tune("pages_per_wave", int(ppw))
     case = synth.decode_case(92, 32, 8, 128, lens, shuffle=True, spare_frac=0.2)
     pre = split_newest(case)
     knew, vnew = newest_rows(case)
@@ -626,7 +626,7 @@ def test_partition_order_bit_identical(ppw, lens, monkeypatch):
     ref = o.attend()
     got = {}
     for rot in ("0", "1"):
-        monkeypatch.setenv("KVFP8_PARTITION_ROTATE", rot)
+        tune("partition_rotate", int(rot))
         label = f"partition order rotate={rot} ppw={ppw} lens={lens}"
         say(label)
         full = GpuLayer(case)
@@ -674,12 +674,12 @@ def test_wide_groups(label, wl, Hq, Hkv, D, lens, fp8, window, values):
 
 @pytest.mark.parametrize("variant", ["2x1", "2x1s1"])
 @pytest.mark.parametrize("ppw", ["1", "3", "auto"])
-def test_wide_groups_shapes_and_runs(variant, ppw, monkeypatch):
-    monkeypatch.setenv("KVFP8_SPLIT_VARIANT", variant)
+def test_wide_groups_shapes_and_runs(variant, ppw, tune):
+    tune("split_shape", variant)
     if ppw == "auto":
-        monkeypatch.delenv("KVFP8_PAGES_PER_WAVE", raising=False)
+        tune("pages_per_wave", None)
     else:
-        monkeypatch.setenv("KVFP8_PAGES_PER_WAVE", ppw)
+        tune("pages_per_wave", int(ppw))
     case = synth.decode_case(196, 64, 4, 128, [1000, 129, 2], shuffle=True, spare_frac=0.2)
     g = GpuLayer(case)
     o = OracleLayer(case)

@@ -113,10 +113,10 @@ def test_prefill(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values):
 @pytest.mark.parametrize("groups", ["1", "2", "3"])
 @pytest.mark.parametrize("fmt,D,G", [("fp8_e4m3", 128, 4), ("fp8_e4m3", 64, 8),
                                      ("fp8_e5m2", 128, 2), ("bf16", 64, 4)])
-def test_prefill_column_groups(groups, fmt, D, G, monkeypatch):
+def test_prefill_column_groups(groups, fmt, D, G, tune):
     # every column-group count of the kernel, all rows compared (counts above
     # what a shape supports fall back to its largest)
-    monkeypatch.setenv("KVFP8_PREFILL_COLUMN_GROUPS", groups)
+    tune("prefill_column_groups", int(groups))
     case = synth.prefill_case(153, 2 * G, 2, D, [700, 333], [700, 200], shuffle=True,
                               spare_frac=0.2)
     g = GpuLayer(case, fmt=fmt)
@@ -244,8 +244,8 @@ def test_prefill_dynamic_scales(label, wl, Hq, Hkv, D, lens, chunks, fmt, window
 
 
 @pytest.mark.parametrize("groups", ["1", "2", "3"])
-def test_prefill_dynamic_column_groups(groups, monkeypatch):
-    monkeypatch.setenv("KVFP8_PREFILL_COLUMN_GROUPS", groups)
+def test_prefill_dynamic_column_groups(groups, tune):
+    tune("prefill_column_groups", int(groups))
     case = synth.prefill_case(163, 16, 4, 128, [700, 333], [700, 200], shuffle=True,
                               spare_frac=0.2, values="spread")
     g = GpuLayer(case, dyn="per_token_head")
@@ -317,8 +317,8 @@ def test_prefill_fp8_attention(label, wl, Hq, Hkv, D, lens, chunks, fmt, window,
 
 
 @pytest.mark.parametrize("groups", ["1", "2", "3"])
-def test_prefill_fp8_attention_column_groups(groups, monkeypatch):
-    monkeypatch.setenv("KVFP8_PREFILL_COLUMN_GROUPS", groups)
+def test_prefill_fp8_attention_column_groups(groups, tune):
+    tune("prefill_column_groups", int(groups))
     case = synth.prefill_case(174, 16, 4, 128, [700, 333], [700, 200], shuffle=True,
                               spare_frac=0.2)
     g = GpuLayer(case, attn="fp8")
@@ -367,11 +367,11 @@ SPLIT_CASES = [
 @pytest.mark.parametrize("label,wl,Hq,Hkv,D,lens,chunks,fmt,window,values,attn,dyn", SPLIT_CASES,
                          ids=[c[0] for c in SPLIT_CASES])
 def test_prefill_key_split(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, values, attn, dyn,
-                           monkeypatch):
+                           tune):
     # a short chunk over a long context: the plan splits the keys (the
     # workspace size says so), the merge gives the oracle's rows, and the
     # unsplit kernel agrees to the same bound
-    monkeypatch.delenv("KVFP8_PREFILL_KEY_PARTS", raising=False)
+    tune("prefill_key_parts", None)
     case = synth.prefill_case(wl, Hq, Hkv, D, lens, chunks, shuffle=True, spare_frac=0.2,
                               values=values)
     g = GpuLayer(case, window=window, fmt=fmt, attn=attn, dyn=dyn)
@@ -391,11 +391,11 @@ def test_prefill_key_split(label, wl, Hq, Hkv, D, lens, chunks, fmt, window, val
 
 
 @pytest.mark.parametrize("parts", ["2", "7", "200"])
-def test_prefill_forced_key_partitions(parts, monkeypatch):
+def test_prefill_forced_key_partitions(parts, tune):
     # any partition count, whole prompts included (partitions past a row's
     # position stay empty); 200 asks for more partitions than tiles, so every
     # partition is one tile and the merge takes two chunks
-    monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", parts)
+    tune("prefill_key_parts", int(parts))
     case = synth.prefill_case(188, 16, 4, 128, [3000, 700, 40], [40, 700, 40], shuffle=True,
                               spare_frac=0.2)
     for window in (0, 100):
@@ -406,11 +406,11 @@ def test_prefill_forced_key_partitions(parts, monkeypatch):
 
 
 @pytest.mark.parametrize("split", [False, True])
-def test_prefill_rows_before_position_zero_are_zero(split, monkeypatch):
+def test_prefill_rows_before_position_zero_are_zero(split, tune):
     # a chunk longer than the context: its first rows sit at negative
     # positions and give zeros; the others attend [0, pos]
     if split:
-        monkeypatch.setenv("KVFP8_PREFILL_KEY_PARTS", "2")
+        tune("prefill_key_parts", 2)
     case = synth.prefill_case(189, 16, 4, 128, [64, 100], [64, 30], shuffle=True)
     g = GpuLayer(case)
     o = OracleLayer(case)
