@@ -110,12 +110,15 @@ def lib():
         L.kvq_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
         L.kvq_stream_read.argtypes = [vp, i64, vp, i32, vp]
         L.kvq_set_tuning.argtypes = [i32, i32]
+        L.kvq_paged_decode_attention_noalloc.argtypes = [dp, vp, i32, vp, vp, vp, i64, vp, i32,
+                                                         vp, i32, i32, vp, vp, vp]
         for f in ("kvq_kv_cache_write", "kvq_decode_workspace_bytes", "kvq_decode_step",
                   "kvq_paged_decode_attention", "kvq_kv_scale_from_amax",
                   "kvq_e4m3_quantize", "kvq_e5m2_quantize", "kvq_profile_begin",
                   "kvq_profile_end", "kvq_kv_cache_write_dynamic",
                   "kvq_decode_step_dynamic", "kvq_paged_prefill_attention",
-                  "kvq_prefill_workspace_bytes", "kvq_stream_read", "kvq_set_tuning"):
+                  "kvq_prefill_workspace_bytes", "kvq_stream_read", "kvq_set_tuning",
+                  "kvq_paged_decode_attention_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -297,6 +300,25 @@ def paged_decode_attention(desc, out, q, k_cache, v_cache, block_tables,
         num_pages, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0],
         int(max_context_len), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+# kvq_paged_decode_attention_noalloc's workspace (KVQ_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def paged_decode_attention_noalloc(desc, out, q, k_cache, v_cache, block_tables,
+                                   context_lens, max_context_len, k_scale=None,
+                                   v_scale=None, stream=None):
+    """paged_decode_attention with the library's own device scratch array
+    as the split workspace (no allocation; calls on one device must be
+    ordered). Raises Kvfp8Error (workspace too small) when the plan needs
+    more than NOALLOC_SCRATCH_BYTES."""
+    out_dtype, num_pages, _ = _decode_checks(desc, out, q, k_cache, v_cache, block_tables,
+                                             context_lens, k_scale, v_scale, None)
+    _check("kvq_paged_decode_attention_noalloc", lib().kvq_paged_decode_attention_noalloc(
+        ctypes.byref(desc), _ptr(out), out_dtype, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        num_pages, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), q.shape[0],
+        int(max_context_len), _ptr(k_scale), _ptr(v_scale), _stream(stream)))
 
 
 def decode_step(desc, k_new, v_new, k_cache, v_cache, out, q, block_tables,

@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvfp8.so")
 SOURCES = ["api.cpp", "kv_cache_write.hip", "paged_decode.hip", "paged_decode_d64.hip",
            "paged_decode_d128.hip", "paged_decode_d256.hip", "paged_prefill.hip",
-           "stream_read.hip"]
+           "stream_read.hip", "decode_noalloc.hip"]
 OBJDIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -256,6 +256,33 @@ int kvq_paged_decode_attention(const kvq_layer_desc* desc, void* out,
                                size_t workspace_bytes, void* stream);
 
 /*
+ * kvq_paged_decode_attention_noalloc - kvq_paged_decode_attention for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). The same kernels
+ * and results, bit for bit; the split workspace is a library-owned device
+ * array of KVQ_NOALLOC_SCRATCH_BYTES (16 MiB) per device, which each device
+ * the library runs on holds until the process ends. The call allocates
+ * nothing. Every call on one device shares that device's array and leaves
+ * its contents behind (nothing in it needs clearing), so calls on one
+ * device must be ordered (one stream, or synchronised streams): calls that
+ * overlap on one device race.
+ *   arguments as for kvq_paged_decode_attention, without the workspace
+ * Returns KVQ_ERR_WORKSPACE_TOO_SMALL, before any device call, when the
+ * plan for (desc, num_seqs, max_context_len) needs more workspace than the
+ * array holds (kvq_decode_workspace_bytes reports the need): for example
+ * 64 sequences of 131072 positions of a 32 q / 8 KV head layer.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int kvq_paged_decode_attention_noalloc(const kvq_layer_desc* desc, void* out,
+                                       int32_t out_dtype, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       int64_t num_pages, const int32_t* block_tables,
+                                       int32_t max_pages_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t max_context_len, const float* k_scale,
+                                       const float* v_scale, void* stream);
+
+/*
  * kvq_decode_step - one decode step of a layer in one call: the cache write
  * of every sequence's newest token followed by the attention, i.e. exactly
  *     kvq_kv_cache_write(k_new, v_new, slot of position L-1 of each sequence)

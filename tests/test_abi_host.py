@@ -295,3 +295,15 @@ def test_tuning_overrides_are_explicit(tune, monkeypatch):
     for knob, good in ((0, 64), (1, 0), (2, 211), (3, 3), (4, 7)):
         assert L.kvq_set_tuning(knob, good) == OK
         assert L.kvq_set_tuning(knob, -1) == OK
+
+
+def test_noalloc_size_limit_is_checked_on_the_host(L):
+    """The no-allocation decode entry point rejects a plan whose workspace
+    exceeds its device array before touching any device."""
+    d = kv.layer_desc(32, 8, 128)
+    assert kv.decode_workspace_bytes(d, 64, 131072) > kv.NOALLOC_SCRATCH_BYTES
+    st = L.kvq_paged_decode_attention_noalloc(ctypes.byref(d), FAKE, 0, FAKE, FAKE, FAKE, 16,
+                                              FAKE, 8192, FAKE, 64, 131072, FAKE, FAKE, None)
+    assert st == WS_SMALL
+    assert L.kvq_paged_decode_attention_noalloc(None, FAKE, 0, FAKE, FAKE, FAKE, 16, FAKE, 8192,
+                                                FAKE, 1, 16, FAKE, FAKE, None) == INVALID
