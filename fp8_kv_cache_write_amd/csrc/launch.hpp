@@ -68,8 +68,9 @@ int tuning_override(int knob);
 // Waves per work-group of the split kernel.
 constexpr int kSplitWaves = 4;
 
-// Partitions the reduce kernel reads per chunk, at most (one per lane).
-constexpr int kReduceChunk = 64;
+// Partitions the reduce kernel reads per chunk, at most (two per lane); the
+// workspaces end with this many partial slots of slack.
+constexpr int kReduceChunk = 128;
 
 // fused = true: the split kernel also writes k_new / v_new into the caches at
 // position L-1 of every sequence (p.k_cache / p.v_cache must be writable).

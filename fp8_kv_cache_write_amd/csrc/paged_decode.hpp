@@ -208,14 +208,17 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   const int c = lane & 15;              // MFMA column
   const int part_pages = NW * p.pages_per_wave;
 
-  // Column c < G: query c (high half of P); G <= c < 2G: query c - G (low
-  // half of P); other columns idle. With G > 8 (wide) the 16 columns hold
-  // queries only, and P*V runs twice into the same accumulator: once with
-  // the high halves, once with the low ones. The all-FP8 mode has no low
-  // halves (P is e4m3 on purpose).
+  // Column c < G: query c (high half of P); 8 <= c < 8 + G: query c - 8
+  // (low half of P); other columns idle. The low half of query g sits 8
+  // columns after its high half for every G <= 8, so the final fold of the
+  // low columns into the high ones is one fixed DPP row shift. With G > 8
+  // (wide) the 16 columns hold queries only, and P*V runs twice into the
+  // same accumulator: once with the high halves, once with the low ones.
+  // The all-FP8 mode has no low halves (P is e4m3 on purpose).
   constexpr bool wide = WIDE;           // G > 8 (the launcher picks the instance)
-  const int g = c < G ? c : ((!ATT8 && !wide && c < 2 * G) ? c - G : -1);
-  const bool lo_col = !ATT8 && !wide && (c >= G) && (c < 2 * G);
+  constexpr bool has_lo = !ATT8 && !wide;
+  const bool lo_col = has_lo && c >= 8 && c - 8 < G;
+  const int g = c < G ? c : (lo_col ? c - 8 : -1);
 
   // Loads that do not depend on the context length go out before it is
   // known, so a work-group waits for one memory round trip, not two, before
@@ -942,34 +945,49 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   // A NaN logit (a NaN query element or cache code) leaves l NaN but may
   // never raise the running max; carry it in m so the merges keep it.
   if (l_run != l_run) m_run = __builtin_nanf("");
-  if constexpr (!ATT8 && !wide) {
+  if constexpr (has_lo) {
+    // column c + 8 (the low half of query c) into column c: DPP row_shl:8
+    // within each 16-lane row (the MFMA column index is lane % 16)
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[blk][e] += __shfl_down(acc[blk][e], G);
+      for (int e = 0; e < 4; ++e)
+        acc[blk][e] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc[blk][e]),
+                                                               0x108, 0xF, 0xF, true));
   }
 
+  // The wave's unnormalised rows into LDS, 16 bytes at a time: lane (qd, c)
+  // holds 4 consecutive dims for each (block group, e) (fp8 layout: dims
+  // 64 i + 16 qd + 4 e + r from acc[4 i + r][e]; bf16 layout: dims
+  // 32 i + 8 qd + 4 j + r' from acc[2 i + (r' % 2)][2 j + r' / 2]).
   if (c < G) {
     if (qd == 0) {
       sm_m[wave][c] = m_run;
       sm_l[wave][c] = l_run;
     }
+    float* const orow = reinterpret_cast<float*>(my_region) + c * D;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
+      for (int i = 0; i < NBLK / 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int d;
-        if constexpr (FP8) d = 64 * (blk / 4) + 16 * qd + 4 * e + (blk % 4);
-        else d = 32 * (blk / 2) + 8 * qd + 2 * e + (blk % 2);
-        reinterpret_cast<float*>(my_region)[c * D + d] = acc[blk][e];
-      }
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<f32x4*>(orow + 64 * i + 16 * qd + 4 * e) =
+              f32x4{acc[4 * i][e], acc[4 * i + 1][e], acc[4 * i + 2][e], acc[4 * i + 3][e]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < NBLK / 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          *reinterpret_cast<f32x4*>(orow + 32 * i + 8 * qd + 4 * j) =
+              f32x4{acc[2 * i][2 * j], acc[2 * i + 1][2 * j], acc[2 * i][2 * j + 1],
+                    acc[2 * i + 1][2 * j + 1]};
     }
   }
   __syncthreads();
 
-  // ---- merge the waves of this partition ----------------------------------
-  for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
-    const int gg = i / D, d = i % D;
+  // ---- merge the waves of this partition, 4 dims per thread ---------------
+  for (int i = threadIdx.x; i < G * D / 4; i += NW * kWave) {
+    const int gg = (4 * i) / D, d = (4 * i) % D;
     float M = -INFINITY;
     bool nan_m = false;
 #pragma unroll
@@ -978,26 +996,43 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
       nan_m |= mw != mw;
       M = fmaxf(M, mw);
     }
-    float o = 0.0f, l = 0.0f;
+    f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float l = 0.0f;
     if (nan_m) {
-      M = o = l = __builtin_nanf("");
+      M = l = __builtin_nanf("");
+      o = f32x4{M, M, M, M};
     } else if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float wt = __builtin_amdgcn_exp2f(sm_m[w][gg] - M);
-        o += wt * reinterpret_cast<const float*>(smem + w * REGION)[gg * D + d];
+        const f32x4 ow =
+            *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(smem + w * REGION) +
+                                            gg * D + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += wt * ow[e];
         l += wt * sm_l[w][gg];
       }
     }
     const int hq = h * G + gg;
     const int64_t row = (int64_t)b * p.num_q_heads + hq;
     if (p.direct) {
-      const float r = (l > 0.0f || l != l) ? o / l * vs : 0.0f;   // NaN stays NaN
-      if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
-      else reinterpret_cast<float*>(p.out)[row * D + d] = r;
+      const bool live = l > 0.0f || l != l;                     // NaN stays NaN
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = live ? o[e] / l * vs : 0.0f;
+      if (p.out_bf16) {
+        const bf16x2 lo2 = __builtin_convertvector((float2_t){r[0], r[1]}, bf16x2);
+        const bf16x2 hi2 = __builtin_convertvector((float2_t){r[2], r[3]}, bf16x2);
+        uint2 w2;
+        w2.x = __builtin_bit_cast(uint32_t, lo2);
+        w2.y = __builtin_bit_cast(uint32_t, hi2);
+        *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(p.out) + row * D + d) = w2;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + d) = r;
+      }
     } else {
       const int64_t slot = row * p.num_parts + part;
-      p.ws_o[slot * D + d] = o;
+      *reinterpret_cast<f32x4*>(p.ws_o + slot * D + d) = o;
       if (d == 0) {
         p.ws_m[slot] = M;
         p.ws_l[slot] = l;
@@ -1012,13 +1047,16 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 // (m = -inf, l = 0) in the slots of partitions a sequence does not reach, so
 // the merge needs neither the context length nor a second round trip. Each
 // wave owns 64 dims of one (sequence, query head) and needs no barrier. The
-// partitions are taken NPC at a time (one chunk for up to 64 partitions):
-// lane j reads m_j and l_j, then lane d the partial outputs o_j[d] of the
-// chunk, all issued before the first wait. The wave max and sum run on DPP row
-// rotations and the gfx950 row swaps (no LDS round trip); the weights w_j
-// reach every lane as broadcast LDS reads, four at a time. A partition of
-// weight 0 adds nothing (its o may never have been written), and a later
-// chunk with a larger max rescales what the earlier ones summed.
+// partitions are taken NPC at a time (one chunk for up to 128 partitions):
+// lane j reads m_j and l_j (two per lane past 64), and the partial outputs
+// are read as 16-byte pieces: lane (pg, dq) = (lane / 16, lane % 16) holds
+// dims 4 dq .. 4 dq + 3 of partitions pg, pg + 4, ..., so a chunk is NPC / 4
+// loads per lane, all issued before the first wait. The wave max and sum run
+// on DPP row rotations and the gfx950 row swaps (no LDS round trip); the
+// weights w_j reach the lanes through LDS. A partition of weight 0 adds
+// nothing (its o may never have been written), and a later chunk with a
+// larger max rescales what the earlier ones summed. The four partition
+// groups of a dim are summed at the end with the row swaps.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -1042,15 +1080,18 @@ __device__ __forceinline__ float wave_all(float x) {
 
 template <int D, int NPC>
 __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const DecodeParams p) {
-  static_assert(NPC % 4 == 0 && NPC <= kWave, "a chunk is at most one wave of partitions");
+  static_assert(NPC % 4 == 0 && (NPC <= kWave || NPC % kWave == 0) && NPC <= kReduceChunk,
+                "a chunk is at most one wave of partitions, or whole waves of them");
   // One wave per work-group: work-group x merges dims 64*(x mod D/64) .. +63
   // of query head x / (D/64), so the partials of a row are read by D/64
   // compute units at once rather than one.
   constexpr int kSlices = D / kWave;
-  __shared__ __align__(16) float sw[1][NPC];
+  constexpr int MPL = NPC > kWave ? NPC / kWave : 1;   // partitions per lane (m, l)
+  constexpr int OPL = NPC / 4;                         // 16-byte partial loads per lane
+  __shared__ __align__(16) float sw[NPC];
   const int lane = threadIdx.x;
-  const int wave = 0;
-  const int d = (int)(blockIdx.x % kSlices) * kWave + lane;
+  const int pg = lane >> 4, dq = lane & 15;
+  const int d0 = (int)(blockIdx.x % kSlices) * kWave + 4 * dq;
   const int hq = (int)(blockIdx.x / kSlices);
   const int b = blockIdx.y;
   if (p.row_limit && b >= *p.row_limit) return;   // past the last row (prefill merge)
@@ -1059,26 +1100,40 @@ __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const Decode
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
   const float* mrow = p.ws_m + row * np;
   const float* lrow = p.ws_l + row * np;
-  const float* orow = p.ws_o + row * np * D;
+  const float* orow = p.ws_o + row * np * D + d0;
   const float vs = p.v_scale ? p.v_scale[p.scale_per_head ? h : 0] : 1.0f;
 
   float M = -INFINITY, L = 0.0f;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   bool any_nan = false;                   // a NaN partial makes the row NaN
   for (int base = 0; base < np; base += NPC) {
     // Every load of the chunk, unconditionally: the workspace ends with a
-    // chunk's worth of slack, and slots past this row's partitions (other
-    // rows' partials, slack) get weight 0 below.
-    const float mv = mrow[base + lane];
-    const float lv = lrow[base + lane];
-    float ov[NPC];
+    // chunk's worth of slack (and the m and l regions are followed by
+    // others), and slots past this row's partitions (other rows' partials,
+    // slack) get weight 0 below.
+    float mv[MPL], lv[MPL];
 #pragma unroll
-    for (int u = 0; u < NPC; ++u) ov[u] = orow[(int64_t)(base + u) * D + d];
-    const bool in = lane < NPC && base + lane < np;
-    const float mj = in ? mv : -INFINITY;
-    const float lj = in ? lv : 0.0f;
-    any_nan |= __builtin_amdgcn_ballot_w64(mj != mj) != 0ull;
-    const float Mn = fmaxf(M, wave_all<true>(mj));
+    for (int k = 0; k < MPL; ++k) {
+      mv[k] = mrow[base + k * kWave + lane];
+      lv[k] = lrow[base + k * kWave + lane];
+    }
+    f32x4 ov[OPL];
+#pragma unroll
+    for (int u = 0; u < OPL; ++u)
+      ov[u] = *reinterpret_cast<const f32x4*>(orow + (int64_t)(base + 4 * u + pg) * D);
+    float mj[MPL], lj[MPL], mloc = -INFINITY;
+    bool nan_here = false;
+#pragma unroll
+    for (int k = 0; k < MPL; ++k) {
+      const int j = k * kWave + lane;
+      const bool in = j < NPC && base + j < np;
+      mj[k] = in ? mv[k] : -INFINITY;
+      lj[k] = in ? lv[k] : 0.0f;
+      nan_here |= mj[k] != mj[k];
+      mloc = fmaxf(mloc, mj[k]);
+    }
+    any_nan |= __builtin_amdgcn_ballot_w64(nan_here) != 0ull;
+    const float Mn = fmaxf(M, wave_all<true>(mloc));
     // weights relative to Mn (to 0 while nothing is attended: all weights 0);
     // what earlier chunks summed is rescaled to it
     const float Mr = Mn == -INFINITY ? 0.0f : Mn;
@@ -1087,33 +1142,54 @@ __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const Decode
     for (int e = 0; e < 4; ++e) acc[e] *= r;
     L *= r;
     M = Mn;
-    const float wj = in ? __builtin_amdgcn_exp2f(mj - Mr) : 0.0f;   // 0 for m_j = -inf
-    L += wave_all<false>(wj * lj);
-    if (lane < NPC) sw[wave][lane] = wj;
+    float wl = 0.0f;
 #pragma unroll
-    for (int u = 0; u < NPC; u += 4) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&sw[wave][u]);
-      const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+    for (int k = 0; k < MPL; ++k) {
+      const int j = k * kWave + lane;
+      const float wj = mj[k] != -INFINITY ? __builtin_amdgcn_exp2f(mj[k] - Mr) : 0.0f;
+      wl += wj * lj[k];
+      if (j < NPC) sw[j] = wj;
+    }
+    L += wave_all<false>(wl);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w[e], w[e] != 0.0f ? ov[u + e] : 0.0f, acc[e]);
+    for (int u = 0; u < OPL; ++u) {
+      const float w = sw[4 * u + pg];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, w != 0.0f ? ov[u][e] : 0.0f, acc[e]);
     }
   }
-  const float o = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  const float r = any_nan ? __builtin_nanf("") : (L > 0.0f ? o / L * vs : 0.0f);
-  if (p.out_bf16) reinterpret_cast<__bf16*>(p.out)[row * D + d] = (__bf16)r;
-  else reinterpret_cast<float*>(p.out)[row * D + d] = r;
+  // the four partition groups of each dim: lanes dq, dq + 16, dq + 32, dq + 48
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = wave_sum_col(acc[e]);
+  if (pg != 0) return;
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r[e] = any_nan ? __builtin_nanf("") : (L > 0.0f ? acc[e] / L * vs : 0.0f);
+  if (p.out_bf16) {
+    const bf16x2 lo2 = __builtin_convertvector((float2_t){r[0], r[1]}, bf16x2);
+    const bf16x2 hi2 = __builtin_convertvector((float2_t){r[2], r[3]}, bf16x2);
+    uint2 w2;
+    w2.x = __builtin_bit_cast(uint32_t, lo2);
+    w2.y = __builtin_bit_cast(uint32_t, hi2);
+    *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(p.out) + row * D + d0) = w2;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + d0) = r;
+  }
 }
 
 template <int D>
 static void launch_reduce(const DecodeParams& pr, int num_seqs, hipStream_t stream) {
   const dim3 grid((unsigned)(pr.num_q_heads * (D / kWave)), (unsigned)num_seqs);
-  static_assert(kReduceChunk == 64, "the largest chunk below is the workspace's slack");
+  static_assert(kReduceChunk == 128, "the largest chunk below is the workspace's slack");
   if (pr.num_parts <= 16)
     hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 16>), grid, dim3(kWave), 0, stream, pr);
   else if (pr.num_parts <= 32)
     hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 32>), grid, dim3(kWave), 0, stream, pr);
-  else
+  else if (pr.num_parts <= 64)
     hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 64>), grid, dim3(kWave), 0, stream, pr);
+  else
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 128>), grid, dim3(kWave), 0, stream, pr);
 }
 
 // Arithmetic modes of the split kernel.
