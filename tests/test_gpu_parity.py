@@ -402,6 +402,43 @@ def test_full_llama8b_128k(llama8b_128k, variant):
             f"mean={d.mean():.3e} (reported, not gated)")
 
 
+@pytest.mark.parametrize("L", [8192, 32768])
+@pytest.mark.parametrize("variant", ["fp8-per-head", "fp8-scale1"])
+def test_full_llama8b_mid_contexts_decode_step(L, variant):
+    """The 8B layer at 8192 and 32768 positions (the plan's LDS-staged runs
+    of 4 and 16 pages) through kvq_decode_step with the default plan: the
+    cache holds positions 0 .. L-2, the step writes position L-1 and attends
+    over all L. Cache bytes bit-exact against the oracle's write of every
+    position; attention to the gate and the tight bound."""
+    case = full_case(synth.LLAMA8B, 32, 8, 128, [L])
+    per_head = variant == "fp8-per-head"
+    scales = ([1.0], [1.0]) if variant == "fp8-scale1" else None
+    o = OracleLayer(case, per_head=per_head, scales=scales)
+    import copy
+    pre = copy.copy(case)
+    pre.k_new, pre.v_new, pre.slots = case.k_new[:-1], case.v_new[:-1], case.slots[:-1]
+    sc = (o.ks, o.vs) if per_head else scales
+    g = GpuLayer(pre, per_head=per_head, scales=sc)
+    ws = kv.alloc_workspace(g.desc, 1, L)
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev())
+    kv.decode_step(g.desc, bf16_dev(case.k_new[-1:]), bf16_dev(case.v_new[-1:]), g.k_cache,
+                   g.v_cache, out, g.q, g.block_tables, i32_dev(case.lens), L, g.k_scale,
+                   g.v_scale, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g.k_cache), o.k_cache)
+    assert np.array_equal(host(g.v_cache), o.v_cache)
+    ref = o.attend()
+    mx, mean = errors(out, ref)
+    label = f"8B-{L}-{variant}-decode-step"
+    say(f"[{label}] max_abs={mx:.3e} mean_abs={mean:.3e}")
+    assert mx <= GATE_MAX_ABS and mean <= GATE_MEAN_ABS, (label, mx, mean)
+    assert mx <= tight_bound(ref), (label, mx)
+    unq = unquantised_reference(case)
+    d = np.abs(host(out).astype(np.float64) - unq)
+    say(f"[{label}] error vs unquantised bf16 attention: max={d.max():.3e} "
+        f"mean={d.mean():.3e} (reported, not gated)")
+
+
 def test_full_batched_concurrency8_with_step_write():
     lens = synth.batched_lens()
     case = full_case(synth.BATCHED, 32, 8, 128, lens, shuffle=True, spare_frac=0.1)

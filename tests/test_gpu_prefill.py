@@ -161,6 +161,40 @@ def test_prefill_llama8b_8k_whole_prompt_sampled():
     check(torch.from_numpy(out[rows]), ref, o, case, "prefill-8B-8k-sampled")
 
 
+def test_prefill_llama8b_32k_whole_prompt_every_query_block():
+    """The 32768-token whole-prompt prefill of the 8B layer (the prefill the
+    benchmark times): one row of every 48-row query block (the plan's block
+    for this shape; its offset in the block varies) checked against the
+    decode kernel, which the full-size decode tests pin to the oracle, at
+    context pos + 1, all in one batched decode call; and 64 of those rows,
+    spread from the first block to the last, against the oracle itself."""
+    L = 32768
+    case = synth.prefill_case(synth.LLAMA8B, 32, 8, 128, [L], [L])
+    g = GpuLayer(case)
+    out = host(gpu_prefill(g, case))
+    blk = 48
+    rows = np.array([b * blk + (7 * b) % blk for b in range(L // blk)] + [L - 1], np.int32)
+    rows = np.unique(rows)
+    B = rows.size
+    q_rows = torch.from_numpy(np.ascontiguousarray(case.q[rows]).view(np.int16)).to(dev()) \
+        .view(torch.bfloat16)
+    bt = i32_dev(np.repeat(case.block_tables, B, axis=0))
+    lens = i32_dev(rows + 1)
+    dec = torch.empty((B, 32, 128), dtype=torch.float32, device=dev())
+    ws = kv.alloc_workspace(g.desc, B, L)
+    kv.paged_decode_attention(g.desc, dec, q_rows, g.k_cache, g.v_cache, bt, lens, L,
+                              g.k_scale, g.v_scale, ws)
+    torch.cuda.synchronize()
+    d = np.abs(out[rows] - host(dec))
+    bound = 2.0 ** -8 * vmax(None, case) + 1e-5
+    say(f"[prefill-8B-32k-every-block] {B} rows vs decode: max_abs={d.max():.3e} bound={bound:.3e}")
+    assert np.all(np.isfinite(out[rows])) and d.max() <= bound, (float(d.max()), bound)
+    o = OracleLayer(case)
+    sub = rows[np.linspace(0, B - 1, 64).round().astype(int)]
+    ref = oracle_prefill(o, case, sub)
+    check(torch.from_numpy(out[sub]), ref, o, case, "prefill-8B-32k-whole-sampled")
+
+
 def test_prefill_llama8b_32k_chunk_sampled():
     # a 2048-row chunk at the end of a 32768-position context
     case = synth.prefill_case(synth.LLAMA8B, 32, 8, 128, [32768], [2048])
