@@ -659,6 +659,130 @@ def prefill_bench(torch, kv, w, lengths, steps, warmup, scales="per_kv_head", at
                           "algorithmic_flops": 4 * D * Hq * max(lengths) * (max(lengths) + 1) // 2})
 
 
+def stack_point(torch, kv, stack, steps, warmup):
+    """One layer stack: graph-timed µs per layer step, the split kernel's
+    mean launch time (kernel-timestamped events over eager steps), the same
+    bytes read by a plain streaming read, and the ratios."""
+    ms = time_steps_graph(torch, stack, steps, warmup)
+    _, split_ms, _ = time_steps(torch, kv, stack, 3, 1)
+    NL = stack.NL
+    d0 = stack.layers[0]["desc"]
+    split_bytes = stack.split_bytes(d0) + stack.write_bytes(d0)
+    us = ms * 1e3 / NL
+    step_gbs = stack.total_step_bytes() / (ms * 1e-3) / 1e9
+    split_us = split_ms * 1e3 if split_ms else None
+    return dict(layers=NL, us_per_layer_step=round(us, 3), step_gbs=round(step_gbs, 1),
+                step_frac_hbm=round(step_gbs / HBM_PEAK_GBS, 4),
+                split_us=round(split_us, 3) if split_us else None,
+                split_gbs=round(split_bytes / (split_us * 1e-6) / 1e9, 1) if split_us else None,
+                split_frac_hbm=round(split_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                if split_us else None,
+                split_bytes=split_bytes), split_bytes
+
+
+def other_workloads(torch, kv, steps, warmup):
+    """The other decode workloads, each as a graph-timed layer stack of at
+    least 2 GiB of cache: the batched step (8 sequences of 18k-22k positions,
+    shuffled pool, each step writing 8 new tokens), the 70B layer at 131072
+    positions, the head_dim 256 layer at 65536, and the gpt-oss-like layer
+    types at 32768 (full-attention fp8 layers; window-128 bf16 skip
+    layers). Each point carries the split kernel's time against a plain
+    read of the same bytes (same_size_read_us)."""
+    import synth
+    out = {}
+    W = WORKLOADS
+    cfgs = [
+        ("batched_8x18k-22k", W["batched"], [int(x) for x in synth.batched_lens()],
+         dict(shuffle=True, spare_frac=0.1)),
+        ("llama70b_131072", W["llama70b"], [131072], {}),
+        ("hd256_65536", W["hd256"], [65536], {}),
+        ("gptoss_full_fp8_32768", W["gptoss"], [32768], {}),
+    ]
+    for name, w, lens, kw in cfgs:
+        per_layer = sum(lens) * w["Hkv"] * w["D"] * 2
+        NL = layers_for(per_layer, hi=64)
+        st = LayerStack(kv, torch, len(lens), w["Hq"], w["Hkv"], w["D"], lens, NL, seed=11,
+                        **kw)
+        pt, sb = stack_point(torch, kv, st, steps, warmup)
+        del st
+        torch.cuda.empty_cache()
+        rd = same_size_read_us(torch, kv, sb)
+        pt["same_size_read_us"] = round(rd, 3)
+        pt["split_over_same_size_read"] = round(pt["split_us"] / rd, 4) if pt["split_us"] else None
+        pt["step_over_same_size_read"] = round(pt["us_per_layer_step"] / rd, 4)
+        pt["shape"] = dict(batch=len(lens), q_heads=w["Hq"], kv_heads=w["Hkv"], head_dim=w["D"],
+                           contexts=f"{min(lens)}..{max(lens)}" if len(lens) > 1 else lens[0])
+        log(f"workload {name}: {pt['us_per_layer_step']:.2f} us/layer step "
+            f"({pt['step_frac_hbm'] * 100:.1f} % of peak), split {pt['split_us']} us, "
+            f"read {rd:.2f} us")
+        out[name] = pt
+    # the gpt-oss window layers: window 128, bf16 cache (the skip path)
+    w = W["gptoss"]
+    st = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [32768], 32, "bf16", window=128,
+                    seed=12)
+    ms = time_steps_graph(torch, st, steps, warmup)
+    out["gptoss_window128_bf16_32768"] = dict(
+        layers=32, us_per_layer_step=round(ms * 1e3 / 32, 3),
+        note="reads the last 128 positions: launch-bound (its caches stay in the Infinity Cache)")
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
+def quantisation_error(torch, kv):
+    """Error of fp8 attention (per-KV-head scales, amax/448) against
+    unquantised bf16 attention on the same inputs: the 8B layer (normal
+    values) and the 70B layer (drifting V with heavy-tail rows) at 131072
+    positions, drawn by synth. The unquantised reference is the library's
+    bf16-cache path on the same bf16 K/V and q, which the full-size parity
+    tests hold within 3e-6 of the float64 oracle."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    res = {}
+    for name, wl, Hq, values in (("llama8b_131072", synth.LLAMA8B, 32, "normal"),
+                                 ("llama70b_131072", synth.LLAMA70B, 64, "drift")):
+        case = synth.decode_case(wl, Hq, 8, 128, [131072], values=values)
+        k, v, q = bf16(case.k_new), bf16(case.v_new), bf16(case.q)
+        slots = torch.from_numpy(case.slots).to(dev)
+        bt = torch.from_numpy(case.block_tables).to(dev)
+        lens = torch.from_numpy(case.lens).to(dev)
+        outs = {}
+        for dt in ("fp8_e4m3", "bf16"):
+            d = kv.layer_desc(Hq, 8, 128, dt, "per_kv_head")
+            kc = torch.empty(kv.cache_shape(d, case.num_pages), dtype=torch.uint8, device=dev)
+            vc = torch.empty_like(kc)
+            ks = vs = None
+            if d.fp8:
+                ks = torch.empty(8, dtype=torch.float32, device=dev)
+                vs = torch.empty(8, dtype=torch.float32, device=dev)
+                kv.kv_scale_from_amax(d, k, ks)
+                kv.kv_scale_from_amax(d, v, vs)
+            kv.kv_cache_write(d, k, v, slots, kc, vc, ks, vs)
+            o = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
+            kv.paged_decode_attention(d, o, q, kc, vc, bt, lens, 131072, ks, vs,
+                                      kv.alloc_workspace(d, 1, 131072))
+            torch.cuda.synchronize()
+            outs[dt] = o.double()
+            del kc, vc
+        diff = (outs["fp8_e4m3"] - outs["bf16"]).abs()
+        res[name] = dict(max_abs=float(diff.max()), mean_abs=float(diff.mean()),
+                         output_max_abs=float(outs["bf16"].abs().max()))
+        log(f"quantisation error {name}: max {res[name]['max_abs']:.3e} "
+            f"mean {res[name]['mean_abs']:.3e}")
+        del k, v, q, outs
+        torch.cuda.empty_cache()
+    res["how"] = ("fp8 e4m3 cache with per-KV-head scales amax/448 against the bf16 cache on "
+                  "the same inputs (synth workloads llama8b and llama70b-drift); reported, "
+                  "not gated")
+    return res
+
+
 def cpu_baseline(w, ctx, min_seconds=10.0):
     """The float64 oracle on the headline layer (all heads, full context),
     repeated until at least min_seconds of wall time."""
@@ -720,6 +844,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="print the prefill sweep only (no decode headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other decode workloads (batched, 70B, head_dim 256, "
+                         "gpt-oss layer types) and the quantisation-error report")
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling PMC byte counters)")
@@ -891,6 +1018,9 @@ def main():
     if not args.no_sweep and args.workload == "llama8b":
         contexts = [16, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
         result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
+    if not args.no_workloads and args.workload == "llama8b":
+        result["workloads"] = other_workloads(torch, kv, args.sweep_steps, 2)
+        result["quantisation_error_vs_bf16"] = quantisation_error(torch, kv)
     if not args.no_sweep and args.workload == "gptoss":
         result["gptoss_sweep"] = gptoss_sweep(torch, kv, w, [8192, 32768, 65536, 131072],
                                               args.sweep_steps, 2)
