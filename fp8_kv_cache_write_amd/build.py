@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvfp8.so")
-SOURCES = ["api.cpp", "kv_cache_write.hip", "paged_decode.hip", "paged_decode_d64.hip",
+SOURCES = ["api.cpp", "prefill_plan.cpp", "kv_cache_write.hip", "paged_decode.hip", "paged_decode_d64.hip",
            "paged_decode_d128.hip", "paged_decode_d256.hip", "paged_prefill.hip",
            "stream_read.hip", "decode_noalloc.hip"]
 OBJDIR = os.path.join(HERE, "_build")

@@ -37,7 +37,9 @@ def lib():
     """Load liboracle.so, building it with gcc first if it is missing."""
     global _lib
     if _lib is None:
-        path = os.path.join(_HERE, "liboracle.so")
+        # ORACLE_LIB names another build of oracle.c (the sanitizer test
+        # loads liboracle_asan.so this way)
+        path = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
         if not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)

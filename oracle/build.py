@@ -17,6 +17,22 @@ CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
           "-shared", "-pthread", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
 
+LIB_SANITIZED = os.path.join(HERE, "liboracle_asan.so")
+# AddressSanitizer and UndefinedBehaviorSanitizer build of the same source,
+# for the CPU test tier (loaded with libasan preloaded; see the sanitizer test).
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    cmd = ["gcc", *CFLAGS, *SANITIZE, SRC, "-o", LIB_SANITIZED + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_SANITIZED + ".tmp", LIB_SANITIZED)
+    return LIB_SANITIZED
+
+
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
     if verbose:

@@ -46,6 +46,48 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
+# ---- guard bands ------------------------------------------------------------
+# Every device buffer the library writes in these helpers (caches, scale
+# pools, outputs, workspaces) sits inside a larger allocation whose first and
+# last GUARD bytes hold a fixed pattern; check_guards() after each call
+# confirms that no kernel wrote outside its buffer.
+GUARD = 4096
+GUARD_BYTE = 0xA5
+
+
+def guarded(shape, dtype, fill=None, registry=None):
+    """A device tensor of shape/dtype inside a guarded allocation (the
+    buffer itself 256-byte aligned, as the workspaces need); fill: a value,
+    a host numpy array of the same bytes, or None (left uninitialised). The
+    allocation and the buffer's size go into registry (a list) for
+    check_guards."""
+    elem = torch.empty((), dtype=dtype).element_size()
+    n = 1
+    for x in shape:
+        n *= int(x)
+    nbytes = n * elem
+    big = torch.full((GUARD + nbytes + GUARD,), GUARD_BYTE, dtype=torch.uint8, device=dev())
+    inner = big[GUARD:GUARD + nbytes].view(dtype).view(*shape)
+    if isinstance(fill, np.ndarray):
+        inner.view(torch.uint8).view(-1).copy_(
+            torch.from_numpy(np.ascontiguousarray(fill).view(np.uint8).reshape(-1)).to(dev()))
+    elif fill is not None:
+        inner.fill_(fill)
+    if registry is not None:
+        registry.append((big, nbytes))
+    return inner
+
+
+def check_guards(registry, label=""):
+    """Every guard band of the registered allocations still holds its
+    pattern."""
+    torch.cuda.synchronize()
+    for big, nbytes in registry:
+        ok = bool((big[:GUARD] == GUARD_BYTE).all()) and \
+            bool((big[GUARD + nbytes:] == GUARD_BYTE).all())
+        assert ok, f"{label}: a kernel wrote outside a buffer of {nbytes} bytes"
+
+
 class GpuLayer:
     """One layer on the GPU: poisoned caches, scales calibrated by the
     library, every position of the case written by the library. dyn:
@@ -65,17 +107,18 @@ class GpuLayer:
         self.v_new = bf16_dev(case.v_new)
         self.slots = i64_dev(case.slots)
         pc = synth.poisoned_cache(case.num_pages, case.num_kv_heads, case.head_dim, fp8)
-        self.k_cache = u8_dev(pc)
-        self.v_cache = u8_dev(pc)
+        self.guards = []                       # the caches' and scales' guard bands
+        self.k_cache = guarded(pc.shape, torch.uint8, pc, self.guards)
+        self.v_cache = guarded(pc.shape, torch.uint8, pc, self.guards)
         n = case.num_kv_heads if per_head else 1
         if self.dyn:
             shape = kv.scale_pool_shape(self.desc, case.num_pages)
-            self.k_scale = torch.full(shape, float("nan"), dtype=torch.float32, device=dev())
-            self.v_scale = torch.full(shape, float("nan"), dtype=torch.float32, device=dev())
+            self.k_scale = guarded(shape, torch.float32, float("nan"), self.guards)
+            self.v_scale = guarded(shape, torch.float32, float("nan"), self.guards)
         elif fp8:
             if scales is None:
-                self.k_scale = torch.empty(n, dtype=torch.float32, device=dev())
-                self.v_scale = torch.empty(n, dtype=torch.float32, device=dev())
+                self.k_scale = guarded((n,), torch.float32, None, self.guards)
+                self.v_scale = guarded((n,), torch.float32, None, self.guards)
                 kv.kv_scale_from_amax(self.desc, self.k_new, self.k_scale)
                 kv.kv_scale_from_amax(self.desc, self.v_new, self.v_scale)
             else:
@@ -89,21 +132,23 @@ class GpuLayer:
         else:
             kv.kv_cache_write(self.desc, self.k_new, self.v_new, self.slots, self.k_cache,
                               self.v_cache, self.k_scale, self.v_scale)
+        check_guards(self.guards, "cache write")
         self.q = bf16_dev(case.q)
         self.block_tables = i32_dev(case.block_tables)
         self.context_lens = i32_dev(case.lens)
 
     def attend(self, out_dtype=torch.float32, block_tables=None, q=None):
         c = self.case
-        out = torch.empty((c.num_seqs, c.num_q_heads, c.head_dim), dtype=out_dtype,
-                          device=dev())
-        ws = kv.alloc_workspace(self.desc, c.num_seqs, c.max_context_len)
+        reg = list(self.guards)
+        out = guarded((c.num_seqs, c.num_q_heads, c.head_dim), out_dtype, None, reg)
+        n = kv.decode_workspace_bytes(self.desc, c.num_seqs, c.max_context_len)
+        ws = guarded((n,), torch.uint8, None, reg) if n else None
         kv.paged_decode_attention(self.desc, out, self.q if q is None else q,
                                   self.k_cache, self.v_cache,
                                   self.block_tables if block_tables is None else block_tables,
                                   self.context_lens, c.max_context_len, self.k_scale,
                                   self.v_scale, ws)
-        torch.cuda.synchronize()
+        check_guards(reg, "decode attention")
         return out
 
     def scales_host(self):

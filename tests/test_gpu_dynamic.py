@@ -15,7 +15,8 @@ import torch
 import fp8_kv_cache_write_amd as kv
 import oracle
 import synth
-from _gpu import GpuLayer, OracleLayer, bf16_dev, dev, errors, host, i32_dev
+from _gpu import (GpuLayer, OracleLayer, bf16_dev, check_guards, dev, errors, guarded, host,
+                  i32_dev)
 from test_gpu_parity import (GATE_MAX_ABS, GATE_MEAN_ABS, newest_rows, say, split_newest)
 
 pytestmark = pytest.mark.gpu
@@ -191,13 +192,14 @@ def test_dynamic_nan_token_makes_its_heads_nan():
 
 
 def run_decode_step_dynamic(g, case, knew, vnew):
-    out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=torch.float32,
-                      device=dev())
-    ws = kv.alloc_workspace(g.desc, case.num_seqs, case.max_context_len)
+    reg = list(g.guards)
+    out = guarded((case.num_seqs, case.num_q_heads, case.head_dim), torch.float32, None, reg)
+    n = kv.decode_workspace_bytes(g.desc, case.num_seqs, case.max_context_len)
+    ws = guarded((n,), torch.uint8, None, reg) if n else None
     kv.decode_step_dynamic(g.desc, bf16_dev(knew), bf16_dev(vnew), g.k_cache, g.v_cache, out,
                            g.q, i32_dev(case.block_tables), i32_dev(case.lens),
                            case.max_context_len, g.k_scale, g.v_scale, ws)
-    torch.cuda.synchronize()
+    check_guards(reg, "dynamic decode step")
     return out
 
 

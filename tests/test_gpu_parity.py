@@ -20,7 +20,7 @@ import fp8_kv_cache_write_amd as kv
 import oracle
 import synth
 from _gpu import (BF16, FP8, GATE_MAX_ABS, GATE_MEAN_ABS, GpuLayer, OracleLayer,
-                  bf16_dev, dev, errors, host, i32_dev, i64_dev,
+                  bf16_dev, check_guards, dev, errors, guarded, host, i32_dev, i64_dev,
                   unquantised_reference)
 
 pytestmark = pytest.mark.gpu
@@ -419,12 +419,7 @@ def test_full_llama8b_mid_contexts_decode_step(L, variant):
     pre.k_new, pre.v_new, pre.slots = case.k_new[:-1], case.v_new[:-1], case.slots[:-1]
     sc = (o.ks, o.vs) if per_head else scales
     g = GpuLayer(pre, per_head=per_head, scales=sc)
-    ws = kv.alloc_workspace(g.desc, 1, L)
-    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev())
-    kv.decode_step(g.desc, bf16_dev(case.k_new[-1:]), bf16_dev(case.v_new[-1:]), g.k_cache,
-                   g.v_cache, out, g.q, g.block_tables, i32_dev(case.lens), L, g.k_scale,
-                   g.v_scale, ws)
-    torch.cuda.synchronize()
+    out = run_decode_step(g, case, case.k_new[-1:], case.v_new[-1:])
     assert np.array_equal(host(g.k_cache), o.k_cache)
     assert np.array_equal(host(g.v_cache), o.v_cache)
     ref = o.attend()
@@ -558,13 +553,14 @@ def newest_rows(case):
 
 
 def run_decode_step(g, case, knew, vnew, out_dtype=torch.float32):
-    out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=out_dtype,
-                      device=dev())
-    ws = kv.alloc_workspace(g.desc, case.num_seqs, case.max_context_len)
+    reg = list(g.guards)
+    out = guarded((case.num_seqs, case.num_q_heads, case.head_dim), out_dtype, None, reg)
+    n = kv.decode_workspace_bytes(g.desc, case.num_seqs, case.max_context_len)
+    ws = guarded((n,), torch.uint8, None, reg) if n else None
     kv.decode_step(g.desc, bf16_dev(knew), bf16_dev(vnew), g.k_cache, g.v_cache, out, g.q,
                    i32_dev(case.block_tables), i32_dev(case.lens), case.max_context_len,
                    g.k_scale, g.v_scale, ws)
-    torch.cuda.synchronize()
+    check_guards(reg, "decode step")
     return out
 
 

@@ -20,7 +20,7 @@ import torch
 import fp8_kv_cache_write_amd as kv
 import oracle
 import synth
-from _gpu import GpuLayer, OracleLayer, dev, host, i32_dev
+from _gpu import GpuLayer, OracleLayer, check_guards, dev, guarded, host, i32_dev
 from test_gpu_parity import GATE_MAX_ABS, GATE_MEAN_ABS, say
 
 pytestmark = pytest.mark.gpu
@@ -39,17 +39,19 @@ def _gpu():
 def gpu_prefill(g, case, out_dtype=torch.float32, split=False, context_lens=None):
     # split: pass the workspace that lets the plan split the keys; the output
     # starts as NaN, so a row the kernels never write shows
-    out = torch.full((case.num_query_rows, case.num_q_heads, case.head_dim), float("nan"),
-                     dtype=out_dtype, device=dev())
+    reg = list(g.guards)
+    out = guarded((case.num_query_rows, case.num_q_heads, case.head_dim), out_dtype,
+                  float("nan"), reg)
     ws = None
     if split:
-        ws = kv.alloc_prefill_workspace(g.desc, case.num_seqs, case.max_query_len,
-                                        case.block_tables.shape[1])
+        n = kv.prefill_workspace_bytes(g.desc, case.num_seqs, case.max_query_len,
+                                       case.block_tables.shape[1])
+        ws = guarded((n,), torch.uint8, None, reg) if n else None
     lens = g.context_lens if context_lens is None else i32_dev(context_lens)
     kv.paged_prefill_attention(g.desc, out, g.q, g.k_cache, g.v_cache, g.block_tables,
                                i32_dev(case.query_start), lens, case.max_query_len,
                                g.k_scale, g.v_scale, workspace=ws)
-    torch.cuda.synchronize()
+    check_guards(reg, "prefill attention")
     return out
 
 
