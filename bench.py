@@ -258,6 +258,33 @@ def same_size_read_us(torch, kv, nbytes, min_total=2 * GIB, reps=10):
     return best
 
 
+def same_size_read_kernel_us(torch, kv, nbytes, min_total=2 * GIB, reps=4):
+    """The plain streaming read of nbytes per launch timed like the split
+    kernel: kernel-timestamped HIP event pairs (kvq_profile_begin/end) around
+    eager launches over distinct buffers; the mean kernel time, best of 1024
+    and 4096 work-groups."""
+    nbytes = nbytes // 16 * 16
+    n = max(8, min(256, math.ceil(min_total / nbytes)))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(n)]
+    best = None
+    for blocks in (1024, 4096):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        for b in bufs[:2]:
+            kv.stream_read(b, sink)
+        torch.cuda.synchronize()
+        kv.profile_begin(reps * n)
+        for _ in range(reps):
+            for b in bufs:
+                kv.stream_read(b, sink)
+        ms, cnt = kv.profile_end()
+        us = ms * 1e3 / cnt if cnt else None
+        if us is not None:
+            best = us if best is None else min(best, us)
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
 def time_steps_graph(torch, stack, steps, warmup, per_step=False):
     """The step captured once as a HIP graph, replayed: mean ms per step
     (and, with per_step, the sorted ms of every replay of a second pass).
@@ -475,12 +502,17 @@ def sweep(torch, kv, w, contexts, steps, warmup):
             torch.cuda.empty_cache()
             # (from 4096 positions: smaller reads would run from the Infinity Cache)
             read_us = same_size_read_us(torch, kv, split_bytes) if ctx >= 4096 else None
+            read_k = same_size_read_kernel_us(torch, kv, split_bytes) if ctx >= 4096 else None
+            split_us = split_ms * 1e3 if split_ms else None
             rows.append(dict(cache=dt, context=ctx, layers=NL, us_per_layer=round(us_layer, 3),
                              kv_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
-                             split_us=round(split_ms * 1e3, 3) if split_ms else None,
+                             split_us=round(split_us, 3) if split_us else None,
                              same_size_read_us=round(read_us, 3) if read_us else None,
                              step_over_same_size_read=round(us_layer / read_us, 3)
-                             if read_us else None))
+                             if read_us else None,
+                             same_size_read_kernel_us=round(read_k, 3) if read_k else None,
+                             split_over_same_size_read_kernel=round(split_us / read_k, 3)
+                             if read_k and split_us else None))
             log(f"sweep {dt:8s} ctx={ctx:6d} layers={NL:3d} {us_layer:8.2f} us/layer "
                 f"{gbs:7.1f} GB/s split={rows[-1]['split_us']} us read={read_us} us")
     fits = {}
@@ -707,14 +739,17 @@ def other_workloads(torch, kv, steps, warmup):
         del st
         torch.cuda.empty_cache()
         rd = same_size_read_us(torch, kv, sb)
+        rk = same_size_read_kernel_us(torch, kv, sb)
         pt["same_size_read_us"] = round(rd, 3)
-        pt["split_over_same_size_read"] = round(pt["split_us"] / rd, 4) if pt["split_us"] else None
         pt["step_over_same_size_read"] = round(pt["us_per_layer_step"] / rd, 4)
+        pt["same_size_read_kernel_us"] = round(rk, 3) if rk else None
+        pt["split_over_same_size_read_kernel"] = (round(pt["split_us"] / rk, 4)
+                                                  if pt["split_us"] and rk else None)
         pt["shape"] = dict(batch=len(lens), q_heads=w["Hq"], kv_heads=w["Hkv"], head_dim=w["D"],
                            contexts=f"{min(lens)}..{max(lens)}" if len(lens) > 1 else lens[0])
         log(f"workload {name}: {pt['us_per_layer_step']:.2f} us/layer step "
             f"({pt['step_frac_hbm'] * 100:.1f} % of peak), split {pt['split_us']} us, "
-            f"read {rd:.2f} us")
+            f"read {rd:.2f} us (graph) {rk} us (kernel events)")
         out[name] = pt
     # the gpt-oss window layers: window 128, bf16 cache (the skip path)
     w = W["gptoss"]
@@ -1010,10 +1045,16 @@ def main():
     # the same read, one launch per layer's split bytes, graph-replayed: the
     # time a kernel with no attention work needs for this layer's bytes
     rd_us = same_size_read_us(torch, kv, split_bytes)
+    rk_us = same_size_read_kernel_us(torch, kv, split_bytes)
     result["measured_ceilings"]["same_size_read_us"] = round(rd_us, 3)
-    result["measured_ceilings"]["split_kernel_over_same_size_read"] = (
-        round(split_ms * 1e3 / rd_us, 4) if split_ms else None)
     result["measured_ceilings"]["step_over_same_size_read"] = round(ms * 1e3 / NL / rd_us, 4)
+    result["measured_ceilings"]["same_size_read_kernel_us"] = round(rk_us, 3) if rk_us else None
+    result["measured_ceilings"]["split_kernel_over_same_size_read_kernel"] = (
+        round(split_ms * 1e3 / rk_us, 4) if split_ms and rk_us else None)
+    result["measured_ceilings"]["same_size_read_how"] = (
+        "kvq_stream_read of the split kernel's bytes per launch over distinct buffers: "
+        "same_size_read_us is the graph-replayed time per launch (compare with the step), "
+        "same_size_read_kernel_us the kernel-event time (timed as the split kernel is)")
 
     if not args.no_sweep and args.workload == "llama8b":
         contexts = [16, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]

@@ -547,8 +547,14 @@ int kvq_stream_read(const void* src, int64_t n_bytes, uint32_t* sink, int32_t nu
   if (n_bytes < 0 || n_bytes % 16 != 0 || num_blocks <= 0) return KVQ_ERR_INVALID_ARG;
   if (n_bytes == 0) return KVQ_OK;
   if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4)) return KVQ_ERR_INVALID_ARG;
-  return launch_stream_read(src, n_bytes, sink, num_blocks, static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_prof.on && g_prof.used < g_prof.max) {
+    e0 = g_prof.ev[2 * g_prof.used];
+    e1 = g_prof.ev[2 * g_prof.used + 1];
+    g_prof.used++;
+  }
+  return launch_stream_read(src, n_bytes, sink, num_blocks, static_cast<hipStream_t>(stream), e0,
+                            e1) == hipSuccess
              ? KVQ_OK
              : KVQ_ERR_HIP;
 }

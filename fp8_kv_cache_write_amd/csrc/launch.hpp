@@ -26,7 +26,8 @@ hipError_t launch_quantize(int fmt, const float* x, int64_t n, const float* scal
 // A plain streaming read of n_bytes (a multiple of 16) with one XOR checksum
 // word per work-group written to sink[0..num_blocks) (stream_read.hip).
 hipError_t launch_stream_read(const void* src, int64_t n_bytes, uint32_t* sink,
-                              int num_blocks, hipStream_t stream);
+                              int num_blocks, hipStream_t stream, hipEvent_t ev_before,
+                              hipEvent_t ev_after);
 
 // Everything the split-decode and reduce kernels read; passed by value.
 struct DecodeParams {

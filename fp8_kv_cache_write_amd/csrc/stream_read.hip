@@ -4,6 +4,8 @@
 // into an XOR checksum, one 32-bit word per work-group. There is no other
 // work, so its rate is what the chip's memory system gives a read-only
 // stream.
+#include <hip/hip_ext.h>
+
 #include "launch.hpp"
 
 namespace kvfp8 {
@@ -54,9 +56,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(
 }  // namespace
 
 hipError_t launch_stream_read(const void* src, int64_t n_bytes, uint32_t* sink,
-                              int num_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)num_blocks), dim3(kStreamThreads), 0,
-                     stream, static_cast<const u32x4*>(src), n_bytes / 16, sink);
+                              int num_blocks, hipStream_t stream, hipEvent_t ev_before,
+                              hipEvent_t ev_after) {
+  if (ev_before && ev_after) {
+    // the events take the kernel's own start and end timestamps, as for the
+    // split-decode kernel, so the two are timed alike
+    hipExtLaunchKernelGGL(stream_read_kernel, dim3((unsigned)num_blocks), dim3(kStreamThreads),
+                          0, stream, ev_before, ev_after, 0, static_cast<const u32x4*>(src),
+                          n_bytes / 16, sink);
+  } else {
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)num_blocks), dim3(kStreamThreads), 0,
+                       stream, static_cast<const u32x4*>(src), n_bytes / 16, sink);
+  }
   return hipGetLastError();
 }
 

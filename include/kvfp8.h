@@ -460,8 +460,8 @@ int kvq_set_tuning(int32_t knob, int32_t value);
 /*
  * Profiling aid (not thread-safe): between kvq_profile_begin and
  * kvq_profile_end the library records a HIP event pair around every launch of
- * the split-decode kernel (up to max_launches of them) on the stream of that
- * launch. kvq_profile_end synchronises those events and returns the summed
+ * the split-decode kernel and of kvq_stream_read's kernel (up to
+ * max_launches of them) on the stream of that launch. kvq_profile_end synchronises those events and returns the summed
  * kernel time in milliseconds and the number of launches recorded.
  */
 int kvq_profile_begin(int32_t max_launches);

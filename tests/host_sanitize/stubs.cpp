@@ -76,7 +76,8 @@ hipError_t launch_quantize(int fmt, const float*, int64_t n, const float*, uint8
   return hipSuccess;
 }
 
-hipError_t launch_stream_read(const void*, int64_t n_bytes, uint32_t*, int, hipStream_t) {
+hipError_t launch_stream_read(const void*, int64_t n_bytes, uint32_t*, int, hipStream_t,
+                              hipEvent_t, hipEvent_t) {
   g_log.reads++;
   g_log.last_tokens = n_bytes;
   return hipSuccess;
