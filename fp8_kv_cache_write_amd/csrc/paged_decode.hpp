@@ -201,8 +201,11 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
   // (the plan decides; it is an ordering only, every partition still runs).
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int rot = p.rotate ? (int)(blockIdx.y + gridDim.y * blockIdx.z) : 0;
-  const int part = (int)((blockIdx.x + rot) % gridDim.x);
+  // (the grid is (num_parts, num_kv_heads, num_seqs): the sizes come from
+  // the parameters, which arrive with the first kernel-argument load, rather
+  // than from the dispatch's hidden arguments, a second dependent load)
+  const int rot = p.rotate ? (int)(blockIdx.y + (unsigned)p.num_kv_heads * blockIdx.z) : 0;
+  const int part = (int)((blockIdx.x + (unsigned)rot) % (unsigned)p.num_parts);
   const int G = p.group;
   const int qd = lane >> 4;             // row quad of the MFMA layout
   const int c = lane & 15;              // MFMA column
@@ -1094,7 +1097,6 @@ __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const Decode
   const int d0 = (int)(blockIdx.x % kSlices) * kWave + 4 * dq;
   const int hq = (int)(blockIdx.x / kSlices);
   const int b = blockIdx.y;
-  if (p.row_limit && b >= *p.row_limit) return;   // past the last row (prefill merge)
   const int h = hq / p.group;
   const int np = p.num_parts;
   const int64_t row = (int64_t)b * p.num_q_heads + hq;
@@ -1161,6 +1163,10 @@ __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const Decode
   // the four partition groups of each dim: lanes dq, dq + 16, dq + 32, dq + 48
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc[e] = wave_sum_col(acc[e]);
+  // rows past the last row of a prefill merge write nothing (their loads
+  // above stayed inside the workspace, which holds every grid row; the test
+  // comes last so that its dependent load does not delay theirs)
+  if (p.row_limit && b >= *p.row_limit) return;
   if (pg != 0) return;
   f32x4 r;
 #pragma unroll
