@@ -240,11 +240,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     }
   };
 
-  float m_run[NCG], l_run[NCG];
+  // m_run: running maximum (log2 domain); neg_m: -m_run, or 0 while m_run is
+  // -inf (every logit so far masked), the exponent's offset; it changes only
+  // when m_run does
+  float m_run[NCG], neg_m[NCG], l_run[NCG];
   f32x4 acc[NCG][NBLK];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     m_run[cg] = -INFINITY;
+    neg_m[cg] = -0.0f;
     l_run[cg] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) acc[cg][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -283,50 +287,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     }
     if (t + 1 < ntiles) stage(t + 1, pid_next0, pid_next1);
 
-    // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
-    f32x4 sacc[NCG][2];
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg)
-#pragma unroll
-      for (int pg = 0; pg < 2; ++pg) sacc[cg][pg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < NK; ++s) {
-#pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
-        if constexpr (ATT8) {
-          // the K codes themselves are the operand (fp8 x fp8 MFMA)
-          const uint4 w = tk[pg][s / 2];
-          const long kop8 = (long)((s % 2 == 0) ? (((uint64_t)w.y << 32) | w.x)
-                                                : (((uint64_t)w.w << 32) | w.z));
-#pragma unroll
-          for (int cg = 0; cg < NCG; ++cg) {
-            if constexpr (FMT == kFmtE5M2)
-              sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(
-                  kop8, (long)qop8[cg][s], sacc[cg][pg], 0, 0, 0);
-            else
-              sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-                  kop8, (long)qop8[cg][s], sacc[cg][pg], 0, 0, 0);
-          }
-          continue;
-        }
-        bf16x8 kop;
-        if constexpr (FP8) {
-          const uint4 w = tk[pg][s / 2];
-          kop = (s % 2 == 0) ? fp8x8_to_bf16x8<FMT>(w.x, w.y) : fp8x8_to_bf16x8<FMT>(w.z, w.w);
-        } else {
-          kop = bits_to_bf16x8(tk[pg][s]);
-        }
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[cg][s], sacc[cg][pg],
-                                                                 0, 0, 0);
-      }
-    }
-
-    // ---- masks (boundary tiles only) ----------------------------------------
+    // ---- masks of the V codes (boundary tiles only) -------------------------
     const int k0 = (first_page + 2 * t) * kPage;            // first key of the tile
-    // causal / window / missing pages: those logits become -inf
-    const bool need_mask = k0 < free_lo || k0 + 2 * kPage - 1 > free_hi || pid0 < 0 || pid1 < 0;
     // masked keys get p = 0, but unwritten rows (positions >= L) and rows of
     // missing pages may hold NaN codes, and 0 * NaN is NaN: zero those rows'
     // V codes in the tile registers (rows 4qd..4qd+3 of each page per lane)
@@ -360,31 +322,93 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       }
     }
 
-    // static scales: raw logits, c_log2 >= 0 applied inside the exponent;
-    // dynamic: each row's logits times c_log2 s_k (row), exponent scale 1
-    float csk[2][4];
-    if constexpr (DYN) {
+    // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
+    // One straight-line block: the q k^T MFMAs with the K expansion, and the
+    // V expansion for P*V among them (independent VALU work that issues while
+    // the matrix core runs). The MFMA phases run at raised wave priority: the
+    // other wave on the SIMD (from the other work-group on the CU) then fills
+    // the issue slots between this wave's MFMAs with its own VALU work (the
+    // softmax), rather than both waves sitting in the same phase (measured:
+    // 2-3 % faster at long prompts).
+    f32x4 sacc[NCG][2];
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg)
+    for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) csk[pg][e] = c_log2 * sk[pg][e];
+      for (int pg = 0; pg < 2; ++pg) sacc[cg][pg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        if constexpr (ATT8) {
+          // the K codes themselves are the operand (fp8 x fp8 MFMA)
+          const uint4 w = tk[pg][s / 2];
+          const long kop8 = (long)((s % 2 == 0) ? (((uint64_t)w.y << 32) | w.x)
+                                                : (((uint64_t)w.w << 32) | w.z));
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            if constexpr (FMT == kFmtE5M2)
+              sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(
+                  kop8, (long)qop8[cg][s], sacc[cg][pg], 0, 0, 0);
+            else
+              sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                  kop8, (long)qop8[cg][s], sacc[cg][pg], 0, 0, 0);
+          }
+          continue;
+        }
+        bf16x8 kop;
+        if constexpr (FP8) {
+          const uint4 w = tk[pg][s / 2];
+          kop = (s % 2 == 0) ? fp8x8_to_bf16x8<FMT>(w.x, w.y) : fp8x8_to_bf16x8<FMT>(w.z, w.w);
+        } else {
+          kop = bits_to_bf16x8(tk[pg][s]);
+        }
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          sacc[cg][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[cg][s], sacc[cg][pg],
+                                                                 0, 0, 0);
+      }
     }
-    bf16x8 pop[NCG];
-    uint64_t pop8[ATT8 ? NCG : 1];
-    float fb[ATT8 ? NCG : 1];          // all-FP8: weight 2^(tile max - running max)
+    // P*V A operands: V^T block blk (16 dims x 32 keys); fp8 codes expanded
+    // exactly to bf16, a register shuffle for a bf16 cache
+    uint4 vop[ATT8 ? 1 : NBLK];
+    if constexpr (!ATT8) {
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      // static scales: raw logits, the scale applied inside the exponent;
-      // all-FP8: logits scaled here (s_q differs per column)
-      const float cexp = (DYN || ATT8) ? 1.0f : c_log2;
-      float x[2][4];
+      for (int blk = 0; blk < NBLK; ++blk) {
+        if constexpr (FP8) {
+          const int i = blk / 4, ep = blk % 4;
+          const uint4 wa = tv[0][i], wb = tv[1][i];
+          const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
+          const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
+          vop[blk] =
+              __builtin_bit_cast(uint4, cat(fp8x4_to_bf16x4<FMT>(da), fp8x4_to_bf16x4<FMT>(db)));
+        } else {
+          const int i = blk / 2, ep = blk % 2;
+          const uint4 wa = tv[0][i], wb = tv[1][i];
+          vop[blk] = ep == 0 ? make_uint4(wa.x, wa.y, wb.x, wb.y) : make_uint4(wa.z, wa.w, wb.z, wb.w);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+    // static scales: raw logits, c_log2 >= 0 applied inside the exponent;
+    // dynamic: each row's logits times c_log2 s_k (row), exponent scale 1;
+    // all-FP8: logits scaled here (s_q differs per column)
+    const float cexp = (DYN || ATT8) ? 1.0f : c_log2;
+    if constexpr (DYN || ATT8) {
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg)
+      for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          x[pg][e] = DYN ? sacc[cg][pg][e] * csk[pg][e]
-                         : (ATT8 ? sacc[cg][pg][e] * cq[cg] : sacc[cg][pg][e]);
-      if (need_mask) {
+        for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[cg][pg][e] *= DYN ? c_log2 * sk[pg][e] : cq[cg];
+    }
+    // causal / window / missing pages: those logits become -inf
+    const bool need_mask = k0 < free_lo || k0 + 2 * kPage - 1 > free_hi || pid0 < 0 || pid1 < 0;
+    if (need_mask) {
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
         const int lo_c = p.window > 0 ? qpos[cg] + 1 - p.window : 0;
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
@@ -392,20 +416,35 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int kp = k0 + pg * kPage + 4 * qd + e;
-            if (!(page_ok && kp <= qpos[cg] && kp >= lo_c)) x[pg][e] = -INFINITY;
+            if (!(page_ok && kp <= qpos[cg] && kp >= lo_c)) sacc[cg][pg][e] = -INFINITY;
           }
         }
       }
-      // online softmax (log2 domain), lazy rescale
-      float tmax = x[0][0];
+    }
+
+    // ---- online softmax (log2 domain), lazy rescale --------------------------
+    // Every column group's tile maximum first, then one (rarely taken) branch
+    // for the rescales, so the exponentials and the P*V MFMAs below form one
+    // block in which the scheduler overlaps a group's exponentials with the
+    // previous group's MFMAs.
+    float tmax[NCG];
+    bool grow[NCG];
+    bool any_grow = false;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float mx = sacc[cg][0][0];
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tmax = vmax(tmax, x[pg][e]);
-      tmax = col_max(tmax) * cexp;
-      const bool grow = tmax > m_run[cg] + kLazyLog2;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
-        const float m_new = grow ? tmax : m_run[cg];
+        for (int e = 0; e < 4; ++e) mx = vmax(mx, sacc[cg][pg][e]);
+      tmax[cg] = col_max(mx) * cexp;
+      grow[cg] = tmax[cg] > m_run[cg] + kLazyLog2;
+      any_grow |= grow[cg];
+    }
+    if (__builtin_amdgcn_ballot_w64(any_grow) != 0ull) {
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        const float m_new = grow[cg] ? tmax[cg] : m_run[cg];
         const float alpha = m_new == m_run[cg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[cg] - m_new);
 #pragma unroll
         for (int i = 0; i < NBLK; ++i)
@@ -413,14 +452,20 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
           for (int e = 0; e < 4; ++e) acc[cg][i][e] *= alpha;
         l_run[cg] *= alpha;
         m_run[cg] = m_new;
+        neg_m[cg] = m_new == -INFINITY ? -0.0f : -m_new;
       }
-      const float m_use = m_run[cg] == -INFINITY ? 0.0f : m_run[cg];
+    }
+
+    // ---- P and P*V, column group by column group (raised priority) -----------
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
       if constexpr (ATT8) {
         // P of this 32-position block as e4m3 relative to the block's own max
         // (tmax); the normaliser takes the FP32 values
-        const bool live = tmax != -INFINITY;
-        const float mb = live ? tmax : 0.0f;
-        fb[cg] = live ? __builtin_amdgcn_exp2f(tmax - m_use) : 0.0f;
+        const bool live = tmax[cg] != -INFINITY;
+        const float mb = live ? tmax[cg] : 0.0f;
+        const float fb = live ? __builtin_amdgcn_exp2f(tmax[cg] + neg_m[cg]) : 0.0f;
         float ps = -0.0f;
         uint32_t pw[2];
 #pragma unroll
@@ -428,24 +473,44 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
           float pe[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pe[e] = __builtin_amdgcn_exp2f(x[pg][e] - mb);
+            pe[e] = __builtin_amdgcn_exp2f(sacc[cg][pg][e] - mb);
             ps += pe[e];
           }
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(pe[0], pe[1], 0, false);
           w = __builtin_amdgcn_cvt_pk_fp8_f32(pe[2], pe[3], w, true);
           pw[pg] = (uint32_t)w;
         }
-        pop8[cg] = ((uint64_t)pw[1] << 32) | pw[0];
-        l_run[cg] += fb[cg] * ps;
+        const uint64_t pop8 = ((uint64_t)pw[1] << 32) | pw[0];
+        l_run[cg] += fb * ps;
+        // fp8 x fp8 products of the block, each added into the FP32 sum with
+        // its weight fb (level 1: the MFMA over 32 positions; level 2: FP32)
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+          const int i = blk / 4, ep = blk % 4;
+          const uint4 wa = tv[0][i], wb = tv[1][i];
+          const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
+          const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
+          const long vop8 = (long)(((uint64_t)db << 32) | da);
+          f32x4 tpv;
+          if constexpr (FMT == kFmtE5M2)
+            tpv = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(vop8, (long)pop8,
+                                                             f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          else
+            tpv = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop8, (long)pop8,
+                                                             f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[cg][blk][e] += fb * tpv[e];
+        }
         continue;
       }
       float ps = -0.0f;                    // -0 + p is p: no add for the first term
+      bf16x8 pop;
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
         float pe[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[pg][e], cexp, -m_use));
+          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[cg][pg][e], cexp, neg_m[cg]));
           ps += pe[e];
         }
         // dynamic scales: the row's V scale joins P (the normaliser took p)
@@ -456,58 +521,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         // P^T operand: k index 8qd + 4pg + e is key row 4qd+e of page pg
         const bf16x4 p4 = __builtin_convertvector((f32x4){pe[0], pe[1], pe[2], pe[3]}, bf16x4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pop[cg][4 * pg + e] = p4[e];
+        for (int e = 0; e < 4; ++e) pop[4 * pg + e] = p4[e];
       }
       l_run[cg] += ps;
-    }
-
-    // ---- P*V: one k=32 MFMA per 16-dim block and column group --------------
-    if constexpr (ATT8) {
-      // fp8 x fp8 products of the block, each added into the FP32 sum with
-      // its weight fb (level 1: the MFMA over 32 positions; level 2: FP32)
+      // one k=32 MFMA per 16-dim block
 #pragma unroll
-      for (int blk = 0; blk < NBLK; ++blk) {
-        const int i = blk / 4, ep = blk % 4;
-        const uint4 wa = tv[0][i], wb = tv[1][i];
-        const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
-        const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
-        const long vop = (long)(((uint64_t)db << 32) | da);
-        f32x4 tpv[NCG];
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-          if constexpr (FMT == kFmtE5M2)
-            tpv[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(
-                vop, (long)pop8[cg], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-          else
-            tpv[cg] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-                vop, (long)pop8[cg], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        }
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[cg][blk][e] += fb[cg] * tpv[cg][e];
-      }
-      continue;
-    }
-#pragma unroll
-    for (int blk = 0; blk < NBLK; ++blk) {
-      uint4 vb;
-      if constexpr (FP8) {
-        const int i = blk / 4, ep = blk % 4;
-        const uint4 wa = tv[0][i], wb = tv[1][i];
-        const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
-        const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
-        vb = __builtin_bit_cast(uint4, cat(fp8x4_to_bf16x4<FMT>(da), fp8x4_to_bf16x4<FMT>(db)));
-      } else {
-        const int i = blk / 2, ep = blk % 2;
-        const uint4 wa = tv[0][i], wb = tv[1][i];
-        vb = ep == 0 ? make_uint4(wa.x, wa.y, wb.x, wb.y) : make_uint4(wa.z, wa.w, wb.z, wb.w);
-      }
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg)
-        acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vb), pop[cg],
+      for (int blk = 0; blk < NBLK; ++blk)
+        acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vop[blk]), pop,
                                                                acc[cg][blk], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- key split: this partition's unnormalised partial (m, l, o) -------------
