@@ -201,24 +201,54 @@ SCALE_TEXT = {"per_kv_head": "per-KV-head scales", "per_tensor": "per-tensor sca
               "per_token_head": "dynamic per-token, per-KV-head scales"}
 
 
+_SLEEP_HZ = []
+
+
+def gpu_head_start(torch, launches):
+    """Occupy the GPU (torch's spin kernel) for about 0.06 ms per launch that
+    follows, at least 20 ms: the host then enqueues those launches while the
+    GPU waits, and kernel-event timestamps bracket GPU work only. A launch
+    with an event pair costs the host more time (about 40 us per layer step)
+    than the split kernel takes below about 64k positions, so without a head
+    start the pairs would time the host's launch rate."""
+    if not _SLEEP_HZ:
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(10_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_HZ.append(1e7 / (e0.elapsed_time(e1) * 1e-3))
+    ms = min(400.0, max(20.0, 0.06 * launches))
+    torch.cuda._sleep(int(ms * 1e-3 * _SLEEP_HZ[0]))
+
+
 def time_steps(torch, kv, stack, steps, warmup, profile=True):
-    """Eager steps: mean ms per step, and (with profile) the split kernel's
-    mean duration from the library's kernel-timestamped HIP events."""
+    """Eager steps: mean ms per step (no profiling events: the host's launch
+    rate included, as a caller that does not capture a graph sees it) and,
+    with profile, the split kernel's mean duration from the library's
+    kernel-timestamped HIP events over a second pass of the same steps that
+    starts behind a GPU head start (gpu_head_start)."""
     for _ in range(warmup):
         stack.step()
     torch.cuda.synchronize()
-    if profile:
-        kv.profile_begin(steps * stack.NL)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
         stack.step()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    split_ms, n = kv.profile_end() if profile else (0.0, 0)
+    if not profile:
+        return ms, None, 0
+    kv.profile_begin(steps * stack.NL)
+    gpu_head_start(torch, steps * stack.NL)
+    for _ in range(steps):
+        stack.step()
+    split_ms, n = kv.profile_end()
     return ms, (split_ms / n if n else None), n
 
 
@@ -261,8 +291,8 @@ def same_size_read_us(torch, kv, nbytes, min_total=2 * GIB, reps=10):
 def same_size_read_kernel_us(torch, kv, nbytes, min_total=2 * GIB, reps=4):
     """The plain streaming read of nbytes per launch timed like the split
     kernel: kernel-timestamped HIP event pairs (kvq_profile_begin/end) around
-    eager launches over distinct buffers; the mean kernel time, best of 1024
-    and 4096 work-groups."""
+    eager launches over distinct buffers, behind a GPU head start; the mean
+    kernel time, best of 1024 and 4096 work-groups."""
     nbytes = nbytes // 16 * 16
     n = max(8, min(256, math.ceil(min_total / nbytes)))
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(n)]
@@ -273,6 +303,7 @@ def same_size_read_kernel_us(torch, kv, nbytes, min_total=2 * GIB, reps=4):
             kv.stream_read(b, sink)
         torch.cuda.synchronize()
         kv.profile_begin(reps * n)
+        gpu_head_start(torch, reps * n)
         for _ in range(reps):
             for b in bufs:
                 kv.stream_read(b, sink)
@@ -885,6 +916,12 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    ap.add_argument("--trace-point", action="store_true",
+                    help="for a kernel trace: 20 graph-replayed decode steps of --workload at "
+                         "--context (all layers of the workload's cache type), then plain "
+                         "streaming reads of the split kernel's bytes per launch (1024 and "
+                         "4096 work-groups, no events), so the profiler times both kernels "
+                         "the same way")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -915,6 +952,30 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.trace_point:
+        ctx = args.context or w["ctx"]
+        if not ctx:
+            print("--trace-point needs --context for this workload", file=sys.stderr)
+            sys.exit(2)
+        NL = args.layers or layers_for(ctx * w["Hkv"] * w["D"] * 2, hi=64)
+        stack = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, args.cache,
+                           seed=ctx, attn=args.attn, scales=args.scales)
+        ms = time_steps_graph(torch, stack, 20, 3)
+        nb = stack.split_bytes(stack.descs[0]) // 16 * 16
+        del stack
+        torch.cuda.empty_cache()
+        n = max(8, min(256, math.ceil(2 * GIB / nb)))
+        bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(n)]
+        for blocks in (1024, 4096):
+            sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+            for _ in range(4):
+                for b in bufs:
+                    kv.stream_read(b, sink)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(workload=args.workload, context=ctx, layers=NL,
+                              us_per_layer_step_graph=round(ms * 1e3 / NL, 3),
+                              read_bytes_per_launch=nb, read_buffers=n)))
+        return
     if args.prefill_only:
         res = prefill_bench(torch, kv, WORKLOADS["llama8b"], PREFILL_LENGTHS, 5, 2,
                             scales=args.scales, attn=args.attn)
@@ -1027,7 +1088,8 @@ def main():
             "launch_us": round(split_ms * 1e3, 3) if split_ms else None,
             "launches_timed": nsplit,
             "timed_with": "kernel-timestamped HIP event pairs around every split-kernel launch "
-                          "of the eager steps (kvq_profile_begin/end)",
+                          "of a pass of eager steps enqueued behind a GPU head start "
+                          "(kvq_profile_begin/end)",
             "algorithmic_bytes_per_launch": split_bytes,
         },
     }
