@@ -325,17 +325,18 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     // ---- logits S^T[key row 4qd+e of page pg][column c], per column group ----
     // One straight-line block: the q k^T MFMAs with the K expansion, and the
     // V expansion for P*V among them (independent VALU work that issues while
-    // the matrix core runs). The MFMA phases run at raised wave priority: the
-    // other wave on the SIMD (from the other work-group on the CU) then fills
-    // the issue slots between this wave's MFMAs with its own VALU work (the
-    // softmax), rather than both waves sitting in the same phase (measured:
-    // 2-3 % faster at long prompts).
+    // the matrix core runs). In the bf16-arithmetic modes the MFMA phases run
+    // at raised wave priority: the other wave on the SIMD (from the other
+    // work-group on the CU) then fills the issue slots between this wave's
+    // MFMAs with its own VALU work (the softmax), rather than both waves
+    // sitting in the same phase (measured: 3-4 % faster at long prompts; the
+    // all-FP8 mode, with no K/V expansion, measured 2-3 % slower with it).
     f32x4 sacc[NCG][2];
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) sacc[cg][pg] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!ATT8) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
 #pragma unroll
@@ -457,7 +458,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     }
 
     // ---- P and P*V, column group by column group (raised priority) -----------
-    __builtin_amdgcn_s_setprio(1);
+    uint64_t pop8[ATT8 ? NCG : 1];
+    float fb[ATT8 ? NCG : 1];          // all-FP8: weight 2^(tile max - running max)
+    if constexpr (!ATT8) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       if constexpr (ATT8) {
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         // (tmax); the normaliser takes the FP32 values
         const bool live = tmax[cg] != -INFINITY;
         const float mb = live ? tmax[cg] : 0.0f;
-        const float fb = live ? __builtin_amdgcn_exp2f(tmax[cg] + neg_m[cg]) : 0.0f;
+        const float fbw = live ? __builtin_amdgcn_exp2f(tmax[cg] + neg_m[cg]) : 0.0f;
         float ps = -0.0f;
         uint32_t pw[2];
 #pragma unroll
@@ -480,28 +483,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
           w = __builtin_amdgcn_cvt_pk_fp8_f32(pe[2], pe[3], w, true);
           pw[pg] = (uint32_t)w;
         }
-        const uint64_t pop8 = ((uint64_t)pw[1] << 32) | pw[0];
-        l_run[cg] += fb * ps;
-        // fp8 x fp8 products of the block, each added into the FP32 sum with
-        // its weight fb (level 1: the MFMA over 32 positions; level 2: FP32)
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) {
-          const int i = blk / 4, ep = blk % 4;
-          const uint4 wa = tv[0][i], wb = tv[1][i];
-          const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
-          const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
-          const long vop8 = (long)(((uint64_t)db << 32) | da);
-          f32x4 tpv;
-          if constexpr (FMT == kFmtE5M2)
-            tpv = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(vop8, (long)pop8,
-                                                             f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-          else
-            tpv = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop8, (long)pop8,
-                                                             f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[cg][blk][e] += fb * tpv[e];
-        }
-        continue;
+        pop8[cg] = ((uint64_t)pw[1] << 32) | pw[0];
+        fb[cg] = fbw;
+        l_run[cg] += fbw * ps;
+        continue;                          // P*V below, every column group at once
       }
       float ps = -0.0f;                    // -0 + p is p: no add for the first term
       bf16x8 pop;
@@ -529,6 +514,34 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       for (int blk = 0; blk < NBLK; ++blk)
         acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vop[blk]), pop,
                                                                acc[cg][blk], 0, 0, 0);
+    }
+    if constexpr (ATT8) {
+      // fp8 x fp8 products of the block, each added into the FP32 sum with
+      // its weight fb (level 1: the MFMA over 32 positions; level 2: FP32);
+      // every column group's MFMA of a block issues before the adds, so each
+      // add finds its product ready
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const int i = blk / 4, ep = blk % 4;
+        const uint4 wa = tv[0][i], wb = tv[1][i];
+        const uint32_t da = ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w;
+        const uint32_t db = ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w;
+        const long vop8 = (long)(((uint64_t)db << 32) | da);
+        f32x4 tpv[NCG];
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          if constexpr (FMT == kFmtE5M2)
+            tpv[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(
+                vop8, (long)pop8[cg], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          else
+            tpv[cg] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                vop8, (long)pop8[cg], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[cg][blk][e] += fb[cg] * tpv[cg][e];
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   }
