@@ -1049,17 +1049,26 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_split_kernel(
 // over every planned partition: the split kernel leaves an empty partial
 // (m = -inf, l = 0) in the slots of partitions a sequence does not reach, so
 // the merge needs neither the context length nor a second round trip. Each
-// wave owns 64 dims of one (sequence, query head) and needs no barrier. The
+// wave owns SW dims of one (sequence, query head) and needs no barrier. The
 // partitions are taken NPC at a time (one chunk for up to 128 partitions):
 // lane j reads m_j and l_j (two per lane past 64), and the partial outputs
-// are read as 16-byte pieces: lane (pg, dq) = (lane / 16, lane % 16) holds
-// dims 4 dq .. 4 dq + 3 of partitions pg, pg + 4, ..., so a chunk is NPC / 4
-// loads per lane, all issued before the first wait. The wave max and sum run
-// on DPP row rotations and the gfx950 row swaps (no LDS round trip); the
-// weights w_j reach the lanes through LDS. A partition of weight 0 adds
-// nothing (its o may never have been written), and a later chunk with a
-// larger max rescales what the earlier ones summed. The four partition
-// groups of a dim are summed at the end with the row swaps.
+// are read as 16-byte pieces: lane (pg, dq) = (lane / (SW/4), lane % (SW/4))
+// holds dims 4 dq .. 4 dq + 3 of partitions pg, pg + PG, pg + 2 PG, ...
+// (PG = 256 / SW partition groups), so a chunk is NPC / PG loads per lane,
+// all issued before the first wait. The slice width shrinks as the
+// partitions grow (64 dims up to 32 partitions, 32 for 64, 16 for 128), so
+// a lane never holds more than 8 pieces and more work-groups share a row.
+// The wave max and sum run on DPP row rotations and the gfx950 row swaps (no
+// LDS round trip); the weights w_j reach the lanes through LDS. A partition
+// of weight 0 adds nothing (its o may never have been written), and a later
+// chunk with a larger max rescales what the earlier ones summed. The
+// partition groups of a dim are summed at the end, inside rows with DPP
+// rotations and across rows with the row swaps.
+template <int NPC>
+constexpr int reduce_slice_dims() {
+  return NPC <= 32 ? 64 : (NPC <= 64 ? 32 : 16);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -1083,18 +1092,22 @@ __device__ __forceinline__ float wave_all(float x) {
 
 template <int D, int NPC>
 __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const DecodeParams p) {
-  static_assert(NPC % 4 == 0 && (NPC <= kWave || NPC % kWave == 0) && NPC <= kReduceChunk,
+  constexpr int SW = reduce_slice_dims<NPC>();        // dims per work-group
+  constexpr int DQ = SW / 4;                           // lanes per partition group
+  constexpr int PG = kWave / DQ;                       // partition groups
+  static_assert(NPC % PG == 0 && (NPC <= kWave || NPC % kWave == 0) && NPC <= kReduceChunk &&
+                    D % SW == 0,
                 "a chunk is at most one wave of partitions, or whole waves of them");
-  // One wave per work-group: work-group x merges dims 64*(x mod D/64) .. +63
-  // of query head x / (D/64), so the partials of a row are read by D/64
-  // compute units at once rather than one.
-  constexpr int kSlices = D / kWave;
+  // One wave per work-group: work-group x merges dims SW*(x mod D/SW) ..
+  // +SW-1 of query head x / (D/SW), so the partials of a row are read by
+  // D/SW compute units at once rather than one.
+  constexpr int kSlices = D / SW;
   constexpr int MPL = NPC > kWave ? NPC / kWave : 1;   // partitions per lane (m, l)
-  constexpr int OPL = NPC / 4;                         // 16-byte partial loads per lane
+  constexpr int OPL = NPC / PG;                        // 16-byte partial loads per lane
   __shared__ __align__(16) float sw[NPC];
   const int lane = threadIdx.x;
-  const int pg = lane >> 4, dq = lane & 15;
-  const int d0 = (int)(blockIdx.x % kSlices) * kWave + 4 * dq;
+  const int pg = lane / DQ, dq = lane % DQ;
+  const int d0 = (int)(blockIdx.x % kSlices) * SW + 4 * dq;
   const int hq = (int)(blockIdx.x / kSlices);
   const int b = blockIdx.y;
   const int h = hq / p.group;
@@ -1122,7 +1135,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const Decode
     f32x4 ov[OPL];
 #pragma unroll
     for (int u = 0; u < OPL; ++u)
-      ov[u] = *reinterpret_cast<const f32x4*>(orow + (int64_t)(base + 4 * u + pg) * D);
+      ov[u] = *reinterpret_cast<const f32x4*>(orow + (int64_t)(base + PG * u + pg) * D);
     float mj[MPL], lj[MPL], mloc = -INFINITY;
     bool nan_here = false;
 #pragma unroll
@@ -1155,14 +1168,19 @@ __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const Decode
     L += wave_all<false>(wl);
 #pragma unroll
     for (int u = 0; u < OPL; ++u) {
-      const float w = sw[4 * u + pg];
+      const float w = sw[PG * u + pg];
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, w != 0.0f ? ov[u][e] : 0.0f, acc[e]);
     }
   }
-  // the four partition groups of each dim: lanes dq, dq + 16, dq + 32, dq + 48
+  // the partition groups of each dim: lanes dq, dq + DQ, dq + 2 DQ, ...
+  // (rotations by 8 and 4 inside each row of 16 lanes, then the row swaps)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = wave_sum_col(acc[e]);
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (DQ <= 8) acc[e] += dpp_mov<0x128>(acc[e]);   // row_ror:8
+    if constexpr (DQ <= 4) acc[e] += dpp_mov<0x124>(acc[e]);   // row_ror:4
+    acc[e] = wave_sum_col(acc[e]);
+  }
   // rows past the last row of a prefill merge write nothing (their loads
   // above stayed inside the workspace, which holds every grid row; the test
   // comes last so that its dependent load does not delay theirs)
@@ -1184,18 +1202,20 @@ __global__ __launch_bounds__(kWave) void paged_decode_reduce_kernel(const Decode
   }
 }
 
+template <int D, int NPC>
+static void launch_reduce_chunk(const DecodeParams& pr, int num_seqs, hipStream_t stream) {
+  const dim3 grid((unsigned)(pr.num_q_heads * (D / reduce_slice_dims<NPC>())),
+                  (unsigned)num_seqs);
+  hipLaunchKernelGGL((paged_decode_reduce_kernel<D, NPC>), grid, dim3(kWave), 0, stream, pr);
+}
+
 template <int D>
 static void launch_reduce(const DecodeParams& pr, int num_seqs, hipStream_t stream) {
-  const dim3 grid((unsigned)(pr.num_q_heads * (D / kWave)), (unsigned)num_seqs);
   static_assert(kReduceChunk == 128, "the largest chunk below is the workspace's slack");
-  if (pr.num_parts <= 16)
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 16>), grid, dim3(kWave), 0, stream, pr);
-  else if (pr.num_parts <= 32)
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 32>), grid, dim3(kWave), 0, stream, pr);
-  else if (pr.num_parts <= 64)
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 64>), grid, dim3(kWave), 0, stream, pr);
-  else
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<D, 128>), grid, dim3(kWave), 0, stream, pr);
+  if (pr.num_parts <= 16) launch_reduce_chunk<D, 16>(pr, num_seqs, stream);
+  else if (pr.num_parts <= 32) launch_reduce_chunk<D, 32>(pr, num_seqs, stream);
+  else if (pr.num_parts <= 64) launch_reduce_chunk<D, 64>(pr, num_seqs, stream);
+  else launch_reduce_chunk<D, 128>(pr, num_seqs, stream);
 }
 
 // Arithmetic modes of the split kernel.
