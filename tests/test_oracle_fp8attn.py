@@ -14,6 +14,7 @@ reference for P are this library's reading of what the pages leave open.
 import math
 
 import numpy as np
+import pytest
 
 import oracle
 import synth
@@ -137,3 +138,128 @@ def test_close_to_plain_attention_on_random_data():
                                  0, 0.0, ks, vs)
     d = np.abs(a - b)
     assert d.max() < 0.05 and d.max() > 0
+
+
+# ------------------------------------ second formulation: numpy brute force --
+def _e4m3_encode(x32):
+    """Saturating round-to-nearest-even e4m3 codes of float32 values, written
+    from the format's value table (torch's float8_e4m3fn decode of the 256
+    codes, independent of the oracle's codec): the nearest representable
+    magnitude, a tie going to the even code (even mantissa), |x| >= 448 to
+    448, the sign bit from x."""
+    from test_oracle_attention import _decode_table
+    pos = _decode_table(FP8)[:0x7F]                       # codes 0x00..0x7E, 0 .. 448
+    x32 = np.asarray(x32, np.float32)
+    a = np.minimum(np.abs(x32.astype(np.float64)), 448.0)
+    i = np.clip(np.searchsorted(pos, a), 1, 0x7E)        # pos[i-1] <= a <= pos[i]
+    lo, hi = pos[i - 1], pos[i]
+    up = (hi - a < a - lo) | ((hi - a == a - lo) & (i % 2 == 0))
+    code = np.where(up, i, i - 1).astype(np.uint8)
+    return np.where(np.signbit(x32), code | 0x80, code).astype(np.uint8)
+
+
+def _fp8attn_brute(case, kc, vc, dtype, ks, vs, window, reference="block"):
+    """All-FP8 decode attention in vectorised numpy float64, on the same cache
+    codes: q per row as e4m3 codes of fp32(q / s_q), s_q = fp32(amax) / 448;
+    logits (q~ s_q) . (k~ s_k) / sqrt(D); P = e4m3(fp32(exp(z - M))). With
+    reference "block", M is the largest logit of the position's aligned
+    32-position block and the blocks merge with weights e^(M_j - M); with
+    "row", M is the row's largest logit (the plain reading). The normaliser
+    sums the unquantised exp(z - M) either way."""
+    from test_oracle_attention import _decode_table, _layout_offsets
+    B, Hq, D = case.q.shape
+    Hkv = case.num_kv_heads
+    G = Hq // Hkv
+    koff, voff = _layout_offsets(D, 1)
+    tab = _decode_table(dtype)
+    t8 = _decode_table(FP8)
+    kx = tab[kc[:, :, koff]] * np.asarray(ks, np.float64)[None, :, None, None]
+    vx = tab[vc[:, :, voff]] * np.asarray(vs, np.float64)[None, :, None, None]
+    q32 = synth.bits_to_f32(case.q)
+    sq = np.abs(q32).max(axis=2).astype(np.float32) / np.float32(448.0)         # [B][Hq]
+    qv = t8[_e4m3_encode(q32 / sq[:, :, None])] * sq[:, :, None].astype(np.float64)
+    out = np.zeros((B, Hq, D))
+    for b, L in enumerate(case.lens):
+        lo = max(0, L - window) if window else 0
+        t = np.arange(lo, L)
+        if t.size == 0:
+            continue
+        pages = case.block_tables[b, t // 16]
+        for h in range(Hkv):
+            kt = kx[pages, h, t % 16]
+            vt = vx[pages, h, t % 16]
+            z = qv[b, h * G:(h + 1) * G] @ kt.T / math.sqrt(D)                # [G][n]
+            if reference == "row":
+                e = np.exp(z - z.max(axis=1, keepdims=True))
+                p = t8[_e4m3_encode(e.astype(np.float32))]
+                out[b, h * G:(h + 1) * G] = (p @ vt) / e.sum(axis=1, keepdims=True)
+                continue
+            blk = t // 32 - t[0] // 32
+            nb = blk[-1] + 1
+            mb = np.full((G, nb), -np.inf)
+            for j in range(nb):
+                mb[:, j] = z[:, blk == j].max(axis=1)
+            e = np.exp(z - mb[:, blk])
+            p = t8[_e4m3_encode(e.astype(np.float32))]
+            w = np.exp(mb - mb.max(axis=1, keepdims=True))[:, blk]             # e^(M_j - M)
+            out[b, h * G:(h + 1) * G] = ((p * w) @ vt) / (e * w).sum(axis=1, keepdims=True)
+    return out
+
+
+def test_e4m3_encoder_of_the_brute_force():
+    # the table encoder against the pages' worked example and the format's
+    # rounding rules (ties to even, saturation, subnormals)
+    assert _e4m3_encode(np.float32(0.01) / (np.float32(3.2) / np.float32(448))) == 0x3B
+    assert _e4m3_encode(np.float32(0.40625)) == oracle.e4m3_encode(0.40625)
+    assert _e4m3_encode(np.float32(1000.0)) == 0x7E and _e4m3_encode(np.float32(-500)) == 0xFE
+    assert _e4m3_encode(np.float32(1.0625)) == 0x38       # tie 1.0 / 1.125 -> even code
+    assert _e4m3_encode(np.float32(1.1875)) == 0x3A       # tie 1.125 / 1.25 -> even code
+    assert _e4m3_encode(np.float32(2.0 ** -10)) == 0x00   # tie 0 / 2^-9 -> 0
+    assert _e4m3_encode(np.float32(3 * 2.0 ** -10)) == 0x02
+    r = np.random.default_rng(3)
+    x = (r.standard_normal(20000) * 8).astype(np.float32)
+    want = np.array([oracle.e4m3_encode(v) for v in x[:2000]], np.uint8)
+    assert np.array_equal(_e4m3_encode(x[:2000]), want)
+
+
+FP8ATTN_CASES = {
+    # name: (seed, Hq, Hkv, D, lens, values, dtype, windows, k-scale factors, v-scale factors)
+    "tiny": (61, 4, 2, 64, [256], "tiny", FP8, (0,), [1, 3], [2, 0.5]),
+    "gqa4_ragged_window": (62, 16, 4, 64, [300, 77, 513, 16, 1], "tiny", FP8, (0, 100, 33),
+                           [1, 2.5, 0.3, 7], [4, 0.2, 1, 9]),
+    "g8_drift": (63, 16, 2, 128, [2100], "drift", FP8, (0,), [1, 0.5], [1, 2]),
+    "e5m2": (64, 8, 2, 64, [150, 260], "tiny", oracle.E5M2, (0,), [1, 40], [30, 1]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8ATTN_CASES))
+def test_fp8attn_matches_a_numpy_brute_force(name):
+    """The oracle's all-FP8 attention against a second, vectorised
+    formulation on the same codes, with distinct static scales per KV head.
+    The plain reading (P relative to the row's largest logit instead of its
+    32-position block's) is computed beside it and its distance reported:
+    both readings quantise the same products, and the block reading keeps
+    more of each block's small probabilities above the e4m3 subnormal range."""
+    seed, Hq, Hkv, D, lens, values, dtype, windows, kf, vf = FP8ATTN_CASES[name]
+    case = synth.decode_case(seed, Hq, Hkv, D, lens, shuffle=True, spare_frac=0.2, values=values)
+    ks = oracle.scale_from_amax(case.k_new, True, fmt=dtype) * np.array(kf, np.float32)
+    vs = oracle.scale_from_amax(case.v_new, True, fmt=dtype) * np.array(vf, np.float32)
+    kc = synth.poisoned_cache(case.num_pages, Hkv, D, True)
+    vc = kc.copy()
+    oracle.kv_cache_write(kc, vc, case.k_new, case.v_new, case.slots, dtype, True, ks, vs)
+    for w in windows:
+        got = oracle.attention_fp8attn(case.q, kc, vc, case.block_tables, case.lens, Hkv, dtype,
+                                       True, w, 0.0, ks, vs)
+        want = _fp8attn_brute(case, kc, vc, dtype, ks, vs, w)
+        scale = max(1.0, np.max(np.abs(want)))
+        assert np.max(np.abs(got - want)) / scale <= 1e-12, (name, w)
+        plain = _fp8attn_brute(case, kc, vc, dtype, ks, vs, w, reference="row")
+        exact = oracle.attention(case.q, kc, vc, case.block_tables, case.lens, Hkv, dtype,
+                                 True, w, 0.0, ks, vs)
+        e_block = np.abs(got - exact)
+        e_plain = np.abs(plain - exact)
+        print(f"[fp8attn {name} window {w}] block vs plain max {np.max(np.abs(got - plain)):.3e}; "
+              f"vs bf16-arithmetic attention: block max {e_block.max():.3e} mean "
+              f"{e_block.mean():.3e}, plain max {e_plain.max():.3e} mean {e_plain.mean():.3e} "
+              f"(output scale {scale:.2f})")
+        assert e_block.mean() <= e_plain.mean() * 1.5 + 1e-12, (name, w)
