@@ -111,8 +111,9 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // costed as k * run (pages each CU streams) with a small penalty per extra
 // co-resident work-group (measured: two work-groups of 32 pages per CU take
 // ~3.5 % longer than one of 64). One work-group per CU (one wave per SIMD)
-// uses the LDS-staged tile shape, so a wave keeps its next tile in flight
-// while it computes; more use the register shape. When one partition per
+// uses the LDS-staged tile shape up to head_dim 128, so a wave keeps its next
+// tile in flight while it computes; more, and head_dim 256, use the register
+// shape. When one partition per
 // sequence is cheap enough (short contexts, sliding windows) the split kernel
 // writes the output itself and the reduce kernel is skipped.
 //
@@ -161,7 +162,12 @@ Plan make_plan(const kvq_layer_desc* d, int num_seqs, int max_context_len) {
   // a staged tile: K and V of two pages, with dynamic scales their 2 x 16 fp32 each
   const int64_t tile_bytes = 2 * 2 * page_block + (dynamic_scales(d) ? 2 * 2 * 16 * 4 : 0);
   const bool ring_fits = kSplitWaves * tile_bytes <= 64 * 1024;
-  int slots = (k_best == 1 && ring_fits) ? 1 : 0;
+  // At head_dim 256 a 2-page tile is 16 KiB per wave: the staged ring fills
+  // the whole 64 KiB and a wave's tile occupies 64 VGPRs either way; the
+  // register shape measured faster there (fp8, 8 q / 2 KV heads, one
+  // sequence: 8192 positions 10.55 -> 10.29 us, 32768 13.70 -> 13.14,
+  // 65536 19.07 -> 19.03, 131072 29.74 -> 29.37 per layer step).
+  int slots = (k_best == 1 && ring_fits && d->head_dim <= 128) ? 1 : 0;
   int64_t direct_ppw = (pages_max + kSplitWaves - 1) / kSplitWaves;
   direct_ppw = (direct_ppw + 1) / 2 * 2;
   if (direct_ppw <= std::max<int64_t>(ppw, 8)) {
