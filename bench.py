@@ -515,6 +515,131 @@ def gptoss_sweep(torch, kv, w, contexts, steps, warmup, window=128, per_type=12)
     return out
 
 
+TRACE_POINTS = [
+    ("llama8b_32768", ["--context", "32768"]),
+    ("llama8b_65536", ["--context", "65536"]),
+    ("llama8b_98304", ["--context", "98304"]),
+    ("hd256_65536", ["--workload", "hd256", "--context", "65536"]),
+    ("gptoss_full_32768", ["--workload", "gptoss", "--context", "32768"]),
+]
+
+
+def trace_point_kernel_times(args, timeout=150):
+    """One trace point in a child `rocprofv3 --kernel-trace -- bench.py
+    --trace-point ARGS` (graph-replayed decode steps, then plain reads of the
+    split kernel's bytes per launch at 1024 and 4096 work-groups): the split
+    kernel's and the read's mean dispatch times (the read: the better
+    work-group count). None when the run fails or leaves no trace. Runs in
+    the trace server, a process that never touches the GPU."""
+    import csv
+    import glob
+    import shutil
+    import subprocess
+    import tempfile
+    exe = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(exe):
+        return None
+    env = dict(os.environ, TMPDIR="/tmp")
+    with tempfile.TemporaryDirectory(dir="/tmp") as d:
+        cmd = [exe, "--kernel-trace", "-d", d, "-o", "tp", "--output-format", "csv", "--",
+               sys.executable, os.path.abspath(__file__), "--trace-point", *args]
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout, env=env,
+                               cwd=ROOT)
+        except (subprocess.TimeoutExpired, OSError):
+            return None
+        # the profiler may end with a fault of its own after the program has
+        # finished: the trace is used when the program's own line printed
+        if not any(l.startswith("{") for l in r.stdout.splitlines()):
+            return None
+        split, read = [], {}
+        for f in glob.glob(os.path.join(d, "**", "tp_kernel_trace.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    n = row["Kernel_Name"]
+                    dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                    if "paged_decode_split_kernel" in n:
+                        split.append(dur)
+                    elif "stream_read_kernel" in n:
+                        wg = int(row["Grid_Size_X"]) // int(row["Workgroup_Size_X"])
+                        read.setdefault(wg, []).append(dur)
+    if not split or not read:
+        return None
+    sp = sum(split) / len(split)
+    rd = min(sum(v) / len(v) for v in read.values())
+    return dict(split_us=round(sp, 3), read_us=round(rd, 3), ratio=round(sp / rd, 4),
+                split_launches=len(split))
+
+
+def trace_server():
+    """`bench.py --trace-server`: one JSON request per stdin line ({"args":
+    [...]}), one JSON reply per line (trace_point_kernel_times). The bench
+    starts it before it initialises the GPU, so the profiler runs start from a
+    process that never touched the GPU."""
+    for line in sys.stdin:
+        try:
+            req = json.loads(line)
+            res = trace_point_kernel_times(req["args"])
+        except Exception:      # a malformed request or a failed run: no result
+            res = None
+        sys.stdout.write(json.dumps(res) + "\n")
+        sys.stdout.flush()
+
+
+def start_trace_server():
+    """The trace server as a child process (before any GPU use), or None."""
+    import subprocess
+    try:
+        return subprocess.Popen([sys.executable, os.path.abspath(__file__), "--trace-server"],
+                                stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True, cwd=ROOT)
+    except OSError:
+        return None
+
+
+def kernel_trace_ratios(server, points=TRACE_POINTS, timeout=200):
+    """The split kernel against a plain read of the same bytes, both timed by
+    the profiler's dispatch timestamps, per point ({point: {split_us, read_us,
+    ratio, split_launches}}, None for a point without a result; None with no
+    server). Kernel-event pairs cannot time the graph-replayed split kernel,
+    and in eager launches it runs about 1.4 us longer than under graph
+    replay."""
+    import select
+    if server is None or server.poll() is not None:
+        return None
+    out = {}
+    for name, args in points:
+        out[name] = None
+        try:
+            server.stdin.write(json.dumps({"args": args}) + "\n")
+            server.stdin.flush()
+            ready, _, _ = select.select([server.stdout], [], [], timeout)
+            if not ready:
+                log(f"kernel trace {name}: no reply in {timeout} s")
+                server.kill()
+                break
+            res = json.loads(server.stdout.readline() or "null")
+        except (OSError, ValueError):
+            break
+        out[name] = res
+        if res:
+            log(f"kernel trace {name}: split {res['split_us']:.2f} us, same-size read "
+                f"{res['read_us']:.2f} us ({res['ratio']:.3f}x)")
+        else:
+            log(f"kernel trace {name}: no result")
+    return out
+
+
+def stop_trace_server(server):
+    if server is None:
+        return
+    try:
+        server.stdin.close()
+        server.wait(timeout=10)
+    except Exception:
+        server.kill()
+
+
 def sweep(torch, kv, w, contexts, steps, warmup):
     rows = []
     for dt in ("fp8_e4m3", "bf16"):
@@ -916,6 +1041,10 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling PMC byte counters)")
+    ap.add_argument("--trace-server", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--no-kernel-trace", action="store_true",
+                    help="skip the rocprofv3 kernel-trace comparison of the split kernel with a "
+                         "plain read (child processes, about a minute)")
     ap.add_argument("--trace-point", action="store_true",
                     help="for a kernel trace: 20 graph-replayed decode steps of --workload at "
                          "--context (all layers of the workload's cache type), then plain "
@@ -924,12 +1053,23 @@ def main():
                          "the same way")
     args = ap.parse_args()
 
+    if args.trace_server:
+        trace_server()
+        return
+
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(each sequence and KV head is independent; sharding is the caller's). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    # the profiler's child processes start from a process that has not
+    # touched the GPU: the trace server, started first
+    tracer = None
+    if (args.workload == "llama8b" and not args.no_sweep and not args.no_kernel_trace
+            and not args.prefill_only and not args.trace_point and not args.copy_calibration):
+        tracer = start_trace_server()
 
     import torch
     import fp8_kv_cache_write_amd as kv
@@ -1121,6 +1261,10 @@ def main():
     if not args.no_sweep and args.workload == "llama8b":
         contexts = [16, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 98304, 131072]
         result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["split_vs_read_kernel_trace"] = kernel_trace_ratios(tracer)
+    stop_trace_server(tracer)
     if not args.no_workloads and args.workload == "llama8b":
         result["workloads"] = other_workloads(torch, kv, args.sweep_steps, 2)
         result["quantisation_error_vs_bf16"] = quantisation_error(torch, kv)
