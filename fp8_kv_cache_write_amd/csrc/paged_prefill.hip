@@ -426,8 +426,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     // ---- online softmax (log2 domain), lazy rescale --------------------------
     // Every column group's tile maximum first, then one (rarely taken) branch
     // for the rescales, so the exponentials and the P*V MFMAs below form one
-    // block in which the scheduler overlaps a group's exponentials with the
-    // previous group's MFMAs.
+    // straight-line block that the scheduler is free to interleave (a branch
+    // per group used to split it).
     float tmax[NCG];
     bool grow[NCG];
     bool any_grow = false;
