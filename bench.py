@@ -531,7 +531,6 @@ def trace_point_kernel_times(args, timeout=150):
     kernel's and the read's mean dispatch times (the read: the better
     work-group count). None when the run fails or leaves no trace. Runs in
     the trace server, a process that never touches the GPU."""
-    import csv
     import glob
     import shutil
     import subprocess
@@ -552,17 +551,26 @@ def trace_point_kernel_times(args, timeout=150):
         # finished: the trace is used when the program's own line printed
         if not any(l.startswith("{") for l in r.stdout.splitlines()):
             return None
-        split, read = [], {}
-        for f in glob.glob(os.path.join(d, "**", "tp_kernel_trace.csv"), recursive=True):
-            with open(f) as fh:
-                for row in csv.DictReader(fh):
-                    n = row["Kernel_Name"]
-                    dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
-                    if "paged_decode_split_kernel" in n:
-                        split.append(dur)
-                    elif "stream_read_kernel" in n:
-                        wg = int(row["Grid_Size_X"]) // int(row["Workgroup_Size_X"])
-                        read.setdefault(wg, []).append(dur)
+        return split_read_times(
+            glob.glob(os.path.join(d, "**", "tp_kernel_trace.csv"), recursive=True))
+
+
+def split_read_times(trace_csvs):
+    """From rocprofv3 kernel-trace CSV files: the split kernel's mean
+    dispatch time, the plain read's (the better of its work-group counts)
+    and their ratio, or None when either kernel is missing."""
+    import csv
+    split, read = [], {}
+    for f in trace_csvs:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                n = row["Kernel_Name"]
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                if "paged_decode_split_kernel" in n:
+                    split.append(dur)
+                elif "stream_read_kernel" in n:
+                    wg = int(row["Grid_Size_X"]) // int(row["Workgroup_Size_X"])
+                    read.setdefault(wg, []).append(dur)
     if not split or not read:
         return None
     sp = sum(split) / len(split)
