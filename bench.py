@@ -657,7 +657,8 @@ def sweep(torch, kv, w, contexts, steps, warmup):
             NL = layers_for(per_layer)
             st = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, dt, seed=ctx)
             ms = time_steps_graph(torch, st, steps, warmup)
-            _, split_ms, _ = time_steps(torch, kv, st, 2, 1)
+            # eager steps (no graph, no events), then the event-timed pass
+            ms_eager, split_ms, _ = time_steps(torch, kv, st, 3, 1)
             us_layer = ms * 1e3 / NL
             gbs = st.total_kv_bytes() / (ms * 1e-3) / 1e9
             d0 = st.layers[0]["desc"]
@@ -669,6 +670,7 @@ def sweep(torch, kv, w, contexts, steps, warmup):
             read_k = same_size_read_kernel_us(torch, kv, split_bytes) if ctx >= 4096 else None
             split_us = split_ms * 1e3 if split_ms else None
             rows.append(dict(cache=dt, context=ctx, layers=NL, us_per_layer=round(us_layer, 3),
+                             us_per_layer_eager=round(ms_eager * 1e3 / NL, 3),
                              kv_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
                              split_us=round(split_us, 3) if split_us else None,
                              same_size_read_us=round(read_us, 3) if read_us else None,
@@ -680,12 +682,14 @@ def sweep(torch, kv, w, contexts, steps, warmup):
             log(f"sweep {dt:8s} ctx={ctx:6d} layers={NL:3d} {us_layer:8.2f} us/layer "
                 f"{gbs:7.1f} GB/s split={rows[-1]['split_us']} us read={read_us} us")
     fits = {}
+    fits_eager = {}
     for dt in ("fp8_e4m3", "bf16"):
-        pts = [(r["context"], r["us_per_layer"]) for r in rows
-               if r["cache"] == dt and r["context"] >= 8192]
-        if len(pts) >= 2:
-            s, b = fit([p[0] for p in pts], [p[1] for p in pts])
-            fits[dt] = dict(slope_us_per_token=s, intercept_us=b)
+        for key, dst in (("us_per_layer", fits), ("us_per_layer_eager", fits_eager)):
+            pts = [(r["context"], r[key]) for r in rows
+                   if r["cache"] == dt and r["context"] >= 8192]
+            if len(pts) >= 2:
+                s, b = fit([p[0] for p in pts], [p[1] for p in pts])
+                dst[dt] = dict(slope_us_per_token=s, intercept_us=b)
     out = dict(points=rows, fit_range="8192..%d" % max(contexts),
                graph_kernel_floor_us=round(graph_kernel_floor(torch), 3))
     if "fp8_e4m3" in fits and "bf16" in fits:
@@ -695,6 +699,12 @@ def sweep(torch, kv, w, contexts, steps, warmup):
         ds = bb["slope_us_per_token"] - f["slope_us_per_token"]
         out["break_even_context"] = ((f["intercept_us"] - bb["intercept_us"]) / ds
                                      if ds > 0 else None)
+    # the same fit over eager steps (each layer's calls launched from the
+    # host, no graph): a second intercept beside the graph-replayed one
+    if "fp8_e4m3" in fits_eager and "bf16" in fits_eager:
+        out["fits_eager"] = fits_eager
+        out["slope_ratio_fp8_over_bf16_eager"] = (fits_eager["fp8_e4m3"]["slope_us_per_token"] /
+                                                  fits_eager["bf16"]["slope_us_per_token"])
     return out
 
 
