@@ -542,14 +542,26 @@ def trace_point_kernel_times(args, timeout=150):
     with tempfile.TemporaryDirectory(dir="/tmp") as d:
         cmd = [exe, "--kernel-trace", "-d", d, "-o", "tp", "--output-format", "csv", "--",
                sys.executable, os.path.abspath(__file__), "--trace-point", *args]
+        # the profiler and the program under it in a process group of their
+        # own, so that a run past its time limit is ended whole
         try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout, env=env,
-                               cwd=ROOT)
-        except (subprocess.TimeoutExpired, OSError):
+            proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                                    text=True, env=env, cwd=ROOT, start_new_session=True)
+        except OSError:
+            return None
+        try:
+            stdout, _ = proc.communicate(timeout=timeout)
+        except subprocess.TimeoutExpired:
+            import signal
+            try:
+                os.killpg(proc.pid, signal.SIGKILL)
+            except OSError:
+                pass
+            proc.communicate()
             return None
         # the profiler may end with a fault of its own after the program has
         # finished: the trace is used when the program's own line printed
-        if not any(l.startswith("{") for l in r.stdout.splitlines()):
+        if not any(l.startswith("{") for l in stdout.splitlines()):
             return None
         return split_read_times(
             glob.glob(os.path.join(d, "**", "tp_kernel_trace.csv"), recursive=True))
