@@ -424,12 +424,19 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     }
 
     // ---- online softmax (log2 domain), lazy rescale --------------------------
-    // Every column group's tile maximum first, then one (rarely taken) branch
-    // for the rescales, so the exponentials and the P*V MFMAs below form one
+    // Every column group's test first, then one (rarely taken) branch for the
+    // rescales, so the exponentials and the P*V MFMAs below form one
     // straight-line block that the scheduler is free to interleave (a branch
-    // per group used to split it).
-    float tmax[NCG];
-    bool grow[NCG];
+    // per group used to split it). A column's maximum passes
+    // m_run + kLazyLog2 exactly when one of its four lanes' maxima does
+    // (c >= 0, and rounding is monotone), so the bf16-arithmetic modes test
+    // each lane's own maximum and reduce across the column's lanes only
+    // inside the branch: the same decisions, without two lane exchanges per
+    // group and tile. The all-FP8 mode needs the column maximum on every
+    // tile (its P is quantised relative to it).
+    float lmax[NCG];
+    float tmax[ATT8 ? NCG : 1];
+    bool grow[ATT8 ? NCG : 1];
     bool any_grow = false;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
@@ -438,14 +445,25 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = vmax(mx, sacc[cg][pg][e]);
-      tmax[cg] = col_max(mx) * cexp;
-      grow[cg] = tmax[cg] > m_run[cg] + kLazyLog2;
-      any_grow |= grow[cg];
+      if constexpr (ATT8) {
+        tmax[cg] = col_max(mx) * cexp;
+        grow[cg] = tmax[cg] > m_run[cg] + kLazyLog2;
+        any_grow |= grow[cg];
+      } else {
+        lmax[cg] = mx;
+        any_grow |= mx * cexp > m_run[cg] + kLazyLog2;
+      }
     }
     if (__builtin_amdgcn_ballot_w64(any_grow) != 0ull) {
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        const float m_new = grow[cg] ? tmax[cg] : m_run[cg];
+        float m_new;
+        if constexpr (ATT8) {
+          m_new = grow[cg] ? tmax[cg] : m_run[cg];
+        } else {
+          const float cmax = col_max(lmax[cg]) * cexp;
+          m_new = cmax > m_run[cg] + kLazyLog2 ? cmax : m_run[cg];
+        }
         const float alpha = m_new == m_run[cg] ? 1.0f : __builtin_amdgcn_exp2f(m_run[cg] - m_new);
 #pragma unroll
         for (int i = 0; i < NBLK; ++i)
