@@ -157,6 +157,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
       }
     c_log2 = -c_log2;
   }
+  const float rcp_c = 1.0f / c_log2;   // (the lazy bar's unit change; inf for c = 0)
   // All-FP8 mode: every column's query row as e4m3 codes, s_q per column
   uint64_t qop8[ATT8 ? NCG : 1][ATT8 ? NK : 1];
   float cq[NCG];                    // logit scale of each column group's column
@@ -243,12 +244,17 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
   // m_run: running maximum (log2 domain); neg_m: -m_run, or 0 while m_run is
   // -inf (every logit so far masked), the exponent's offset; it changes only
   // when m_run does
-  float m_run[NCG], neg_m[NCG], l_run[NCG];
+  // t_raw (static scales, bf16 arithmetic): the lazy bar in raw-logit units,
+  // (m_run + kLazyLog2) / c; a lane whose raw maximum passes it takes the
+  // rescale branch, which decides on the scaled maximum itself
+  constexpr bool RAW_BAR = !ATT8 && !DYN;
+  float m_run[NCG], neg_m[NCG], l_run[NCG], t_raw[RAW_BAR ? NCG : 1];
   f32x4 acc[NCG][NBLK];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     m_run[cg] = -INFINITY;
     neg_m[cg] = -0.0f;
+    if constexpr (RAW_BAR) t_raw[cg] = -INFINITY;
     l_run[cg] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) acc[cg][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -451,7 +457,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         any_grow |= grow[cg];
       } else {
         lmax[cg] = mx;
-        any_grow |= mx * cexp > m_run[cg] + kLazyLog2;
+        if constexpr (RAW_BAR) any_grow |= mx > t_raw[cg];
+        else any_grow |= mx * cexp > m_run[cg] + kLazyLog2;
       }
     }
     if (__builtin_amdgcn_ballot_w64(any_grow) != 0ull) {
@@ -472,6 +479,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         l_run[cg] *= alpha;
         m_run[cg] = m_new;
         neg_m[cg] = m_new == -INFINITY ? -0.0f : -m_new;
+        if constexpr (RAW_BAR) t_raw[cg] = (m_new + kLazyLog2) * rcp_c;
       }
     }
 
