@@ -1147,10 +1147,13 @@ def main():
                               read_bytes_per_launch=nb, read_buffers=n)))
         return
     if args.prefill_only:
-        res = prefill_bench(torch, kv, WORKLOADS["llama8b"], PREFILL_LENGTHS, 5, 2,
-                            scales=args.scales, attn=args.attn)
-        res["chunked"] = chunked_prefill_bench(torch, kv, WORKLOADS["llama8b"], CHUNKED_PREFILL,
-                                               5, 2, scales=args.scales, attn=args.attn)
+        # the 8B layer by default; --workload picks another layer shape
+        # (hd256: the head_dim-256 prefill the vLLM post finds slower in fp8)
+        res = prefill_bench(torch, kv, w, PREFILL_LENGTHS, 5, 2, scales=args.scales,
+                            attn=args.attn)
+        res["workload"] = args.workload
+        res["chunked"] = chunked_prefill_bench(torch, kv, w, CHUNKED_PREFILL, 5, 2,
+                                               scales=args.scales, attn=args.attn)
         print(json.dumps(res))
         return
     ctx = args.context or w["ctx"]
