@@ -1,11 +1,13 @@
 """Accumulation precision of the matrix instructions (tests/hw/
-mfma_accumulation.hip, run as a child process): the bf16 MFMA that every
-bf16-arithmetic path uses sums exact products like an FP32 accumulator, so
-its paths need no second accumulation level inside a tile; the fp8 MFMA of
-the all-FP8 mode keeps a shorter intermediate sum, as Hopper's FP8 tensor
-cores do ("vLLM FP8 KV-Cache and Attention Quantization Update", section
-"Two-Level Accumulation for Accuracy"), which is why that mode promotes each
-32-position block into the FP32 running sum."""
+mfma_accumulation.hip, run as a child process). The bf16 MFMA that every
+bf16-arithmetic path uses sums exact products like an FP32 accumulator. The
+fp8 MFMA of the all-FP8 mode sums each instruction's 32 products to about
+13 bits, but carries its accumulator at FP32: chaining it gives what adding
+each instruction's result in FP32 gives, up to rounding order. So neither
+has the long-contraction loss of Hopper's FP8 tensor cores ("vLLM FP8
+KV-Cache and Attention Quantization Update", section "Two-Level Accumulation
+for Accuracy"); the all-FP8 mode folds each 32-position block into FP32
+because its P is quantised relative to the block's own maximum."""
 
 import json
 import os
@@ -37,3 +39,6 @@ def test_mfma_accumulation_precision():
     # all-FP8 mode's parity bar (its P codes step by 1/16)
     assert r["fp8_16x16x32_chain"] <= 2.0 ** -10, r
     assert r["fp8_16x16x128"] <= 2.0 ** -10, r
+    # the fp8 accumulator itself: chained = folded in FP32, up to a few
+    # FP32 roundings of the running sum
+    assert r["fp8_chain_minus_fp32_fold"] <= 4 * 2.0 ** -24, r
