@@ -208,6 +208,22 @@ def test_prefill_llama8b_32k_chunk_sampled():
     check(torch.from_numpy(out[rows]), ref, o, case, "prefill-8B-32k-chunk-sampled")
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_llama8b_one_wave_chunk_sampled(split):
+    # a 2500-row chunk over 65536 positions: 424 work-groups of three column
+    # groups, one wave (the plan keeps three groups for a chunk over a long
+    # key range rather than 632 groups of two in a partial second wave);
+    # with a workspace the plan may split the keys instead; rows from the
+    # first, middle and last query blocks against the oracle
+    case = synth.prefill_case(synth.LLAMA8B, 32, 8, 128, [65536], [2500])
+    g = GpuLayer(case)
+    out = host(gpu_prefill(g, case, split=split))
+    o = OracleLayer(case)
+    rows = np.array([0, 1, 47, 48, 1249, 1250, 2451, 2452, 2499], np.int32)
+    ref = oracle_prefill(o, case, rows)
+    check(torch.from_numpy(out[rows]), ref, o, case, f"prefill-8B-2500-over-64k split={split}")
+
+
 @pytest.mark.parametrize("fmt,attn", [("fp8_e4m3", "bf16"), ("bf16", "bf16"),
                                       ("fp8_e4m3", "fp8")])
 def test_prefill_nan_rows(fmt, attn):
