@@ -66,11 +66,23 @@ __device__ __forceinline__ float col_sum(float x) {
 
 }  // namespace
 
+// Head dim 256, fp8 cache, bf16 arithmetic with static scales, two column
+// groups: the tile's K and V codes are read from LDS as they are used (K per
+// pair of q k^T steps, V per group of four P*V blocks, every V block
+// expanded once and used by both column groups) instead of all at the top of
+// the tile, which frees the registers of the second column group at two
+// waves per SIMD (one group keeps the codes in registers: faster there).
 template <int D, int FMT, int NCG, bool DYN, bool ATT8>
-__global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
-    const PrefillParams p) {
+constexpr bool prefill_jit() {
+  return D >= 256 && FMT != kFmtBf16 && NCG >= 2 && !DYN && !ATT8;
+}
+
+template <int D, int FMT, int NCG, bool DYN, bool ATT8>
+__global__ __launch_bounds__(kPrefillWaves * kWave, (prefill_jit<D, FMT, NCG, DYN, ATT8>() ? 2 : 1))
+void paged_prefill_kernel(const PrefillParams p) {
   constexpr int NW = kPrefillWaves;
   constexpr bool FP8 = FMT != kFmtBf16;
+  constexpr bool JIT = prefill_jit<D, FMT, NCG, DYN, ATT8>();
   constexpr int E = FP8 ? 1 : 2;
   constexpr int PB = kPage * D * E;     // bytes of one (page, head) block
   constexpr int NI = PB / 1024;         // 1 KiB loads per page per tensor
@@ -92,11 +104,24 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
 
   // ---- which (sequence, KV head, key partition, query block): XCD-aware ---
   // Consecutive logical blocks share a (sequence, KV head, key partition),
-  // so the query blocks reading the same keys run on one XCD (one L2).
-  const int per_xcd = (int)gridDim.x / kNumXcd;
-  const int logical = (int)(blockIdx.x % kNumXcd) * per_xcd + (int)(blockIdx.x / kNumXcd);
+  // so the query blocks reading the same keys run on one XCD (one L2). With
+  // fewer (sequence, KV head) units than XCDs a unit spans several XCDs, and
+  // each would take a contiguous, heaviest-first run of its causal blocks:
+  // one XCD all the long rows, another all the short ones. There, without a
+  // key split (whose blocks all see one partition) and when the grid has at
+  // least two waves of work-groups (two per CU on 256 CUs), the blocks go
+  // round-robin over the XCDs in heaviest-first order instead, so every XCD
+  // drains an even mix (head dim 256, 2 KV heads, a 32768-token prompt:
+  // 601 -> 942 TFLOP/s; with a single wave the grouped order measured as
+  // fast or faster).
   const int per_bh = p.qblocks * p.num_parts;
   const int total = p.num_seqs * p.num_kv_heads * per_bh;
+  const bool round_robin =
+      p.num_seqs * p.num_kv_heads < kNumXcd && p.num_parts == 1 && total >= 2 * 2 * 256;
+  const int per_xcd = (int)gridDim.x / kNumXcd;
+  const int logical = round_robin ? (int)blockIdx.x
+                                  : (int)(blockIdx.x % kNumXcd) * per_xcd +
+                                        (int)(blockIdx.x / kNumXcd);
   if (logical >= total) return;
   const int bh = logical / per_bh;
   const int part = (logical % per_bh) / p.qblocks;
@@ -273,15 +298,22 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const uint8_t* slot = smem + (t & 1) * TILE;
-    uint4 tk[2][NI], tv[2][NI];
+    // this lane's 16 bytes of 1 KiB chunk i of page pg's K (kv = 0) or V
+    auto lds_code = [&](int pg, int kv, int i) -> uint4 {
+      return *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + kv * NI + i) +
+                                             16 * lane);
+    };
+    uint4 tk[2][JIT ? 1 : NI], tv[2][JIT ? 1 : NI];
+    if constexpr (!JIT) {
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
+      for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        tk[pg][i] = *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + i) + 16 * lane);
-        tv[pg][i] =
-            *reinterpret_cast<const uint4*>(slot + 1024 * (2 * NI * pg + NI + i) + 16 * lane);
-      }
+        for (int i = 0; i < NI; ++i) {
+          tk[pg][i] = lds_code(pg, 0, i);
+          tv[pg][i] = lds_code(pg, 1, i);
+        }
+    }
+    uint32_t vkeep8[2] = {~0u, ~0u};     // JIT: the V-code masks, applied as V is read
     // dynamic scales of this lane's rows 4qd..4qd+3 of each page
     f32x4 sk[2], sv[2];
     if constexpr (DYN) {
@@ -316,8 +348,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
           for (int e = 0; e < 4; ++e)
             if (!(page_ok && k0 + pg * kPage + 4 * qd + e < L)) sk[pg][e] = sv[pg][e] = 0.0f;
         }
+        if constexpr (JIT) vkeep8[pg] = keep8;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
+        for (int i = 0; i < (JIT ? 0 : NI); ++i) {
           if constexpr (FP8) {
             tv[pg][i].x &= keep8; tv[pg][i].y &= keep8; tv[pg][i].z &= keep8; tv[pg][i].w &= keep8;
           } else {
@@ -365,7 +398,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         }
         bf16x8 kop;
         if constexpr (FP8) {
-          const uint4 w = tk[pg][s / 2];
+          const uint4 w = JIT ? lds_code(pg, 0, s / 2) : tk[pg][s / 2];
           kop = (s % 2 == 0) ? fp8x8_to_bf16x8<FMT>(w.x, w.y) : fp8x8_to_bf16x8<FMT>(w.z, w.w);
         } else {
           kop = bits_to_bf16x8(tk[pg][s]);
@@ -378,8 +411,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     }
     // P*V A operands: V^T block blk (16 dims x 32 keys); fp8 codes expanded
     // exactly to bf16, a register shuffle for a bf16 cache
-    uint4 vop[ATT8 ? 1 : NBLK];
-    if constexpr (!ATT8) {
+    uint4 vop[(ATT8 || JIT) ? 1 : NBLK];
+    if constexpr (!ATT8 && !JIT) {
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk) {
         if constexpr (FP8) {
@@ -486,6 +519,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
     // ---- P and P*V, column group by column group (raised priority) -----------
     uint64_t pop8[ATT8 ? NCG : 1];
     float fb[ATT8 ? NCG : 1];          // all-FP8: weight 2^(tile max - running max)
+    bf16x8 popj[JIT ? NCG : 1];        // JIT: every group's P, for the block-major P*V
     if constexpr (!ATT8) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
@@ -535,11 +569,35 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void paged_prefill_kernel(
         for (int e = 0; e < 4; ++e) pop[4 * pg + e] = p4[e];
       }
       l_run[cg] += ps;
+      if constexpr (JIT) {
+        popj[cg] = pop;
+        continue;                          // P*V below, block by block
+      }
       // one k=32 MFMA per 16-dim block
 #pragma unroll
       for (int blk = 0; blk < NBLK; ++blk)
         acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vop[blk]), pop,
                                                                acc[cg][blk], 0, 0, 0);
+    }
+    if constexpr (JIT) {
+      // V^T block blk (16 dims x 32 keys) expanded once, used by every
+      // column group; each 16-byte read of V codes serves four blocks
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint4 wa = lds_code(0, 1, i), wb = lds_code(1, 1, i);
+#pragma unroll
+        for (int ep = 0; ep < 4; ++ep) {
+          const int blk = 4 * i + ep;
+          const uint32_t da = (ep == 0 ? wa.x : ep == 1 ? wa.y : ep == 2 ? wa.z : wa.w) & vkeep8[0];
+          const uint32_t db = (ep == 0 ? wb.x : ep == 1 ? wb.y : ep == 2 ? wb.z : wb.w) & vkeep8[1];
+          const bf16x8 vb = bits_to_bf16x8(__builtin_bit_cast(
+              uint4, cat(fp8x4_to_bf16x4<FMT>(da), fp8x4_to_bf16x4<FMT>(db))));
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg)
+            acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, popj[cg], acc[cg][blk],
+                                                                   0, 0, 0);
+        }
+      }
     }
     if constexpr (ATT8) {
       // fp8 x fp8 products of the block, each added into the FP32 sum with
@@ -646,20 +704,31 @@ hipError_t launch_prefill_shape(const PrefillParams& p, int64_t total, hipStream
 template <int D, int FMT, bool DYN, bool ATT8>
 hipError_t launch_prefill_typed(PrefillParams p, const PrefillPlan& pl, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
-  constexpr int NCG_MAX = D >= 256 ? 1 : (D == 128 && FMT == kFmtBf16 ? 2 : 3);
+  // column groups per wave the registers hold (two at head dim 256 with the
+  // just-in-time codes of the fp8, static-scale, bf16-arithmetic instance)
+  constexpr int NCG_MAX = D >= 256 ? (prefill_jit<D, FMT, 2, DYN, ATT8>() ? 2 : 1)
+                                   : (D == 128 && FMT == kFmtBf16 ? 2 : 3);
   p.pos_per_block = pl.pos_per_block;
   p.qblocks = pl.qblocks;
+  PrefillPlan plc = pl;
+  if (plc.ncg > NCG_MAX && D >= 256) {
+    // the plan allows two groups at head dim 256; the other instances there
+    // hold one: fewer rows per work-group, more work-groups
+    p.pos_per_block = pl.pos_per_block / pl.ncg * NCG_MAX;
+    p.qblocks = (p.max_query_len + p.pos_per_block - 1) / p.pos_per_block;
+    plc.ncg = NCG_MAX;
+  }
   p.num_parts = pl.num_parts;
   p.part_tiles = pl.part_tiles;
   const int64_t total = (int64_t)p.num_seqs * p.num_kv_heads * p.qblocks * p.num_parts;
   if (total == 0) return hipSuccess;
-  if (pl.ncg > NCG_MAX) return hipErrorInvalidValue;
+  if (plc.ncg > NCG_MAX) return hipErrorInvalidValue;
   if constexpr (NCG_MAX >= 3) {
-    if (pl.ncg == 3)
+    if (plc.ncg == 3)
       return launch_prefill_shape<D, FMT, 3, DYN, ATT8>(p, total, stream, ev_before, ev_after);
   }
   if constexpr (NCG_MAX >= 2) {
-    if (pl.ncg == 2)
+    if (plc.ncg == 2)
       return launch_prefill_shape<D, FMT, 2, DYN, ATT8>(p, total, stream, ev_before, ev_after);
   }
   return launch_prefill_shape<D, FMT, 1, DYN, ATT8>(p, total, stream, ev_before, ev_after);
