@@ -104,20 +104,21 @@ void paged_prefill_kernel(const PrefillParams p) {
 
   // ---- which (sequence, KV head, key partition, query block): XCD-aware ---
   // Consecutive logical blocks share a (sequence, KV head, key partition),
-  // so the query blocks reading the same keys run on one XCD (one L2). With
-  // fewer (sequence, KV head) units than XCDs a unit spans several XCDs, and
-  // each would take a contiguous, heaviest-first run of its causal blocks:
-  // one XCD all the long rows, another all the short ones. There, without a
-  // key split (whose blocks all see one partition) and when the grid has at
-  // least two waves of work-groups (two per CU on 256 CUs), the blocks go
-  // round-robin over the XCDs in heaviest-first order instead, so every XCD
-  // drains an even mix (head dim 256, 2 KV heads, a 32768-token prompt:
-  // 601 -> 942 TFLOP/s; with a single wave the grouped order measured as
-  // fast or faster).
+  // so the query blocks reading the same keys run on one XCD (one L2). When
+  // the (sequence, KV head) units do not divide evenly over the XCDs, the
+  // contiguous runs cut units apart, and a causal unit's blocks run
+  // heaviest first: one XCD gets the long rows of a unit, another its short
+  // ones. There, without a key split (whose blocks all see one partition)
+  // and when the grid has at least two waves of work-groups (two per CU on
+  // 256 CUs), the blocks go round-robin over the XCDs in heaviest-first
+  // order instead, so every XCD drains an even mix. Measured at whole
+  // prompts: 2 units (head dim 256) 601 -> 942 TFLOP/s, 10 units 963 ->
+  // 1095, 12 units 1025 -> 1113; with 8 or 24 units the grouped order is
+  // 3-7 % faster, and with a single wave as fast or faster.
   const int per_bh = p.qblocks * p.num_parts;
   const int total = p.num_seqs * p.num_kv_heads * per_bh;
-  const bool round_robin =
-      p.num_seqs * p.num_kv_heads < kNumXcd && p.num_parts == 1 && total >= 2 * 2 * 256;
+  const bool round_robin = (p.num_seqs * p.num_kv_heads) % kNumXcd != 0 && p.num_parts == 1 &&
+                           total >= 2 * 2 * 256;
   const int per_xcd = (int)gridDim.x / kNumXcd;
   const int logical = round_robin ? (int)blockIdx.x
                                   : (int)(blockIdx.x % kNumXcd) * per_xcd +
