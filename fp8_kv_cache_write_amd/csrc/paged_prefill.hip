@@ -113,8 +113,8 @@ void paged_prefill_kernel(const PrefillParams p) {
   // 256 CUs), the blocks go round-robin over the XCDs in heaviest-first
   // order instead, so every XCD drains an even mix. Measured at whole
   // prompts: 2 units (head dim 256) 601 -> 942 TFLOP/s, 10 units 963 ->
-  // 1095, 12 units 1025 -> 1113; with 8 or 24 units the grouped order is
-  // 3-7 % faster, and with a single wave as fast or faster.
+  // 1095, 12 units 1025 -> 1113; with 8 units of one prompt the grouped
+  // order is 3-7 % faster, and with a single wave as fast or faster.
   const int per_bh = p.qblocks * p.num_parts;
   const int total = p.num_seqs * p.num_kv_heads * per_bh;
   // A grid of one wave (more work-groups than CUs, at most two per CU) runs
@@ -122,8 +122,21 @@ void paged_prefill_kernel(const PrefillParams p) {
   // takes the r-th heaviest block and the second the r-th lightest (blocks
   // ranked by weight across units), so no CU holds two long rows (1024-2048
   // token prompts 3-6 % faster, head dim 256 at 4096 tokens 18 %).
+  // Several sequences of unequal work split unevenly over the XCDs too
+  // (each takes whole units): round-robin as well, unless every sequence
+  // has max_query_len rows over a short key range (a batch of equal whole
+  // prompts, where the grouped order is 6-14 % faster). Ragged batches:
+  // 16384 + 2048 tokens 613 -> 939 TFLOP/s, 12000 / 3000 / 6000 / 500
+  // tokens 395 -> 898.
   const int units = p.num_seqs * p.num_kv_heads;
-  const bool round_robin = units % kNumXcd != 0 && p.num_parts == 1 && total >= 2 * 2 * 256;
+  bool round_robin = p.num_parts == 1 && total >= 2 * 2 * 256;
+  if (round_robin && units % kNumXcd == 0) {
+    round_robin = false;
+    if (p.num_seqs > 1) {
+      const bool long_keys = (int64_t)p.max_pages_per_seq * kPage >= 2LL * p.max_query_len;
+      round_robin = long_keys || p.query_start[p.num_seqs] != p.num_seqs * p.max_query_len;
+    }
+  }
   const bool pair_up = p.num_parts == 1 && total > 256 && total <= 2 * 256;
   const int per_xcd = (int)gridDim.x / kNumXcd;
   int logical;

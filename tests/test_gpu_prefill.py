@@ -224,6 +224,26 @@ def test_prefill_llama8b_one_wave_chunk_sampled(split):
     check(torch.from_numpy(out[rows]), ref, o, case, f"prefill-8B-2500-over-64k split={split}")
 
 
+@pytest.mark.parametrize("lens", [[16384, 2048], [4096, 4096, 4096]],
+                         ids=["ragged", "equal"])
+def test_prefill_llama8b_batch_sampled(lens):
+    # whole prompts of several sequences, 16 or 24 (sequence, KV head) units
+    # and two or more waves of work-groups: a ragged batch takes the
+    # round-robin block order, a batch of equal prompts the XCD-grouped one;
+    # rows from the first, middle and last query blocks of every sequence
+    case = synth.prefill_case(synth.LLAMA8B, 32, 8, 128, lens, lens, shuffle=True)
+    g = GpuLayer(case)
+    out = host(gpu_prefill(g, case))
+    o = OracleLayer(case)
+    rows = []
+    for b, n in enumerate(lens):
+        q0 = int(case.query_start[b])
+        rows += [q0, q0 + 47, q0 + 48, q0 + n // 2, q0 + n - 1]
+    rows = np.array(rows, np.int32)
+    ref = oracle_prefill(o, case, rows)
+    check(torch.from_numpy(out[rows]), ref, o, case, f"prefill-8B-batch-{lens}")
+
+
 @pytest.mark.parametrize("fmt,attn", [("fp8_e4m3", "bf16"), ("bf16", "bf16"),
                                       ("fp8_e4m3", "fp8")])
 def test_prefill_nan_rows(fmt, attn):
