@@ -74,7 +74,7 @@ __device__ __forceinline__ float col_sum(float x) {
 // waves per SIMD (one group keeps the codes in registers: faster there).
 template <int D, int FMT, int NCG, bool DYN, bool ATT8>
 constexpr bool prefill_jit() {
-  return D >= 256 && FMT != kFmtBf16 && NCG >= 2 && !DYN && !ATT8;
+  return D >= 256 && (FMT == kFmtBf16 || NCG >= 2) && !DYN && !ATT8;
 }
 
 template <int D, int FMT, int NCG, bool DYN, bool ATT8>
@@ -341,7 +341,9 @@ void paged_prefill_kernel(const PrefillParams p) {
           tv[pg][i] = lds_code(pg, 1, i);
         }
     }
-    uint32_t vkeep8[2] = {~0u, ~0u};     // JIT: the V-code masks, applied as V is read
+    // JIT: the V-code masks (fp8: a byte per row; bf16: rows 4qd+{0,1} and
+    // 4qd+{2,3} as halves), applied as V is read
+    uint32_t vkeep8[2] = {~0u, ~0u}, vkeep_lo[2] = {~0u, ~0u}, vkeep_hi[2] = {~0u, ~0u};
     // dynamic scales of this lane's rows 4qd..4qd+3 of each page
     f32x4 sk[2], sv[2];
     if constexpr (DYN) {
@@ -376,7 +378,11 @@ void paged_prefill_kernel(const PrefillParams p) {
           for (int e = 0; e < 4; ++e)
             if (!(page_ok && k0 + pg * kPage + 4 * qd + e < L)) sk[pg][e] = sv[pg][e] = 0.0f;
         }
-        if constexpr (JIT) vkeep8[pg] = keep8;
+        if constexpr (JIT) {
+          vkeep8[pg] = keep8;
+          vkeep_lo[pg] = keep_lo;
+          vkeep_hi[pg] = keep_hi;
+        }
 #pragma unroll
         for (int i = 0; i < (JIT ? 0 : NI); ++i) {
           if constexpr (FP8) {
@@ -429,7 +435,7 @@ void paged_prefill_kernel(const PrefillParams p) {
           const uint4 w = JIT ? lds_code(pg, 0, s / 2) : tk[pg][s / 2];
           kop = (s % 2 == 0) ? fp8x8_to_bf16x8<FMT>(w.x, w.y) : fp8x8_to_bf16x8<FMT>(w.z, w.w);
         } else {
-          kop = bits_to_bf16x8(tk[pg][s]);
+          kop = bits_to_bf16x8(JIT ? lds_code(pg, 0, s) : tk[pg][s]);
         }
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg)
@@ -607,7 +613,26 @@ void paged_prefill_kernel(const PrefillParams p) {
         acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bits_to_bf16x8(vop[blk]), pop,
                                                                acc[cg][blk], 0, 0, 0);
     }
-    if constexpr (JIT) {
+    if constexpr (JIT && !FP8) {
+      // bf16 cache: each 16-byte read of V per page serves two blocks
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        uint4 wa = lds_code(0, 1, i), wb = lds_code(1, 1, i);
+        wa.x &= vkeep_lo[0]; wa.y &= vkeep_hi[0]; wa.z &= vkeep_lo[0]; wa.w &= vkeep_hi[0];
+        wb.x &= vkeep_lo[1]; wb.y &= vkeep_hi[1]; wb.z &= vkeep_lo[1]; wb.w &= vkeep_hi[1];
+#pragma unroll
+        for (int ep = 0; ep < 2; ++ep) {
+          const int blk = 2 * i + ep;
+          const bf16x8 vb = bits_to_bf16x8(ep == 0 ? make_uint4(wa.x, wa.y, wb.x, wb.y)
+                                                   : make_uint4(wa.z, wa.w, wb.z, wb.w));
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg)
+            acc[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, popj[cg], acc[cg][blk],
+                                                                   0, 0, 0);
+        }
+      }
+    }
+    if constexpr (JIT && FP8) {
       // V^T block blk (16 dims x 32 keys) expanded once, used by every
       // column group; each 16-byte read of V codes serves four blocks
 #pragma unroll

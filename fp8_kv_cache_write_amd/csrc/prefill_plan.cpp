@@ -18,11 +18,11 @@ namespace {
 constexpr int kPlanPage = 16;       // positions per page
 
 // Column groups per wave the registers allow (each shares the tile's
-// fp8 -> bf16 expansion and LDS reads). At head dim 256 an fp8 cache allows
-// two in its static-scale, bf16-arithmetic instance (its K/V codes are read
-// just in time); the launcher gives the others one.
+// fp8 -> bf16 expansion and LDS reads). At head dim 256 the static-scale,
+// bf16-arithmetic instances allow two (their K/V codes are read just in
+// time); the launcher gives the others one.
 int prefill_ncg_max(int head_dim, int fmt) {
-  if (head_dim >= 256) return fmt == KVQ_BF16 ? 1 : 2;
+  if (head_dim >= 256) return 2;
   return head_dim == 128 && fmt == KVQ_BF16 ? 2 : 3;
 }
 
