@@ -66,15 +66,19 @@ __device__ __forceinline__ float col_sum(float x) {
 
 }  // namespace
 
-// Head dim 256, fp8 cache, bf16 arithmetic with static scales, two column
-// groups: the tile's K and V codes are read from LDS as they are used (K per
-// pair of q k^T steps, V per group of four P*V blocks, every V block
-// expanded once and used by both column groups) instead of all at the top of
-// the tile, which frees the registers of the second column group at two
-// waves per SIMD (one group keeps the codes in registers: faster there).
+// Bf16 arithmetic with static scales at head dim 256 (two column groups;
+// one as well for a bf16 cache), and a bf16 cache at head dim 128 (three
+// groups): the tile's K and V codes are read from LDS as they are used (K
+// per q k^T step or pair of steps, V per group of P*V blocks, every V block
+// expanded once and used by each column group) instead of all at the top of
+// the tile, which frees the registers of one more column group at two waves
+// per SIMD. (An fp8 cache at one group keeps the codes in registers: faster
+// there.)
 template <int D, int FMT, int NCG, bool DYN, bool ATT8>
 constexpr bool prefill_jit() {
-  return D >= 256 && (FMT == kFmtBf16 || NCG >= 2) && !DYN && !ATT8;
+  return ((D >= 256 && (FMT == kFmtBf16 || NCG >= 2)) ||
+          (D == 128 && FMT == kFmtBf16 && NCG >= 3)) &&
+         !DYN && !ATT8;
 }
 
 template <int D, int FMT, int NCG, bool DYN, bool ATT8>
@@ -757,14 +761,14 @@ hipError_t launch_prefill_shape(const PrefillParams& p, int64_t total, hipStream
 template <int D, int FMT, bool DYN, bool ATT8>
 hipError_t launch_prefill_typed(PrefillParams p, const PrefillPlan& pl, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
-  // column groups per wave the registers hold (two at head dim 256 with the
-  // just-in-time codes of the fp8, static-scale, bf16-arithmetic instance)
-  constexpr int NCG_MAX = D >= 256 ? (prefill_jit<D, FMT, 2, DYN, ATT8>() ? 2 : 1)
-                                   : (D == 128 && FMT == kFmtBf16 ? 2 : 3);
+  // column groups per wave the registers hold (at head dim 256: two with
+  // the just-in-time codes of the static-scale, bf16-arithmetic instances;
+  // a bf16 cache at head dim 128: three with them)
+  constexpr int NCG_MAX = D >= 256 ? (prefill_jit<D, FMT, 2, DYN, ATT8>() ? 2 : 1) : 3;
   p.pos_per_block = pl.pos_per_block;
   p.qblocks = pl.qblocks;
   PrefillPlan plc = pl;
-  if (plc.ncg > NCG_MAX && D >= 256) {
+  if (plc.ncg > NCG_MAX) {
     // the plan allows two groups at head dim 256; the other instances there
     // hold one: fewer rows per work-group, more work-groups
     p.pos_per_block = pl.pos_per_block / pl.ncg * NCG_MAX;

@@ -18,12 +18,13 @@ namespace {
 constexpr int kPlanPage = 16;       // positions per page
 
 // Column groups per wave the registers allow (each shares the tile's
-// fp8 -> bf16 expansion and LDS reads). At head dim 256 the static-scale,
-// bf16-arithmetic instances allow two (their K/V codes are read just in
-// time); the launcher gives the others one.
+// fp8 -> bf16 expansion and LDS reads): three up to head dim 128 (a bf16
+// cache at 128 with its K/V codes read just in time), two at 256 (the
+// static-scale, bf16-arithmetic instances, just in time); the launcher gives
+// the instances that hold fewer what they hold.
 int prefill_ncg_max(int head_dim, int fmt) {
-  if (head_dim >= 256) return 2;
-  return head_dim == 128 && fmt == KVQ_BF16 ? 2 : 3;
+  (void)fmt;
+  return head_dim >= 256 ? 2 : 3;
 }
 
 }  // namespace
