@@ -444,6 +444,9 @@ const char* kvq_status_string(int32_t status);
  *                                410, 211, 212, 411 (a shape a mode is not
  *                                built for fails the launch with KVQ_ERR_HIP)
  *   KVQ_TUNE_PREFILL_COLUMN_GROUPS  1..3 query column groups per prefill wave
+ *                                (capped at what the layer's kernel holds:
+ *                                3 up to head_dim 128, 2 at 256 with static
+ *                                scales and bf16 arithmetic, else 1)
  *   KVQ_TUNE_PREFILL_KEY_PARTS   >= 1 key partitions of a prefill with a
  *                                workspace (1: no split)
  * Returns KVQ_ERR_INVALID_ARG for an unknown knob or a value out of range.
