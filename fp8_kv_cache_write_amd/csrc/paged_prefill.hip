@@ -108,30 +108,26 @@ void paged_prefill_kernel(const PrefillParams p) {
 
   // ---- which (sequence, KV head, key partition, query block): XCD-aware ---
   // Consecutive logical blocks share a (sequence, KV head, key partition),
-  // so the query blocks reading the same keys run on one XCD (one L2). When
-  // the (sequence, KV head) units do not divide evenly over the XCDs, the
-  // contiguous runs cut units apart, and a causal unit's blocks run
-  // heaviest first: one XCD gets the long rows of a unit, another its short
-  // ones. There, without a key split (whose blocks all see one partition)
-  // and when the grid has at least two waves of work-groups (two per CU on
-  // 256 CUs), the blocks go round-robin over the XCDs in heaviest-first
-  // order instead, so every XCD drains an even mix. Measured at whole
-  // prompts: 2 units (head dim 256) 601 -> 942 TFLOP/s, 10 units 963 ->
-  // 1095, 12 units 1025 -> 1113; with 8 units of one prompt the grouped
-  // order is 3-7 % faster, and with a single wave as fast or faster.
+  // so the query blocks reading the same keys run on one XCD (one L2), a
+  // causal unit's blocks heaviest first. Two cases take another order
+  // (none with a key split, whose blocks all see one partition):
+  //  * the (sequence, KV head) units do not divide evenly over the XCDs, or
+  //    several sequences have unequal work (rows, or a long key range):
+  //    the contiguous runs would give one XCD the long rows and another the
+  //    short ones. With at least two waves of work-groups (two per CU on
+  //    256 CUs) the blocks go round-robin over the XCDs in heaviest-first
+  //    order instead. Measured at whole prompts: 2 units (head dim 256)
+  //    601 -> 942 TFLOP/s, 10 units 963 -> 1095, 12 units 1025 -> 1113,
+  //    ragged batches 16384 + 2048 tokens 617 -> 1013, 12000 / 3000 / 6000
+  //    / 500 tokens 397 -> 920; the 8 units of one prompt, or a batch of
+  //    equal prompts, keep the grouped order (3-14 % faster there);
+  //  * a grid of one wave (more work-groups than CUs, at most two per CU)
+  //    runs every block at once, two to a CU: the first work-group of each
+  //    CU takes the r-th heaviest block and the second the r-th lightest
+  //    (ranked across units), so no CU holds two long rows (1024-2048-token
+  //    prompts 3-6 % faster, head dim 256 at 4096 tokens 18 %).
   const int per_bh = p.qblocks * p.num_parts;
   const int total = p.num_seqs * p.num_kv_heads * per_bh;
-  // A grid of one wave (more work-groups than CUs, at most two per CU) runs
-  // every block at once, two to a CU: there the first work-group of each CU
-  // takes the r-th heaviest block and the second the r-th lightest (blocks
-  // ranked by weight across units), so no CU holds two long rows (1024-2048
-  // token prompts 3-6 % faster, head dim 256 at 4096 tokens 18 %).
-  // Several sequences of unequal work split unevenly over the XCDs too
-  // (each takes whole units): round-robin as well, unless every sequence
-  // has max_query_len rows over a short key range (a batch of equal whole
-  // prompts, where the grouped order is 6-14 % faster). Ragged batches:
-  // 16384 + 2048 tokens 613 -> 939 TFLOP/s, 12000 / 3000 / 6000 / 500
-  // tokens 395 -> 898.
   const int units = p.num_seqs * p.num_kv_heads;
   bool round_robin = p.num_parts == 1 && total >= 2 * 2 * 256;
   if (round_robin && units % kNumXcd == 0) {
