@@ -18,6 +18,14 @@ def cache_fmt(fp8, fmt):
     return fmt if fmt is not None else ("fp8_e4m3" if fp8 else "bf16")
 GATE_MAX_ABS = 1e-2      # attention gate (max-abs, unit-scale inputs)
 GATE_MEAN_ABS = 1e-3     # attention gate (mean-abs)
+# All-FP8 arithmetic: one flip (a probability rounded to the neighbouring
+# e4m3 code) moves only its own (row, q head) pair, by up to an eighth of
+# |v_j - o| there. With few pairs over few positions one flip alone can lift
+# the mean above the gate (8 pairs over 8-9 positions: one step of a
+# probability near 0.53 moved its pair by up to 0.058, the case's mean to 1.24
+# of the gate); from this many pairs on, one such flip (that pair's mean
+# error was 0.017) adds under a third of the gate, and the mean gate applies.
+FLIP_DILUTION_PAIRS = 64
 
 
 def dev():

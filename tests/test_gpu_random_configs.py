@@ -8,7 +8,8 @@ bit. Every configuration is one the library documents as supported. The
 parity bars: the attention gate and the tight bound in the bf16-arithmetic
 modes; in the all-FP8 mode (where FP32 against float64 logit rounding can
 move a probability across an e4m3 rounding boundary, by at most an eighth of
-it), the mean gate everywhere, the max gate on rows of at least 512
+it), the mean gate on cases of at least 64 (row, q head) pairs, the max
+gate on rows of at least 512
 attended positions, where a flip is diluted, and on every row the bound of
 two flips: a quarter of the row's largest attended |v|."""
 
@@ -17,7 +18,7 @@ import pytest
 import torch
 
 import synth
-from _gpu import GpuLayer, OracleLayer, bf16_dev, host
+from _gpu import FLIP_DILUTION_PAIRS, GpuLayer, OracleLayer, bf16_dev, host
 from test_gpu_parity import GATE_MAX_ABS, GATE_MEAN_ABS
 from test_gpu_parity import check_attention, newest_rows, run_decode_step, say, split_newest
 
@@ -60,7 +61,8 @@ def check_fp8attn_rows(g, o, case, window, label):
     d = np.abs(got - ref)
     scale = max(1.0, float(np.abs(ref).max()))
     say(f"[{label}] max_abs={d.max():.3e} mean_abs={d.mean():.3e} (output scale {scale:.2f})")
-    assert d.mean() <= GATE_MEAN_ABS * scale, label
+    if d.shape[0] * d.shape[1] >= FLIP_DILUTION_PAIRS:
+        assert d.mean() <= GATE_MEAN_ABS * scale, label
     v = np.abs(synth.bits_to_f32(case.v_new)).astype(np.float64)       # [T][Hkv][D]
     G = case.num_q_heads // case.num_kv_heads
     for b, L in enumerate(case.lens):

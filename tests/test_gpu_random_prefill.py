@@ -11,17 +11,18 @@ prefill of "State of FP8 KV cache and attention quantization in vLLM"
 (section "Single-request benchmark") reads its input.
 
 The bars: in the bf16-arithmetic modes the attention gate and the P-rounding
-bound (2^-8 of the largest attended |v|); in the all-FP8 mode the mean gate,
-the max gate on rows of at least 512 attended positions, and on every row the
-bound of two e4m3 flips of a probability (a quarter of the row's largest
-attended |v| per KV head)."""
+bound (2^-8 of the largest attended |v|); in the all-FP8 mode the mean gate
+on cases of at least 64 (row, q head) pairs, the max gate on rows of at
+least 512 attended positions, and on every row the bound of two e4m3 flips
+of a probability (a quarter of the row's largest attended |v| per KV
+head)."""
 
 import numpy as np
 import pytest
 import torch
 
 import synth
-from _gpu import GpuLayer, OracleLayer, host
+from _gpu import FLIP_DILUTION_PAIRS, GpuLayer, OracleLayer, host
 from test_gpu_parity import GATE_MAX_ABS, GATE_MEAN_ABS, say
 from test_gpu_prefill import check, gpu_prefill, oracle_prefill
 
@@ -92,7 +93,8 @@ def check_fp8attn_rows(out, ref, case, chunks, window, label):
     d = np.abs(got - ref)
     scale = max(1.0, float(np.abs(ref).max()))
     say(f"[{label}] max_abs={d.max():.3e} mean_abs={d.mean():.3e} (output scale {scale:.2f})")
-    assert d.mean() <= GATE_MEAN_ABS * scale, label
+    if d.shape[0] * d.shape[1] >= FLIP_DILUTION_PAIRS:
+        assert d.mean() <= GATE_MEAN_ABS * scale, label
     v = np.abs(synth.bits_to_f32(case.v_new)).astype(np.float64).max(axis=2)   # [T][Hkv]
     G = case.num_q_heads // case.num_kv_heads
     row = 0
