@@ -91,8 +91,9 @@ enum kvq_status {
                                      inconsistent shapes */
   KVQ_ERR_UNSUPPORTED = -2,       /* head_dim not in {64,128,256}, page size
                                      not 16, Hq % Hkv != 0, group > 16 (either
-                                     arithmetic mode), dynamic scales with
-                                     KVQ_ATTN_FP8 or Hkv > 256 */
+                                     arithmetic mode), Hkv > 65535,
+                                     KVQ_ATTN_FP8 over a bf16 cache, dynamic
+                                     scales with KVQ_ATTN_FP8 or Hkv > 256 */
   KVQ_ERR_WORKSPACE_TOO_SMALL = -3,
   KVQ_ERR_HIP = -4                /* a HIP runtime call or launch failed */
 };

@@ -71,6 +71,7 @@ def attend(L, desc, out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, P=8, bt=FAKE, mp=8,
     (dict(head_dim=512), UNSUPPORTED),
     (dict(num_q_heads=30, num_kv_heads=8), UNSUPPORTED),
     (dict(num_q_heads=68, num_kv_heads=4), UNSUPPORTED),   # group 17 > 16
+    (dict(num_q_heads=65536, num_kv_heads=65536), UNSUPPORTED),   # Hkv > 65535
     (dict(num_q_heads=0), INVALID),
     (dict(sliding_window=-1), INVALID),
     (dict(sm_scale=-1.0), INVALID),
