@@ -434,6 +434,36 @@ def test_full_llama8b_mid_contexts_decode_step(L, variant):
         f"mean={d.mean():.3e} (reported, not gated)")
 
 
+@pytest.mark.timeout(900)
+def test_full_llama8b_1m_decode_step():
+    """The 8B layer at 1048576 positions (65536 pages, 2 GiB of fp8 cache)
+    through kvq_decode_step with the default plan: the longest context any
+    test runs. There the plan finds no co-resident run of at most 64 pages
+    and falls back to 64-page runs in 256 partitions per KV head, read into
+    registers; the reduce merges 256 partitions per row. Cache bytes
+    bit-exact against the oracle's write of every position; attention to
+    the gate and the tight bound: the two-level FP32 sums do not drift over
+    a million positions."""
+    L = 1 << 20
+    case = full_case(synth.LLAMA8B, 32, 8, 128, [L])
+    say("1M: oracle write")
+    o = OracleLayer(case)
+    import copy
+    pre = copy.copy(case)
+    pre.k_new, pre.v_new, pre.slots = case.k_new[:-1], case.v_new[:-1], case.slots[:-1]
+    say("1M: gpu write + decode step")
+    g = GpuLayer(pre, scales=(o.ks, o.vs))
+    out = run_decode_step(g, case, case.k_new[-1:], case.v_new[-1:])
+    assert np.array_equal(host(g.k_cache), o.k_cache)
+    assert np.array_equal(host(g.v_cache), o.v_cache)
+    say("1M: oracle attention")
+    ref = o.attend()
+    mx, mean = errors(out, ref)
+    say(f"[8B-1M-decode-step] max_abs={mx:.3e} mean_abs={mean:.3e}")
+    assert mx <= GATE_MAX_ABS and mean <= GATE_MEAN_ABS, (mx, mean)
+    assert mx <= tight_bound(ref), mx
+
+
 def test_full_batched_concurrency8_with_step_write():
     lens = synth.batched_lens()
     case = full_case(synth.BATCHED, 32, 8, 128, lens, shuffle=True, spare_frac=0.1)
