@@ -638,6 +638,40 @@ def test_decode_step_equals_write_then_attend(label, Hq, Hkv, D, lens, fp8, wind
     assert mx <= GATE_MAX_ABS and mean <= GATE_MEAN_ABS and mx <= tight_bound(ref)
 
 
+def test_decode_step_max_batch():
+    """65535 sequences (the most one call takes) of 0 to 40 positions each,
+    one decode step: 131070 (sequence, KV head) work-groups in one launch,
+    batch index up to the grid's limit in the write, the split kernel and
+    the output rows. Cache bytes bit-exact against the oracle, the step equal
+    to the two-call path bit for bit, attention to the gate and the tight
+    bound; empty sequences give zero rows."""
+    B = 65535
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2026, 65535])))
+    lens = [int(x) for x in r.integers(0, 41, size=B)]
+    say(f"max batch: {B} sequences, {sum(lens)} positions")
+    case = synth.decode_case(93, 8, 2, 64, lens, shuffle=True, spare_frac=0.1)
+    pre = split_newest(case)
+    knew, vnew = newest_rows(case)
+    o = OracleLayer(case)
+    ref_gpu = GpuLayer(case)
+    sc = ref_gpu.scales_host()
+    assert np.array_equal(sc[0], o.ks) and np.array_equal(sc[1], o.vs)
+    g = GpuLayer(pre, scales=sc)
+    g.case = case
+    g.q = bf16_dev(case.q)
+    out = run_decode_step(g, case, knew, vnew)
+    assert np.array_equal(host(g.k_cache), o.k_cache)
+    assert np.array_equal(host(g.v_cache), o.v_cache)
+    assert np.array_equal(host(out), host(ref_gpu.attend()))
+    got = host(out)
+    empty = np.asarray(lens) == 0
+    assert np.all(got[empty] == 0.0)
+    ref = o.attend()
+    mx, mean = errors(out, ref)
+    say(f"[max-batch] max_abs={mx:.3e} mean_abs={mean:.3e}")
+    assert mx <= GATE_MAX_ABS and mean <= GATE_MEAN_ABS and mx <= tight_bound(ref)
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_decode_step_every_tile_variant(variant, tune):
     tune("split_shape", variant)

@@ -244,6 +244,25 @@ def test_prefill_llama8b_batch_sampled(lens):
     check(torch.from_numpy(out[rows]), ref, o, case, f"prefill-8B-batch-{lens}")
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_max_batch(split):
+    # 65535 sequences (the most one call takes) of 1 to 24 positions, each
+    # with a chunk of 0 to 4 new rows at its end: the batch index up to the
+    # grid's limit and the round-robin block order over 131070 (sequence,
+    # KV head) units; empty chunks write nothing. Every row against the
+    # oracle.
+    B = 65535
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2026, 65535, 2])))
+    lens = [int(x) for x in r.integers(1, 25, size=B)]
+    chunks = [int(min(L, x)) for L, x in zip(lens, r.integers(0, 5, size=B))]
+    say(f"prefill max batch: {B} sequences, {sum(chunks)} query rows, split={split}")
+    case = synth.prefill_case(94, 8, 2, 64, lens, chunks, shuffle=True, spare_frac=0.1)
+    g = GpuLayer(case)
+    out = gpu_prefill(g, case, split=split)
+    o = OracleLayer(case)
+    check(out, oracle_prefill(o, case), o, case, f"prefill-max-batch-split={split}")
+
+
 @pytest.mark.parametrize("fmt,attn", [("fp8_e4m3", "bf16"), ("bf16", "bf16"),
                                       ("fp8_e4m3", "fp8")])
 def test_prefill_nan_rows(fmt, attn):
