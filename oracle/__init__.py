@@ -252,7 +252,7 @@ def kv_cache_write_dyn(k_cache, v_cache, k, v, slots, dtype, mode, k_pool, v_poo
     v = np.ascontiguousarray(v, dtype=np.uint16)
     slots = np.ascontiguousarray(slots, dtype=np.int64)
     T, H, D = k.shape
-    assert mode in (PER_TOKEN, PER_TOKEN_HEAD) and H <= 64
+    assert mode in (PER_TOKEN, PER_TOKEN_HEAD) and H <= 256
     for a in (k_cache, v_cache):
         assert a.flags.c_contiguous and a.dtype == np.uint8
     for a in (k_pool, v_pool):

@@ -557,7 +557,7 @@ void orc_kv_cache_write_dyn(int H, int D, int dtype, int mode, const uint16_t* k
                             const uint16_t* v, const int64_t* slots, int64_t T,
                             uint8_t* kc, uint8_t* vc, int64_t num_pages, float* ks_pool,
                             float* vs_pool) {
-  float sk[64], sv[64];
+  float sk[256], sv[256];   /* H <= 256, the library's limit for these modes */
   for (int64_t t = 0; t < T; ++t) {
     int64_t slot = slots[t];
     if (slot < 0 || slot / 16 >= num_pages) continue;

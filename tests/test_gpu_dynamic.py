@@ -60,6 +60,8 @@ WRITE_CASES = [
     ("d128-e4m3", 32, 8, 128, [1000, 33, 1], "fp8_e4m3"),
     ("d256-e5m2", 8, 2, 256, [500, 40], "fp8_e5m2"),
     ("d128-e5m2-h1", 4, 1, 128, [200], "fp8_e5m2"),
+    # the most KV heads the dynamic modes take (per-head maxima in LDS)
+    ("d128-h256", 256, 256, 128, [60, 9], "fp8_e4m3"),
 ]
 
 
@@ -210,6 +212,7 @@ def run_decode_step_dynamic(g, case, knew, vnew):
     ("d256-e5m2", 8, 2, 256, [777, 31], "fp8_e5m2", 0),
     ("g8", 64, 8, 128, [2050, 48], "fp8_e4m3", 0),
     ("g16", 64, 4, 128, [1500, 20], "fp8_e4m3", 0),
+    ("h256", 256, 256, 64, [300, 5, 0], "fp8_e4m3", 0),
 ])
 def test_dynamic_decode_step_equals_write_then_attend(label, Hq, Hkv, D, lens, fmt, window, dyn):
     say(f"dynamic decode step {label} {dyn}")
