@@ -24,7 +24,7 @@ from test_gpu_parity import check_attention, newest_rows, run_decode_step, say, 
 
 pytestmark = pytest.mark.gpu
 
-NUM_CASES = 200
+NUM_CASES = 600
 
 
 def draw(i):

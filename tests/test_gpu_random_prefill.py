@@ -28,7 +28,7 @@ from test_gpu_prefill import check, gpu_prefill, oracle_prefill
 
 pytestmark = pytest.mark.gpu
 
-NUM_CASES = 120
+NUM_CASES = 300
 ORACLE_BUDGET = 3e8      # sum over rows of attended positions x Hq x D
 
 
