@@ -113,6 +113,20 @@ def test_fp8attn_full_llama8b_128k():
         f"max={d.max():.3e} mean={d.mean():.3e} (the e4m3 rounding of q and P; reported)")
 
 
+@pytest.mark.timeout(900)
+def test_fp8attn_full_llama8b_1m():
+    # the all-FP8 arithmetic over 1048576 positions (32768 P blocks per
+    # row, 256 partitions per KV head): each fp8 MFMA rounds its own
+    # 32-product sum, every block's product joins the FP32 sum, and the
+    # output stays within the gate of the float64 oracle
+    case = synth.decode_case(synth.LLAMA8B, 32, 8, 128, [1 << 20])
+    say("full 8B 1M fp8 attention: gpu")
+    g = GpuLayer(case, attn="fp8")
+    say("full 8B 1M fp8 attention: oracle")
+    o = OracleLayer(case, attn="fp8")
+    check(g, o, "8B-1M-fp8attn")
+
+
 def test_fp8attn_full_llama70b_128k_drift():
     case = synth.decode_case(synth.LLAMA70B, 64, 8, 128, [131072], values="drift")
     g = GpuLayer(case, attn="fp8")
