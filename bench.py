@@ -17,6 +17,7 @@ Default run (about a minute of GPU time):
     "Single-request benchmark"), the fp8/bf16 slope ratio and the break-even
     context, beside the cost of one dependent launch in a captured graph (the
     floor under the intercept);
+  * the fp8 step at 262144, 524288 and 1048576 positions (long_contexts);
   * roofline of the split kernel from HIP events around its launches;
   * the float64 CPU oracle timed on the host as a reported baseline.
 
@@ -660,6 +661,24 @@ def stop_trace_server(server):
         server.kill()
 
 
+def long_contexts(torch, kv, w, contexts, steps, warmup):
+    """The fp8 decode step past 131072 positions (per-KV-head scales, one
+    sequence, graph-replayed): at least 2 GiB of cache per stack."""
+    rows = []
+    for ctx in contexts:
+        per_layer = ctx * w["Hkv"] * w["D"] * 2
+        NL = layers_for(per_layer, lo=4)
+        st = LayerStack(kv, torch, 1, w["Hq"], w["Hkv"], w["D"], [ctx], NL, "fp8_e4m3", seed=ctx)
+        ms = time_steps_graph(torch, st, steps, warmup)
+        gbs = st.total_kv_bytes() / (ms * 1e-3) / 1e9
+        del st
+        torch.cuda.empty_cache()
+        rows.append(dict(context=ctx, layers=NL, us_per_layer=round(ms * 1e3 / NL, 3),
+                         kv_gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4)))
+        log(f"long context {ctx:8d} layers={NL:2d} {ms * 1e3 / NL:9.2f} us/layer {gbs:7.1f} GB/s")
+    return rows
+
+
 def sweep(torch, kv, w, contexts, steps, warmup):
     rows = []
     for dt in ("fp8_e4m3", "bf16"):
@@ -1296,6 +1315,8 @@ def main():
         result["sweep"] = sweep(torch, kv, w, contexts, args.sweep_steps, 2)
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+        result["long_contexts"] = long_contexts(torch, kv, w, [262144, 524288, 1048576],
+                                                args.sweep_steps, 2)
         result["split_vs_read_kernel_trace"] = kernel_trace_ratios(tracer)
     stop_trace_server(tracer)
     if not args.no_workloads and args.workload == "llama8b":
