@@ -743,7 +743,7 @@ template <int D, int FMT, int NCG, bool DYN, bool ATT8>
 hipError_t launch_prefill_shape(const PrefillParams& p, int64_t total, hipStream_t stream,
                                 hipEvent_t ev_before, hipEvent_t ev_after) {
   const int64_t grid = (total + kNumXcd - 1) / kNumXcd * kNumXcd;
-  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;   // no launch: too many blocks
   if (ev_before && ev_after) {
     hipExtLaunchKernelGGL((paged_prefill_kernel<D, FMT, NCG, DYN, ATT8>), dim3((unsigned)grid),
                           dim3(kPrefillWaves * kWave), 0, stream, ev_before, ev_after, 0, p);

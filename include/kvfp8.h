@@ -370,6 +370,9 @@ int kvq_decode_step_dynamic(const kvq_layer_desc* desc, const void* k_new,
  *                 stream. Too small: KVQ_ERR_WORKSPACE_TOO_SMALL.
  *   other arguments as for kvq_paged_decode_attention (static scales or the
  *   pools of dynamic per-token scales; KVQ_ATTN_FP8 with static scales).
+ * A call that would need more than 2^31 - 1 work-groups (num_seqs x Hkv x
+ * query blocks of max_query_len x key partitions) launches nothing and
+ * returns KVQ_ERR_HIP.
  */
 int kvq_paged_prefill_attention(const kvq_layer_desc* desc, void* out,
                                 int32_t out_dtype, const void* q,

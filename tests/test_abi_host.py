@@ -13,7 +13,7 @@ import fp8_kv_cache_write_amd as kv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvfp8.h")
 
-OK, INVALID, UNSUPPORTED, WS_SMALL = 0, -1, -2, -3
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIP_ERR = 0, -1, -2, -3, -4
 
 
 @pytest.fixture(scope="module")
@@ -248,6 +248,9 @@ def test_prefill_argument_checks(L):
     assert pf(kv.layer_desc(32, 8, 128, "bf16", attn="fp8")) == UNSUPPORTED
     assert pf(kv.layer_desc(32, 8, 128, scale_mode="per_token"), ks=FAKE_ODD) == INVALID
     assert pf(kv.layer_desc(32, 8, 96)) == UNSUPPORTED
+    # more work-groups than one launch takes (65535 sequences x 4096 KV heads
+    # x 22 query blocks): refused on the host before any device call
+    assert pf(kv.layer_desc(4096, 4096, 64), B=65535, mq=4096) == HIP_ERR
 
 
 def test_prefill_workspace_plan(tune):
